@@ -1,0 +1,359 @@
+"""Pins for the CPU oracle: what the pages and mathematics fix, not the oracle itself.
+
+Every expected value below is printed on the pages (fixtures under
+tests/golden/, each with its citation), a closed form, an invariant, a
+textbook/library routine, or a brute force on tiny inputs.  Runs without a GPU.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import nf4, qlora
+from tests.conftest import golden_kv, read_golden
+from workloads import bf16_bits_as_f32, make_layer, random_weights
+
+
+def printed_levels():
+    return np.array([float(v) for v in read_golden("nf4_levels_printed.txt")])
+
+
+# ----------------------------------------------------------------------------
+# codebook -- chkda "NF4: Choose the codebook to fit the distribution"
+# ----------------------------------------------------------------------------
+def test_codebook_reproduces_printed_levels():
+    c = nf4.nf4_codebook().astype(np.float64)
+    printed = printed_levels()
+    assert printed.size == 16
+    # every level rounds to the printed 4-decimal value
+    assert np.all(np.abs(c - printed) < 5e-5), np.abs(c - printed).max()
+
+
+def test_codebook_structure():
+    c = nf4.nf4_codebook()
+    assert c.dtype == np.float32 and c.size == 16
+    assert c.view(np.uint32)[7] == 0                 # exact +0.0
+    assert c[0] == np.float32(-1.0) and c[15] == np.float32(1.0)
+    assert np.all(np.diff(c) > 0)                    # strictly increasing
+    assert (c < 0).sum() == 7 and (c > 0).sum() == 8
+
+
+def test_codebook_level9_worked_example_five_decimals():
+    kv = golden_kv("worked_examples.txt")
+    c9 = float(nf4.nf4_codebook()[int(kv["nf4.code"][0])])
+    assert abs(c9 - float(kv["nf4.level_5dp"][0])) < 5e-6
+
+
+@pytest.mark.parametrize("p_max", [0.9677, 0.96770833, 0.9677000, 0.9678])
+def test_codebook_reading_window_excludes_nearby_constants(p_max):
+    """The printed table pins p_max to a narrow window (reading R1): nearby
+    round constants fail at least one printed level or the 5-decimal C[9]."""
+    c = nf4.nf4_codebook_f64(p_max)
+    printed = printed_levels()
+    ok4 = all(round(a, 4) == b for a, b in zip(c, printed))
+    ok5 = round(c[9], 5) == 0.16093
+    assert not (ok4 and ok5)
+
+
+def test_midpoints_are_exact():
+    c = nf4.nf4_codebook()
+    m = nf4.nf4_midpoints()
+    for j in range(15):
+        from fractions import Fraction
+        assert Fraction(m[j]) == (Fraction(float(c[j])) + Fraction(float(c[j + 1]))) / 2
+
+
+# ----------------------------------------------------------------------------
+# nearest-level quantizer -- chkda "Quantizing and dequantizing with the codebook"
+# ----------------------------------------------------------------------------
+def _codes_with_unit_scale(x: np.ndarray) -> np.ndarray:
+    """Quantize values of [-1, 1] in blocks whose absmax is exactly 1."""
+    x = np.asarray(x, dtype=np.float32)
+    n = x.size
+    nblk = -(-n // 63)
+    blocks = np.zeros((nblk, 64), dtype=np.float32)
+    blocks[:, 0] = 1.0
+    flat = blocks[:, 1:].reshape(-1)
+    flat[:n] = x
+    blocks[:, 1:] = flat.reshape(nblk, 63)
+    codes, scale = nf4.quantize_blocks(blocks)
+    assert np.all(scale == 1.0)
+    return codes.reshape(nblk, 64)[:, 1:].reshape(-1)[:n]
+
+
+def test_quantizer_matches_exact_bruteforce_random():
+    rng = np.random.default_rng(1)
+    x = rng.uniform(-1, 1, 3000).astype(np.float32)
+    got = _codes_with_unit_scale(x)
+    want = np.array([nf4.nearest_level_bruteforce(v) for v in x])
+    assert np.array_equal(got, want)
+
+
+def test_quantizer_adversarial_points():
+    """Exact midpoints (ties -> smaller index), their fp32 neighbours, +-0,
+    tiny and subnormal values, the levels themselves and +-1."""
+    c = nf4.nf4_codebook()
+    m = nf4.nf4_midpoints()
+    pts = [0.0, -0.0, 1.0, -1.0, 1e-45, -1e-45, 1e-38, -1e-38]
+    pts += list(c)
+    for mj in m:
+        f = np.float32(mj)
+        pts += [f, np.nextafter(f, np.float32(2)), np.nextafter(f, np.float32(-2))]
+    x = np.array(pts, dtype=np.float32)
+    got = _codes_with_unit_scale(x)
+    want = np.array([nf4.nearest_level_bruteforce(v) for v in x])
+    assert np.array_equal(got, want)
+
+
+def test_ties_go_to_smaller_index():
+    c = nf4.nf4_codebook()
+    m = nf4.nf4_midpoints()
+    ties = [j for j in range(15) if float(np.float32(m[j])) == m[j]]
+    assert len(ties) >= 1
+    got = _codes_with_unit_scale(np.array([m[j] for j in ties], dtype=np.float32))
+    assert list(got) == ties
+
+
+def test_all_zero_block_gets_exact_zero_code():
+    codes, scale = nf4.quantize_blocks(np.zeros(128, np.float32))
+    assert np.all(scale == 0) and np.all(codes == 7)
+    assert nf4.nf4_codebook()[7] == 0
+
+
+def test_worked_example_nf4():
+    kv = golden_kv("worked_examples.txt")
+    s = np.float32(float(kv["nf4.scale"][0]))
+    w = np.float32(float(kv["nf4.weight"][0]))
+    block = np.zeros(64, np.float32)
+    block[0], block[1] = s, w
+    codes, scale = nf4.quantize_blocks(block)
+    assert scale[0] == s
+    assert codes[1] == int(kv["nf4.code"][0]) == int(kv["nf4.code_binary"][0], 2)
+    assert codes[0] == 15 and np.all(codes[2:] == 7)
+    assert abs(float(w / s) - float(kv["nf4.normalised"][0])) < 1e-7
+    rec = nf4.dequantize_blocks(codes, scale)[1]
+    # the page multiplies the 5-decimal level by the scale, so the printed
+    # 0.32186 carries the level's rounding error (<= 5e-6) times the scale
+    assert abs(float(rec) - float(kv["nf4.reconstructed_5dp"][0])) <= float(s) * 5e-6
+    # nibble order (reading R4): code 15 low, code 9 high -> 0x9F; zeros -> 0x77
+    packed = nf4.pack_codes(codes)
+    assert packed[0] == 0x9F and np.all(packed[1:] == 0x77) and packed.size == 32
+    assert np.array_equal(nf4.unpack_codes(packed, 64), codes)
+
+
+def test_round_trip_bound_half_gap():
+    w = random_weights(3, (64, 64 * 40), std=1.0)
+    codes, scale = nf4.quantize_blocks(w)
+    c = nf4.nf4_codebook().astype(np.float64)
+    gaps = np.diff(c)
+    blk = np.arange(w.size) // 64
+    x = (w.reshape(-1) / scale[blk]).astype(np.float32).astype(np.float64)
+    err = np.abs(x - c[codes])
+    # the error is at most half of the gap of the interval x falls in
+    idx = np.clip(np.searchsorted(c, x) - 1, 0, 14)
+    assert np.all(err <= gaps[idx] / 2 + 1e-12)
+    assert err.max() <= (c[1] - c[0]) / 2 + 1e-12 and (c[1] - c[0]) / 2 < 0.1520
+
+
+def test_ragged_tail_block():
+    w = random_weights(4, (1, 64 * 3 + 10))
+    codes, scale = nf4.quantize_blocks(w)
+    assert codes.size == w.size and scale.size == 4
+    assert scale[3] == np.abs(w.reshape(-1)[192:]).max()
+
+
+# ----------------------------------------------------------------------------
+# Int8 absmax -- chkda "First, how does k-bit quantization work?"
+# ----------------------------------------------------------------------------
+def test_worked_example_int8():
+    kv = golden_kv("worked_examples.txt")
+    x = np.array([float(v) for v in kv["int8.x"]], np.float32)
+    q, c = nf4.int8_absmax_quantize(x)
+    assert c == np.float32(float(kv["int8.c"][0]))
+    assert list(q) == [int(v) for v in kv["int8.q"]]
+    xhat = nf4.int8_dequantize(q, c)
+    assert [round(float(v), 4) for v in xhat] == [float(v) for v in kv["int8.xhat_4dp"]]
+    assert xhat[1] == np.float32(38) / np.float32(127)
+
+
+def test_int8_range_and_zero_input():
+    rng = np.random.default_rng(2)
+    for _ in range(50):
+        x = rng.standard_normal(256).astype(np.float32)
+        q, c = nf4.int8_absmax_quantize(x)
+        assert q.min() >= -127 and q.max() <= 127
+        assert np.abs(q).max() == 127
+    q, c = nf4.int8_absmax_quantize(np.zeros(16, np.float32))
+    assert np.all(q == 0) and c != 0
+
+
+# ----------------------------------------------------------------------------
+# double quantization -- chkda "Double quantization and double dequantization"
+# ----------------------------------------------------------------------------
+def test_bits_per_weight():
+    kv = golden_kv("worked_examples.txt")
+    for n in (4096 * 4096, 11008 * 4096, 22016 * 8192, 256 * 512):
+        b = nf4.storage_bits_per_weight(n)
+        assert b["scales_before"] == float(kv["dq.before"][0])
+        assert b["scales_after"] == float(kv["dq.after"][0])
+        assert b["scales_before"] - b["scales_after"] == float(kv["dq.saved"][0])
+        assert round(b["codes"] + b["scales_after"], 3) == 4.127
+
+
+def test_tree_sum_pairs_stride_halving():
+    # stride-halving pairs (0,2),(1,3) then (0,1): (1e16 - 1e16) + (1 + 1) = 2;
+    # a sequential sum gives 1 and an adjacent-pair tree gives 0 in float64.
+    v = np.array([1e16, 1.0, -1e16, 1.0])
+    assert nf4.tree_sum_f64(v) == 2.0
+    assert ((v[0] + v[1]) + v[2]) + v[3] == 1.0
+    assert (v[0] + v[1]) + (v[2] + v[3]) == 0.0
+
+
+def test_tree_sum_exact_and_padded():
+    v = np.arange(1, 1001, dtype=np.float64)
+    assert nf4.tree_sum_f64(v) == 500500.0
+    assert nf4.tree_sum_f64(np.array([3.5])) == 3.5
+
+
+def test_mean_close_to_exact_sum():
+    s = np.abs(random_weights(5, (1000 * 64,))).reshape(-1, 64).max(axis=1)
+    mean = nf4.scales_mean(s)
+    exact = math.fsum(float(v) for v in s) / s.size
+    assert abs(float(mean) - exact) <= np.spacing(np.float32(exact))
+
+
+def test_double_quant_worked_int8_example():
+    """Scales whose mean is 0 reduce double quantization to the printed Int8
+    example on (s - mean) = [-1, 0.3, 1, -0.3]."""
+    s = np.array([-1.0, 0.3, 1.0, -0.3], np.float32)
+    c2, c1, mean = nf4.double_quantize(s)
+    assert mean == 0 and c1[0] == 127
+    assert list(c2) == [-127, 38, 127, -38]
+    shat = nf4.double_dequantize_scales(c2, c1, mean)
+    assert [round(float(v), 4) for v in shat] == [-1.0, 0.2992, 1.0, -0.2992]
+
+
+def test_double_quant_round_trip_bound_and_ragged_groups():
+    w = random_weights(6, (37, 64 * 300))          # nb = 11100: ragged last group
+    codes, s = nf4.quantize_blocks(w)
+    c2, c1, mean = nf4.double_quantize(s)
+    assert c1.size == -(-s.size // 256)
+    shat = nf4.double_dequantize_scales(c2, c1, mean)
+    centred = (s - mean).astype(np.float32)
+    for g in range(c1.size):
+        sl = slice(g * 256, (g + 1) * 256)
+        a_g = np.abs(centred[sl]).max()
+        err = np.abs(shat[sl].astype(np.float64) - s[sl])
+        assert np.all(err <= a_g / 254 * (1 + 1e-6) + 4 * np.spacing(s[sl]))
+    assert np.all(np.abs(c2.astype(int)) <= 127)
+
+
+def test_zero_group_and_zero_tensor():
+    c2, c1, mean = nf4.double_quantize(np.zeros(300, np.float32))
+    assert mean == 0 and np.all(c2 == 0) and np.all(c1 == 127)
+    q = nf4.quantize(np.zeros((4, 64), np.float32))
+    bits = nf4.dequantize(q)
+    assert np.all((bits & 0x7FFF) == 0)           # +-0 exactly
+
+
+def test_bf16_rne_matches_torch_conversion():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal(20000).astype(np.float32) * np.float32(3)
+    # exact ties: low 16 bits 0x8000, both parities of the kept bit
+    hi = rng.integers(0x3000, 0x4F00, 4000, dtype=np.uint32) | (rng.integers(0, 2, 4000, dtype=np.uint32) << 15)
+    ties = ((hi << np.uint32(16)) | np.uint32(0x8000)).view(np.float32)   # both parities of the kept bit
+    x = np.concatenate([x, ties, np.array([0.0, -0.0, 1e-40, -3e-39], np.float32)])
+    assert np.all(np.isfinite(x))
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(nf4.bf16_rne_bits(x), want)
+
+
+def test_double_dequant_error_bound():
+    w = random_weights(8, (64, 64 * 64))
+    q = nf4.quantize(w)
+    what = nf4.bf16_bits_to_f32(nf4.dequantize(q)).astype(np.float64)
+    shat = nf4.double_dequantize_scales(q["c2"], q["c1"], q["mean"]).astype(np.float64)
+    blk = np.arange(w.size) // 64
+    c = nf4.nf4_codebook().astype(np.float64)[q["codes"]]
+    s = q["absmax"].astype(np.float64)[blk]
+    bound = 0.1520 * s + np.abs(s - shat[blk]) + 2.0 ** -8 * np.abs(c * shat[blk]) + 1e-12
+    assert np.all(np.abs(w.reshape(-1) - what) <= bound)
+
+
+# ----------------------------------------------------------------------------
+# the linear layer -- chkda "How does it work?", "Merging LoRA weights ...";
+# fromzero2ai "Why Does This Save Memory?"
+# ----------------------------------------------------------------------------
+def test_parameter_count():
+    kv = golden_kv("worked_examples.txt")
+    d, k, r = (int(kv[f"params.{n}"][0]) for n in "dkr")
+    n = qlora.trainable_parameters(d, k, r)
+    assert n == int(kv["params.count"][0])
+    assert d * k == int(kv["params.full"][0]) and d * k // n == int(kv["params.ratio"][0])
+    a = np.zeros((r, k)); b = np.zeros((d, r))
+    assert a.size + b.size == n
+
+
+def _tiny_layer(seed=0, m=5, d=6, k=7, r=3):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((d, k)), rng.standard_normal((m, k)), rng.standard_normal((r, k)),
+            rng.standard_normal((d, r)), rng.standard_normal((m, d)))
+
+
+def test_b_zero_and_alpha_zero_leave_base_output():
+    w, x, a, b, _ = _tiny_layer()
+    base = x @ w.T
+    y0, _ = qlora.forward(w, x, a, np.zeros_like(b), 16.0)
+    y1, _ = qlora.forward(w, x, a, b, 0.0)
+    assert np.array_equal(y0, base) and np.array_equal(y1, base)
+    _, da, _ = qlora.backward(w, x, np.ones((x.shape[0], w.shape[0])), a, np.zeros_like(b), 16.0)
+    assert np.all(da == 0)
+
+
+def test_merge_equivalence():
+    w, x, a, b, _ = _tiny_layer(1, m=9, d=16, k=12, r=4)
+    y, _ = qlora.forward(w, x, a, b, 8.0)
+    ym = x @ qlora.merged_weight(w, a, b, 8.0).T
+    assert np.allclose(y, ym, rtol=1e-12, atol=1e-12)
+
+
+def test_forward_reduces_to_matmul_of_merged_weight_rank_one():
+    # r = 1, alpha = 1: Y = X (W + b a)^T, computed as an explicit sum of outer products
+    w, x, a, b, _ = _tiny_layer(2, m=3, d=4, k=5, r=1)
+    y, u = qlora.forward(w, x, a, b, 1.0)
+    for i in range(3):
+        for o in range(4):
+            want = sum(x[i, j] * (w[o, j] + b[o, 0] * a[0, j]) for j in range(5))
+            assert abs(y[i, o] - want) < 1e-12
+    assert np.allclose(u[:, 0], [sum(x[i, j] * a[0, j] for j in range(5)) for i in range(3)])
+
+
+def test_backward_central_finite_differences():
+    w, x, a, b, dy = _tiny_layer(3)
+    alpha = 6.0
+    dx, da, db = qlora.backward(w, x, dy, a, b, alpha)
+
+    def loss(xx, aa, bb):
+        y, _ = qlora.forward(w, xx, aa, bb, alpha)
+        return float(np.sum(dy * y))
+
+    h = 1e-6
+    for arr, grad, which in ((x, dx, 0), (a, da, 1), (b, db, 2)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            p = arr.copy(); p[idx] += h
+            mm = arr.copy(); mm[idx] -= h
+            args_p = [x, a, b]; args_m = [x, a, b]
+            args_p[which] = p; args_m[which] = mm
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        assert np.allclose(num, grad, rtol=1e-6, atol=1e-7), which
+
+
+def test_workload_inputs_are_bf16_and_seeded():
+    l1 = make_layer(0, 0, 8, 64, 4, 2)
+    l2 = make_layer(0, 0, 8, 64, 4, 2)
+    assert np.array_equal(l1.w0, l2.w0) and np.array_equal(l1.x, l2.x)
+    assert l1.x.dtype == np.uint16 and l1.w0.dtype == np.float32
+    xf = bf16_bits_as_f32(l1.x)
+    assert np.all(np.isfinite(xf))
