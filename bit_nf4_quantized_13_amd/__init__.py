@@ -1,0 +1,250 @@
+"""Python binding of libqlora_nf4.so -- the MI355X QLoRA NF4 linear layer.
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  torch supplies device memory (outputs and workspaces are allocated
+as torch tensors) and the current HIP stream.  There is no fallback: if the
+library is not built, importing the binding raises.
+
+Functions carry the C ABI's names (include/qlora_nf4.h):
+
+    qlora_nf4_quantize(W0)                    -> NF4Weight
+    qlora_nf4_dequantize(w)                   -> bf16 [d, k]
+    qlora_linear_fwd(w, x, A, B, alpha)       -> (Y, U)
+    qlora_linear_bwd(w, x, dY, A, B, alpha, U=None, need_dx=True) -> (dX, dA, dB)
+    qlora_nf4_codebook(), qlora_nf4_thresholds()   (host only, no GPU needed)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+from .build import LIB_PATH
+
+QLORA_OK, QLORA_EINVAL, QLORA_ENOTSUP, QLORA_EALIGN, QLORA_EWORKSPACE, QLORA_EHIP = range(6)
+BLOCK = 64
+DQ_BLOCK = 256
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m bit_nf4_quantized_13_amd.build` "
+        "(there is no CPU fallback)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class _CWeight(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("absmax_q", ctypes.c_void_p),
+                ("absmax_scale", ctypes.c_void_p), ("absmax_mean", ctypes.c_void_p),
+                ("d", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("block", ctypes.c_int32), ("dq_block", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+_WP = ctypes.POINTER(_CWeight)
+
+_SIGS = {
+    "qlora_abi_version": (ctypes.c_int, []),
+    "qlora_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "qlora_nf4_codebook": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float)]),
+    "qlora_nf4_thresholds": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float)]),
+    "qlora_nf4_quantize_workspace": (_SZ, [_I64, _I64, _I32, _I32]),
+    "qlora_nf4_quantize": (ctypes.c_int, [_P, _WP, _P, _SZ, _P]),
+    "qlora_nf4_dequantize": (ctypes.c_int, [_WP, _P, _P]),
+    "qlora_linear_workspace": (_SZ, [_I64, _I64, _I64, _I32]),
+    "qlora_linear_fwd": (ctypes.c_int, [_WP, _P, _I64, _P, _P, _I32, ctypes.c_float, _P, _P, _P,
+                                        _SZ, _P]),
+    "qlora_linear_bwd": (ctypes.c_int, [_WP, _P, _P, _P, _P, _P, _I64, _I32, ctypes.c_float, _P,
+                                        _P, _P, _P, _SZ, _P]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class QloraError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        super().__init__(f"{call}: {status_str(status)}")
+        self.status = status
+
+
+def status_str(status: int) -> str:
+    return _lib.qlora_status_str(int(status)).decode()
+
+
+def _check(status: int, call: str) -> None:
+    if status != QLORA_OK:
+        raise QloraError(status, call)
+
+
+def library() -> ctypes.CDLL:
+    """The loaded ctypes handle (for tests that call the C ABI directly)."""
+    return _lib
+
+
+def abi_version() -> int:
+    return int(_lib.qlora_abi_version())
+
+
+def qlora_nf4_codebook() -> list[float]:
+    out = (ctypes.c_float * 16)()
+    _check(_lib.qlora_nf4_codebook(out), "qlora_nf4_codebook")
+    return list(out)
+
+
+def qlora_nf4_thresholds() -> list[float]:
+    out = (ctypes.c_float * 15)()
+    _check(_lib.qlora_nf4_thresholds(out), "qlora_nf4_thresholds")
+    return list(out)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev_tensor(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+@dataclass
+class NF4Weight:
+    """Device buffers of one quantized W0 [d x k] (see qlora_nf4_weight)."""
+    codes: torch.Tensor          # uint8 [d*k/2]
+    absmax_q: torch.Tensor       # int8 [nb]
+    absmax_scale: torch.Tensor   # float32 [G]
+    absmax_mean: torch.Tensor    # float32 [1]
+    d: int
+    k: int
+    block: int = BLOCK
+    dq_block: int = DQ_BLOCK
+
+    @staticmethod
+    def empty(d: int, k: int, device="cuda") -> "NF4Weight":
+        nb = (d * k) // BLOCK
+        g = -(-nb // DQ_BLOCK)
+        return NF4Weight(torch.empty(d * k // 2, dtype=torch.uint8, device=device),
+                         torch.empty(nb, dtype=torch.int8, device=device),
+                         torch.empty(g, dtype=torch.float32, device=device),
+                         torch.empty(1, dtype=torch.float32, device=device), d, k)
+
+    def c_struct(self) -> _CWeight:
+        return _CWeight(self.codes.data_ptr(), self.absmax_q.data_ptr(),
+                        self.absmax_scale.data_ptr(), self.absmax_mean.data_ptr(),
+                        self.d, self.k, self.block, self.dq_block)
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size()
+                   for t in (self.codes, self.absmax_q, self.absmax_scale, self.absmax_mean))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def quantize_workspace_bytes(d: int, k: int) -> int:
+    return int(_lib.qlora_nf4_quantize_workspace(d, k, BLOCK, DQ_BLOCK))
+
+
+def linear_workspace_bytes(m: int, d: int, k: int, r: int) -> int:
+    return int(_lib.qlora_linear_workspace(m, d, k, r))
+
+
+def qlora_nf4_quantize(w0: torch.Tensor, out: NF4Weight | None = None,
+                       workspace: torch.Tensor | None = None) -> NF4Weight:
+    """NF4 + double quantization of fp32 W0 [d, k] on the current stream."""
+    _dev_tensor(w0, torch.float32, "W0")
+    d, k = w0.shape
+    w = out if out is not None else NF4Weight.empty(d, k, w0.device)
+    ws_bytes = quantize_workspace_bytes(d, k)
+    ws = workspace if workspace is not None else _workspace(ws_bytes, w0.device)
+    cw = w.c_struct()
+    _check(_lib.qlora_nf4_quantize(w0.data_ptr(), ctypes.byref(cw), ws.data_ptr(),
+                                   ws.numel(), _stream()), "qlora_nf4_quantize")
+    return w
+
+
+def qlora_nf4_dequantize(w: NF4Weight, out: torch.Tensor | None = None) -> torch.Tensor:
+    """doubleDequant of W0 into bf16 [d, k]."""
+    y = out if out is not None else torch.empty((w.d, w.k), dtype=torch.bfloat16,
+                                                device=w.codes.device)
+    cw = w.c_struct()
+    _check(_lib.qlora_nf4_dequantize(ctypes.byref(cw), y.data_ptr(), _stream()),
+           "qlora_nf4_dequantize")
+    return y
+
+
+def qlora_linear_fwd(w: NF4Weight, x: torch.Tensor, a: torch.Tensor, b: torch.Tensor,
+                     alpha: float, save_u: bool = True, out: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None):
+    """Y = x What^T + (alpha/r) (x A^T) B^T.  Returns (Y bf16 [M, d], U fp32 [M, r] or None)."""
+    _dev_tensor(x, torch.bfloat16, "x")
+    _dev_tensor(a, torch.bfloat16, "A")
+    _dev_tensor(b, torch.bfloat16, "B")
+    m, r = x.shape[0], a.shape[0]
+    y = out if out is not None else torch.empty((m, w.d), dtype=torch.bfloat16, device=x.device)
+    u = torch.empty((m, r), dtype=torch.float32, device=x.device) if save_u else None
+    ws = workspace if workspace is not None else _workspace(
+        linear_workspace_bytes(m, w.d, w.k, r), x.device)
+    cw = w.c_struct()
+    _check(_lib.qlora_linear_fwd(ctypes.byref(cw), x.data_ptr(), m, a.data_ptr(), b.data_ptr(), r,
+                                 float(alpha), y.data_ptr(), _ptr(u), ws.data_ptr(), ws.numel(),
+                                 _stream()), "qlora_linear_fwd")
+    return y, u
+
+
+def qlora_linear_bwd(w: NF4Weight, x: torch.Tensor, dy: torch.Tensor, a: torch.Tensor,
+                     b: torch.Tensor, alpha: float, u: torch.Tensor | None = None,
+                     need_dx: bool = True, workspace: torch.Tensor | None = None,
+                     outs: tuple | None = None):
+    """Returns (dX bf16 [M, k] or None, dA fp32 [r, k], dB fp32 [d, r])."""
+    _dev_tensor(x, torch.bfloat16, "x")
+    _dev_tensor(dy, torch.bfloat16, "dY")
+    _dev_tensor(a, torch.bfloat16, "A")
+    _dev_tensor(b, torch.bfloat16, "B")
+    if u is not None:
+        _dev_tensor(u, torch.float32, "U")
+    m, r = x.shape[0], a.shape[0]
+    if outs is not None:
+        dx, da, db = outs
+    else:
+        dx = torch.empty((m, w.k), dtype=torch.bfloat16, device=x.device) if need_dx else None
+        da = torch.empty((r, w.k), dtype=torch.float32, device=x.device)
+        db = torch.empty((w.d, r), dtype=torch.float32, device=x.device)
+    ws = workspace if workspace is not None else _workspace(
+        linear_workspace_bytes(m, w.d, w.k, r), x.device)
+    cw = w.c_struct()
+    _check(_lib.qlora_linear_bwd(ctypes.byref(cw), x.data_ptr(), dy.data_ptr(), a.data_ptr(),
+                                 b.data_ptr(), _ptr(u), m, r, float(alpha), _ptr(dx), da.data_ptr(),
+                                 db.data_ptr(), ws.data_ptr(), ws.numel(), _stream()),
+           "qlora_linear_bwd")
+    return dx, da, db
+
+
+def adapter_scale(alpha: float, r: int) -> float:
+    """alpha / r as the library computes it (fp32)."""
+    import numpy as np
+    return float(np.float32(alpha) / np.float32(r))
+
+
+__all__ = [
+    "NF4Weight", "QloraError", "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd",
+    "qlora_linear_bwd", "qlora_nf4_codebook", "qlora_nf4_thresholds", "status_str", "library",
+    "abi_version", "quantize_workspace_bytes", "linear_workspace_bytes", "adapter_scale",
+    "BLOCK", "DQ_BLOCK",
+]

@@ -1,0 +1,223 @@
+// The C ABI (include/qlora_nf4.h): argument validation, workspace layout and
+// the launch sequence of each call.  No allocation, no synchronisation, no
+// global mutable state; every check runs before the first launch.
+#include "qlora_nf4.h"
+
+#include <cmath>
+#include <cstring>
+
+#include "launch.hpp"
+
+using namespace qnf4;
+
+namespace {
+
+constexpr int64_t kMaxWeights = int64_t(1) << 30;  // 2^24 NF4 blocks: 65536 DQ groups
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Shape and format checks shared by every call that takes a weight.
+int check_weight(const qlora_nf4_weight *w, bool need_data) {
+    if (!w) return QLORA_EINVAL;
+    if (w->d <= 0 || w->k <= 0) return QLORA_EINVAL;
+    if (w->block != QLORA_NF4_BLOCK || w->dq_block != QLORA_NF4_DQ_BLOCK) return QLORA_ENOTSUP;
+    if (w->k % QLORA_NF4_BLOCK != 0) return QLORA_EINVAL;
+    if (w->d > kMaxWeights / w->k) return QLORA_ENOTSUP;
+    if (need_data) {
+        if (!w->codes || !w->absmax_q || !w->absmax_scale || !w->absmax_mean) return QLORA_EINVAL;
+        if (!aligned(w->codes, 16) || !aligned(w->absmax_scale, 4) || !aligned(w->absmax_mean, 4))
+            return QLORA_EALIGN;
+    }
+    return QLORA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_EHIP; }
+
+// ---- workspace layouts ------------------------------------------------------
+struct QuantWs {
+    size_t absmax, group_sum, total;
+};
+QuantWs quant_ws(int64_t d, int64_t k) {
+    const int64_t nb = d * k / QLORA_NF4_BLOCK;
+    const int64_t g = (nb + QLORA_NF4_DQ_BLOCK - 1) / QLORA_NF4_DQ_BLOCK;
+    QuantWs q;
+    q.absmax = 0;
+    q.group_sum = round_up(sizeof(float) * nb, 256);
+    q.total = q.group_sum + round_up(sizeof(double) * g, 256);
+    return q;
+}
+
+struct LinWs {
+    size_t shat, u, bt, g, part, total;
+};
+LinWs lin_ws(int64_t M, int64_t d, int64_t k, int r) {
+    LinWs l;
+    size_t off = 0;
+    l.shat = off;
+    off += round_up(sizeof(float) * (d * k / QLORA_NF4_BLOCK), 256);
+    l.u = off;
+    off += round_up(sizeof(float) * M * r, 256);
+    l.bt = off;
+    off += round_up(sizeof(uint16_t) * d * r, 256);
+    l.g = off;
+    off += round_up(sizeof(float) * M * r, 256);
+    l.part = off;
+    const size_t pd = sizeof(float) * cols_skinny_splits(M, d) * d * 2 * r;
+    const size_t pk = sizeof(float) * cols_skinny_splits(M, k) * k * 2 * r;
+    off += round_up(pd > pk ? pd : pk, 256);
+    l.total = off;
+    return l;
+}
+
+int check_linear(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M, const qlora_bf16 *A,
+                 const qlora_bf16 *B, int32_t r, float alpha) {
+    int st = check_weight(w, true);
+    if (st != QLORA_OK) return st;
+    if (!x || !A || !B) return QLORA_EINVAL;
+    if (M <= 0 || r <= 0) return QLORA_EINVAL;
+    if (!std::isfinite(alpha)) return QLORA_EINVAL;
+    if (r > QLORA_MAX_RANK) return QLORA_ENOTSUP;
+    if (w->d % 8 != 0) return QLORA_ENOTSUP;  // bf16 rows of [M x d] must be 16-byte aligned
+    if (!aligned(x, 16) || !aligned(A, 16) || !aligned(B, 2)) return QLORA_EALIGN;
+    return QLORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qlora_abi_version(void) { return QLORA_ABI_VERSION; }
+
+const char *qlora_status_str(int status) {
+    switch (status) {
+        case QLORA_OK: return "QLORA_OK: success";
+        case QLORA_EINVAL: return "QLORA_EINVAL: invalid argument (null pointer, size <= 0, k % block != 0, non-finite alpha)";
+        case QLORA_ENOTSUP: return "QLORA_ENOTSUP: unsupported configuration (block != 64, dq_block != 256, r > 128, d % 8 != 0, tensor too large)";
+        case QLORA_EALIGN: return "QLORA_EALIGN: misaligned pointer (16-byte alignment required)";
+        case QLORA_EWORKSPACE: return "QLORA_EWORKSPACE: workspace missing or too small";
+        case QLORA_EHIP: return "QLORA_EHIP: HIP launch or runtime error";
+        default: return "unknown qlora status";
+    }
+}
+
+int qlora_nf4_codebook(float out[16]) {
+    if (!out) return QLORA_EINVAL;
+    std::memcpy(out, nf4_consts().level, sizeof(float) * 16);
+    return QLORA_OK;
+}
+
+int qlora_nf4_thresholds(float out[15]) {
+    if (!out) return QLORA_EINVAL;
+    std::memcpy(out, nf4_consts().thresh, sizeof(float) * 15);
+    return QLORA_OK;
+}
+
+size_t qlora_nf4_quantize_workspace(int64_t d, int64_t k, int32_t block, int32_t dq_block) {
+    qlora_nf4_weight w{};
+    w.d = d;
+    w.k = k;
+    w.block = block;
+    w.dq_block = dq_block;
+    if (check_weight(&w, false) != QLORA_OK) return 0;
+    return quant_ws(d, k).total;
+}
+
+int qlora_nf4_quantize(const float *W0, const qlora_nf4_weight *w, void *ws, size_t ws_bytes,
+                       void *stream) {
+    int st = check_weight(w, true);
+    if (st != QLORA_OK) return st;
+    if (!W0) return QLORA_EINVAL;
+    if (!aligned(W0, 16)) return QLORA_EALIGN;
+    const QuantWs q = quant_ws(w->d, w->k);
+    if (!ws || ws_bytes < q.total) return QLORA_EWORKSPACE;
+    if (!aligned(ws, 16)) return QLORA_EALIGN;
+    (void)hipGetLastError();
+    char *base = static_cast<char *>(ws);
+    return hip_status(launch_quantize(W0, w->d * w->k, w->codes, w->absmax_q, w->absmax_scale,
+                                      w->absmax_mean, reinterpret_cast<float *>(base + q.absmax),
+                                      reinterpret_cast<double *>(base + q.group_sum),
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int qlora_nf4_dequantize(const qlora_nf4_weight *w, qlora_bf16 *W_out, void *stream) {
+    int st = check_weight(w, true);
+    if (st != QLORA_OK) return st;
+    if (!W_out) return QLORA_EINVAL;
+    if (!aligned(W_out, 16)) return QLORA_EALIGN;
+    (void)hipGetLastError();
+    return hip_status(launch_dequantize(w->codes, w->absmax_q, w->absmax_scale, w->absmax_mean,
+                                        w->d * w->k, W_out, static_cast<hipStream_t>(stream)));
+}
+
+size_t qlora_linear_workspace(int64_t M, int64_t d, int64_t k, int32_t r) {
+    if (M <= 0 || d <= 0 || k <= 0 || r <= 0 || r > QLORA_MAX_RANK) return 0;
+    if (k % QLORA_NF4_BLOCK != 0 || d > kMaxWeights / k) return 0;
+    return lin_ws(M, d, k, r).total;
+}
+
+int qlora_linear_fwd(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M,
+                     const qlora_bf16 *A, const qlora_bf16 *B, int32_t r, float alpha,
+                     qlora_bf16 *Y, float *U_save, void *ws, size_t ws_bytes, void *stream) {
+    int st = check_linear(w, x, M, A, B, r, alpha);
+    if (st != QLORA_OK) return st;
+    if (!Y) return QLORA_EINVAL;
+    if (!aligned(Y, 16) || (U_save && !aligned(U_save, 4))) return QLORA_EALIGN;
+    const LinWs l = lin_ws(M, w->d, w->k, r);
+    if (!ws || ws_bytes < l.total) return QLORA_EWORKSPACE;
+    if (!aligned(ws, 16)) return QLORA_EALIGN;
+    (void)hipGetLastError();
+    char *base = static_cast<char *>(ws);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const float scale = alpha / static_cast<float>(r);
+    float *U = U_save ? U_save : reinterpret_cast<float *>(base + l.u);
+    const Nf4Weights nw{w->codes, w->absmax_q, w->absmax_scale, w->absmax_mean, w->d, w->k};
+    hipError_t e = launch_rows_skinny(x, A, M, w->k, r, U, s);
+    if (e == hipSuccess)
+        e = launch_gemm_fwd(nw, x, M, U, B, r, scale, Y, reinterpret_cast<float *>(base + l.shat), s);
+    return hip_status(e);
+}
+
+int qlora_linear_bwd(const qlora_nf4_weight *w, const qlora_bf16 *x, const qlora_bf16 *dY,
+                     const qlora_bf16 *A, const qlora_bf16 *B, const float *U, int64_t M,
+                     int32_t r, float alpha, qlora_bf16 *dX, float *dA, float *dB, void *ws,
+                     size_t ws_bytes, void *stream) {
+    int st = check_linear(w, x, M, A, B, r, alpha);
+    if (st != QLORA_OK) return st;
+    if (!dY || !dA || !dB) return QLORA_EINVAL;
+    if (!aligned(dY, 16) || (dX && !aligned(dX, 16)) || !aligned(dA, 4) || !aligned(dB, 4) ||
+        (U && !aligned(U, 4)))
+        return QLORA_EALIGN;
+    const LinWs l = lin_ws(M, w->d, w->k, r);
+    if (!ws || ws_bytes < l.total) return QLORA_EWORKSPACE;
+    if (!aligned(ws, 16)) return QLORA_EALIGN;
+    (void)hipGetLastError();
+    char *base = static_cast<char *>(ws);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const float scale = alpha / static_cast<float>(r);
+    const int64_t d = w->d, k = w->k;
+    float *Uw = reinterpret_cast<float *>(base + l.u);
+    uint16_t *Bt = reinterpret_cast<uint16_t *>(base + l.bt);
+    float *G = reinterpret_cast<float *>(base + l.g);
+    float *part = reinterpret_cast<float *>(base + l.part);
+    const Nf4Weights nw{w->codes, w->absmax_q, w->absmax_scale, w->absmax_mean, d, k};
+
+    hipError_t e = hipSuccess;
+    const float *Uin = U;
+    if (!Uin) {
+        e = launch_rows_skinny(x, A, M, k, r, Uw, s);
+        Uin = Uw;
+    }
+    if (e == hipSuccess) e = launch_transpose_bf16(B, d, r, Bt, s);             // B^T [r x d]
+    if (e == hipSuccess) e = launch_rows_skinny(dY, Bt, M, d, r, G, s);         // G = dY B
+    if (e == hipSuccess)                                                        // dB = s dY^T U
+        e = launch_cols_skinny(dY, Uin, M, d, r, scale, part, cols_skinny_splits(M, d), dB, 0, s);
+    if (e == hipSuccess)                                                        // dA = s G^T X
+        e = launch_cols_skinny(x, G, M, k, r, scale, part, cols_skinny_splits(M, k), dA, 1, s);
+    if (e == hipSuccess && dX)                                                  // dX = dY What + s G A
+        e = launch_gemm_dx(nw, dY, M, G, A, r, scale, dX, reinterpret_cast<float *>(base + l.shat), s);
+    return hip_status(e);
+}
+
+}  // extern "C"

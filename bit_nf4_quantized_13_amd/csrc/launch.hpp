@@ -1,0 +1,53 @@
+// Host-side launchers of the HIP kernels (internal; the public surface is
+// include/qlora_nf4.h).  All launchers enqueue on `stream` and return the
+// hipError_t of the launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "common.hpp"
+
+namespace qnf4 {
+
+const Nf4Consts &nf4_consts();  // built once on the host (nf4_table.cpp)
+
+// ---- quantize (three kernels) --------------------------------------------
+hipError_t launch_quantize(const float *W0, int64_t n, uint8_t *codes, int8_t *c2, float *c1,
+                           float *mean, float *absmax_ws, double *group_sum_ws, hipStream_t s);
+
+// ---- standalone double dequant --------------------------------------------
+hipError_t launch_dequantize(const uint8_t *codes, const int8_t *c2, const float *c1,
+                             const float *mean, int64_t n, uint16_t *out, hipStream_t s);
+
+// ---- skinny GEMMs ----------------------------------------------------------
+// out[M x R] (fp32) = In[M x K] (bf16) * W[R x K]^T (bf16), R <= 128.
+hipError_t launch_rows_skinny(const uint16_t *in, const uint16_t *w, int64_t M, int64_t K, int R,
+                              float *out, hipStream_t s);
+// dst[C x R] = transpose(src[R x C]) for bf16.
+hipError_t launch_transpose_bf16(const uint16_t *src, int64_t R, int64_t C, uint16_t *dst, hipStream_t s);
+// part[S][N][2R] = split-M partial sums of In^T * [hi(V) | lo(V)], In [M x N]
+// bf16, V [M x R] fp32; then out = scale * sum over splits of (hi + lo part),
+// written as out[N x R] (transpose_out = 0) or out[R x N] (transpose_out = 1).
+int cols_skinny_splits(int64_t M, int64_t N);
+hipError_t launch_cols_skinny(const uint16_t *in, const float *v, int64_t M, int64_t N, int R,
+                              float scale, float *part, int splits, float *out, int transpose_out,
+                              hipStream_t s);
+
+// ---- fused NF4 dequant GEMMs ----------------------------------------------
+struct Nf4Weights {
+    const uint8_t *codes;
+    const int8_t *c2;
+    const float *c1;
+    const float *mean;
+    int64_t d, k;
+};
+// Y[M x d] = bf16( X[M x k] What^T + [hi(sU) | lo(sU)] [B | B]^T ),  U [M x r] fp32.
+// shat_ws: workspace of d*k/64 floats for the dequantized block scales.
+hipError_t launch_gemm_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, const float *U,
+                           const uint16_t *B, int r, float s, uint16_t *Y, float *shat_ws,
+                           hipStream_t st);
+// dX[M x k] = bf16( dY[M x d] What + [hi(sG) | lo(sG)] [A ; A] ),  G [M x r] fp32
+hipError_t launch_gemm_dx(const Nf4Weights &w, const uint16_t *dy, int64_t M, const float *G,
+                          const uint16_t *A, int r, float s, uint16_t *dX, float *shat_ws,
+                          hipStream_t st);
+
+}  // namespace qnf4

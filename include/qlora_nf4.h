@@ -1,0 +1,185 @@
+/*
+ * qlora_nf4.h -- C ABI of the MI355X (gfx950) QLoRA NF4 linear-layer library.
+ *
+ * One QLoRA linear layer: a frozen base weight W0 [d x k] stored as blockwise
+ * 4-bit NormalFloat (NF4) with double-quantized block constants, plus a
+ * trainable low-rank adapter:
+ *
+ *     h = W0 x + (alpha / r) B (A x)          x in R^k, A [r x k], B [d x r]
+ *
+ * (fromzero2ai.dev "LoRA and QLoRA", sections "Linear Layer Deconstruction"
+ * and "Low-Rank Matrix Factorization"; chkda.github.io "Why do we need LoRA
+ * and QLoRA?", "How does it work?".)  Rows of X [M x k] are the inputs, so
+ * the batched form is Y = X What^T + s (X A^T) B^T with s = alpha / r and What
+ * the bf16 weights recovered by doubleDequant (chkda, "Double quantization
+ * and double dequantization").  No bias term.
+ *
+ * Conventions for every call
+ *   - All array arguments are DEVICE pointers, allocated, owned and freed by
+ *     the caller; the library never allocates, frees or keeps a pointer past
+ *     the call.  Matrices are dense and row-major.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously; the library never synchronises.
+ *   - Outputs are overwritten, never accumulated; outputs must not alias
+ *     inputs or each other.
+ *   - bf16 values are passed as their raw 16-bit patterns (qlora_bf16).
+ *   - Every argument is validated before anything is launched: a call that
+ *     returns an error other than QLORA_EHIP has no device side effects.
+ *   - Inputs are assumed finite; NaN or Inf in W0, x, A, B or dY gives
+ *     undefined (but memory-safe) results.
+ *   - Calls are reentrant: the library holds no mutable global state (the
+ *     NF4 table is computed once, on first use, behind a thread-safe
+ *     initialiser).  Calls that share a workspace must be ordered on one
+ *     stream.
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define QLORA_OK          0  /* success                                                  */
+#define QLORA_EINVAL      1  /* null pointer, size <= 0, k % block != 0, non-finite alpha */
+#define QLORA_ENOTSUP     2  /* block != 64, dq_block != 256, r > 128, tensor too large   */
+#define QLORA_EALIGN      3  /* a pointer read/written with 128-bit accesses is not 16-byte aligned */
+#define QLORA_EWORKSPACE  4  /* workspace NULL or smaller than the *_workspace() size     */
+#define QLORA_EHIP        5  /* a HIP launch or runtime error (hipGetLastError)          */
+
+#define QLORA_NF4_BLOCK     64   /* weights per NF4 block (chkda, "Quantizing and dequantizing with the codebook") */
+#define QLORA_NF4_DQ_BLOCK  256  /* block constants per second-level group (chkda, "Double quantization ...")   */
+#define QLORA_MAX_RANK      128
+
+typedef uint16_t qlora_bf16; /* raw bfloat16 bits */
+
+/*
+ * The stored form of W0 (chkda, "Double quantization and double
+ * dequantization": W_NF4 codes in blocks of 64, the quantized block
+ * constants c2 in groups of 256, one fp32 second-level scale c1 per group,
+ * and the mean subtracted before quantizing the constants).  All pointers
+ * are device memory owned by the caller.  With N = d*k, nb = N/64 and
+ * G = ceil(nb/256):
+ *   codes        uint8 [N/2]  byte t = code[2t] | code[2t+1] << 4, codes in
+ *                             row-major order of W0 (16-byte aligned)
+ *   absmax_q     int8  [nb]   c2, in [-127, 127]
+ *   absmax_scale float [G]    c1 (4-byte aligned)
+ *   absmax_mean  float [1]    the mean of the nb block absmax values
+ *   d, k                      W0 shape, d >= 1, k >= 1, k % block == 0
+ *   block, dq_block           must be 64 and 256
+ */
+typedef struct {
+    uint8_t *codes;
+    int8_t  *absmax_q;
+    float   *absmax_scale;
+    float   *absmax_mean;
+    int64_t  d, k;
+    int32_t  block, dq_block;
+} qlora_nf4_weight;
+
+/* Bytes of device workspace qlora_nf4_quantize needs for this shape
+ * (0 for invalid arguments). */
+size_t qlora_nf4_quantize_workspace(int64_t d, int64_t k, int32_t block, int32_t dq_block);
+
+/*
+ * qlora_nf4_quantize -- NF4 + double quantization of W0.
+ * chkda, "Quantizing and dequantizing with the codebook": per block of 64
+ * (row-major flattening) scale = max|w|, each w/scale goes to the nearest of
+ * the 16 NF4 levels (ties to the smaller index; an all-zero block gets the
+ * exact-zero level); "Double quantization and double dequantization" with the
+ * Int8 absmax rule of "First, how does k-bit quantization work?": the block
+ * scales minus their mean are quantized to int8 per group of 256 with
+ * c1 = 127 / max|s - mean| (a zero group stores zeros and c1 = 127).
+ *   W0  device fp32 [d x k], 16-byte aligned, read only.
+ *   w   host struct: shape fields and the four output arrays (all written).
+ *   ws  device workspace of >= qlora_nf4_quantize_workspace(...) bytes,
+ *       16-byte aligned; its contents on entry are ignored.
+ * The result is bit-identical on every run (fixed-order fp64 mean).
+ */
+int qlora_nf4_quantize(const float *W0, const qlora_nf4_weight *w,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * qlora_nf4_dequantize -- doubleDequant into a dense bf16 matrix.
+ * chkda, "Double quantization and double dequantization":
+ *   scale[j] = fp32(c2[j] / c1[j/256]) + mean          (IEEE fp32 ops)
+ *   W[i]     = BF16(C[code[i]] * scale[i/64])          (one RNE rounding)
+ *   W_out  device bf16 [d x k], 16-byte aligned, written.
+ */
+int qlora_nf4_dequantize(const qlora_nf4_weight *w, qlora_bf16 *W_out, void *stream);
+
+/* Bytes of device workspace qlora_linear_fwd / qlora_linear_bwd need for
+ * these sizes (the same figure serves both calls; 0 for invalid arguments). */
+size_t qlora_linear_workspace(int64_t M, int64_t d, int64_t k, int32_t r);
+
+/*
+ * qlora_linear_fwd -- Y = X What^T + (alpha/r) (X A^T) B^T.
+ * chkda, "Double quantization and double dequantization" (the full QLoRA
+ * expression, Y = X doubleDequant(c1, c2, W_NF4) + X L1 L2 with L1 = A^T,
+ * L2 = B^T and the scale alpha/r of "How does alpha/r control adapter
+ * strength?").  What is expanded from the NF4 codes on the fly, bit-identical
+ * to qlora_nf4_dequantize; products accumulate in fp32.
+ *   x      device bf16 [M x k], 16-byte aligned
+ *   A      device bf16 [r x k], 16-byte aligned;  B device bf16 [d x r]
+ *   r      1..128; alpha finite
+ *   Y      device bf16 [M x d], written
+ *   U_save device fp32 [M x r] or NULL: if given, receives U = X A^T (the
+ *          adapter's inner activation, needed by the backward)
+ *   ws     device workspace of >= qlora_linear_workspace(M, d, k, r) bytes.
+ */
+int qlora_linear_fwd(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M,
+                     const qlora_bf16 *A, const qlora_bf16 *B, int32_t r, float alpha,
+                     qlora_bf16 *Y, float *U_save, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * qlora_linear_bwd -- gradients of the layer for an upstream gradient dY.
+ * chkda, "Double quantization and double dequantization": backpropagation
+ * runs through the reconstructed base weights into the adapters only; the
+ * 4-bit weights get no gradient.  With s = alpha/r, U = X A^T, G = dY B:
+ *   dX = dY What + s G A        dA = s G^T X        dB = s dY^T U
+ *   x   device bf16 [M x k];  dY device bf16 [M x d] (16-byte aligned)
+ *   A, B, r, alpha as in qlora_linear_fwd
+ *   U   device fp32 [M x r] from qlora_linear_fwd's U_save, or NULL to
+ *       recompute it
+ *   dX  device bf16 [M x k], written; or NULL to skip the input gradient
+ *   dA  device fp32 [r x k], written;  dB device fp32 [d x r], written
+ *   ws  device workspace of >= qlora_linear_workspace(M, d, k, r) bytes.
+ * Reductions over M run in a fixed order: results are bit-identical on
+ * every run.
+ */
+int qlora_linear_bwd(const qlora_nf4_weight *w, const qlora_bf16 *x, const qlora_bf16 *dY,
+                     const qlora_bf16 *A, const qlora_bf16 *B, const float *U,
+                     int64_t M, int32_t r, float alpha,
+                     qlora_bf16 *dX, float *dA, float *dB,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * qlora_nf4_codebook -- host-only: copies the library's 16 fp32 NF4 levels
+ * (chkda, "NF4: Choose the codebook to fit the distribution"; built as in
+ * "Building the NF4 codebook" from standard-normal quantiles) into out[16].
+ * Needs no GPU.
+ */
+int qlora_nf4_codebook(float out[16]);
+
+/*
+ * qlora_nf4_thresholds -- host-only: the 15 fp32 decision thresholds T_j used
+ * by the quantizer; x goes to level j+1 or above iff fp32 x >= T_j, where
+ * T_j is the smallest fp32 strictly above the exact midpoint of levels j and
+ * j+1 (chkda: nearest level, ties to the smaller index).  Needs no GPU.
+ */
+int qlora_nf4_thresholds(float out[15]);
+
+/* Static description of a status code (never NULL). */
+const char *qlora_status_str(int status);
+
+/* ABI version of this header/library pair. */
+int qlora_abi_version(void);
+#define QLORA_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QLORA_NF4_H */

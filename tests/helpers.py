@@ -1,0 +1,86 @@
+"""Shared helpers of the GPU parity tests (host-side comparison logic only)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+from oracle import nf4, qlora
+from workloads import bf16_bits_as_f32
+
+REL_FRO_TOL = 5e-3      # relative Frobenius error bound for GEMM outputs and gradients
+MAX_ABS_TOL = 2e-2      # max |out - ref| <= MAX_ABS_TOL * rms(ref)
+
+
+def say(msg: str) -> None:
+    """Name the case before a GPU step so a fault is attributable."""
+    print(f"[case] {msg}", file=sys.stderr, flush=True)
+
+
+def to_dev_bf16(bits: np.ndarray):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).cuda()
+
+
+def to_dev_f32(a: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def bf16_to_host_bits(t) -> np.ndarray:
+    import torch
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bf16_to_host_f64(t) -> np.ndarray:
+    return bf16_bits_as_f32(bf16_to_host_bits(t)).astype(np.float64)
+
+
+def assert_close(out: np.ndarray, ref: np.ndarray, what: str,
+                 rel_tol: float = REL_FRO_TOL, abs_tol: float = MAX_ABS_TOL,
+                 bf16_output: bool = False) -> dict:
+    """Relative Frobenius <= rel_tol and max |out - ref| <= abs_tol * rms(ref).
+
+    bf16_output: the output is stored in bf16, whose own rounding is up to
+    |ref| * 2^-8 (half an ulp, at most 2^-8 relative).  Where a heavy-tailed
+    output makes that rounding alone exceed abs_tol * rms(ref), the
+    per-element bound becomes abs_tol * rms(ref) + |ref| * 2^-8.
+    """
+    out = np.asarray(out, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert out.shape == ref.shape, (what, out.shape, ref.shape)
+    assert np.all(np.isfinite(out)), f"{what}: non-finite output"
+    diff = out - ref
+    nref = np.linalg.norm(ref)
+    rms = nref / np.sqrt(ref.size) if ref.size else 0.0
+    if nref == 0:
+        assert np.all(out == 0), f"{what}: reference is exactly zero, output is not"
+        return {"rel_fro": 0.0, "max_abs_over_rms": 0.0}
+    rel = np.linalg.norm(diff) / nref
+    mx = np.abs(diff).max() / rms
+    assert rel <= rel_tol, f"{what}: relative Frobenius error {rel:.3e} > {rel_tol}"
+    if bf16_output and mx > abs_tol:
+        excess = np.abs(diff) - (abs_tol * rms + np.abs(ref) * 2.0 ** -8)
+        assert excess.max() <= 0, f"{what}: error beyond bf16 output rounding: {excess.max():.3e}"
+    else:
+        assert mx <= abs_tol, f"{what}: max abs error {mx:.3e} x rms(ref) > {abs_tol}"
+    return {"rel_fro": float(rel), "max_abs_over_rms": float(mx)}
+
+
+class OracleLayer:
+    """The oracle's view of one layer: its own quantization of W0 and What."""
+
+    def __init__(self, w0: np.ndarray):
+        self.d, self.k = w0.shape
+        self.q = nf4.quantize(w0)
+        self.w_hat_bits = nf4.dequantize(self.q, (self.d, self.k))
+        self.w_hat = nf4.bf16_bits_to_f32(self.w_hat_bits).reshape(self.d, self.k)
+
+    def forward(self, x_bits, a_bits, b_bits, alpha):
+        return qlora.forward(self.w_hat, bf16_bits_as_f32(x_bits), bf16_bits_as_f32(a_bits),
+                             bf16_bits_as_f32(b_bits), alpha)
+
+    def backward(self, x_bits, dy_bits, a_bits, b_bits, alpha):
+        return qlora.backward(self.w_hat, bf16_bits_as_f32(x_bits), bf16_bits_as_f32(dy_bits),
+                              bf16_bits_as_f32(a_bits), bf16_bits_as_f32(b_bits), alpha)

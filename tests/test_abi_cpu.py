@@ -1,0 +1,159 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol,
+returns the same NF4 table as the oracle bit for bit, and rejects invalid
+arguments with the documented status before launching anything.  No GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_nf4_quantized_13_amd as q
+from oracle import nf4
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "qlora_nf4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd", "qlora_linear_bwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(q.build.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_abi_version():
+    text = open(HEADER).read()
+    want = int(re.search(r"#define QLORA_ABI_VERSION (\d+)", text).group(1))
+    assert q.abi_version() == want
+
+
+def test_codebook_bit_identical_to_oracle():
+    lib_levels = np.array(q.qlora_nf4_codebook(), dtype=np.float32)
+    assert np.array_equal(lib_levels.view(np.uint32), nf4.nf4_codebook().view(np.uint32))
+
+
+def test_thresholds_are_smallest_fp32_above_midpoints():
+    t = np.array(q.qlora_nf4_thresholds(), dtype=np.float32)
+    m = nf4.nf4_midpoints()
+    assert np.all(t.astype(np.float64) > m)
+    below = np.nextafter(t, np.float32(-2)).astype(np.float64)
+    assert np.all(below <= m)
+
+
+def test_status_strings():
+    for code in range(6):
+        assert q.status_str(code).startswith("QLORA_")
+    assert q.status_str(99) == "unknown qlora status"
+
+
+def test_workspace_sizes():
+    assert q.quantize_workspace_bytes(4096, 4096) >= 4 * 4096 * 4096 // 64
+    lib = q.library()
+    assert lib.qlora_nf4_quantize_workspace(4096, 100, 64, 256) == 0      # k % 64 != 0
+    assert lib.qlora_nf4_quantize_workspace(4096, 4096, 32, 256) == 0     # block != 64
+    assert lib.qlora_nf4_quantize_workspace(0, 4096, 64, 256) == 0
+    assert q.linear_workspace_bytes(4096, 4096, 4096, 8) > 0
+    assert lib.qlora_linear_workspace(16, 256, 512, 0) == 0
+    assert lib.qlora_linear_workspace(16, 256, 512, 129) == 0
+    assert lib.qlora_linear_workspace(16, 256, 500, 8) == 0
+
+
+# fake, never-dereferenced device addresses: every call below fails validation
+FAKE = 0x7F0000000000
+FAKE_MIS = FAKE + 2
+
+
+def weight(d=256, k=512, codes=FAKE, c2=FAKE, c1=FAKE, mean=FAKE, block=64, dq=256):
+    return q._CWeight(codes, c2, c1, mean, d, k, block, dq)
+
+
+def quant(w, w0=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return q.library().qlora_nf4_quantize(w0, ctypes.byref(w), ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("w,w0,ws,ws_bytes,status", [
+    (weight(), None, FAKE, 1 << 30, q.QLORA_EINVAL),
+    (weight(codes=None), FAKE, FAKE, 1 << 30, q.QLORA_EINVAL),
+    (weight(mean=None), FAKE, FAKE, 1 << 30, q.QLORA_EINVAL),
+    (weight(d=0), FAKE, FAKE, 1 << 30, q.QLORA_EINVAL),
+    (weight(k=-64), FAKE, FAKE, 1 << 30, q.QLORA_EINVAL),
+    (weight(k=100), FAKE, FAKE, 1 << 30, q.QLORA_EINVAL),
+    (weight(block=32), FAKE, FAKE, 1 << 30, q.QLORA_ENOTSUP),
+    (weight(dq=128), FAKE, FAKE, 1 << 30, q.QLORA_ENOTSUP),
+    (weight(d=1 << 20, k=1 << 12), FAKE, FAKE, 1 << 40, q.QLORA_ENOTSUP),
+    (weight(), FAKE_MIS, FAKE, 1 << 30, q.QLORA_EALIGN),
+    (weight(codes=FAKE + 8), FAKE, FAKE, 1 << 30, q.QLORA_EALIGN),
+    (weight(), FAKE, None, 1 << 30, q.QLORA_EWORKSPACE),
+    (weight(), FAKE, FAKE, 16, q.QLORA_EWORKSPACE),
+])
+def test_quantize_rejects_invalid_arguments(w, w0, ws, ws_bytes, status):
+    assert quant(w, w0, ws, ws_bytes) == status
+
+
+def test_quantize_null_weight_struct():
+    assert q.library().qlora_nf4_quantize(FAKE, None, FAKE, 1 << 30, None) == q.QLORA_EINVAL
+
+
+def test_dequantize_rejects_invalid_arguments():
+    lib = q.library()
+    assert lib.qlora_nf4_dequantize(ctypes.byref(weight()), None, None) == q.QLORA_EINVAL
+    assert lib.qlora_nf4_dequantize(ctypes.byref(weight()), FAKE_MIS, None) == q.QLORA_EALIGN
+    assert lib.qlora_nf4_dequantize(ctypes.byref(weight(block=128)), FAKE, None) == q.QLORA_ENOTSUP
+
+
+def fwd(w=None, x=FAKE, m=16, a=FAKE, b=FAKE, r=8, alpha=16.0, y=FAKE, u=None, ws=FAKE,
+        ws_bytes=1 << 30):
+    w = w or weight()
+    return q.library().qlora_linear_fwd(ctypes.byref(w), x, m, a, b, r, alpha, y, u, ws, ws_bytes, None)
+
+
+def bwd(w=None, x=FAKE, dy=FAKE, a=FAKE, b=FAKE, u=None, m=16, r=8, alpha=16.0, dx=FAKE,
+        da=FAKE, db=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    w = w or weight()
+    return q.library().qlora_linear_bwd(ctypes.byref(w), x, dy, a, b, u, m, r, alpha, dx, da, db,
+                                        ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), q.QLORA_EINVAL), (dict(a=None), q.QLORA_EINVAL), (dict(b=None), q.QLORA_EINVAL),
+    (dict(y=None), q.QLORA_EINVAL), (dict(m=0), q.QLORA_EINVAL), (dict(r=0), q.QLORA_EINVAL),
+    (dict(r=129), q.QLORA_ENOTSUP), (dict(alpha=float("nan")), q.QLORA_EINVAL),
+    (dict(alpha=float("inf")), q.QLORA_EINVAL), (dict(w=weight(d=252)), q.QLORA_ENOTSUP),
+    (dict(x=FAKE_MIS), q.QLORA_EALIGN), (dict(a=FAKE + 4), q.QLORA_EALIGN),
+    (dict(y=FAKE_MIS), q.QLORA_EALIGN), (dict(u=FAKE + 1), q.QLORA_EALIGN),
+    (dict(ws=None), q.QLORA_EWORKSPACE), (dict(ws_bytes=64), q.QLORA_EWORKSPACE),
+    (dict(w=weight(k=100)), q.QLORA_EINVAL), (dict(w=weight(codes=None)), q.QLORA_EINVAL),
+])
+def test_fwd_rejects_invalid_arguments(kw, status):
+    assert fwd(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dy=None), q.QLORA_EINVAL), (dict(da=None), q.QLORA_EINVAL), (dict(db=None), q.QLORA_EINVAL),
+    (dict(m=-1), q.QLORA_EINVAL), (dict(r=200), q.QLORA_ENOTSUP),
+    (dict(dy=FAKE_MIS), q.QLORA_EALIGN), (dict(dx=FAKE_MIS), q.QLORA_EALIGN),
+    (dict(da=FAKE + 2), q.QLORA_EALIGN), (dict(ws_bytes=0), q.QLORA_EWORKSPACE),
+])
+def test_bwd_rejects_invalid_arguments(kw, status):
+    assert bwd(**kw) == status
+
+
+def test_valid_call_without_gpu_reports_hip_error():
+    """With no device present a valid call must fail with QLORA_EHIP, not crash."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: this check is for hosts without one")
+    w = weight()
+    assert quant(w) == q.QLORA_EHIP
