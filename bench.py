@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark of the QLoRA NF4 linear layer on one MI355X (gfx950).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one pass of the whole hot path over the layer4096 workload
+(W0 4096 x 4096 fp32 ~ N(0, 0.02^2); x: M = 4096 tokens = batch 4 x sequence
+1024; r = 8, alpha = 16; synthetic, seeded):
+    qlora_nf4_quantize(W0)           NF4 codes + double-quantized constants
+    qlora_linear_fwd                 Y = X What^T + s (X A^T) B^T
+    qlora_linear_bwd                 dX, dA, dB
+All inputs are resident in HBM before the timed region.  `value` is the
+forward + backward algorithmic flops per step (4 M d k + 6 M r (d + k)) over
+the measured time of the whole step (quantization included), in TFLOP/s.
+
+The same run measures the decode-shaped forward (decode workload: W0 4096 x
+4096 and 14336 x 4096, M in {1, 4, 16}, r = 16, alpha = 32) as GB/s of packed
+NF4 bytes, rotating over weight copies totalling more than 512 MB so that
+neither the 256 MB Infinity Cache nor L2 serves them.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "QLoRA linear fwd+bwd TFLOP/s at M=4096; NF4 weight GB/s at M=16 forward"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def fwd_flops(m, d, k, r):
+    return 2 * m * d * k + 2 * m * r * (d + k)
+
+
+def bwd_flops(m, d, k, r):
+    return 2 * m * d * k + 4 * m * r * (d + k)
+
+
+def source_sha(name: str) -> str:
+    path = os.path.join(ROOT, "bit_nf4_quantized_13_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, source: str, launches_bytes: float | None):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they
+    were taken on the current kernel source (else None)."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            t = json.load(f)
+        if t.get("source_sha") != source_sha(source):
+            return None
+        return float(t["hbm_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream the library launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, e0):
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e1.record()
+        self.pairs.append((e0, e1))
+
+    def total_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs)
+
+
+def run_layer_bench(q, torch, steps, warmup):
+    from workloads import WORKLOADS, workload_layer
+    from tests.helpers import to_dev_bf16, to_dev_f32
+    wl = WORKLOADS["layer4096"]
+    p = wl.projections[0]
+    m, d, k, r, alpha = wl.m[0], p.d, p.k, wl.r, wl.alpha
+    log(f"layer4096: generating inputs d={d} k={k} M={m} r={r}")
+    inp = workload_layer("layer4096")
+    w0 = to_dev_f32(inp.w0)
+    x, a, b, dy = (to_dev_bf16(t) for t in (inp.x, inp.a, inp.b, inp.dy))
+    wq = q.NF4Weight.empty(d, k)
+    qws = torch.empty(q.quantize_workspace_bytes(d, k), dtype=torch.uint8, device="cuda")
+    lws = torch.empty(q.linear_workspace_bytes(m, d, k, r), dtype=torch.uint8, device="cuda")
+    y = torch.empty((m, d), dtype=torch.bfloat16, device="cuda")
+    u = torch.empty((m, r), dtype=torch.float32, device="cuda")
+    dx = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
+    da = torch.empty((r, k), dtype=torch.float32, device="cuda")
+    db = torch.empty((d, r), dtype=torch.float32, device="cuda")
+
+    tq, tf, tb = Timer(torch), Timer(torch), Timer(torch)
+
+    def step(timed):
+        e = tq.start() if timed else None
+        q.qlora_nf4_quantize(w0, out=wq, workspace=qws)
+        if timed:
+            tq.stop(e)
+            e = tf.start()
+        q.qlora_linear_fwd(wq, x, a, b, alpha, out=y, u_out=u, workspace=lws)
+        if timed:
+            tf.stop(e)
+            e = tb.start()
+        q.qlora_linear_bwd(wq, x, dy, a, b, alpha, u=u, workspace=lws, outs=(dx, da, db))
+        if timed:
+            tb.stop(e)
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"layer4096: timing {steps} steps")
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        step(True)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    total_ms = ev0.elapsed_time(ev1)
+    ms_step = total_ms / steps
+    flops = fwd_flops(m, d, k, r) + bwd_flops(m, d, k, r)
+    phases = {"quantize_ms": tq.total_ms() / steps, "fwd_ms": tf.total_ms() / steps,
+              "bwd_ms": tb.total_ms() / steps}
+    fb_ms = phases["fwd_ms"] + phases["bwd_ms"]
+    return {
+        "m": m, "d": d, "k": k, "r": r, "alpha": alpha, "ms_per_step": ms_step,
+        "wall_ms_per_step": wall_ms / steps,
+        "tflops_step": flops / (ms_step * 1e-3) / 1e12,
+        "tflops_fwd_bwd": flops / (fb_ms * 1e-3) / 1e12,
+        "phases": phases, "flops": flops,
+        "quantize_gbs": (d * k * 4 + d * k // 2 + d * k // 64) / (phases["quantize_ms"] * 1e-3) / 1e9,
+    }
+
+
+def run_decode_bench(q, torch, iters=50):
+    from workloads import WORKLOADS, workload_layer
+    from tests.helpers import to_dev_bf16, to_dev_f32
+    wl = WORKLOADS["decode"]
+    out = {}
+    for pi, p in enumerate(wl.projections):
+        inp = workload_layer("decode", pi)
+        packed = p.d * p.k // 2
+        copies = max(2, -(-512 * 2**20 // packed) + 1)
+        log(f"decode {p.name}: quantizing {copies} weight copies ({copies * packed / 2**20:.0f} MiB packed)")
+        w0 = to_dev_f32(inp.w0)
+        ws = [q.qlora_nf4_quantize(w0) for _ in range(copies)]
+        del w0
+        a, b = to_dev_bf16(inp.a), to_dev_bf16(inp.b)
+        for m in wl.m:
+            x = to_dev_bf16(inp.x[:m])
+            y = torch.empty((m, p.d), dtype=torch.bfloat16, device="cuda")
+            lws = torch.empty(q.linear_workspace_bytes(m, p.d, p.k, wl.r), dtype=torch.uint8,
+                              device="cuda")
+            for i in range(copies):
+                q.qlora_linear_fwd(ws[i], x, a, b, wl.alpha, save_u=False, out=y, workspace=lws)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for it in range(iters):
+                q.qlora_linear_fwd(ws[it % copies], x, a, b, wl.alpha, save_u=False, out=y,
+                                   workspace=lws)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / iters
+            gbs = packed / (us * 1e-6) / 1e9
+            out[f"{p.name}_m{m}"] = {"us_per_call": round(us, 3), "packed_gbs": round(gbs, 1),
+                                     "hbm_frac_packed": round(gbs / HBM_PEAK_GBS, 4)}
+            log(f"decode {p.name} M={m}: {us:.2f} us/call, {gbs:.0f} GB/s packed")
+        del ws
+        torch.cuda.empty_cache()
+    return out
+
+
+def run_cpu_baseline(target_s=15.0):
+    """The oracle as it stands, on a bounded sample of the layer4096 step:
+    quantize + doubleDequant of the full W0 and fp64 forward + backward for
+    the first `ms` tokens; reported as fp64 TFLOP/s of those tokens' flops."""
+    import numpy as np
+    from oracle import nf4, qlora
+    from workloads import WORKLOADS, bf16_bits_as_f32, workload_layer
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        threads = 1
+    wl = WORKLOADS["layer4096"]
+    p = wl.projections[0]
+    inp = workload_layer("layer4096")
+    ms = 256
+    x = bf16_bits_as_f32(inp.x[:ms])
+    dy = bf16_bits_as_f32(inp.dy[:ms])
+    a, b = bf16_bits_as_f32(inp.a), bf16_bits_as_f32(inp.b)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        qd = nf4.quantize(inp.w0)
+        w_hat = nf4.bf16_bits_to_f32(nf4.dequantize(qd, inp.w0.shape))
+        qlora.forward(w_hat, x, a, b, wl.alpha)
+        qlora.backward(w_hat, x, dy, a, b, wl.alpha)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 50:
+            break
+    flops = (fwd_flops(ms, p.d, p.k, wl.r) + bwd_flops(ms, p.d, p.k, wl.r)) * reps
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"layer4096 step on the first {ms} of 4096 tokens (oracle quantize + "
+                      f"doubleDequant of the full 4096x4096 W0, fp64 fwd+bwd), {reps} reps, "
+                      f"{el:.1f} s; numpy/OpenBLAS threads={threads}, "
+                      f"host cpus={len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the layer's multi-GPU sharding is a design note only)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_nf4_quantized_13_amd as q
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    lay = run_layer_bench(q, torch, args.steps, args.warmup)
+    m, d, k, r = lay["m"], lay["d"], lay["k"], lay["r"]
+    # dominant kernel: the forward dequant-GEMM, timed through qlora_linear_fwd
+    fwd_ms = lay["phases"]["fwd_ms"]
+    achieved = fwd_flops(m, d, k, r) / (fwd_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "qlora_linear_fwd (nf4_gemm_kernel<fwd> + U kernel)",
+                "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic_from_profiles("nf4_gemm_fwd", "gemm.hip", None),
+                "work_per_launch": f"2*M*d*k + 2*M*r*(d+k) = {fwd_flops(m, d, k, r)} flop"}
+    decode = None if args.skip_decode else run_decode_bench(q, torch)
+    cpu = None
+    if not args.skip_cpu_baseline:
+        log("cpu baseline: timing the oracle on a bounded sample")
+        cpu = run_cpu_baseline()
+    line = {
+        "metric": METRIC, "value": round(lay["tflops_step"], 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(lay["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "layer4096: W0 4096x4096 NF4 (block 64, DQ block 256), M=4096 "
+                               "(batch 4 x seq 1024), r=8, alpha=16; step = quantize + fwd + bwd",
+                   "global_batch": 4, "seq_len": 1024, "parallelism": "none (1 GPU)"},
+        "fwd_bwd_tflops": round(lay["tflops_fwd_bwd"], 3),
+        "phases_ms": {kk: round(v, 4) for kk, v in lay["phases"].items()},
+        "quantize_gbs": round(lay["quantize_gbs"], 1),
+        "roofline": roofline,
+        "decode_fwd": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

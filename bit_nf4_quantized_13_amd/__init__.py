@@ -191,14 +191,17 @@ def qlora_nf4_dequantize(w: NF4Weight, out: torch.Tensor | None = None) -> torch
 
 def qlora_linear_fwd(w: NF4Weight, x: torch.Tensor, a: torch.Tensor, b: torch.Tensor,
                      alpha: float, save_u: bool = True, out: torch.Tensor | None = None,
-                     workspace: torch.Tensor | None = None):
+                     u_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
     """Y = x What^T + (alpha/r) (x A^T) B^T.  Returns (Y bf16 [M, d], U fp32 [M, r] or None)."""
     _dev_tensor(x, torch.bfloat16, "x")
     _dev_tensor(a, torch.bfloat16, "A")
     _dev_tensor(b, torch.bfloat16, "B")
     m, r = x.shape[0], a.shape[0]
     y = out if out is not None else torch.empty((m, w.d), dtype=torch.bfloat16, device=x.device)
-    u = torch.empty((m, r), dtype=torch.float32, device=x.device) if save_u else None
+    if u_out is not None:
+        u = _dev_tensor(u_out, torch.float32, "U")
+    else:
+        u = torch.empty((m, r), dtype=torch.float32, device=x.device) if save_u else None
     ws = workspace if workspace is not None else _workspace(
         linear_workspace_bytes(m, w.d, w.k, r), x.device)
     cw = w.c_struct()
