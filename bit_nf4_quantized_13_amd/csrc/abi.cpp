@@ -50,13 +50,20 @@ QuantWs quant_ws(int64_t d, int64_t k) {
 }
 
 struct LinWs {
-    size_t shat, u, bt, g, part, total;
+    size_t shat, ext_a, ext_b, wbf, u, bt, g, part, total;
 };
 LinWs lin_ws(int64_t M, int64_t d, int64_t k, int r) {
     LinWs l;
     size_t off = 0;
     l.shat = off;
     off += round_up(sizeof(float) * (d * k / QLORA_NF4_BLOCK), 256);
+    const int64_t ke = gemm_ext_cols(r);
+    l.ext_a = off;
+    off += round_up(sizeof(uint16_t) * M * ke, 256);
+    l.ext_b = off;
+    off += round_up(sizeof(uint16_t) * (d > k ? d : k) * ke, 256);
+    l.wbf = off;
+    off += round_up(sizeof(uint16_t) * gemm_wbf_elems(M, d, k), 256);
     l.u = off;
     off += round_up(sizeof(float) * M * r, 256);
     l.bt = off;
@@ -69,6 +76,11 @@ LinWs lin_ws(int64_t M, int64_t d, int64_t k, int r) {
     off += round_up(pd > pk ? pd : pk, 256);
     l.total = off;
     return l;
+}
+
+GemmWs gemm_ws(char *base, const LinWs &l) {
+    return GemmWs{reinterpret_cast<float *>(base + l.shat), reinterpret_cast<uint16_t *>(base + l.ext_a),
+                  reinterpret_cast<uint16_t *>(base + l.ext_b), reinterpret_cast<uint16_t *>(base + l.wbf)};
 }
 
 int check_linear(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M, const qlora_bf16 *A,
@@ -175,7 +187,7 @@ int qlora_linear_fwd(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M,
     const Nf4Weights nw{w->codes, w->absmax_q, w->absmax_scale, w->absmax_mean, w->d, w->k};
     hipError_t e = launch_rows_skinny(x, A, M, w->k, r, U, s);
     if (e == hipSuccess)
-        e = launch_gemm_fwd(nw, x, M, U, B, r, scale, Y, reinterpret_cast<float *>(base + l.shat), s);
+        e = launch_gemm_fwd(nw, x, M, U, B, r, scale, Y, gemm_ws(base, l), s);
     return hip_status(e);
 }
 
@@ -216,7 +228,7 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const qlora_bf16 *x, const qlora
     if (e == hipSuccess)                                                        // dA = s G^T X
         e = launch_cols_skinny(x, G, M, k, r, scale, part, cols_skinny_splits(M, k), dA, 1, s);
     if (e == hipSuccess && dX)                                                  // dX = dY What + s G A
-        e = launch_gemm_dx(nw, dY, M, G, A, r, scale, dX, reinterpret_cast<float *>(base + l.shat), s);
+        e = launch_gemm_dx(nw, dY, M, G, A, r, scale, dX, gemm_ws(base, l), s);
     return hip_status(e);
 }
 

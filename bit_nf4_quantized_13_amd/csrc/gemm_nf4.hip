@@ -10,33 +10,38 @@
 // weights into the adapters only.
 //
 // Design (MI355X, one 256-thread workgroup per 512 x 128 output tile):
-//  * Wave w owns output rows [128 w, 128 w + 128) and all 128 columns: 4 x 4
-//    MFMA 32x32x16 tiles, fp32 accumulators in 256 AGPRs.  A 512-row tile means
-//    every expanded weight feeds 512 rows, halving the expansion work per MFMA
-//    relative to a 256-row tile.
-//  * The activation tile (X or dY, 512 x 64 bf16) goes global -> LDS by DMA
-//    (buffer_load ... lds, 1 KiB = 8 rows per instruction, XOR-swizzled 16-byte
-//    chunks), double-buffered and issued one k-step ahead.
-//  * The weight operand is expanded once per workgroup into a double-buffered
-//    LDS bf16 tile [128 n][64 k]: the packed codes and block scales of step k
-//    are loaded into registers two steps ahead, and the expansion of step k+1 --
-//    BF16(C[code] * scale), bit-identical to qlora_nf4_dequantize -- runs
-//    between the MFMAs of step k.  The 16 levels live in a VGPR (lane j holds
-//    C[j % 16]) and are looked up with ds_bpermute, so the two operand rings
-//    use exactly the 160 KiB of LDS.  Forward: a thread expands 32 consecutive
-//    weights of one row.  dX (the reduction runs over W0 rows): a thread
-//    expands 4 rows x 8 columns and writes them k-contiguous, i.e. the
-//    transpose happens in registers.
-//  * k order inside a 64-deep step is permuted (lane half h takes k = 32 h ..
-//    32 h + 31 as four 8-wide MFMA slices) for both tiles.
-//  * The adapter term is appended as extra k-steps with operands
-//    [hi(sV) | lo(sV)] and [W' | W'] (hi = bf16(v), lo = bf16(v - hi)).
+//  * Wave w owns output rows [128 w, 128 w + 128) and all 128 columns: 8 x 8
+//    MFMA 16x16x32 tiles, fp32 accumulators in 256 AGPRs.
+//  * The activation operand (X or dY) goes straight from global memory into
+//    registers in the MFMA operand layout: a wave reads only its own rows, so
+//    no LDS staging is needed.  With the 16x16x32 layout one 16-byte load per
+//    lane covers 16 rows x 64 bytes; the 16 loads of the next k-step are spread
+//    one per MFMA group so the vector-memory path never blocks MFMA issue.
+//  * The weight operand is expanded once per workgroup into LDS as bf16
+//    [128 n][64 k] tiles -- BF16(C[code] * scale), bit-identical to
+//    qlora_nf4_dequantize -- in a ring of 4 stages, two k-steps ahead of its
+//    use, so one barrier per two k-steps suffices.  Packed codes and block
+//    scales arrive in registers four steps ahead.  The 16 levels live in a
+//    VGPR (lane j holds C[j % 16]) and are looked up with ds_bpermute; the
+//    lookup, the multiply and the LDS write of each 8-weight piece are spread
+//    over four MFMA groups so their latency hides behind the MFMAs.
+//    Forward: a thread expands 32 consecutive weights of one W0 row.  dX (the
+//    reduction runs over W0 rows): a thread expands 4 rows x 8 columns and
+//    writes them k-contiguous, i.e. the transpose happens in registers.
+//  * The MFMA takes the weight fragment as its first operand, so each lane
+//    ends with 4 consecutive output columns of one row (8-byte stores).
+//  * The adapter term is appended as extra k-steps whose operands the
+//    preparation kernel lays out in memory: [hi(sV) | lo(sV) | 0] and
+//    [W' | W' | 0] (hi = bf16(v), lo = bf16(v - hi), rows padded to a
+//    multiple of 64).
 //  * Workgroups are renumbered so each XCD walks a contiguous run of tiles.
 //
-// MFMA v_mfma_f32_32x32x16_bf16 layout (wave64):
-//   A (32 x 16): lane l holds A[l % 32][8 (l / 32) .. +7]
-//   B (16 x 32): lane l holds B[8 (l / 32) .. +7][l % 32]
-//   D (32 x 32): lane l, register v: D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32]
+// MFMA v_mfma_f32_16x16x32_bf16 layout (wave64), g = lane / 16:
+//   first operand  (16 x 32): lane l holds P[l % 16][8 g .. 8 g + 7]
+//   second operand (32 x 16): lane l holds Q[8 g .. 8 g + 7][l % 16]
+//   result         (16 x 16): lane l, register v: D[4 g + v][l % 16]
+// k order inside a 64-deep step: slice s (32 k) lane group g takes
+// k = 32 s + 8 g .. + 7, identically for both operands.
 #include <type_traits>
 
 #include "launch.hpp"
@@ -45,6 +50,11 @@ namespace qnf4 {
 namespace {
 
 constexpr int BM = 512, BN = 128, BK = 64;
+constexpr int NTHREADS = 512;                 // 8 waves, two per SIMD
+constexpr int WM = BM / (NTHREADS / 64);      // rows per wave (64)
+constexpr int MI = WM / 16;                   // 16-row MFMA tiles per wave (4)
+constexpr int A_STAGE = BM * BK * 2;          // 64 KiB activation tile
+constexpr int B_STAGE = BN * BK * 2;          // 16 KiB weight tile
 
 struct GemmArgs {
     const uint16_t *a;      // activation operand [M x Kd] bf16 (X or dY)
@@ -52,25 +62,30 @@ struct GemmArgs {
     const uint8_t *codes;   // W0 [d x k] packed NF4
     const float *shat;      // dequantized block scales [d * k / 64]
     int64_t d, k;
-    const float *ext_v;     // U (forward) or G (dX): [M x r] fp32
-    const uint16_t *ext_w;  // B [d x r] (forward) or A [r x k] (dX)
-    int r;
-    float s;
+    const uint16_t *ext_a;  // [M x Ke] bf16: [hi(s V) | lo(s V) | 0]
+    const uint16_t *ext_b;  // [N x Ke] bf16: [W' | W' | 0]
+    int64_t Ke;             // multiple of 64
+    const uint16_t *wbf;    // dequantized weight operand [N x ldw] bf16 (non-expanding kernel)
+    int64_t ldw;            // forward: What [d x k], ldw = k; dX: What^T [k x ldw], ldw = d rounded up to 64
     uint16_t *out;          // Y or dX [M x N] bf16
 };
 
 template <int V>
 using IC = std::integral_constant<int, V>;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
-
-__device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+__device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
-
-__device__ __forceinline__ uint32_t comp(const uint4 &v, int i) {
-    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+// c += a b in place.  Written as one instruction with the accumulator tied to
+// an AGPR tuple: with 64 accumulator tiles the register allocator otherwise
+// splits the chains and shuttles them between AGPRs and VGPRs.  The operands
+// come straight from memory loads (no VALU producer), and each accumulator is
+// touched once per 64 MFMAs, so no extra wait states are needed.
+__device__ __forceinline__ void mfma16_acc(uint4 a, uint4 b, f32x4 &c) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                 : "+a"(c)
+                 : "v"(__builtin_bit_cast(u32x4, a)), "v"(__builtin_bit_cast(u32x4, b)));
 }
 
 // Raw buffer resource over [base, base + bytes): 32-bit offsets, descriptor in
@@ -84,37 +99,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
     void *p = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
     return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, n, 0x00020000);
 }
-
-__device__ __forceinline__ __attribute__((address_space(3))) void *lds_ptr(const void *p) {
-    return reinterpret_cast<__attribute__((address_space(3))) void *>(reinterpret_cast<uintptr_t>(p));
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
-// global -> LDS transfer: lane l writes LDS bytes [dst + size*l, +size)
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void *dst, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(dst), 16, voff, 0, 0, 0);
-}
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, const void *dst, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(dst), 4, voff, 0, 0, 0);
+__device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
 
-__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t T) {
+// Workgroup -> output tile.  Consecutive workgroups go to the 8 XCDs in turn;
+// each XCD takes a contiguous run u of the tile order, and the tile order walks
+// bands of 8 tile columns, all tile rows of a band before the next band.  An
+// XCD's concurrently running tiles then share 4-8 activation slabs and 8
+// weight slabs in its L2 instead of one slab of one and 32 of the other.
+__device__ __forceinline__ void tile_of(int64_t b, int64_t tiles_m, int64_t tiles_n, int64_t &mt, int64_t &nt) {
+    const int64_t T = tiles_m * tiles_n;
     const int64_t x = b % 8, y = b / 8, q = T / 8, rem = T % 8;
-    return x * q + (x < rem ? x : rem) + y;
+    const int64_t u = x * q + (x < rem ? x : rem) + y;
+    constexpr int64_t GN = 8;
+    const int64_t band = u / (tiles_m * GN);
+    const int64_t w = (tiles_n - band * GN) < GN ? (tiles_n - band * GN) : GN;
+    const int64_t r = u - band * tiles_m * GN;
+    mt = r / w;
+    nt = band * GN + r % w;
 }
 
-// s_waitcnt immediate (gfx9 encoding): at most `vm` vector-memory operations
-// outstanding, no LDS operation outstanding.
-constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (0x7 << 4); }
-
-// 8 codes of one dword (element i in nibble i) -> 8 levels C[code].  `lv`
-// holds C[lane % 16] in every lane; ds_bpermute returns lane q's value for a
-// byte index 4 q.  Byte j of e4 / o4 is 4 * nibble(2j) / 4 * nibble(2j+1); the
-// masks go through an opaque v_and so the compiler keeps the one-instruction
-// v_bfe_u32 byte extracts.
-__device__ __forceinline__ uint32_t opaque_and(uint32_t x, uint32_t m) {
-    uint32_t r;
-    asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(m));
-    return r;
-}
 // Marks the point where a value loaded steps earlier is first used: nothing
 // computed from it can be hoisted above this point (where the load would
 // still be in flight and its wait would stall the MFMA stream).
@@ -123,43 +131,78 @@ __device__ __forceinline__ T pin(T v) {
     asm volatile("" : "+v"(v));
     return v;
 }
-struct Levels8 {
-    float v[8];
-};
-__device__ __forceinline__ float level(uint32_t byte_index, int lv) {
-    return __int_as_float(__builtin_amdgcn_ds_bpermute((int)byte_index, lv));
+// C[code] for a byte address whose bits 2..5 hold the code: `lv` holds
+// C[lane % 16] in every lane and ds_bpermute returns lane (addr / 4)'s value.
+__device__ __forceinline__ float level(uint32_t addr, int lv) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((int)addr, lv));
 }
-__device__ __forceinline__ Levels8 fetch_levels(uint32_t w, int lv) {
-    const uint32_t e4 = opaque_and(w << 2, 0x3C3C3C3Cu);
-    const uint32_t o4 = opaque_and(w >> 2, 0x3C3C3C3Cu);
-    Levels8 l;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        l.v[2 * j] = level(__builtin_amdgcn_ubfe(e4, 8 * j, 8), lv);
-        l.v[2 * j + 1] = level(__builtin_amdgcn_ubfe(o4, 8 * j, 8), lv);
-    }
-    return l;
+// 4 * nibble e of w as a ds_bpermute byte address (bits 2..5; bits 0..1 are
+// dropped by the lane-index division): bits 4e-2 .. 4e+3 of w.
+__device__ __forceinline__ uint32_t code_addr(uint32_t w, int e) {
+    if (e == 0) return (w << 2) & 0x3Cu;
+    if (e == 7) return w >> 26;
+    return __builtin_amdgcn_ubfe(w, 4 * e - 2, 6);
 }
 
-template <bool DX>
-__global__ __launch_bounds__(256) void nf4_gemm_kernel(GemmArgs p, Nf4Consts tab) {
-    __shared__ uint4 sA0[BM * 8], sA1[BM * 8];  // activation tiles (2 x 64 KiB)
-    __shared__ uint4 sB0[BN * 8], sB1[BN * 8];  // expanded weight tiles (2 x 16 KiB)
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+__device__ __forceinline__ uint4 lds_read16(uint32_t byte_addr) {
+    __builtin_assume((byte_addr & 15) == 0);
+    return __builtin_bit_cast(uint4, *reinterpret_cast<const lds_u32x4 *>(byte_addr));
+}
+__device__ __forceinline__ void lds_write16(uint32_t byte_addr, uint4 v) {
+    __builtin_assume((byte_addr & 15) == 0);
+    *reinterpret_cast<lds_u32x4 *>(byte_addr) = __builtin_bit_cast(u32x4, v);
+}
+__device__ __forceinline__ void lds_write8(uint32_t byte_addr, uint2 v) {
+    *reinterpret_cast<lds_u32x2 *>(byte_addr) = __builtin_bit_cast(u32x2, v);
+}
+__device__ __forceinline__ void lds_write4(uint32_t byte_addr, uint32_t v) {
+    *reinterpret_cast<__attribute__((address_space(3))) uint32_t *>(byte_addr) = v;
+}
 
-    auto At = [&](auto S) __attribute__((always_inline)) -> uint4 * {
+// global -> LDS transfer of 16 bytes per lane: lane l writes LDS bytes
+// [dst + 16 l, +16) (dst is wave-uniform and goes to M0)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void *dst, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, reinterpret_cast<__attribute__((address_space(3))) void *>(reinterpret_cast<uintptr_t>(dst)), 16, voff,
+        soff, 0, 0);
+}
+
+// s_waitcnt immediates (gfx9 encoding): at most `vm` vector-memory operations
+// outstanding, no LDS operation outstanding.
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (0x7 << 4); }
+// at most `vm` vector-memory operations outstanding, LDS operations untouched
+constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// EXPAND: the weight tile of each k-step is expanded from the packed codes in
+// the workgroup (one expansion per output tile row: the choice when the grid
+// has a single tile row).  Otherwise it is transferred like the activation
+// tile from a dequantized bf16 copy written once per call.
+template <bool DX, bool EXPAND>
+__global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Consts tab) {
+    // Two stages of the activation tile [512 rows][64 k] and of the weight tile
+    // [128 rows][64 k] (160 KiB).  One object per buffer so that the compiler can
+    // tell them apart when it places waits for the global->LDS transfers.
+    __shared__ u32x4 sA0[A_STAGE / 16], sA1[A_STAGE / 16];
+    __shared__ u32x4 sB0[B_STAGE / 16], sB1[B_STAGE / 16];
+    auto Aof = [&](auto S) __attribute__((always_inline)) -> u32x4 * {
         if constexpr (decltype(S)::value == 0) return sA0;
         else return sA1;
     };
-    auto Bt = [&](auto S) __attribute__((always_inline)) -> uint4 * {
+    auto Bof = [&](auto S) __attribute__((always_inline)) -> u32x4 * {
         if constexpr (decltype(S)::value == 0) return sB0;
         else return sB1;
     };
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int ml = lane & 31, h = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, g = lane >> 4;
     const int64_t tiles_n = (p.N + BN - 1) / BN, tiles_m = (p.M + BM - 1) / BM;
-    const int64_t t = xcd_remap(blockIdx.x, tiles_m * tiles_n);
-    const int64_t mt = t / tiles_n, nt = t % tiles_n;
+    int64_t mt, nt;
+    tile_of(blockIdx.x, tiles_m, tiles_n, mt, nt);
     const int64_t m_base = mt * BM, n_base = nt * BN;
     const int64_t nK = (p.Kd + BK - 1) / BK;
     const int64_t kb = p.k / 64;  // NF4 blocks per W0 row
@@ -170,325 +213,528 @@ __global__ __launch_bounds__(256) void nf4_gemm_kernel(GemmArgs p, Nf4Consts tab
     for (int j = 1; j < 16; ++j) lvf = (lane & 15) == j ? tab.level[j] : lvf;
     const int lv = __float_as_int(lvf);
 
-    // ---- activation tile: DMA, 8 rows per instruction ---------------------------
-    // instruction i of wave w fills rows 8 g .. 8 g + 7, g = 16 w + i; lane l lands
-    // in slot l = row 8 g + l/8, physical chunk l%8, logical chunk (l%8) ^ (l/8).
+    // ---- activation tile: global -> LDS transfers of 8 rows x 128 B ---------------
+    // Wave w moves and reads only its own rows WM w .. WM w + WM - 1 (transfer b:
+    // rows WM w + 8 b ..).  Lane l lands in row 8 b + l / 8, physical chunk l % 8,
+    // which holds logical chunk (l % 8) ^ ((row >> 1) & 7) = (l % 8) ^ ((l / 16 + 4 b) & 7).
     // Rows past M read as zero.  Pieces past Kd (dX with d % 64 != 0) read the
     // next row's data: finite values that meet weight rows that are exactly zero.
     const int64_t rows_here = (p.M - m_base) < BM ? (p.M - m_base) : BM;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + m_base * p.Kd, rows_here * p.Kd * 2);
-    const uint32_t voff_a =
-        (uint32_t)((((128 * wave + (lane >> 3)) * p.Kd) + 8 * ((lane & 7) ^ (lane >> 3))) * 2);
-    const uint32_t group_bytes = (uint32_t)(8 * p.Kd * 2);
-    auto issue_a = [&](int64_t kt, auto S) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            dma16(ra, At(S) + (16 * wave + i) * 64, voff_a + i * group_bytes + (uint32_t)kt * (BK * 2));
+    const int dma_row = WM * wave + (lane >> 3);  // + 8 b
+    const uint32_t voff_a0 = (uint32_t)(((int64_t)dma_row * p.Kd + 8 * ((lane & 7) ^ ((lane >> 4) & 7))) * 2);
+    const uint32_t voff_a1 = (uint32_t)(((int64_t)dma_row * p.Kd + 8 * ((lane & 7) ^ (((lane >> 4) + 4) & 7))) * 2);
+    const uint32_t row8_bytes = (uint32_t)(8 * p.Kd * 2);
+    auto issue_a = [&](int64_t kt, auto S, int b) __attribute__((always_inline)) {
+        dma16(ra, Aof(S) + (WM * wave + 8 * b) * 8, (b & 1) ? voff_a1 : voff_a0,
+              (uint32_t)b * row8_bytes + (uint32_t)kt * (BK * 2));
+    };
+    // fragment reads (A: row WM w + 16 i + r16; B: row 16 j + r16; chunk 4 s + g),
+    // physical chunk (4 s + g) ^ ((r16 >> 1) & 7) in both tiles
+    const int frag0 = r16 * 8 + ((0 + g) ^ ((r16 >> 1) & 7));  // in 16-byte units
+    const int frag1 = r16 * 8 + ((4 + g) ^ ((r16 >> 1) & 7));
+    const int arow = WM * wave * 8;
+    auto read_a = [&](auto S, int s, int i) __attribute__((always_inline)) -> uint4 {
+        return __builtin_bit_cast(uint4, Aof(S)[arow + (s ? frag1 : frag0) + 128 * i]);
     };
 
-    // ---- weight operand: codes and block scales, register loads -----------------
+    // ---- weight tiles [128 n][64 k], same chunk layout ------------------------------
+    auto read_b = [&](auto S, int s, int j) __attribute__((always_inline)) -> uint4 {
+        return __builtin_bit_cast(uint4, Bof(S)[(s ? frag1 : frag0) + 128 * j]);
+    };
+    // transfer (non-expanding kernel): rows n_base .., 8 per transfer, wave w moves
+    // rows 16 w .. 16 w + 15; rows past N read as zero
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(p.wbf + n_base * p.ldw, EXPAND ? 0 : ((p.N - n_base) < BN ? (p.N - n_base) : BN) * p.ldw * 2);
+    const int wrow = 16 * wave + (lane >> 3);  // + 8 u
+    const uint32_t voff_w0 = (uint32_t)(((int64_t)wrow * p.ldw + 8 * ((lane & 7) ^ ((lane >> 4) & 7))) * 2);
+    const uint32_t voff_w1 = (uint32_t)(((int64_t)wrow * p.ldw + 8 * ((lane & 7) ^ (((lane >> 4) + 4) & 7))) * 2);
+    const uint32_t wrow8_bytes = (uint32_t)(8 * p.ldw * 2);
+    auto issue_w = [&](int64_t kt, auto S, int u) __attribute__((always_inline)) {
+        dma16(rw, Bof(S) + (16 * wave + 8 * u) * 8, u ? voff_w1 : voff_w0,
+              (uint32_t)u * wrow8_bytes + (uint32_t)kt * (BK * 2));
+    };
+
+    // ---- weight data (expanding kernel): codes and block scales, register loads ------
+    // forward: thread t -> weight row n_base + t/4, k = 16 (t%4) .. +15 of the step
+    //   (rows past d clamp to d-1: finite values in columns never stored)
+    // dX: thread t -> W0 rows kt*64 + 2 (t/16) .. +1, columns n_base + 8 (t%16) .. +7
+    //   (rows past d read as zero codes and zero scales: exactly zero weights)
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.codes, p.d * p.k / 2);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.shat, p.d * kb * 4);
-    // forward: thread t -> weight row n_base + t/2, k = 32 (t%2) .. +31 of the step
-    //   (rows past d clamp to d-1: finite values in columns never stored)
-    // dX: thread t -> W0 rows kt*64 + 4 (t/16) .. +3, columns n_base + 8 (t%16) .. +7
-    //   (rows past d read as zero codes and zero scales: exactly zero weights)
     struct Wdata {
-        uint32_t c[4];
-        float s[4];
+        uint32_t c[2];
+        float s[2];
     };
-    uint32_t voff_c[4], voff_s[4];
-    uint32_t step_c, step_s;
+    uint32_t voff_c, voff_s, step_c, step_s, row_c = 0, row_s = 0;
+    uint32_t wr_off[8];  // stage-relative LDS offsets of this thread's expansion writes
+                         // (forward: 16-byte units; dX: 4-byte units)
     if constexpr (!DX) {
-        int64_t n = n_base + (tid >> 1);
+        int64_t n = n_base + (tid >> 2);
         n = n < p.d ? n : p.d - 1;
-        voff_c[0] = (uint32_t)(n * kb * 32 + 16 * (tid & 1));
-        voff_s[0] = (uint32_t)(n * kb * 4);
+        voff_c = (uint32_t)(n * kb * 32 + 8 * (tid & 3));
+        voff_s = (uint32_t)(n * kb * 4);
         step_c = 32;
         step_s = 4;
+        const int row = tid >> 2;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) wr_off[c] = (uint32_t)(row * 8 + ((2 * (tid & 3) + c) ^ ((row >> 1) & 7)));
+#pragma unroll
+        for (int c = 2; c < 8; ++c) wr_off[c] = 0;
     } else {
         const int rg = tid >> 4, cg = tid & 15;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int64_t row = 4 * rg + e;
-            voff_c[e] = (uint32_t)((row * p.k + n_base + 8 * cg) / 2);
-            voff_s[e] = (uint32_t)((row * kb + (n_base + 8 * cg) / 64) * 4);
-        }
+        voff_c = (uint32_t)(((int64_t)(2 * rg) * p.k + n_base + 8 * cg) / 2);
+        voff_s = (uint32_t)(((int64_t)(2 * rg) * kb + (n_base + 8 * cg) / 64) * 4);
+        row_c = (uint32_t)(p.k / 2);
+        row_s = (uint32_t)(kb * 4);
         step_c = (uint32_t)(64 * p.k / 2);
         step_s = (uint32_t)(64 * kb * 4);
+        // column f of the thread's 8 -> tile row n = 8 cg + f, k = 2 rg, 2 rg + 1
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+            const int n = 8 * cg + f;
+            wr_off[f] = (uint32_t)(n * 32 + 4 * ((rg >> 2) ^ ((n >> 1) & 7)) + (rg & 3));
+        }
     }
     auto load_w = [&](int64_t kt, Wdata &wd) __attribute__((always_inline)) {
         const uint32_t k32 = (uint32_t)kt;
         if constexpr (!DX) {
-            const uint4 c = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, voff_c[0] + k32 * step_c, 0, 0));
-            wd.c[0] = c.x; wd.c[1] = c.y; wd.c[2] = c.z; wd.c[3] = c.w;
-            wd.s[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff_s[0] + k32 * step_s, 0, 0));
+            const uint2 c = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rc, voff_c, k32 * step_c, 0));
+            wd.c[0] = c.x;
+            wd.c[1] = c.y;
+            wd.s[0] = __uint_as_float(load4(rs, voff_s, k32 * step_s));
+            wd.s[1] = 0.0f;
         } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                wd.c[e] = __builtin_amdgcn_raw_buffer_load_b32(rc, voff_c[e] + k32 * step_c, 0, 0);
-                wd.s[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff_s[e] + k32 * step_s, 0, 0));
+            for (int e = 0; e < 2; ++e) {
+                wd.c[e] = load4(rc, voff_c, k32 * step_c + e * row_c);
+                wd.s[e] = __uint_as_float(load4(rs, voff_s, k32 * step_s + e * row_s));
             }
         }
     };
-    constexpr int kWloads = DX ? 8 : 2;  // register loads per thread per step
 
-    // ---- expansion of one step's weight tile into LDS (4 slices) ----------------
-    auto expand_slice = [&](const Wdata &wd, int c, auto SB) __attribute__((always_inline)) {
+    constexpr int kWloads = EXPAND ? (DX ? 4 : 2) : 0;  // register loads of weight data per step
+
+    // One 8-weight piece of the expansion in three phases spread over MFMA
+    // groups: 0 = code lookups, 1 = scale multiplies, 2 = bf16 pack + LDS write.
+    // forward piece c: 8 consecutive k of one row (code word c).
+    // dX piece c: columns 4c .. 4c+3 of the thread's 8, two k-consecutive rows each.
+    float lvl[8];
+    auto expand_phase = [&](const Wdata &wd, int c, int phase, u32x4 *stage) __attribute__((always_inline)) {
         if constexpr (!DX) {
-            const Levels8 l = fetch_levels(pin(wd.c[c]), lv);
-            const float sc = pin(wd.s[0]);
-            uint4 o;
-            o.x = pack_bf16x2(l.v[0] * sc, l.v[1] * sc);
-            o.y = pack_bf16x2(l.v[2] * sc, l.v[3] * sc);
-            o.z = pack_bf16x2(l.v[4] * sc, l.v[5] * sc);
-            o.w = pack_bf16x2(l.v[6] * sc, l.v[7] * sc);
-            Bt(SB)[swz(tid >> 1, 4 * (tid & 1) + c)] = o;
+            if (phase == 0) {
+                const uint32_t x = pin(wd.c[c]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) lvl[e] = level(code_addr(x, e), lv);
+            } else if (phase == 1) {
+                const float sc = pin(wd.s[0]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) lvl[e] = lvl[e] * sc;
+            } else {
+                const uint4 o{pack_bf16x2(lvl[0], lvl[1]), pack_bf16x2(lvl[2], lvl[3]),
+                              pack_bf16x2(lvl[4], lvl[5]), pack_bf16x2(lvl[6], lvl[7])};
+                stage[wr_off[c]] = __builtin_bit_cast(u32x4, o);
+            }
         } else {
-            // columns 2c, 2c+1 of this thread's 8; 4 k-consecutive values each
-            const int rg = tid >> 4, cg = tid & 15;
-            uint32_t cw[4];
-            float sc[4];
+            if (phase == 0) {
+                const uint32_t x0 = pin(wd.c[0]), x1 = pin(wd.c[1]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                cw[e] = pin(wd.c[e]);
-                sc[e] = pin(wd.s[e]);
-            }
-#pragma unroll
-            for (int f = 2 * c; f < 2 * c + 2; ++f) {
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = level(4 * __builtin_amdgcn_ubfe(cw[e], 4 * f, 4), lv) * sc[e];
-                const uint2 o = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-                const int n = 8 * cg + f;
-                uint2 *dst = reinterpret_cast<uint2 *>(Bt(SB) + swz(n, rg >> 1)) + (rg & 1);
-                *dst = o;
-            }
-        }
-    };
-
-    f32x16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-    auto read_a = [&](auto S, int ks, uint4 (&a)[4]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = At(S)[swz(128 * wave + 32 * i + ml, 4 * h + ks)];
-    };
-    auto read_b = [&](auto S, int ks, uint4 (&b)[4]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = Bt(S)[swz(32 * j + ml, 4 * h + ks)];
-    };
-    auto mfma_slice = [&](const uint4 (&a)[4], const uint4 (&b)[4]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
-    };
-    auto slices = [&](auto S, auto expand) __attribute__((always_inline)) {
-        uint4 a[4], b[4];
-        read_a(S, 0, a);
-        read_b(S, 0, b);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            uint4 an[4], bn[4];
-            if (ks < 3) {
-                read_a(S, ks + 1, an);
-                read_b(S, ks + 1, bn);
-            }
-            mfma_slice(a, b);
-            expand(ks);
-            if (ks < 3) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    a[i] = an[i];
-                    b[i] = bn[i];
+                for (int q = 0; q < 4; ++q) {
+                    lvl[2 * q] = level(code_addr(x0, 4 * c + q), lv);
+                    lvl[2 * q + 1] = level(code_addr(x1, 4 * c + q), lv);
                 }
+            } else if (phase == 1) {
+                const float s0 = pin(wd.s[0]), s1 = pin(wd.s[1]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    lvl[2 * q] = lvl[2 * q] * s0;
+                    lvl[2 * q + 1] = lvl[2 * q + 1] * s1;
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    reinterpret_cast<uint32_t *>(stage)[wr_off[4 * c + q]] = pack_bf16x2(lvl[2 * q], lvl[2 * q + 1]);
             }
         }
     };
 
-    // One step kt (S = kt % 2): MFMAs on tiles S; A(kt+1) DMA into tile S^1 (last
-    // read in step kt-1); expand step kt+1 (weights loaded two steps ago, `wcur`)
-    // into weight tile S^1; load the weight data of step kt+3 into `wnext`.
-    // Indices past the last step repeat it (uniform operation counts).  Barrier
-    // once this wave's A DMA has landed (its newer weight loads may be in flight).
-    auto step = [&](int64_t kt, auto S, const Wdata &wcur, Wdata &wnext) __attribute__((always_inline)) {
-        using S1 = IC<1 - decltype(S)::value>;
-        issue_a(kt + 1 < nK ? kt + 1 : nK - 1, S1{});
-        load_w(kt + 3 < nK ? kt + 3 : nK - 1, wnext);
-        slices(S, [&](int ks) __attribute__((always_inline)) { expand_slice(wcur, ks, S1{}); });
+    // Accumulators: first written by step 0 (MFMA with a zero addend), then
+    // accumulated in place (mfma16_acc).
+    f32x4 acc[MI][8];
+    uint4 af[2][MI];   // activation fragments: current slice, next slice
+    uint4 bq[4];       // weight fragments, two groups ahead
+    Wdata w0, w1, w2;  // weight data, rotating over three steps
+
+    auto Wset = [&](auto W) __attribute__((always_inline)) -> Wdata & {
+        if constexpr (decltype(W)::value == 0) return w0;
+        else if constexpr (decltype(W)::value == 1) return w1;
+        else return w2;
+    };
+
+    // One k-step kt with R = kt % 6 (every buffer index static), S = kt % 2:
+    //  * MFMAs on tiles A[S], B[S]; A fragments of slice 1 read during slice 0;
+    //  * transfers A(kt+1) into A[S^1];
+    //  * non-expanding: transfers the weight tile of step kt+1 into B[S^1];
+    //    expanding: loads the weight data of step kt+3 into set kt % 3 and
+    //    expands step kt+1 (set (kt+1) % 3) into B[S^1];
+    //  * waits for its own transfers, reads the first A fragments of step kt+1,
+    //    then meets the other waves at the barrier.
+    // Indices past the last step repeat it (uniform operation counts).
+    auto step = [&](int64_t kt, auto RR, auto FIRST) __attribute__((always_inline)) {
+        constexpr int R = decltype(RR)::value;
+        constexpr bool first = decltype(FIRST)::value != 0;
+        using S = IC<R % 2>;
+        using S1 = IC<1 - R % 2>;
+        const Wdata &wc = Wset(IC<(R + 1) % 3>{});
+        Wdata &wl = Wset(IC<R % 3>{});
+        u32x4 *const st_w = Bof(S1{});
+        const int64_t kn = kt + 1 < nK ? kt + 1 : nK - 1;
+        const int64_t kw = kt + 3 < nK ? kt + 3 : nK - 1;
+#pragma unroll
+        for (int grp = 0; grp < 16; ++grp) {
+            const int s = grp >> 3, j = grp & 7;
+            if (grp + 2 < 16) bq[(grp + 2) & 3] = read_b(S{}, (grp + 2) >> 3, (grp + 2) & 7);
+            if (grp == 0) {
+#pragma unroll
+                for (int i = 0; i < MI; ++i) af[1][i] = read_a(S{}, 1, i);
+            }
+            if constexpr (EXPAND) {
+                if (grp < 8) issue_a(kn, S1{}, grp);
+                if (grp == 8) load_w(kw, wl);  // after the transfers: the end-of-step wait counts on it
+                if (j == 1) expand_phase(wc, s, 0, st_w);
+                if (j == 4) expand_phase(wc, s, 1, st_w);
+                if (j == 6) expand_phase(wc, s, 2, st_w);
+            } else {
+                if (grp < 2) issue_w(kn, S1{}, grp);
+                if (grp >= 2 && grp < 10) issue_a(kn, S1{}, grp - 2);
+            }
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                if (first && s == 0) acc[i][j] = mfma16(bq[grp & 3], af[s][i], f32x4{0.f, 0.f, 0.f, 0.f});
+                else mfma16_acc(bq[grp & 3], af[s][i], acc[i][j]);
+            }
+            sched_fence();
+        }
+        // this wave's transfers of step kt+1 landed (the weight-data loads of
+        // this step, issued after them, may still be in flight); expansion
+        // writes done
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kWloads));
+#pragma unroll
+        for (int i = 0; i < MI; ++i) af[0][i] = read_a(S1{}, 0, i);
         __builtin_amdgcn_s_barrier();
-    };
-    auto last_step = [&](auto S) __attribute__((always_inline)) {
-        slices(S, [&](int) __attribute__((always_inline)) {});
+        bq[0] = read_b(S1{}, 0, 0);
+        bq[1] = read_b(S1{}, 0, 1);
+        sched_fence();
     };
 
-    // ---- prologue: A(0) and weight tile 0 ready; weights of steps 1, 2 loaded ----
-    Wdata w0, w1, w2;
-    issue_a(0, IC<0>{});
-    load_w(0, w0);
-    load_w(nK > 1 ? 1 : nK - 1, w1);
-    load_w(nK > 2 ? 2 : nK - 1, w2);
+    // ---- prologue: A(0) and weight tile 0 in LDS; weight data of steps 1, 2 loaded ----
+    if constexpr (EXPAND) {
+        load_w(0, w0);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) expand_slice(w0, c, IC<0>{});
+        for (int b = 0; b < 8; ++b) issue_a(0, IC<0>{}, b);
+        load_w(nK > 1 ? 1 : 0, w1);
+        load_w(nK > 2 ? 2 : nK - 1, w2);
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int ph = 0; ph < 3; ++ph) expand_phase(w0, c, ph, sB0);
+    } else {
+        issue_w(0, IC<0>{}, 0);
+        issue_w(0, IC<0>{}, 1);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) issue_a(0, IC<0>{}, b);
+    }
     __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) af[0][i] = read_a(IC<0>{}, 0, i);
     __syncthreads();
+    bq[0] = read_b(IC<0>{}, 0, 0);
+    bq[1] = read_b(IC<0>{}, 0, 1);
 
-    // ---- main k-loop: 2 steps per trip; three rotating weight-data registers ----
-    // step kt consumes weights of kt+1 and loads kt+3: w1 -> (kt+1), w2 -> (kt+2), w0 -> (kt+3)
-    int64_t kt = 0;
-    for (; kt + 6 < nK; kt += 6) {
-        step(kt + 0, IC<0>{}, w1, w0);
-        step(kt + 1, IC<1>{}, w2, w1);
-        step(kt + 2, IC<0>{}, w0, w2);
-        step(kt + 3, IC<1>{}, w1, w0);
-        step(kt + 4, IC<0>{}, w2, w1);
-        step(kt + 5, IC<1>{}, w0, w2);
+    // ---- main k-loop: step 0 peeled, then six steps per trip -------------------------
+    step(0, IC<0>{}, IC<1>{});
+    int64_t kt = 1;
+    for (; kt + 6 <= nK; kt += 6) {
+        step(kt + 0, IC<1>{}, IC<0>{});
+        step(kt + 1, IC<2>{}, IC<0>{});
+        step(kt + 2, IC<3>{}, IC<0>{});
+        step(kt + 3, IC<4>{}, IC<0>{});
+        step(kt + 4, IC<5>{}, IC<0>{});
+        step(kt + 5, IC<0>{}, IC<0>{});
     }
-    // remaining steps (kt % 6 == 0): all but the last are full steps
-    const int64_t rem = nK - kt;  // 1 .. 6
-    if (rem >= 2) step(kt + 0, IC<0>{}, w1, w0);
-    if (rem >= 3) step(kt + 1, IC<1>{}, w2, w1);
-    if (rem >= 4) step(kt + 2, IC<0>{}, w0, w2);
-    if (rem >= 5) step(kt + 3, IC<1>{}, w1, w0);
-    if (rem >= 6) step(kt + 4, IC<0>{}, w2, w1);
-    if (rem & 1) last_step(IC<0>{});
-    else last_step(IC<1>{});
+    if (kt < nK) step(kt, IC<1>{}, IC<0>{});
+    if (kt + 1 < nK) step(kt + 1, IC<2>{}, IC<0>{});
+    if (kt + 2 < nK) step(kt + 2, IC<3>{}, IC<0>{});
+    if (kt + 3 < nK) step(kt + 3, IC<4>{}, IC<0>{});
+    if (kt + 4 < nK) step(kt + 4, IC<5>{}, IC<0>{});
 
-    // ---- adapter term: extra k-steps [hi(sV) | lo(sV)] x [W' | W'] --------------
-    // Both tiles go through LDS in the main-loop layouts: A' in sA0 (thread t
-    // fills tile rows t, t + 256), W' in sB0 (thread t fills weight-tile row
-    // t/2, k = 32 (t%2) .. +31).
-    const int r = p.r, r2 = 2 * p.r;
-    __builtin_amdgcn_s_waitcnt(0);  // no DMA still in flight
-    for (int e0 = 0; e0 < r2; e0 += BK) {
+    // ---- adapter term: Ke/64 extra k-steps, operands laid out in memory ------------
+    {
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        const __amdgpu_buffer_rsrc_t rea = make_rsrc(p.ext_a + m_base * p.Ke, rows_here * p.Ke * 2);
+        const uint32_t voff_e0 = (uint32_t)(((int64_t)dma_row * p.Ke + 8 * ((lane & 7) ^ ((lane >> 4) & 7))) * 2);
+        const uint32_t voff_e1 = (uint32_t)(((int64_t)dma_row * p.Ke + 8 * ((lane & 7) ^ (((lane >> 4) + 4) & 7))) * 2);
+        const uint32_t row8_e = (uint32_t)(8 * p.Ke * 2);
+        // weight-side operand rows n_base .. +127 (clamped to N-1): transfer u of
+        // wave w covers rows 16 w + 8 u .. + 7
+        const __amdgpu_buffer_rsrc_t reb = make_rsrc(p.ext_b, p.N * p.Ke * 2);
+        uint32_t voff_eb[2];
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-            const int row = tid + 256 * rr;
-            int64_t m = m_base + row;
-            m = m < p.M ? m : p.M - 1;
-#pragma unroll
-            for (int ch = 0; ch < 8; ++ch) {
-                uint32_t wv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    uint32_t pr = 0;
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const int kk = e0 + 8 * ch + 2 * e + hh;
-                        uint32_t bits = 0;
-                        if (kk < r2) {
-                            const float v = p.s * p.ext_v[m * r + (kk < r ? kk : kk - r)];
-                            const uint32_t hb = pack_bf16x2(v, 0.0f) & 0xFFFFu;
-                            bits = kk < r ? hb : (pack_bf16x2(v - bf16_bits_to_f32(hb), 0.0f) & 0xFFFFu);
-                        }
-                        pr |= bits << (16 * hh);
-                    }
-                    wv[e] = pr;
-                }
-                sA0[swz(row, ch)] = uint4{wv[0], wv[1], wv[2], wv[3]};
-            }
-        }
-        {
-            int64_t n = n_base + (tid >> 1);
+        for (int u = 0; u < 2; ++u) {
+            const int row = 16 * wave + 8 * u + (lane >> 3);
+            int64_t n = n_base + row;
             n = n < p.N ? n : p.N - 1;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                uint32_t wv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    uint32_t pr = 0;
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const int kk = e0 + 32 * (tid & 1) + 8 * c + 2 * e + hh;
-                        uint32_t bits = 0;
-                        if (kk < r2) {
-                            const int jj = kk < r ? kk : kk - r;
-                            bits = DX ? p.ext_w[(int64_t)jj * p.k + n] : p.ext_w[n * r + jj];
-                        }
-                        pr |= bits << (16 * hh);
-                    }
-                    wv[e] = pr;
-                }
-                sB0[swz(tid >> 1, 4 * (tid & 1) + c)] = uint4{wv[0], wv[1], wv[2], wv[3]};
-            }
+            voff_eb[u] = (uint32_t)((n * p.Ke + 8 * ((lane & 7) ^ ((row >> 1) & 7))) * 2);
         }
-        __syncthreads();
-        last_step(IC<0>{});
+        const int64_t nE = p.Ke / BK;
+        for (int64_t e = 0; e < nE; ++e) {
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+                dma16(rea, sA0 + (WM * wave + 8 * b) * 8, (b & 1) ? voff_e1 : voff_e0,
+                      (uint32_t)b * row8_e + (uint32_t)e * (BK * 2));
+#pragma unroll
+            for (int u = 0; u < 2; ++u) dma16(reb, sB0 + (16 * wave + 8 * u) * 8, voff_eb[u], (uint32_t)e * (BK * 2));
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+#pragma unroll
+                for (int i = 0; i < MI; ++i) af[0][i] = read_a(IC<0>{}, s, i);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint4 b = read_b(IC<0>{}, s, j);
+#pragma unroll
+                    for (int i = 0; i < MI; ++i) mfma16_acc(b, af[0][i], acc[i][j]);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        // the epilogue reads the accumulators with VALU instructions: let the
+        // last MFMAs (inline asm, invisible to the hazard recognizer) drain
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
     }
 
-    // ---- epilogue: fp32 -> bf16 ----------------------------------------------------
+    // ---- epilogue: lane holds D[m = 16 i + r16][n = 16 j + 4 g .. + 3] ----------------
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t n = n_base + 32 * j + ml;
-        if (n >= p.N) continue;
+    for (int i = 0; i < MI; ++i) {
+        const int64_t m = m_base + WM * wave + 16 * i + r16;
+        if (m >= p.M) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t m = m_base + 128 * wave + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (m < p.M) p.out[m * p.N + n] = (uint16_t)(pack_bf16x2(acc[i][j][v], 0.0f) & 0xFFFFu);
-            }
+        for (int j = 0; j < 8; ++j) {
+            const int64_t n = n_base + 16 * j + 4 * g;
+            if (n >= p.N) continue;
+            const uint2 o{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
+            *reinterpret_cast<uint2 *>(p.out + m * p.N + n) = o;
+        }
     }
 }
 
-// dequantized block scales: shat[j] = fp32(c2[j] / c1[j / 256]) + mean
-__global__ __launch_bounds__(256) void dq_scales_kernel(const int8_t *__restrict__ c2,
-                                                        const float *__restrict__ c1,
-                                                        const float *__restrict__ mean_p, int64_t nb,
-                                                        float *__restrict__ shat) {
-    const float mean = *mean_p;
-    for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < nb; j += (int64_t)gridDim.x * 256)
-        shat[j] = dq_scale(c2[j], c1[j >> 8], mean);
+// Preparation, one launch over three index ranges:
+//   shat[j] = fp32(c2[j] / c1[j / 256]) + mean                    (j < nb)
+//   ext_a[m][c] = hi(s V[m][c]), lo(s V[m][c - r]) or 0 by column  (M x Ke)
+//   ext_b[n][c] = W'[n][c mod r] for c < 2r, else 0                (N x Ke)
+// where W'[n][j] = B[n][j] (forward, B [d x r]) or A[j][n] (dX, A [r x k]).
+struct PrepArgs {
+    const int8_t *c2;
+    const float *c1;
+    const float *mean;
+    int64_t nb;
+    float *shat;
+    const float *V;
+    int64_t M;
+    int r;
+    float s;
+    uint16_t *ext_a;
+    const uint16_t *W;
+    int64_t N;
+    int dx;
+    uint16_t *ext_b;
+    int64_t Ke;
+};
+
+__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
+    const int64_t na = a.M * a.Ke, nbx = a.N * a.Ke;
+    const int64_t total = a.nb + na + nbx;
+    const float mean = *a.mean;
+    for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < total; x += (int64_t)gridDim.x * 256) {
+        if (x < a.nb) {
+            a.shat[x] = dq_scale(a.c2[x], a.c1[x >> 8], mean);
+        } else if (x < a.nb + na) {
+            const int64_t y = x - a.nb, m = y / a.Ke;
+            const int c = (int)(y % a.Ke);
+            uint16_t bits = 0;
+            if (c < 2 * a.r) {
+                const float v = a.s * a.V[m * a.r + (c < a.r ? c : c - a.r)];
+                const uint32_t hb = pack_bf16x2(v, 0.0f) & 0xFFFFu;
+                bits = (uint16_t)(c < a.r ? hb : (pack_bf16x2(v - bf16_bits_to_f32(hb), 0.0f) & 0xFFFFu));
+            }
+            a.ext_a[y] = bits;
+        } else {
+            const int64_t y = x - a.nb - na, n = y / a.Ke;
+            const int c = (int)(y % a.Ke);
+            uint16_t bits = 0;
+            if (c < 2 * a.r) {
+                const int jj = c < a.r ? c : c - a.r;
+                bits = a.dx ? a.W[(int64_t)jj * a.N + n] : a.W[n * a.r + jj];
+            }
+            a.ext_b[y] = bits;
+        }
+    }
+}
+
+// Dequantized weight operand for the non-expanding GEMM: What [d x k]
+// (forward) or What^T [k x ldw] with zero columns d .. ldw-1 (dX), bf16,
+// bit-identical to qlora_nf4_dequantize.  One workgroup per 64 x 64 tile
+// (64 rows of W0 = one NF4 block each): thread t expands row t/4, k = 16 (t%4)
+// .. +15.  The transposed form goes through LDS so both the reads of the codes
+// and the writes of the rows of What^T are contiguous.
+template <bool T>
+__global__ __launch_bounds__(256) void dequant_tile_kernel(const uint8_t *__restrict__ codes,
+                                                           const float *__restrict__ shat, int64_t d, int64_t k,
+                                                           int64_t ldw, Nf4Consts tab, uint16_t *__restrict__ out) {
+    __shared__ uint16_t tile[64][64 + 8];  // [k][d-row] (+8: spread the banks)
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int64_t kb = k / 64;
+    const int64_t tk = blockIdx.x % kb, td = blockIdx.x / kb;
+    const int row = tid >> 2, q = tid & 3;
+    const int64_t n = td * 64 + row;  // W0 row
+    float lvf = tab.level[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) lvf = (lane & 15) == j ? tab.level[j] : lvf;
+    const int lv = __float_as_int(lvf);
+    uint32_t v[8];
+    if (n < d) {
+        const uint2 c = *reinterpret_cast<const uint2 *>(codes + n * (k / 2) + tk * 32 + 8 * q);
+        const float sc = shat[n * kb + tk];
+        const uint32_t cw[2] = {c.x, c.y};
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[4 * h + e] = pack_bf16x2(level(code_addr(cw[h], 2 * e), lv) * sc, level(code_addr(cw[h], 2 * e + 1), lv) * sc);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0;
+    }
+    if constexpr (!T) {
+        if (n < d) {
+            uint4 *dst = reinterpret_cast<uint4 *>(out + n * k + tk * 64 + 16 * q);
+            dst[0] = uint4{v[0], v[1], v[2], v[3]};
+            dst[1] = uint4{v[4], v[5], v[6], v[7]};
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            tile[16 * q + 2 * e][row] = (uint16_t)(v[e] & 0xFFFFu);
+            tile[16 * q + 2 * e + 1][row] = (uint16_t)(v[e] >> 16);
+        }
+        __syncthreads();
+        // row kk of What^T: 64 values (128 B) = 8 threads x 16 B; 256 threads -> 32 rows per pass
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const int kk = 32 * pass + (tid >> 3), c8 = tid & 7;
+            const int64_t col = td * 64 + 8 * c8;
+            if (col < ldw) {
+                const uint16_t *src = &tile[kk][8 * c8];
+                uint4 o;
+                o.x = src[0] | ((uint32_t)src[1] << 16);
+                o.y = src[2] | ((uint32_t)src[3] << 16);
+                o.z = src[4] | ((uint32_t)src[5] << 16);
+                o.w = src[6] | ((uint32_t)src[7] << 16);
+                *reinterpret_cast<uint4 *>(out + (tk * 64 + kk) * ldw + col) = o;
+            }
+        }
+    }
 }
 
 hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, const float *V,
-                  const uint16_t *ext_w, int r, float s, uint16_t *out, float *shat, hipStream_t st) {
-    const int64_t nb = w.d * w.k / 64;
-    int64_t g = (nb + 255) / 256;
-    if (g > 2048) g = 2048;
-    hipLaunchKernelGGL(dq_scales_kernel, dim3((unsigned)g), dim3(256), 0, st, w.c2, w.c1, w.mean, nb, shat);
+                  const uint16_t *ext_w, int r, float s, uint16_t *out, const GemmWs &ws,
+                  hipStream_t st) {
     GemmArgs p;
     p.a = a;
     p.M = M;
     p.N = dx ? w.k : w.d;
     p.Kd = dx ? w.d : w.k;
     p.codes = w.codes;
-    p.shat = shat;
+    p.shat = ws.shat;
     p.d = w.d;
     p.k = w.k;
-    p.ext_v = V;
-    p.ext_w = ext_w;
-    p.r = r;
-    p.s = s;
+    p.ext_a = ws.ext_a;
+    p.ext_b = ws.ext_b;
+    p.Ke = gemm_ext_cols(r);
+    p.wbf = ws.wbf;
+    p.ldw = dx ? (w.d + 63) / 64 * 64 : w.k;
     p.out = out;
-    const int64_t tiles = ((M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-    if (dx)
-        hipLaunchKernelGGL(nf4_gemm_kernel<true>, dim3((unsigned)tiles), dim3(256), 0, st, p, nf4_consts());
-    else
-        hipLaunchKernelGGL(nf4_gemm_kernel<false>, dim3((unsigned)tiles), dim3(256), 0, st, p, nf4_consts());
+    // 32-bit buffer offsets: a 512-row slab of the activation operand and the
+    // whole adapter operand must stay below 2 GiB
+    if ((int64_t)BM * p.Kd * 2 >= (int64_t(1) << 31) || p.N * p.Ke * 2 >= (int64_t(1) << 31) ||
+        (int64_t)BM * p.Ke * 2 >= (int64_t(1) << 31))
+        return hipErrorInvalidValue;
+
+    PrepArgs q;
+    q.c2 = w.c2;
+    q.c1 = w.c1;
+    q.mean = w.mean;
+    q.nb = w.d * w.k / 64;
+    q.shat = ws.shat;
+    q.V = V;
+    q.M = M;
+    q.r = r;
+    q.s = s;
+    q.ext_a = ws.ext_a;
+    q.W = ext_w;
+    q.N = p.N;
+    q.dx = dx ? 1 : 0;
+    q.ext_b = ws.ext_b;
+    q.Ke = p.Ke;
+    const int64_t total = q.nb + M * p.Ke + p.N * p.Ke;
+    int64_t g = (total + 255) / 256;
+    if (g > 4096) g = 4096;
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)g), dim3(256), 0, st, q);
+
+    const int64_t tiles_m = (M + BM - 1) / BM, tiles = tiles_m * ((p.N + BN - 1) / BN);
+    const dim3 grid((unsigned)tiles), block(NTHREADS);
+    if (tiles_m == 1) {
+        if (dx) hipLaunchKernelGGL((nf4_gemm_kernel<true, true>), grid, block, 0, st, p, nf4_consts());
+        else hipLaunchKernelGGL((nf4_gemm_kernel<false, true>), grid, block, 0, st, p, nf4_consts());
+    } else {
+        // dequantized copy of the weight operand, once per call
+        const int64_t rows = dx ? w.k : w.d, cols = dx ? p.ldw : w.k;
+        const dim3 tgrid((unsigned)((w.k / 64) * ((w.d + 63) / 64)));
+        if (dx)
+            hipLaunchKernelGGL(dequant_tile_kernel<true>, tgrid, dim3(256), 0, st, w.codes, ws.shat, w.d, w.k, p.ldw,
+                               nf4_consts(), ws.wbf);
+        else
+            hipLaunchKernelGGL(dequant_tile_kernel<false>, tgrid, dim3(256), 0, st, w.codes, ws.shat, w.d, w.k, p.ldw,
+                               nf4_consts(), ws.wbf);
+        (void)rows;
+        (void)cols;
+        if (dx) hipLaunchKernelGGL((nf4_gemm_kernel<true, false>), grid, block, 0, st, p, nf4_consts());
+        else hipLaunchKernelGGL((nf4_gemm_kernel<false, false>), grid, block, 0, st, p, nf4_consts());
+    }
     return hipGetLastError();
 }
 
 }  // namespace
 
+int64_t gemm_ext_cols(int r) { return (2 * (int64_t)r + BK - 1) / BK * BK; }
+
+int64_t gemm_wbf_elems(int64_t M, int64_t d, int64_t k) {
+    return (M + BM - 1) / BM > 1 ? k * ((d + 63) / 64 * 64) : 0;
+}
+
 hipError_t launch_gemm_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, const float *U,
-                           const uint16_t *B, int r, float s, uint16_t *Y, float *shat_ws,
+                           const uint16_t *B, int r, float s, uint16_t *Y, const GemmWs &ws,
                            hipStream_t st) {
-    return launch(false, w, x, M, U, B, r, s, Y, shat_ws, st);
+    return launch(false, w, x, M, U, B, r, s, Y, ws, st);
 }
 
 hipError_t launch_gemm_dx(const Nf4Weights &w, const uint16_t *dy, int64_t M, const float *G,
-                          const uint16_t *A, int r, float s, uint16_t *dX, float *shat_ws,
+                          const uint16_t *A, int r, float s, uint16_t *dX, const GemmWs &ws,
                           hipStream_t st) {
-    return launch(true, w, dy, M, G, A, r, s, dX, shat_ws, st);
+    return launch(true, w, dy, M, G, A, r, s, dX, ws, st);
 }
 
 }  // namespace qnf4

@@ -40,14 +40,26 @@ struct Nf4Weights {
     const float *mean;
     int64_t d, k;
 };
+// Workspace of one dequant-GEMM call: the dequantized block scales
+// (d*k/64 floats) and the adapter operands laid out as extra k-columns,
+// ext_a [M x Ke] and ext_b [N x Ke] bf16 with Ke = gemm_ext_cols(r).
+// wbf: dequantized bf16 copy of the weight operand, used when the output has
+// more than one 512-row tile row (gemm_wbf_elems(M, d, k) elements, else 0).
+struct GemmWs {
+    float *shat;
+    uint16_t *ext_a;
+    uint16_t *ext_b;
+    uint16_t *wbf;
+};
+int64_t gemm_ext_cols(int r);
+int64_t gemm_wbf_elems(int64_t M, int64_t d, int64_t k);
 // Y[M x d] = bf16( X[M x k] What^T + [hi(sU) | lo(sU)] [B | B]^T ),  U [M x r] fp32.
-// shat_ws: workspace of d*k/64 floats for the dequantized block scales.
 hipError_t launch_gemm_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, const float *U,
-                           const uint16_t *B, int r, float s, uint16_t *Y, float *shat_ws,
+                           const uint16_t *B, int r, float s, uint16_t *Y, const GemmWs &ws,
                            hipStream_t st);
 // dX[M x k] = bf16( dY[M x d] What + [hi(sG) | lo(sG)] [A ; A] ),  G [M x r] fp32
 hipError_t launch_gemm_dx(const Nf4Weights &w, const uint16_t *dy, int64_t M, const float *G,
-                          const uint16_t *A, int r, float s, uint16_t *dX, float *shat_ws,
+                          const uint16_t *A, int r, float s, uint16_t *dX, const GemmWs &ws,
                           hipStream_t st);
 
 }  // namespace qnf4
