@@ -73,7 +73,10 @@ LinWs lin_ws(int64_t M, int64_t d, int64_t k, int r) {
     l.part = off;
     const size_t pd = sizeof(float) * cols_skinny_splits(M, d) * d * 2 * r;
     const size_t pk = sizeof(float) * cols_skinny_splits(M, k) * k * 2 * r;
-    off += round_up(pd > pk ? pd : pk, 256);
+    const size_t pv = sizeof(float) * cols_valu_splits(M) * (round_up(d, 64) + k) * r;
+    size_t part_bytes = pd > pk ? pd : pk;
+    if (r <= 16 && pv > part_bytes) part_bytes = pv;
+    off += round_up(part_bytes, 256);
     l.total = off;
     return l;
 }
@@ -186,8 +189,10 @@ int qlora_linear_fwd(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M,
     float *U = U_save ? U_save : reinterpret_cast<float *>(base + l.u);
     const Nf4Weights nw{w->codes, w->absmax_q, w->absmax_scale, w->absmax_mean, w->d, w->k};
     hipError_t e = launch_rows_skinny(x, A, M, w->k, r, U, s);
-    if (e == hipSuccess)
-        e = launch_gemm_fwd(nw, x, M, U, B, r, scale, Y, gemm_ws(base, l), s);
+    if (e == hipSuccess) {
+        if (M <= 16) e = launch_decode_fwd(nw, x, M, U, B, r, scale, Y, s);  // HBM-bound: stream the codes once
+        else e = launch_gemm_fwd(nw, x, M, U, B, r, scale, Y, gemm_ws(base, l), s);
+    }
     return hip_status(e);
 }
 
@@ -223,10 +228,17 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const qlora_bf16 *x, const qlora
     }
     if (e == hipSuccess) e = launch_transpose_bf16(B, d, r, Bt, s);             // B^T [r x d]
     if (e == hipSuccess) e = launch_rows_skinny(dY, Bt, M, d, r, G, s);         // G = dY B
-    if (e == hipSuccess)                                                        // dB = s dY^T U
-        e = launch_cols_skinny(dY, Uin, M, d, r, scale, part, cols_skinny_splits(M, d), dB, 0, s);
-    if (e == hipSuccess)                                                        // dA = s G^T X
-        e = launch_cols_skinny(x, G, M, k, r, scale, part, cols_skinny_splits(M, k), dA, 1, s);
+    if (r <= 16) {                                                              // dB = s dY^T U, dA = s G^T X
+        float *part_b = part;
+        float *part_a = part + (size_t)cols_valu_splits(M) * round_up(d, 64) * r;
+        if (e == hipSuccess)
+            e = launch_cols_valu_pair(dY, Uin, d, scale, part_b, dB, 0, x, G, k, scale, part_a, dA, 1, M, r, s);
+    } else {
+        if (e == hipSuccess)
+            e = launch_cols_skinny(dY, Uin, M, d, r, scale, part, cols_skinny_splits(M, d), dB, 0, s);
+        if (e == hipSuccess)
+            e = launch_cols_skinny(x, G, M, k, r, scale, part, cols_skinny_splits(M, k), dA, 1, s);
+    }
     if (e == hipSuccess && dX)                                                  // dX = dY What + s G A
         e = launch_gemm_dx(nw, dY, M, G, A, r, scale, dX, gemm_ws(base, l), s);
     return hip_status(e);

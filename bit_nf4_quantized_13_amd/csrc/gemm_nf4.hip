@@ -554,97 +554,108 @@ struct PrepArgs {
     int64_t Ke;
 };
 
-__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
-    const int64_t na = a.M * a.Ke, nbx = a.N * a.Ke;
-    const int64_t total = a.nb + na + nbx;
-    const float mean = *a.mean;
-    for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < total; x += (int64_t)gridDim.x * 256) {
-        if (x < a.nb) {
-            a.shat[x] = dq_scale(a.c2[x], a.c1[x >> 8], mean);
-        } else if (x < a.nb + na) {
-            const int64_t y = x - a.nb, m = y / a.Ke;
-            const int c = (int)(y % a.Ke);
-            uint16_t bits = 0;
-            if (c < 2 * a.r) {
-                const float v = a.s * a.V[m * a.r + (c < a.r ? c : c - a.r)];
-                const uint32_t hb = pack_bf16x2(v, 0.0f) & 0xFFFFu;
-                bits = (uint16_t)(c < a.r ? hb : (pack_bf16x2(v - bf16_bits_to_f32(hb), 0.0f) & 0xFFFFu));
-            }
-            a.ext_a[y] = bits;
-        } else {
-            const int64_t y = x - a.nb - na, n = y / a.Ke;
-            const int c = (int)(y % a.Ke);
-            uint16_t bits = 0;
+// Workgroup ranges: [0, gs) block scales, one per thread; [gs, gs + ga) ext_a
+// and then ext_b, 8 columns (one 16-byte store) per thread.
+__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a, int64_t gs, int64_t ga) {
+    const int64_t b = blockIdx.x;
+    if (b < gs) {
+        const int64_t x = b * 256 + threadIdx.x;
+        if (x < a.nb) a.shat[x] = dq_scale(a.c2[x], a.c1[x >> 8], *a.mean);
+        return;
+    }
+    const uint32_t cgs = (uint32_t)(a.Ke / 8);  // 8-column groups per row
+    const bool is_a = b < gs + ga;
+    const int64_t x = (b - (is_a ? gs : gs + ga)) * 256 + threadIdx.x;
+    const int64_t rows = is_a ? a.M : a.N;
+    const int64_t row = x / cgs;
+    if (row >= rows) return;
+    const int c0 = (int)(x - row * cgs) * 8;
+    uint32_t v[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        uint32_t pr = 0;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int c = c0 + 2 * h + q;
+            uint32_t bits = 0;
             if (c < 2 * a.r) {
                 const int jj = c < a.r ? c : c - a.r;
-                bits = a.dx ? a.W[(int64_t)jj * a.N + n] : a.W[n * a.r + jj];
+                if (is_a) {
+                    const float f = a.s * a.V[row * a.r + jj];
+                    const uint32_t hb = pack_bf16x2(f, 0.0f) & 0xFFFFu;
+                    bits = c < a.r ? hb : (pack_bf16x2(f - bf16_bits_to_f32(hb), 0.0f) & 0xFFFFu);
+                } else {
+                    bits = a.dx ? a.W[(int64_t)jj * a.N + row] : a.W[row * a.r + jj];
+                }
             }
-            a.ext_b[y] = bits;
+            pr |= bits << (16 * q);
         }
+        v[h] = pr;
     }
+    uint16_t *dst = (is_a ? a.ext_a : a.ext_b) + row * a.Ke + c0;
+    *reinterpret_cast<uint4 *>(dst) = uint4{v[0], v[1], v[2], v[3]};
 }
 
 // Dequantized weight operand for the non-expanding GEMM: What [d x k]
 // (forward) or What^T [k x ldw] with zero columns d .. ldw-1 (dX), bf16,
-// bit-identical to qlora_nf4_dequantize.  One workgroup per 64 x 64 tile
-// (64 rows of W0 = one NF4 block each): thread t expands row t/4, k = 16 (t%4)
-// .. +15.  The transposed form goes through LDS so both the reads of the codes
-// and the writes of the rows of What^T are contiguous.
+// bit-identical to qlora_nf4_dequantize.  One workgroup per 64 W0 rows x 256
+// columns; thread t expands an 8 x 8 block: rows 8 (t % 8) .., columns
+// 8 (t / 8) .. (inside one NF4 block, so one scale per row).  Code reads are
+// 32 contiguous bytes per row for 8 lanes; the transposed form transposes the
+// 8 x 8 block in registers (v_perm) and stores 16-byte column pieces, so no
+// LDS is involved and every store is a contiguous 128-byte row segment per 8
+// lanes.
 template <bool T>
 __global__ __launch_bounds__(256) void dequant_tile_kernel(const uint8_t *__restrict__ codes,
                                                            const float *__restrict__ shat, int64_t d, int64_t k,
                                                            int64_t ldw, Nf4Consts tab, uint16_t *__restrict__ out) {
-    __shared__ uint16_t tile[64][64 + 8];  // [k][d-row] (+8: spread the banks)
     const int tid = threadIdx.x, lane = tid & 63;
-    const int64_t kb = k / 64;
-    const int64_t tk = blockIdx.x % kb, td = blockIdx.x / kb;
-    const int row = tid >> 2, q = tid & 3;
-    const int64_t n = td * 64 + row;  // W0 row
+    const int64_t ct = (k + 255) / 256;
+    const int64_t tk = blockIdx.x % ct, td = blockIdx.x / ct;
+    const int ng = tid & 7, kg = tid >> 3;
+    const int64_t n0 = td * 64 + 8 * ng;   // first of this thread's 8 W0 rows
+    const int64_t k0 = tk * 256 + 8 * kg;  // first of its 8 columns
+    if (k0 >= k) return;                   // k % 64 == 0: whole 8-column groups
     float lvf = tab.level[0];
 #pragma unroll
     for (int j = 1; j < 16; ++j) lvf = (lane & 15) == j ? tab.level[j] : lvf;
     const int lv = __float_as_int(lvf);
-    uint32_t v[8];
-    if (n < d) {
-        const uint2 c = *reinterpret_cast<const uint2 *>(codes + n * (k / 2) + tk * 32 + 8 * q);
-        const float sc = shat[n * kb + tk];
-        const uint32_t cw[2] = {c.x, c.y};
+    const int64_t kb = k / 64;
+    // v[e][c2]: row e, columns 2 c2, 2 c2 + 1 (bf16 pair)
+    uint32_t v[8][4];
+    uint32_t cw[8];
+    float sc[8];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                v[4 * h + e] = pack_bf16x2(level(code_addr(cw[h], 2 * e), lv) * sc, level(code_addr(cw[h], 2 * e + 1), lv) * sc);
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0;
+    for (int e = 0; e < 8; ++e) {
+        const int64_t n = n0 + e;
+        cw[e] = n < d ? *reinterpret_cast<const uint32_t *>(codes + n * (k / 2) + k0 / 2) : 0u;
+        sc[e] = n < d ? shat[n * kb + k0 / 64] : 0.0f;
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int c2 = 0; c2 < 4; ++c2) {
+            const uint32_t x = pack_bf16x2(level(code_addr(cw[e], 2 * c2), lv) * sc[e],
+                                           level(code_addr(cw[e], 2 * c2 + 1), lv) * sc[e]);
+            v[e][c2] = n0 + e < d ? x : 0u;  // rows past d: zero columns of What^T
+        }
     if constexpr (!T) {
-        if (n < d) {
-            uint4 *dst = reinterpret_cast<uint4 *>(out + n * k + tk * 64 + 16 * q);
-            dst[0] = uint4{v[0], v[1], v[2], v[3]};
-            dst[1] = uint4{v[4], v[5], v[6], v[7]};
-        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (n0 + e < d)
+                *reinterpret_cast<uint4 *>(out + (n0 + e) * k + k0) = uint4{v[e][0], v[e][1], v[e][2], v[e][3]};
     } else {
+        // column c of the block: rows 0..7 packed as 4 bf16 pairs
+        // (rows 2 e2, 2 e2 + 1) = low halves (c even) or high halves (c odd)
+        // of v[2 e2][c / 2] and v[2 e2 + 1][c / 2]
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            tile[16 * q + 2 * e][row] = (uint16_t)(v[e] & 0xFFFFu);
-            tile[16 * q + 2 * e + 1][row] = (uint16_t)(v[e] >> 16);
-        }
-        __syncthreads();
-        // row kk of What^T: 64 values (128 B) = 8 threads x 16 B; 256 threads -> 32 rows per pass
+        for (int c = 0; c < 8; ++c) {
+            uint32_t o[4];
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            const int kk = 32 * pass + (tid >> 3), c8 = tid & 7;
-            const int64_t col = td * 64 + 8 * c8;
-            if (col < ldw) {
-                const uint16_t *src = &tile[kk][8 * c8];
-                uint4 o;
-                o.x = src[0] | ((uint32_t)src[1] << 16);
-                o.y = src[2] | ((uint32_t)src[3] << 16);
-                o.z = src[4] | ((uint32_t)src[5] << 16);
-                o.w = src[6] | ((uint32_t)src[7] << 16);
-                *reinterpret_cast<uint4 *>(out + (tk * 64 + kk) * ldw + col) = o;
-            }
+            for (int e2 = 0; e2 < 4; ++e2)
+                o[e2] = (c & 1) ? __builtin_amdgcn_perm(v[2 * e2 + 1][c >> 1], v[2 * e2][c >> 1], 0x07060302u)
+                                : __builtin_amdgcn_perm(v[2 * e2 + 1][c >> 1], v[2 * e2][c >> 1], 0x05040100u);
+            *reinterpret_cast<uint4 *>(out + (k0 + c) * ldw + n0) = uint4{o[0], o[1], o[2], o[3]};
         }
     }
 }
@@ -689,10 +700,8 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
     q.dx = dx ? 1 : 0;
     q.ext_b = ws.ext_b;
     q.Ke = p.Ke;
-    const int64_t total = q.nb + M * p.Ke + p.N * p.Ke;
-    int64_t g = (total + 255) / 256;
-    if (g > 4096) g = 4096;
-    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)g), dim3(256), 0, st, q);
+    const int64_t gs = (q.nb + 255) / 256, ga = (M * (p.Ke / 8) + 255) / 256, gb = (p.N * (p.Ke / 8) + 255) / 256;
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(gs + ga + gb)), dim3(256), 0, st, q, gs, ga);
 
     const int64_t tiles_m = (M + BM - 1) / BM, tiles = tiles_m * ((p.N + BN - 1) / BN);
     const dim3 grid((unsigned)tiles), block(NTHREADS);
@@ -702,7 +711,7 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
     } else {
         // dequantized copy of the weight operand, once per call
         const int64_t rows = dx ? w.k : w.d, cols = dx ? p.ldw : w.k;
-        const dim3 tgrid((unsigned)((w.k / 64) * ((w.d + 63) / 64)));
+        const dim3 tgrid((unsigned)(((w.k + 255) / 256) * ((w.d + 63) / 64)));
         if (dx)
             hipLaunchKernelGGL(dequant_tile_kernel<true>, tgrid, dim3(256), 0, st, w.codes, ws.shat, w.d, w.k, p.ldw,
                                nf4_consts(), ws.wbf);

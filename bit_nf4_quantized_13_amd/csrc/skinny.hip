@@ -37,42 +37,61 @@ __device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
 // ---------------------------------------------------------------------------
 constexpr int kRowsMaxTiles = 8;  // R <= 128
 
-template <int NT>
-__global__ __launch_bounds__(256) void rows_skinny_kernel(const uint16_t *__restrict__ in,
-                                                          const uint16_t *__restrict__ w,
-                                                          int64_t M, int64_t K, int R,
-                                                          float *__restrict__ out) {
-    __shared__ f32x4 s_acc[4][NT][64];
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const int n = (int)__builtin_amdgcn_readfirstlane((uint32_t)bytes);
+    void *p = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+template <int NT, int W>  // W waves split K
+__global__ __launch_bounds__(64 * W) void rows_skinny_kernel(const uint16_t *__restrict__ in,
+                                                             const uint16_t *__restrict__ w,
+                                                             int64_t M, int64_t K, int R,
+                                                             float *__restrict__ out) {
+    __shared__ f32x4 s_acc[W][NT][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i = lane & 15, g = lane >> 4;
-    const int64_t m = (int64_t)blockIdx.x * 16 + i;
+    const int64_t m0 = (int64_t)blockIdx.x * 16;
+    const int64_t rows = (M - m0) < 16 ? (M - m0) : 16;
+    // rows past M and W rows past R read as zero (outside the buffers); the
+    // pieces past K of a row are zeroed by the selects below
+    const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + m0 * K, rows * K * 2);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (int64_t)R * K * 2);
     f32x4 acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // Two chunks of 128 k per iteration, all loads issued before the MFMAs
+    // (enough bytes in flight per CU to stream the activations from HBM).
     const int64_t chunks = (K + 127) / 128;
-    for (int64_t c = wave; c < chunks; c += 4) {
-        const int64_t k0 = c * 128 + 32 * g;
-        // K % 8 == 0: each 8-value piece [k0 + 8e, +8) is entirely inside or outside
-        uint4 a[4];
+    for (int64_t c = wave; c < chunks; c += 2 * W) {
+        uint4 a[2][4], b[2][NT][4];
+        bool ok[2][4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            a[e] = uint4{0, 0, 0, 0};
-            if (m < M && k0 + 8 * e < K) a[e] = *reinterpret_cast<const uint4 *>(in + m * K + k0 + 8 * e);
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int j = t * 16 + i;
-            uint4 b[4];
+        for (int u = 0; u < 2; ++u) {
+            const int64_t k0 = (c + W * u) * 128 + 32 * g;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                b[e] = uint4{0, 0, 0, 0};
-                if (j < R && k0 + 8 * e < K)
-                    b[e] = *reinterpret_cast<const uint4 *>(w + (int64_t)j * K + k0 + 8 * e);
-            }
+                ok[u][e] = k0 + 8 * e < K;  // K % 8 == 0: pieces are entirely inside or outside
+                a[u][e] = load16(rin, (uint32_t)((i * K + k0 + 8 * e) * 2));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[t] = mfma16(a[e], b[e], acc[t]);
+                for (int t = 0; t < NT; ++t) b[u][t][e] = load16(rw, (uint32_t)(((t * 16 + i) * K + k0 + 8 * e) * 2));
+            }
         }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint4 av = ok[u][e] ? a[u][e] : uint4{0, 0, 0, 0};
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[t] = mfma16(av, b[u][t][e], acc[t]);
+            }
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) s_acc[wave][t][lane] = acc[t];
@@ -80,8 +99,8 @@ __global__ __launch_bounds__(256) void rows_skinny_kernel(const uint16_t *__rest
     if (wave == 0) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const f32x4 v = (s_acc[0][t][lane] + s_acc[1][t][lane]) +
-                            (s_acc[2][t][lane] + s_acc[3][t][lane]);
+            f32x4 v = s_acc[0][t][lane];
+            for (int q = 1; q < W; ++q) v += s_acc[q][t][lane];
             const int j = t * 16 + i;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -227,15 +246,152 @@ __global__ __launch_bounds__(256) void cols_skinny_reduce_kernel(const float *__
     }
 }
 
+// ---------------------------------------------------------------------------
+// Small-rank column reductions on the vector ALU (R <= 16):
+//   part[sp][n][j] = sum over rows m of split sp of In[m][n] V[m][j]   (fp32)
+// A workgroup owns 512 columns and one row split; lane l of every wave owns
+// columns 8 l .. 8 l + 7 (one 16-byte load per row) and the 4 waves take every
+// 4th row.  V of the split is staged in LDS (each row's R values are read as a
+// broadcast); the 4 wave partials are summed in LDS in a fixed order.
+// ---------------------------------------------------------------------------
+constexpr int kVColsN = 512;
+constexpr int kVRowsMax = 128;  // rows per split
+
+template <int R>
+__global__ __launch_bounds__(256) void cols_valu_kernel(const uint16_t *__restrict__ in,
+                                                        const float *__restrict__ v, int64_t M, int64_t N,
+                                                        int64_t rows_per_split, float *__restrict__ part) {
+    __shared__ float sv[kVRowsMax * R];
+    __shared__ float red[4][kVColsN * R];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t n0 = (int64_t)blockIdx.x * kVColsN + 8 * lane;
+    const int sp = blockIdx.y;
+    const int64_t mbeg = (int64_t)sp * rows_per_split;
+    const int64_t mend = (mbeg + rows_per_split < M) ? mbeg + rows_per_split : M;
+    const int rows = (int)(mend > mbeg ? mend - mbeg : 0);
+    for (int e = tid; e < rows * R; e += 256) sv[e] = v[mbeg * R + e];
+    __syncthreads();
+    // N % 8 == 0: a lane's 8 columns are all inside or all outside
+    const bool col_ok = n0 < N;
+    const int64_t nrows_buf = (M - mbeg) > 0 ? (M - mbeg) : 0;
+    const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + mbeg * N, nrows_buf * N * 2);
+    float acc[8][R];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int j = 0; j < R; ++j) acc[c][j] = 0.0f;
+    for (int r0 = wave; r0 < rows; r0 += 16) {
+        uint4 x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[u] = load16(rin, (uint32_t)(((int64_t)(r0 + 4 * u) * N + n0) * 2));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int rr = r0 + 4 * u;
+            if (rr >= rows || !col_ok) continue;
+            const uint32_t xw[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+            float xf[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                xf[2 * q] = __uint_as_float(xw[q] << 16);
+                xf[2 * q + 1] = __uint_as_float(xw[q] & 0xFFFF0000u);
+            }
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const float vj = sv[rr * R + j];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[c][j] = __builtin_fmaf(xf[c], vj, acc[c][j]);
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int j = 0; j < R; ++j) red[wave][(8 * lane + c) * R + j] = acc[c][j];
+    __syncthreads();
+    for (int e = tid; e < kVColsN * R; e += 256) {
+        const int64_t n = (int64_t)blockIdx.x * kVColsN + e / R;
+        if (n < N) part[((int64_t)sp * N) * R + (int64_t)blockIdx.x * kVColsN * R + e] =
+            (red[0][e] + red[1][e]) + (red[2][e] + red[3][e]);
+    }
+}
+
+// out = scale * sum over splits of part[sp][n][j]: out[n][j] (trans = 0) or
+// out[j][n] (trans = 1).  Two independent jobs in one launch: workgroups
+// [0, g0) for job 0, the rest for job 1.
+struct ColsReduceJob {
+    const float *part;
+    int64_t N;
+    int R, splits, trans;
+    float scale;
+    float *out;
+};
+__global__ __launch_bounds__(256) void cols_valu_reduce_kernel(ColsReduceJob j0, ColsReduceJob j1, int64_t g0) {
+    const bool second = blockIdx.x >= g0;
+    const ColsReduceJob &jb = second ? j1 : j0;
+    const int64_t e = ((int64_t)blockIdx.x - (second ? g0 : 0)) * 256 + threadIdx.x;
+    if (e >= jb.N * jb.R) return;
+    float sum = 0.0f;
+    for (int sp = 0; sp < jb.splits; ++sp) sum += jb.part[(int64_t)sp * jb.N * jb.R + e];
+    const int64_t n = e / jb.R;
+    const int j = (int)(e - n * jb.R);
+    if (jb.trans) jb.out[(int64_t)j * jb.N + n] = jb.scale * sum;
+    else jb.out[e] = jb.scale * sum;
+}
+
+// ---------------------------------------------------------------------------
+// out[M x R] = In W^T for few rows (M * R <= 4096): one wave per output element,
+// a dot product of two K-vectors (16-byte loads, all in flight, then a
+// cross-lane sum in a fixed order).  Spreads the decode-shaped down-projection
+// over the whole chip instead of one workgroup.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void dot_rows_kernel(const uint16_t *__restrict__ in, const uint16_t *__restrict__ w,
+                                                       int64_t M, int64_t K, int R, float *__restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // output element
+    if (e >= M * R) return;
+    const int64_t m = e / R;
+    const int j = (int)(e - m * R);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(in + m * K, K * 2);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(w + (int64_t)j * K, K * 2);
+    float acc = 0.0f;
+    for (int64_t k0 = 0; k0 < K; k0 += 64 * 8 * 8) {
+        uint4 a[8], b[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint32_t off = (uint32_t)((k0 + (u * 64 + lane) * 8) * 2);
+            a[u] = load16(ra, off);  // past K: zero
+            b[u] = load16(rb, off);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint32_t av[4] = {a[u].x, a[u].y, a[u].z, a[u].w}, bv[4] = {b[u].x, b[u].y, b[u].z, b[u].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc = __builtin_fmaf(__uint_as_float(av[q] << 16), __uint_as_float(bv[q] << 16), acc);
+                acc = __builtin_fmaf(__uint_as_float(av[q] & 0xFFFF0000u), __uint_as_float(bv[q] & 0xFFFF0000u), acc);
+            }
+        }
+    }
+    // fixed-order butterfly over the 64 lanes
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) out[e] = acc;
+}
+
 }  // namespace
 
 hipError_t launch_rows_skinny(const uint16_t *in, const uint16_t *w, int64_t M, int64_t K, int R,
                               float *out, hipStream_t s) {
     const dim3 grid((unsigned)((M + 15) / 16));
     const int nt = (R + 15) / 16;
+    // decode-sized M: one wave per output element, spread over the chip
+    if (M * R <= 4096) {
+        hipLaunchKernelGGL(dot_rows_kernel, dim3((unsigned)((M * R + 3) / 4)), dim3(256), 0, s, in, w, M, K, R, out);
+        return hipGetLastError();
+    }
     switch (nt) {
 #define QNF4_ROWS(NTV) \
-    case NTV: hipLaunchKernelGGL(rows_skinny_kernel<NTV>, grid, dim3(256), 0, s, in, w, M, K, R, out); break;
+    case NTV: hipLaunchKernelGGL((rows_skinny_kernel<NTV, 4>), grid, dim3(256), 0, s, in, w, M, K, R, out); break;
         QNF4_ROWS(1) QNF4_ROWS(2) QNF4_ROWS(3) QNF4_ROWS(4)
         QNF4_ROWS(5) QNF4_ROWS(6) QNF4_ROWS(7) QNF4_ROWS(8)
 #undef QNF4_ROWS
@@ -248,6 +404,37 @@ hipError_t launch_transpose_bf16(const uint16_t *src, int64_t R, int64_t C, uint
                                  hipStream_t s) {
     const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
     hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, src, R, C, dst);
+    return hipGetLastError();
+}
+
+int cols_valu_splits(int64_t M) {
+    int64_t splits = (M + kVRowsMax - 1) / kVRowsMax;
+    return (int)(splits < 1 ? 1 : splits);
+}
+
+hipError_t launch_cols_valu_pair(const uint16_t *in0, const float *v0, int64_t N0, float scale0, float *part0,
+                                 float *out0, int trans0, const uint16_t *in1, const float *v1, int64_t N1,
+                                 float scale1, float *part1, float *out1, int trans1, int64_t M, int R,
+                                 hipStream_t s) {
+    const int splits = cols_valu_splits(M);
+    const int64_t rps = kVRowsMax;
+    const dim3 g0((unsigned)((N0 + kVColsN - 1) / kVColsN), (unsigned)splits);
+    const dim3 g1((unsigned)((N1 + kVColsN - 1) / kVColsN), (unsigned)splits);
+    switch (R) {
+#define QNF4_CV(RV)                                                                                       \
+    case RV:                                                                                              \
+        hipLaunchKernelGGL(cols_valu_kernel<RV>, g0, dim3(256), 0, s, in0, v0, M, N0, rps, part0);        \
+        if (in1) hipLaunchKernelGGL(cols_valu_kernel<RV>, g1, dim3(256), 0, s, in1, v1, M, N1, rps, part1); \
+        break;
+        QNF4_CV(1) QNF4_CV(2) QNF4_CV(3) QNF4_CV(4) QNF4_CV(5) QNF4_CV(6) QNF4_CV(7) QNF4_CV(8)
+        QNF4_CV(9) QNF4_CV(10) QNF4_CV(11) QNF4_CV(12) QNF4_CV(13) QNF4_CV(14) QNF4_CV(15) QNF4_CV(16)
+#undef QNF4_CV
+        default: return hipErrorInvalidValue;
+    }
+    ColsReduceJob j0{part0, N0, R, splits, trans0, scale0, out0};
+    ColsReduceJob j1{part1, N1, R, splits, trans1, scale1, out1};
+    const int64_t b0 = (N0 * R + 255) / 256, b1 = in1 ? (N1 * R + 255) / 256 : 0;
+    hipLaunchKernelGGL(cols_valu_reduce_kernel, dim3((unsigned)(b0 + b1)), dim3(256), 0, s, j0, j1, b0);
     return hipGetLastError();
 }
 
