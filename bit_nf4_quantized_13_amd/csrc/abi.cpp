@@ -13,6 +13,7 @@ using namespace qnf4;
 namespace {
 
 constexpr int64_t kMaxWeights = int64_t(1) << 30;  // 2^24 NF4 blocks: 65536 DQ groups
+constexpr int64_t kDecodeMaxK = int64_t(1) << 25;  // 32-bit buffer offsets of X and A rows
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -50,11 +51,17 @@ QuantWs quant_ws(int64_t d, int64_t k) {
 }
 
 struct LinWs {
-    size_t shat, ext_a, ext_b, wbf, u, bt, g, part, total;
+    size_t ctr, dpart, shat, ext_a, ext_b, wbf, u, bt, g, part, total;
 };
+// The decode counters sit first, at the same offset for every shape, so that no
+// other call's data ever lands on them.
 LinWs lin_ws(int64_t M, int64_t d, int64_t k, int r) {
     LinWs l;
     size_t off = 0;
+    l.ctr = off;
+    off += round_up(decode_counter_bytes(), 256);
+    l.dpart = off;
+    off += round_up(decode_part_bytes(M, d, k), 256);
     l.shat = off;
     off += round_up(sizeof(float) * (d * k / QLORA_NF4_BLOCK), 256);
     const int64_t ke = gemm_ext_cols(r);
@@ -188,10 +195,20 @@ int qlora_linear_fwd(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M,
     const float scale = alpha / static_cast<float>(r);
     float *U = U_save ? U_save : reinterpret_cast<float *>(base + l.u);
     const Nf4Weights nw{w->codes, w->absmax_q, w->absmax_scale, w->absmax_mean, w->d, w->k};
-    hipError_t e = launch_rows_skinny(x, A, M, w->k, r, U, s);
-    if (e == hipSuccess) {
-        if (M <= 16) e = launch_decode_fwd(nw, x, M, U, B, r, scale, Y, s);  // HBM-bound: stream the codes once
-        else e = launch_gemm_fwd(nw, x, M, U, B, r, scale, Y, gemm_ws(base, l), s);
+    float *dpart = reinterpret_cast<float *>(base + l.dpart);
+    unsigned long long *ctr = reinterpret_cast<unsigned long long *>(base + l.ctr);
+    hipError_t e = hipSuccess;
+    if (M <= 16 && w->k <= kDecodeMaxK) {
+        // HBM-bound: one pass over the codes; U = X A^T in the same kernel for r <= 16
+        if (r <= 16) {
+            e = launch_decode_fwd(nw, x, M, A, nullptr, B, r, scale, Y, U_save, dpart, ctr, s);
+        } else {
+            e = launch_rows_skinny(x, A, M, w->k, r, U, s);
+            if (e == hipSuccess) e = launch_decode_fwd(nw, x, M, nullptr, U, B, r, scale, Y, nullptr, dpart, ctr, s);
+        }
+    } else {
+        e = launch_rows_skinny(x, A, M, w->k, r, U, s);
+        if (e == hipSuccess) e = launch_gemm_fwd(nw, x, M, U, B, r, scale, Y, gemm_ws(base, l), s);
     }
     return hip_status(e);
 }

@@ -1,30 +1,51 @@
-// Decode-shaped forward (M <= 16 tokens): Y = X What^T + s U B^T, streaming the
-// packed NF4 weights from HBM once.
+// Decode-shaped forward (M <= 16 tokens): Y = X What^T + s (X A^T) B^T in one
+// kernel that streams the packed NF4 weights from HBM once.
 //
 // chkda.github.io "Why do we need LoRA and QLoRA?", "Double quantization and
 // double dequantization": What = doubleDequant(c1, c2, W_NF4) in BF16 feeds the
-// matrix multiplication; with M <= 16 the product is bound by the bytes of the
-// packed weights, so the weights are expanded in registers straight into the
-// MFMA operand and never written anywhere.
+// matrix multiplication.  With M <= 16 the product is bound by the bytes of the
+// packed weights, so this kernel is organised around the cost of expanding a
+// nibble, not around the matrix cores:
 //
-// One 256-thread workgroup per 16 rows of W0.  The four waves split k into
-// contiguous quarters (whole 128-deep groups).  Per group a wave reads its
-// 16 rows x 64 code bytes with one coalesced 16-byte load per lane (four lanes
-// per row) and moves them into the MFMA operand layout with ds_bpermute; the
-// loads of the next group are in flight while the current one is expanded.
+// * A 64-deep block of row n shares one scale s(n,b), so the product is taken
+//   as sum_b s(n,b) * sum_{k in b} X[m][k] C[q(n,k)]: one MFMA pair per block
+//   on the bf16 NF4 levels, then one fp32 FMA per result register.  The only
+//   per-weight work left is the level lookup.  (This rounds the level, not the
+//   scaled weight, to bf16: the same product with a different rounding, well
+//   inside the tolerance of the bf16 What product.)
+// * The lookup maps a code byte (two nibbles) to a packed pair of bf16 levels
+//   through a 256-entry table in LDS, replicated once per lane so that every
+//   lane reads its own bank: one v_perm (address) and one ds_read_b32 per two
+//   weights.
+// * Codes are read with 8-byte loads, four lanes per row and 32 bytes (one
+//   block) per row per load; one ds_bpermute per code dword moves them into the
+//   MFMA operand layout.
+// * Work split: a workgroup (8 waves) takes T tiles of 16 rows and one of S
+//   k-slices; its waves split the slice P ways and the tiles 8/P ways.  X and A
+//   fragments of a wave's k-range stay in registers for all of its tiles.
+//   Partial sums are reduced across waves in LDS in a fixed order; with S > 1
+//   every workgroup stores its partial, and the last of the S workgroups of a
+//   tile group (a counter in the workspace) adds the S partials in slice order,
+//   the adapter term, and writes bf16 Y.  Results do not depend on arrival order.
+// * The LoRA down-projection U = X A^T (r <= 16) rides along: X is already in
+//   registers, so each k-range adds one MFMA pair per block on the A rows.
 //
-// MFMA v_mfma_f32_16x16x32_bf16, g = lane / 16, with the weight rows as the
-// first operand: lane (n = lane % 16, g) holds What[n][8 codes], X the second
-// operand: lane (m = lane % 16, g) holds X[m][8 values]; result lane (m, g),
-// register v: D[n = 4 g + v][m].  Within a 128-deep group the k order is
-// permuted so that lane group g takes the 32 contiguous k = 32 g .. 32 g + 31
-// (one 16-byte code read per lane feeds 4 MFMAs); both operands agree.
+// MFMA v_mfma_f32_16x16x32_bf16, g = lane / 16: first operand lane (m, g)
+// holds X[m][8 k], second operand lane (n, g) holds What[n][the same 8 k],
+// result lane (n, g) register v is D[m = 4 g + v][n].  In block b, MFMA j
+// (j = 0, 1) gives lane group g the k = 64 b + 16 g + 8 j .. + 7.
 #include "launch.hpp"
 
 namespace qnf4 {
 namespace {
 
-constexpr int DEC_ROWS = 16;
+constexpr int DEC_WAVES = 8;
+constexpr int DEC_THREADS = 64 * DEC_WAVES;
+constexpr int DEC_KB = 4;                    // 64-deep blocks per wave per chunk
+constexpr int DEC_MAX_TW = 8;                // tiles per wave
+constexpr int DEC_MAX_GROUPS = 4096;         // counters reserved in the workspace
+constexpr uint32_t DEC_TAG = 0x4E463444u;    // high word of an initialised counter
+constexpr uint32_t DEC_OOB = 0x80000000u;    // buffer offset past every range used here
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
@@ -34,19 +55,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
     void *p = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
     return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, n, 0x00020000);
 }
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
 __device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
                                                    0, 0);
-}
-__device__ __forceinline__ float level(uint32_t addr, int lv) {
-    return __int_as_float(__builtin_amdgcn_ds_bpermute((int)addr, lv));
-}
-// 4 * nibble e of w as a ds_bpermute byte address (bits 2..5; bits 0..1 are
-// dropped by the lane-index division)
-__device__ __forceinline__ uint32_t code_addr(uint32_t w, int e) {
-    if (e == 0) return (w << 2) & 0x3Cu;
-    if (e == 7) return w >> 26;
-    return __builtin_amdgcn_ubfe(w, 4 * e - 2, 6);
 }
 
 struct DecodeArgs {
@@ -56,156 +70,384 @@ struct DecodeArgs {
     const float *mean;
     int64_t d, k;
     const uint16_t *x;     // [M x k] bf16
-    int64_t M;
-    const float *U;        // [M x r] fp32
+    int M;
+    const uint16_t *A;     // [r x k] bf16, read when U is null (r <= 16)
+    const float *U;        // [M x r] fp32 computed beforehand, or null
     const uint16_t *B;     // [d x r] bf16
     int r;
     float s;
     uint16_t *y;           // [M x d] bf16
+    float *u_save;         // [M x r] fp32 or null (fused U only)
+    float *part;           // partials [grid][T + 1][64] f32x4: Y per tile, then U
+    unsigned long long *ctr;  // one per tile group
+    int S, T, P, nbw;      // k-slices, tiles per group, waves per tile subset, blocks per wave
+    int grid_;             // workgroups
 };
 
-// X slab in LDS: M rows x up to DEC_SLAB_K k, rows padded by 16 bytes so that
-// the 16 fragment rows of one read land in 16 different bank groups.
-constexpr int DEC_SLAB_K = 4096;
-constexpr int DEC_MAX_GROUPS = 8;  // 128-deep groups per wave per slab (k per wave <= 1024)
+// Device-coherent 16-byte store / load (sc1: not cached non-coherently in the
+// per-XCD L2), for partial sums handed from one workgroup to another.
+constexpr int DEC_SC1 = 16;
+__device__ __forceinline__ void store16_sc1(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, DEC_SC1);
+}
+__device__ __forceinline__ f32x4 load16_sc1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, DEC_SC1));
+}
 
-template <int NT>  // 16-row weight tiles per workgroup (each wave does all of them)
-__global__ __launch_bounds__(256) void nf4_decode_kernel(DecodeArgs p, Nf4Consts tab) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t dyn_smem[];
-    __shared__ f32x4 red[4][NT][64];
+// B[row][8 g .. 8 g + 7] as a bf16x8 MFMA operand (zero past r or for g >= 2)
+__device__ __forceinline__ uint4 load_bfrag(__amdgpu_buffer_rsrc_t rb, int64_t row, int g, int r, bool ok) {
+    uint4 o{0, 0, 0, 0};
+    if (!ok || 8 * g >= r) return o;
+    if (r % 8 == 0) return load16(rb, (uint32_t)((row * r + 8 * g) * 2));
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        h[e] = 8 * g + e < r ? __builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)((row * r + 8 * g + e) * 2), 0, 0)
+                             : 0u;
+    o.x = h[0] | (h[1] << 16);
+    o.y = h[2] | (h[3] << 16);
+    o.z = h[4] | (h[5] << 16);
+    o.w = h[6] | (h[7] << 16);
+    return o;
+}
+
+template <int TW, int MV>  // TW tiles per wave; MV result registers that can hold m < M
+__global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, Nf4Consts tab) {
+    __shared__ __attribute__((aligned(16))) uint32_t tbl[256 * 64];  // pair table, one copy per lane
+    __shared__ f32x4 red[DEC_WAVES][TW][64];
+    __shared__ f32x4 ured[DEC_WAVES][64];
+    __shared__ __attribute__((aligned(16))) float us[16][20];
+    __shared__ int last_flag;
+
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int r16 = lane & 15, g = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * DEC_ROWS * NT;
-    const int64_t kb = p.k / 64;
-    const int64_t M = p.M;
-    const int xrow_bytes = DEC_SLAB_K * 2 + 16;
-
-    float lvf = tab.level[0];
-#pragma unroll
-    for (int j = 1; j < 16; ++j) lvf = (lane & 15) == j ? tab.level[j] : lvf;
-    const int lv = __float_as_int(lvf);
+    const int n16 = lane & 15, g = lane >> 4;
+    const int S = p.S, P = p.P, T = p.T, M = p.M, r = p.r;
+    const int wg = blockIdx.x, sl = wg % S, grp = wg / S;
+    const int kpart = wave % P, tsub = wave / P;
+    const int64_t d = p.d, k = p.k, kb = k / 64;
+    const int64_t wblk0 = ((int64_t)sl * P + kpart) * p.nbw;  // this wave's blocks [wblk0, wblk1)
+    const int64_t wblk1 = wblk0 + p.nbw < kb ? wblk0 + p.nbw : kb;
+    const int64_t row_g = (int64_t)grp * T * 16;               // first row of the tile group
+    const int64_t row_w = row_g + (int64_t)tsub * TW * 16;     // first row of this wave's tiles
+    const bool fuse_u = p.U == nullptr;
+    const bool u_wave = fuse_u && tsub == 0;
     const float mean = *p.mean;
 
-    const int64_t rows_here = (p.d - n0) < DEC_ROWS * NT ? (p.d - n0) : DEC_ROWS * NT;
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.codes + n0 * (p.k / 2), rows_here * (p.k / 2));
-    const __amdgpu_buffer_rsrc_t rs2 = make_rsrc(p.c2 + n0 * kb, rows_here * kb);
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, M * p.k * 2);
-    // coalesced code read: lane l takes row l / 4 of the tile, bytes 16 (l % 4) ..
-    // of the group's 64; the MFMA wants lane (n, g) = row n, piece g = lane 4 n + g
-    const uint32_t code_voff = (uint32_t)((lane >> 2) * (p.k / 2) + 16 * (lane & 3));
-    const int perm_addr = (4 * r16 + g) * 4;
+    const __amdgpu_buffer_rsrc_t rcode = make_rsrc(p.codes, d * k / 2);
+    const __amdgpu_buffer_rsrc_t rc2 = make_rsrc(p.c2, d * kb);
+    const __amdgpu_buffer_rsrc_t rc1 = make_rsrc(p.c1, ((d * kb + 255) / 256) * 4);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (int64_t)M * k * 2);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, fuse_u ? (int64_t)r * k * 2 : 0);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, d * r * 2);
+    const int64_t part_f4 = (int64_t)p.S > 1 ? (int64_t)(p.grid_) * (T + 1) * 64 : 0;  // f32x4 slots
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.part, part_f4 * 16);
 
-    f32x4 acc[NT];
+    // the group counter, read now and used at the end (tags a fresh workspace)
+    unsigned long long ctr0 = 0;
+    if (S > 1 && tid == 0) ctr0 = __hip_atomic_load(p.ctr + grp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    // thread (tile tt of the group, lane): tt = wave, wave + 8; B fragments for the adapter
+    constexpr int NTT = (2 * DEC_MAX_TW + DEC_WAVES - 1) / DEC_WAVES;
+    uint4 bfr[NTT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < NTT; ++h) {
+        const int tt = wave + DEC_WAVES * h;
+        const int64_t row = row_g + 16 * tt + n16;
+        bfr[h] = load_bfrag(rb, row, g, r, fuse_u && tt < T && row < d);
+    }
 
-    for (int64_t s0 = 0; s0 < p.k; s0 += DEC_SLAB_K) {
-        const int64_t sk = (p.k - s0) < DEC_SLAB_K ? (p.k - s0) : DEC_SLAB_K;  // multiple of 64
-        const int64_t sblocks = sk / 64;
-        // this wave's blocks of the slab [b0, b1), whole 128-deep groups
-        const int64_t per = ((sblocks + 3) / 4 + 1) / 2 * 2;
-        const int64_t b0 = wave * per < sblocks ? wave * per : sblocks;
-        const int64_t b1 = (wave + 1) * per < sblocks ? (wave + 1) * per : sblocks;
-        const int ngroups = (int)((b1 - b0 + 1) / 2);
+    f32x4 acc[TW];
+#pragma unroll
+    for (int t = 0; t < TW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 uacc = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // X slab -> LDS: row m, 16-byte pieces; transfer covers 64 pieces of one row
-        if (s0 > 0) __syncthreads();  // previous slab's fragment reads done
-        {
-            const int64_t pieces = sk / 8;  // per row
-            for (int64_t c = wave; c < M * ((pieces + 63) / 64); c += 4) {
-                const int64_t m = c / ((pieces + 63) / 64), pc = (c % ((pieces + 63) / 64)) * 64;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rx,
-                    reinterpret_cast<__attribute__((address_space(3))) void *>(
-                        reinterpret_cast<uintptr_t>(dyn_smem + m * xrow_bytes + pc * 16)),
-                    16, (uint32_t)((m * p.k + s0 + (pc + lane) * 8) * 2), 0, 0, 0);
+    const uint32_t lane4 = (uint32_t)lane * 4;
+    const int code_src = (4 * n16 + g) * 4;  // lane holding dwords 2 g, 2 g + 1 of row n16
+    const char *tbl_b = reinterpret_cast<const char *>(tbl);
+    // byte i of a code dword -> LDS byte address (byte << 8) | (lane << 2)
+    auto lut4 = [&](uint32_t cd) {
+        uint4 o;
+        o.x = *reinterpret_cast<const uint32_t *>(tbl_b + __builtin_amdgcn_perm(cd, lane4, 0x0C0C0400u));
+        o.y = *reinterpret_cast<const uint32_t *>(tbl_b + __builtin_amdgcn_perm(cd, lane4, 0x0C0C0500u));
+        o.z = *reinterpret_cast<const uint32_t *>(tbl_b + __builtin_amdgcn_perm(cd, lane4, 0x0C0C0600u));
+        o.w = *reinterpret_cast<const uint32_t *>(tbl_b + __builtin_amdgcn_perm(cd, lane4, 0x0C0C0700u));
+        return o;
+    };
+
+    constexpr int NI = TW * DEC_KB;           // (tile, block) items per chunk, tile-major
+    constexpr int NU = (NI + 3) / 4;          // items whose scale this lane computes
+    constexpr int D = NI < 12 ? NI : 12;      // code loads in flight per wave
+    const int nchunks = (p.nbw + DEC_KB - 1) / DEC_KB;
+    for (int ch = 0; ch < nchunks; ++ch) {
+        const int64_t cb = wblk0 + (int64_t)ch * DEC_KB;
+        // codes of item i: lane 4 n + q reads bytes 8 q .. 8 q + 7 of row n's block
+        auto load_code = [&](int i) {
+            const int t = i / DEC_KB, b = i % DEC_KB;
+            const int64_t row = row_w + 16 * t + (lane >> 2);
+            const bool ok = row < d && cb + b < wblk1;
+            const uint32_t off = (uint32_t)(row * (k / 2) + 32 * (cb + b) + 8 * (lane & 3));
+            return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rcode, ok ? off : DEC_OOB, 0, 0));
+        };
+        // X (and A) fragments of the chunk's blocks; blocks past the range read zero
+        uint4 xf[DEC_KB][2], af[DEC_KB][2];
+#pragma unroll
+        for (int b = 0; b < DEC_KB; ++b) {
+            const bool ok = cb + b < wblk1;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const uint32_t off = (uint32_t)((n16 * k + 64 * (cb + b) + 16 * g + 8 * j) * 2);
+                xf[b][j] = load16(rx, ok ? off : DEC_OOB);
+                af[b][j] = u_wave ? load16(ra, ok ? off : DEC_OOB) : uint4{0, 0, 0, 0};
             }
         }
-        // all codes and block constants of this wave's groups, in flight together
-        uint4 cw[NT][DEC_MAX_GROUPS];
-        int c2v[NT][DEC_MAX_GROUPS];
-        float c1v[NT][DEC_MAX_GROUPS];
+        // block constants: this lane takes items i = g + 4 u of row n16
+        int c2v[NU];
+        float c1v[NU];
+        bool okv[NU];
 #pragma unroll
-        for (int q = 0; q < DEC_MAX_GROUPS; ++q) {
-            if (q >= ngroups) break;
-            const int64_t bq = s0 / 64 + b0 + 2 * q;  // first block of the group (row-relative)
-            const int64_t blk = bq + (g >> 1);
+        for (int u = 0; u < NU; ++u) {
+            const int i = g + 4 * u;
+            const int t = i / DEC_KB, b = i % DEC_KB;
+            const int64_t row = row_w + 16 * t + n16;
+            const int64_t blk = cb + b;
+            okv[u] = i < NI && row < d && blk < wblk1;
+            const int64_t jb = row * kb + blk;
+            c2v[u] = (int)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(rc2, okv[u] ? (uint32_t)jb : DEC_OOB, 0, 0);
+            c1v[u] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(rc1, okv[u] ? (uint32_t)((jb >> 8) * 4) : DEC_OOB, 0, 0));
+        }
+        uint2 cw[D];
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                cw[t][q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                         rc, code_voff + (uint32_t)(16 * t * (p.k / 2)) + (uint32_t)(bq * 32), 0, 0));
-                const int row = 16 * t + r16;
-                c2v[t][q] = (int)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(rs2, (uint32_t)(row * kb + blk), 0, 0);
-                const bool ok = n0 + row < p.d;
-                const int64_t jb = ok ? (n0 + row) * kb + (blk < kb ? blk : kb - 1) : 0;
-                c1v[t][q] = p.c1[jb >> 8];
+        for (int i = 0; i < D; ++i) cw[i] = load_code(i);
+        if (ch == 0) {
+            // pair table: entry e = bf16(C[e & 15]) | bf16(C[e >> 4]) << 16 at dword 64 e + lane
+            float lvf = tab.level[0];
+#pragma unroll
+            for (int j = 1; j < 16; ++j) lvf = n16 == j ? tab.level[j] : lvf;
+            const int lv = __float_as_int(lvf);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int flat = tid + DEC_THREADS * i;
+                const int e = flat >> 4;
+                const float lo = __int_as_float(__builtin_amdgcn_ds_bpermute((e & 15) << 2, lv));
+                const float hi = __int_as_float(__builtin_amdgcn_ds_bpermute((e >> 4) << 2, lv));
+                const uint32_t v = pack_bf16x2(lo, hi);
+                reinterpret_cast<uint4 *>(tbl)[flat] = uint4{v, v, v, v};
+            }
+            __syncthreads();
+        }
+        if (u_wave) {  // U partial while the codes are in flight
+#pragma unroll
+            for (int b = 0; b < DEC_KB; ++b) {
+                uacc = mfma16(xf[b][0], af[b][0], uacc);
+                uacc = mfma16(xf[b][1], af[b][1], uacc);
             }
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // X slab in LDS
+        float sreg[NU];
 #pragma unroll
-        for (int q = 0; q < DEC_MAX_GROUPS; ++q) {
-            if (q >= ngroups) break;
-            const bool live_k = b0 + 2 * q + (g >> 1) < b1;  // missing half of an odd tail
-            // X[m][32 g + 8 i .. +7] of the group, m = r16 (rows past M: zero)
-            const int64_t kx = (b0 + 2 * q) * 64 + 32 * g;
-            uint4 xf[4];
+        for (int u = 0; u < NU; ++u) sreg[u] = okv[u] ? dq_scale((int8_t)c2v[u], c1v[u], mean) : 0.0f;
+
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                xf[i] = (r16 < M && live_k)
-                            ? *reinterpret_cast<const uint4 *>(dyn_smem + r16 * xrow_bytes + (kx + 8 * i) * 2)
-                            : uint4{0, 0, 0, 0};
-            }
+        for (int i = 0; i < NI; ++i) {
+            const int t = i / DEC_KB, b = i % DEC_KB;
+            const uint2 c = cw[i % D];
+            if (i + D < NI) cw[i % D] = load_code(i + D);
+            const uint32_t d0 = (uint32_t)__builtin_amdgcn_ds_bpermute(code_src, (int)c.x);
+            const uint32_t d1 = (uint32_t)__builtin_amdgcn_ds_bpermute(code_src, (int)c.y);
+            f32x4 tmp = mfma16(xf[b][0], lut4(d0), f32x4{0.f, 0.f, 0.f, 0.f});
+            tmp = mfma16(xf[b][1], lut4(d1), tmp);
+            const float sc = __int_as_float(
+                __builtin_amdgcn_ds_bpermute((n16 + 16 * (i % 4)) * 4, __float_as_int(sreg[i / 4])));
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const bool live = live_k && (n0 + 16 * t + r16 < p.d);
-                const float sc = live ? dq_scale((int8_t)c2v[t][q], c1v[t][q], mean) : 0.0f;
-                uint32_t cws[4];
-                cws[0] = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_addr, (int)cw[t][q].x);
-                cws[1] = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_addr, (int)cw[t][q].y);
-                cws[2] = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_addr, (int)cw[t][q].z);
-                cws[3] = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_addr, (int)cw[t][q].w);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float w8[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) w8[e] = level(code_addr(cws[i], e), lv) * sc;
-                    const uint4 wv{pack_bf16x2(w8[0], w8[1]), pack_bf16x2(w8[2], w8[3]), pack_bf16x2(w8[4], w8[5]),
-                                   pack_bf16x2(w8[6], w8[7])};
-                    acc[t] = mfma16(wv, xf[i], acc[t]);
-                }
-            }
+            for (int v = 0; v < MV; ++v) acc[t][v] = __builtin_fmaf(sc, tmp[v], acc[t][v]);
         }
     }
-    // cross-wave sum (fixed order), adapter term, bf16 store
+
+    // ---- cross-wave sums (fixed order) --------------------------------------
 #pragma unroll
-    for (int t = 0; t < NT; ++t) red[wave][t][lane] = acc[t];
+    for (int t = 0; t < TW; ++t) red[wave][t][lane] = acc[t];
+    if (u_wave) ured[kpart][lane] = uacc;
     __syncthreads();
-    if (wave < NT) {
-        const int t = wave;
-        const f32x4 v = (red[0][t][lane] + red[1][t][lane]) + (red[2][t][lane] + red[3][t][lane]);
-        const int m = r16;
-        if (m < M) {
+    f32x4 ysum[NTT];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t n = n0 + 16 * t + 4 * g + e;
-                if (n >= p.d) continue;
-                float ad = 0.0f;
-                for (int j = 0; j < p.r; ++j)
-                    ad = __builtin_fmaf(p.U[(int64_t)m * p.r + j], bf16_bits_to_f32(p.B[n * p.r + j]), ad);
-                const float out = v[e] + p.s * ad;
-                p.y[(int64_t)m * p.d + n] = (uint16_t)(pack_bf16x2(out, 0.0f) & 0xFFFFu);
+    for (int h = 0; h < NTT; ++h) {
+        const int tt = wave + DEC_WAVES * h;
+        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (tt < T) {
+            const int ts = tt / TW, t = tt % TW;
+            for (int q = 0; q < P; ++q) a += red[ts * P + q][t][lane];
+        }
+        ysum[h] = a;
+    }
+    f32x4 usum = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (fuse_u && wave == 0)
+        for (int q = 0; q < P; ++q) usum += ured[q][lane];
+
+    if (S > 1) {
+        // publish this slice's partials (slots [wg][tt][lane], then U at [wg][T][lane]);
+        // the last workgroup of the group to arrive adds all S in slice order
+#pragma unroll
+        for (int h = 0; h < NTT; ++h) {
+            const int tt = wave + DEC_WAVES * h;
+            if (tt < T) store16_sc1(rp, (uint32_t)((((int64_t)wg * (T + 1) + tt) * 64 + lane) * 16), ysum[h]);
+        }
+        if (fuse_u && wave == 0) store16_sc1(rp, (uint32_t)((((int64_t)wg * (T + 1) + T) * 64 + lane) * 16), usum);
+        __builtin_amdgcn_s_waitcnt(0);  // stores acknowledged before the count
+        __syncthreads();
+        if (tid == 0) {
+            unsigned long long *c = p.ctr + grp;
+            const unsigned long long tag0 = (unsigned long long)DEC_TAG << 32;
+            if ((ctr0 >> 32) != DEC_TAG) {  // first use of this workspace: tag the counter
+                unsigned long long expect = ctr0;
+                __hip_atomic_compare_exchange_strong(c, &expect, tag0, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
             }
+            const unsigned long long old = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int last = (int)(old & 0xFFFFFFFFull) == S - 1;
+            if (last) __hip_atomic_store(c, tag0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last_flag = last;
+        }
+        __syncthreads();
+        if (!last_flag) return;
+        f32x4 pv[NTT][8];
+#pragma unroll
+        for (int h = 0; h < NTT; ++h) {
+            const int tt = wave + DEC_WAVES * h;
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                pv[h][q] = q < S && tt < T
+                               ? load16_sc1(rp, (uint32_t)((((int64_t)(grp * S + q) * (T + 1) + tt) * 64 + lane) * 16))
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        f32x4 uv[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            uv[q] = fuse_u && wave == 0 && q < S
+                        ? load16_sc1(rp, (uint32_t)((((int64_t)(grp * S + q) * (T + 1) + T) * 64 + lane) * 16))
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h = 0; h < NTT; ++h) {
+            f32x4 a = pv[h][0];
+#pragma unroll
+            for (int q = 1; q < 8; ++q)
+                if (q < S) a += pv[h][q];
+            ysum[h] = a;
+        }
+        f32x4 a = uv[0];
+#pragma unroll
+        for (int q = 1; q < 8; ++q)
+            if (q < S) a += uv[q];
+        usum = a;
+    }
+
+    // ---- adapter term and bf16 store ------------------------------------------
+    if (fuse_u && wave == 0) {
+        // lane (j, g) holds U[4 g + v][j]
+#pragma unroll
+        for (int v = 0; v < 4; ++v) us[4 * g + v][n16] = usum[v];
+        if (p.u_save && grp == 0 && n16 < r) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                if (4 * g + v < M) p.u_save[(4 * g + v) * r + n16] = usum[v];
+        }
+    }
+    __syncthreads();
+    // s U B^T as an MFMA pair: U split into bf16 hi + lo, lane (m, g) holds U[m][8 g .. + 7]
+    uint4 uhi{0, 0, 0, 0}, ulo{0, 0, 0, 0};
+    if (fuse_u && g < 2) {
+        const f32x4 u0 = *reinterpret_cast<const f32x4 *>(&us[n16][8 * g]);
+        const f32x4 u1 = *reinterpret_cast<const f32x4 *>(&us[n16][8 * g + 4]);
+        const float uu[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+        uint32_t h2[4], l2[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            h2[e] = pack_bf16x2(uu[2 * e], uu[2 * e + 1]);
+            l2[e] = pack_bf16x2(uu[2 * e] - bf16_bits_to_f32(h2[e] & 0xFFFFu),
+                                uu[2 * e + 1] - bf16_bits_to_f32(h2[e] >> 16));
+        }
+        uhi = uint4{h2[0], h2[1], h2[2], h2[3]};
+        ulo = uint4{l2[0], l2[1], l2[2], l2[3]};
+    }
+#pragma unroll
+    for (int h = 0; h < NTT; ++h) {
+        const int tt = wave + DEC_WAVES * h;
+        const int64_t row = row_g + 16 * tt + n16;
+        if (tt >= T) continue;
+        f32x4 ad = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (fuse_u) {
+            ad = mfma16(uhi, bfr[h], ad);
+            ad = mfma16(ulo, bfr[h], ad);
+        }
+        if (row >= d) continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int m = 4 * g + v;
+            if (m >= M) continue;
+            float a2 = ad[v];
+            if (!fuse_u) {
+                a2 = 0.0f;
+                for (int j = 0; j < r; ++j)
+                    a2 = __builtin_fmaf(p.U[m * r + j], bf16_bits_to_f32(p.B[row * r + j]), a2);
+            }
+            const float out = ysum[h][v] + p.s * a2;
+            p.y[(int64_t)m * d + row] = (uint16_t)(pack_bf16x2(out, 0.0f) & 0xFFFFu);
         }
     }
 }
 
+struct DecodePlan {
+    int S, T, TW, P, nbw, groups, grid;
+};
+
+DecodePlan decode_plan(int64_t d, int64_t k) {
+    const int64_t kb = k / 64, ntiles = (d + 15) / 16;
+    DecodePlan pl;
+    pl.P = 4;  // two tile subsets of four k-ranges each
+    const int ts = DEC_WAVES / pl.P;
+    int64_t S = (kb + pl.P * DEC_KB - 1) / (pl.P * DEC_KB);  // one chunk per wave
+    if (S > 8) S = 8;
+    pl.S = (int)S;
+    pl.nbw = (int)((kb + S * pl.P - 1) / (S * pl.P));
+    // about one workgroup per compute unit
+    const int64_t t_need = (ntiles * S + 255) / 256;
+    int64_t tw = (t_need + ts - 1) / ts;
+    tw = tw < 1 ? 1 : (tw > DEC_MAX_TW ? DEC_MAX_TW : tw);
+    pl.TW = (int)tw;
+    pl.T = ts * pl.TW;
+    pl.groups = (int)((ntiles + pl.T - 1) / pl.T);
+    if (pl.S > 1 && pl.groups > DEC_MAX_GROUPS) {  // too many counters: one slice
+        pl.S = 1;
+        pl.nbw = (int)((kb + pl.P - 1) / pl.P);
+    }
+    pl.grid = pl.groups * pl.S;
+    return pl;
+}
+
+template <int TW>
+hipError_t launch_tw(const DecodeArgs &a, int mv, int grid, hipStream_t st) {
+    if (mv == 1) hipLaunchKernelGGL((nf4_decode_kernel<TW, 1>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
+    else hipLaunchKernelGGL((nf4_decode_kernel<TW, 4>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
+    return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_decode_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, const float *U,
-                             const uint16_t *B, int r, float s, uint16_t *Y, hipStream_t st) {
-    if (M > 16) return hipErrorInvalidValue;
+size_t decode_counter_bytes() { return sizeof(unsigned long long) * DEC_MAX_GROUPS; }
+
+size_t decode_part_bytes(int64_t M, int64_t d, int64_t k) {
+    if (M < 1 || M > 16) return 0;
+    const DecodePlan pl = decode_plan(d, k);
+    if (pl.S == 1) return 0;
+    return sizeof(f32x4) * (size_t)pl.grid * 64 * ((size_t)pl.T + 1);
+}
+
+hipError_t launch_decode_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, const uint16_t *A, const float *U,
+                             const uint16_t *B, int r, float s, uint16_t *Y, float *U_save, float *part,
+                             unsigned long long *ctr, hipStream_t st) {
+    if (M < 1 || M > 16 || (!U && (!A || r > 16)) || w.k > (int64_t(1) << 25)) return hipErrorInvalidValue;
+    const DecodePlan pl = decode_plan(w.d, w.k);
+    if (pl.S > 1 && (!part || !ctr)) return hipErrorInvalidValue;
     DecodeArgs a;
     a.codes = w.codes;
     a.c2 = w.c2;
@@ -214,19 +456,32 @@ hipError_t launch_decode_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, 
     a.d = w.d;
     a.k = w.k;
     a.x = x;
-    a.M = M;
+    a.M = (int)M;
+    a.A = A;
     a.U = U;
     a.B = B;
     a.r = r;
     a.s = s;
     a.y = Y;
-    // two 16-row tiles per workgroup once there are enough rows to fill the chip
-    const int nt = w.d >= 2 * DEC_ROWS * 512 ? 2 : 1;
-    const dim3 grid((unsigned)((w.d + DEC_ROWS * nt - 1) / (DEC_ROWS * nt)));
-    const size_t lds = (size_t)M * (DEC_SLAB_K * 2 + 16);
-    if (nt == 2) hipLaunchKernelGGL(nf4_decode_kernel<2>, grid, dim3(256), lds, st, a, nf4_consts());
-    else hipLaunchKernelGGL(nf4_decode_kernel<1>, grid, dim3(256), lds, st, a, nf4_consts());
-    return hipGetLastError();
+    a.u_save = U ? nullptr : U_save;
+    a.part = part;
+    a.grid_ = pl.grid;
+    a.ctr = ctr;
+    a.S = pl.S;
+    a.T = pl.T;
+    a.P = pl.P;
+    a.nbw = pl.nbw;
+    const int mv = M == 1 ? 1 : 4;
+    switch (pl.TW) {
+        case 1: return launch_tw<1>(a, mv, pl.grid, st);
+        case 2: return launch_tw<2>(a, mv, pl.grid, st);
+        case 3: return launch_tw<3>(a, mv, pl.grid, st);
+        case 4: return launch_tw<4>(a, mv, pl.grid, st);
+        case 5: return launch_tw<5>(a, mv, pl.grid, st);
+        case 6: return launch_tw<6>(a, mv, pl.grid, st);
+        case 7: return launch_tw<7>(a, mv, pl.grid, st);
+        default: return launch_tw<8>(a, mv, pl.grid, st);
+    }
 }
 
 }  // namespace qnf4

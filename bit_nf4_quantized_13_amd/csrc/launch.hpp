@@ -71,8 +71,16 @@ hipError_t launch_gemm_dx(const Nf4Weights &w, const uint16_t *dy, int64_t M, co
                           const uint16_t *A, int r, float s, uint16_t *dX, const GemmWs &ws,
                           hipStream_t st);
 
-// Decode-shaped forward, M <= 16: Y = X What^T + s U B^T with U [M x r] fp32.
-hipError_t launch_decode_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, const float *U,
-                             const uint16_t *B, int r, float s, uint16_t *Y, hipStream_t st);
+// Decode-shaped forward, M <= 16: Y = X What^T + s U B^T.  U [M x r] fp32 is
+// either given (U != null) or computed in the same kernel from A [r x k]
+// (U == null, r <= 16; written to U_save when that is not null).  part holds
+// decode_part_bytes(M, d, k) bytes of partial sums; ctr points at
+// decode_counter_bytes() bytes of counters that no other kernel writes (the
+// kernel tags them on first use and leaves them ready for the next call).
+size_t decode_counter_bytes();
+size_t decode_part_bytes(int64_t M, int64_t d, int64_t k);
+hipError_t launch_decode_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, const uint16_t *A, const float *U,
+                             const uint16_t *B, int r, float s, uint16_t *Y, float *U_save, float *part,
+                             unsigned long long *ctr, hipStream_t st);
 
 }  // namespace qnf4

@@ -120,8 +120,15 @@ size_t qlora_linear_workspace(int64_t M, int64_t d, int64_t k, int32_t r);
  * chkda, "Double quantization and double dequantization" (the full QLoRA
  * expression, Y = X doubleDequant(c1, c2, W_NF4) + X L1 L2 with L1 = A^T,
  * L2 = B^T and the scale alpha/r of "How does alpha/r control adapter
- * strength?").  What is expanded from the NF4 codes on the fly, bit-identical
- * to qlora_nf4_dequantize; products accumulate in fp32.
+ * strength?").  Products accumulate in fp32.  For M > 16, What is expanded
+ * from the NF4 codes on the fly, bit-identical to qlora_nf4_dequantize.  For
+ * M <= 16 (decode) the 64-weight block scale is applied once to the fp32 sum
+ * over the block, with the NF4 levels in bf16: the same product, rounded
+ * differently (within the library's fwd tolerance of the bf16 What product).
+ * A call with M <= 16 and r <= 16 is one kernel (U = X A^T included); it
+ * keeps counters in the first 32 KiB of the workspace between calls, which
+ * it tags and resets itself: the caller need not clear them, but must not
+ * write into that region between calls.
  *   x      device bf16 [M x k], 16-byte aligned
  *   A      device bf16 [r x k], 16-byte aligned;  B device bf16 [d x r]
  *   r      1..128; alpha finite

@@ -54,7 +54,8 @@ def test_single_layer_workload():
 
 @pytest.mark.parametrize("m,d,k,r", [(1, 256, 512, 8), (300, 320, 192, 8), (257, 512, 320, 1),
                                      (64, 264, 128, 7), (130, 256, 256, 33), (33, 512, 1024, 64),
-                                     (20, 128, 256, 128)])
+                                     (20, 128, 256, 128), (16, 200, 448, 33), (3, 136, 1088, 16),
+                                     (5, 4104, 4096, 16), (16, 64, 64, 1)])
 def test_shapes_ranks_and_ragged_tiles(m, d, k, r):
     inp = make_layer(21, m * 7 + r, d, k, m, r)
     check_layer(inp, 16.0, f"shape m={m} d={d} k={k} r={r}", bf16_rounding_allowance=True)
@@ -71,6 +72,31 @@ def test_decode_shapes_forward(proj, m):
     wl = WORKLOADS["decode"]
     check_layer(workload_layer("decode", proj), wl.alpha, f"decode {wl.projections[proj].name}",
                 m=m, want_bwd=False)
+
+
+def test_decode_workspace_reuse_and_garbage():
+    """The one-kernel decode path keeps per-group counters in the workspace:
+    a workspace full of garbage, reused across calls and shapes, must give the
+    same bits as a fresh zeroed one every time."""
+    import bit_nf4_quantized_13_amd as q
+    say("decode workspace garbage / reuse")
+    inp = make_layer(43, 0, 4096, 4096, 64, 16)
+    w = q.qlora_nf4_quantize(to_dev_f32(inp.w0))
+    xd, ad, bd = (to_dev_bf16(t) for t in (inp.x, inp.a, inp.b))
+    nbytes = max(q.linear_workspace_bytes(m, 4096, 4096, 16) for m in (1, 4, 16, 64))
+    clean = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    dirty = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    for m in (16, 1, 4, 16):
+        ya, ua = q.qlora_linear_fwd(w, xd[:m], ad, bd, 32.0, workspace=clean)
+        yb, ub = q.qlora_linear_fwd(w, xd[:m], ad, bd, 32.0, workspace=dirty)
+        assert torch.equal(ya, yb) and torch.equal(ua, ub), m
+    # a larger-M call in between writes other data into the same workspace
+    q.qlora_linear_fwd(w, xd, ad, bd, 32.0, workspace=dirty)
+    q.qlora_linear_bwd(w, xd, to_dev_bf16(inp.dy), ad, bd, 32.0, workspace=dirty)
+    yb, ub = q.qlora_linear_fwd(w, xd[:16], ad, bd, 32.0, workspace=dirty)
+    ya, ua = q.qlora_linear_fwd(w, xd[:16], ad, bd, 32.0, workspace=clean)
+    assert torch.equal(ya, yb) and torch.equal(ua, ub)
+    torch.cuda.synchronize()
 
 
 def canon(bits: np.ndarray) -> np.ndarray:
