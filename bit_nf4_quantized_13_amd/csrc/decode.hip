@@ -46,6 +46,7 @@ constexpr int DEC_MAX_TW = 8;                // tiles per wave
 constexpr int DEC_MAX_GROUPS = 4096;         // counters reserved in the workspace
 constexpr uint32_t DEC_TAG = 0x4E463444u;    // high word of an initialised counter
 constexpr uint32_t DEC_OOB = 0x80000000u;    // buffer offset past every range used here
+constexpr int DEC_US_LD = 132;               // row stride of U in LDS (r <= 128, 16-byte rows)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
@@ -94,21 +95,20 @@ __device__ __forceinline__ f32x4 load16_sc1(__amdgpu_buffer_rsrc_t r, uint32_t o
     return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, DEC_SC1));
 }
 
-// B[row][8 g .. 8 g + 7] as a bf16x8 MFMA operand (zero past r or for g >= 2)
-__device__ __forceinline__ uint4 load_bfrag(__amdgpu_buffer_rsrc_t rb, int64_t row, int g, int r, bool ok) {
-    uint4 o{0, 0, 0, 0};
-    if (!ok || 8 * g >= r) return o;
-    if (r % 8 == 0) return load16(rb, (uint32_t)((row * r + 8 * g) * 2));
+// B[row][j0 .. j0 + 7] as a bf16x8 MFMA operand (zero past r or when !ok).
+// Straight-line code: every load is issued, out-of-range ones at an offset past
+// the buffer (they read zero).
+__device__ __forceinline__ uint4 load_bfrag(__amdgpu_buffer_rsrc_t rb, int row, int j0, int r, bool ok) {
+    const bool live = ok && j0 < r;
+    if (r % 8 == 0) return load16(rb, live ? (uint32_t)(((int64_t)row * r + j0) * 2) : DEC_OOB);
     uint32_t h[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-        h[e] = 8 * g + e < r ? __builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)((row * r + 8 * g + e) * 2), 0, 0)
-                             : 0u;
-    o.x = h[0] | (h[1] << 16);
-    o.y = h[2] | (h[3] << 16);
-    o.z = h[4] | (h[5] << 16);
-    o.w = h[6] | (h[7] << 16);
-    return o;
+    for (int e = 0; e < 8; ++e) {
+        const bool in = live && j0 + e < r;
+        h[e] = __builtin_amdgcn_raw_buffer_load_b16(rb, in ? (uint32_t)(((int64_t)row * r + j0 + e) * 2) : DEC_OOB,
+                                                     0, 0);
+    }
+    return uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
 }
 
 template <int TW, int MV>  // TW tiles per wave; MV result registers that can hold m < M
@@ -116,36 +116,34 @@ __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, N
     __shared__ __attribute__((aligned(16))) uint32_t tbl[256 * 64];  // pair table, one copy per lane
     __shared__ f32x4 red[DEC_WAVES][TW][64];
     __shared__ f32x4 ured[DEC_WAVES][64];
-    __shared__ __attribute__((aligned(16))) float us[16][20];
+    __shared__ __attribute__((aligned(16))) float us[16][DEC_US_LD];  // U [m][j] for the adapter term
     __shared__ int last_flag;
 
+    // All offsets fit in 31 bits (d k <= 2^30, k <= 2^25): 32-bit index math.
+    // Rows past d land past the end of their buffer and read zero.
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g = lane >> 4;
     const int S = p.S, P = p.P, T = p.T, M = p.M, r = p.r;
     const int wg = blockIdx.x, sl = wg % S, grp = wg / S;
     const int kpart = wave % P, tsub = wave / P;
-    const int64_t d = p.d, k = p.k, kb = k / 64;
-    const int64_t wblk0 = ((int64_t)sl * P + kpart) * p.nbw;  // this wave's blocks [wblk0, wblk1)
-    const int64_t wblk1 = wblk0 + p.nbw < kb ? wblk0 + p.nbw : kb;
-    const int64_t row_g = (int64_t)grp * T * 16;               // first row of the tile group
-    const int64_t row_w = row_g + (int64_t)tsub * TW * 16;     // first row of this wave's tiles
+    const int d = (int)p.d, k = (int)p.k, kb = k / 64, hk = k / 2;
+    const int wblk0 = (sl * P + kpart) * p.nbw;                  // this wave's blocks [wblk0, wblk1)
+    const int wblk1 = wblk0 + p.nbw < kb ? wblk0 + p.nbw : kb;
+    const int row_g = grp * T * 16;                               // first row of the tile group
+    const int row_w = row_g + tsub * TW * 16;                     // first row of this wave's tiles
     const bool fuse_u = p.U == nullptr;
     const bool u_wave = fuse_u && tsub == 0;
-    const float mean = *p.mean;
 
-    const __amdgpu_buffer_rsrc_t rcode = make_rsrc(p.codes, d * k / 2);
-    const __amdgpu_buffer_rsrc_t rc2 = make_rsrc(p.c2, d * kb);
-    const __amdgpu_buffer_rsrc_t rc1 = make_rsrc(p.c1, ((d * kb + 255) / 256) * 4);
+    const __amdgpu_buffer_rsrc_t rcode = make_rsrc(p.codes, (int64_t)d * hk);
+    const __amdgpu_buffer_rsrc_t rc2 = make_rsrc(p.c2, (int64_t)d * kb);
+    const __amdgpu_buffer_rsrc_t rc1 = make_rsrc(p.c1, (((int64_t)d * kb + 255) / 256) * 4);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (int64_t)M * k * 2);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, fuse_u ? (int64_t)r * k * 2 : 0);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, d * r * 2);
-    const int64_t part_f4 = (int64_t)p.S > 1 ? (int64_t)(p.grid_) * (T + 1) * 64 : 0;  // f32x4 slots
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, (int64_t)d * r * 2);
+    const __amdgpu_buffer_rsrc_t rmean = make_rsrc(p.mean, 4);
+    const int64_t part_f4 = p.S > 1 ? (int64_t)p.grid_ * (T + 1) * 64 : 0;  // f32x4 slots
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.part, part_f4 * 16);
-
-    // the group counter, read now and used at the end (tags a fresh workspace)
-    unsigned long long ctr0 = 0;
-    if (S > 1 && tid == 0) ctr0 = __hip_atomic_load(p.ctr + grp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // thread (tile tt of the group, lane): tt = wave, wave + 8; B fragments for the adapter
     constexpr int NTT = (2 * DEC_MAX_TW + DEC_WAVES - 1) / DEC_WAVES;
@@ -153,8 +151,17 @@ __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, N
 #pragma unroll
     for (int h = 0; h < NTT; ++h) {
         const int tt = wave + DEC_WAVES * h;
-        const int64_t row = row_g + 16 * tt + n16;
-        bfr[h] = load_bfrag(rb, row, g, r, fuse_u && tt < T && row < d);
+        bfr[h] = load_bfrag(rb, row_g + 16 * tt + n16, 8 * g, r, tt < T);
+    }
+
+    // a given U [M x r] (r > 16): prefetched, parked in LDS with the table
+    constexpr int NUV = 16 * 128 / DEC_THREADS;
+    float uvv[NUV];
+    const __amdgpu_buffer_rsrc_t ru = make_rsrc(p.U, fuse_u ? 0 : (int64_t)M * r * 4);
+#pragma unroll
+    for (int u = 0; u < NUV; ++u) {
+        const int e = tid + DEC_THREADS * u;
+        uvv[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ru, e < M * r ? (uint32_t)e * 4 : DEC_OOB, 0, 0));
     }
 
     f32x4 acc[TW];
@@ -175,48 +182,65 @@ __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, N
         return o;
     };
 
-    constexpr int NI = TW * DEC_KB;           // (tile, block) items per chunk, tile-major
-    constexpr int NU = (NI + 3) / 4;          // items whose scale this lane computes
-    constexpr int D = NI < 12 ? NI : 12;      // code loads in flight per wave
+    constexpr int NI = TW * DEC_KB;          // (tile, block) items per chunk, tile-major
+    constexpr int NQ = (TW + 3) / 4;         // tiles whose block constants this lane loads
+    constexpr int D = NI;                    // code loads in flight per wave: all of the chunk's
+    const uint32_t tstride = 16u * (uint32_t)hk;  // bytes of codes per 16-row tile
     const int nchunks = (p.nbw + DEC_KB - 1) / DEC_KB;
     for (int ch = 0; ch < nchunks; ++ch) {
-        const int64_t cb = wblk0 + (int64_t)ch * DEC_KB;
+        const int cb = wblk0 + ch * DEC_KB;
+        const int nval = wblk1 - cb;  // blocks of this chunk in range (uniform; may be <= 0)
         // codes of item i: lane 4 n + q reads bytes 8 q .. 8 q + 7 of row n's block
+        const uint32_t code0 = (uint32_t)((row_w + (lane >> 2)) * hk + 32 * cb + 8 * (lane & 3));
         auto load_code = [&](int i) {
             const int t = i / DEC_KB, b = i % DEC_KB;
-            const int64_t row = row_w + 16 * t + (lane >> 2);
-            const bool ok = row < d && cb + b < wblk1;
-            const uint32_t off = (uint32_t)(row * (k / 2) + 32 * (cb + b) + 8 * (lane & 3));
-            return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rcode, ok ? off : DEC_OOB, 0, 0));
+            const uint32_t off = b < nval ? code0 + (uint32_t)t * tstride + 32u * b : DEC_OOB;
+            return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rcode, off, 0, 0));
         };
-        // X (and A) fragments of the chunk's blocks; blocks past the range read zero
+        // X (and A) fragments of the chunk's blocks
+        const uint32_t x0 = (uint32_t)((n16 * k + 64 * cb + 16 * g) * 2);
         uint4 xf[DEC_KB][2], af[DEC_KB][2];
 #pragma unroll
         for (int b = 0; b < DEC_KB; ++b) {
-            const bool ok = cb + b < wblk1;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const uint32_t off = (uint32_t)((n16 * k + 64 * (cb + b) + 16 * g + 8 * j) * 2);
-                xf[b][j] = load16(rx, ok ? off : DEC_OOB);
-                af[b][j] = u_wave ? load16(ra, ok ? off : DEC_OOB) : uint4{0, 0, 0, 0};
+                const uint32_t off = b < nval ? x0 + 128u * b + 16u * j : DEC_OOB;
+                xf[b][j] = load16(rx, off);
+                af[b][j] = u_wave ? load16(ra, off) : uint4{0, 0, 0, 0};
             }
         }
-        // block constants: this lane takes items i = g + 4 u of row n16
-        int c2v[NU];
-        float c1v[NU];
-        bool okv[NU];
+        // block constants: lane (n, g) loads tiles t = g + 4 u of row n: the chunk's
+        // four c2 bytes as one dword and their one c1 (four blocks at a multiple of
+        // four never straddle a 256-block group)
+        const bool c2vec = (kb % 4 == 0) && (cb % 4 == 0);  // uniform
+        uint32_t c2w[NQ];
+        float c1q[NQ][DEC_KB];
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int i = g + 4 * u;
-            const int t = i / DEC_KB, b = i % DEC_KB;
-            const int64_t row = row_w + 16 * t + n16;
-            const int64_t blk = cb + b;
-            okv[u] = i < NI && row < d && blk < wblk1;
-            const int64_t jb = row * kb + blk;
-            c2v[u] = (int)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(rc2, okv[u] ? (uint32_t)jb : DEC_OOB, 0, 0);
-            c1v[u] = __uint_as_float(
-                __builtin_amdgcn_raw_buffer_load_b32(rc1, okv[u] ? (uint32_t)((jb >> 8) * 4) : DEC_OOB, 0, 0));
+        for (int u = 0; u < NQ; ++u) {
+            const int row = row_w + 16 * (g + 4 * u) + n16;
+            const uint32_t jb = (uint32_t)(row * kb + cb);
+            const bool tile_ok = g + 4 * u < TW && nval > 0;
+            if (c2vec) {
+                c2w[u] = __builtin_amdgcn_raw_buffer_load_b32(rc2, tile_ok ? jb : DEC_OOB, 0, 0);
+                const float c1 = __uint_as_float(
+                    __builtin_amdgcn_raw_buffer_load_b32(rc1, tile_ok ? (jb >> 8) * 4 : DEC_OOB, 0, 0));
+#pragma unroll
+                for (int b = 0; b < DEC_KB; ++b) c1q[u][b] = c1;
+            } else {
+                uint32_t w = 0;
+#pragma unroll
+                for (int b = 0; b < DEC_KB; ++b) {
+                    const bool ok = tile_ok && b < nval;
+                    w |= __builtin_amdgcn_raw_buffer_load_b8(rc2, ok ? jb + b : DEC_OOB, 0, 0) << (8 * b);
+                    c1q[u][b] = __uint_as_float(
+                        __builtin_amdgcn_raw_buffer_load_b32(rc1, ok ? ((jb + b) >> 8) * 4 : DEC_OOB, 0, 0));
+                }
+                c2w[u] = w;
+            }
         }
+        // the DQ mean through the vector memory path (a scalar load would make the
+        // wave wait for it before issuing anything else)
+        const float mean = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rmean, 0, 0, 0));
         uint2 cw[D];
 #pragma unroll
         for (int i = 0; i < D; ++i) cw[i] = load_code(i);
@@ -235,6 +259,13 @@ __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, N
                 const uint32_t v = pack_bf16x2(lo, hi);
                 reinterpret_cast<uint4 *>(tbl)[flat] = uint4{v, v, v, v};
             }
+            if (!fuse_u) {
+#pragma unroll
+                for (int u = 0; u < NUV; ++u) {
+                    const int e = tid + DEC_THREADS * u;
+                    if (e < M * r) us[e / r][e % r] = uvv[u];
+                }
+            }
             __syncthreads();
         }
         if (u_wave) {  // U partial while the codes are in flight
@@ -244,27 +275,63 @@ __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, N
                 uacc = mfma16(xf[b][1], af[b][1], uacc);
             }
         }
-        float sreg[NU];
+        // scales of the loaded constants (zero for blocks out of range and rows past d)
+        float sq[NQ][DEC_KB];
 #pragma unroll
-        for (int u = 0; u < NU; ++u) sreg[u] = okv[u] ? dq_scale((int8_t)c2v[u], c1v[u], mean) : 0.0f;
+        for (int u = 0; u < NQ; ++u) {
+            const bool row_ok = row_w + 16 * (g + 4 * u) + n16 < d;
+#pragma unroll
+            for (int b = 0; b < DEC_KB; ++b) {
+                const int8_t c2 = (int8_t)((c2w[u] >> (8 * b)) & 0xFFu);
+                sq[u][b] = row_ok && b < nval ? dq_scale(c2, c1q[u][b], mean) : 0.0f;
+            }
+        }
 
+        // four-stage software pipeline over the items, so that the LDS round
+        // trips of one item overlap the MFMAs of the previous ones:
+        //   A(i): code dwords into MFMA layout (ds_bpermute)
+        //   B(i): NF4 pair lookups (v_perm + ds_read_b32) and the item's scale
+        //   C(i): MFMA pair on the block
+        //   E(i): scaled accumulation into the tile's sum
+        uint32_t cd[2][2];
+        uint4 wv[2][2];
+        float scv[4];
+        f32x4 tmp[2];
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int t = i / DEC_KB, b = i % DEC_KB;
-            const uint2 c = cw[i % D];
-            if (i + D < NI) cw[i % D] = load_code(i + D);
-            const uint32_t d0 = (uint32_t)__builtin_amdgcn_ds_bpermute(code_src, (int)c.x);
-            const uint32_t d1 = (uint32_t)__builtin_amdgcn_ds_bpermute(code_src, (int)c.y);
-            f32x4 tmp = mfma16(xf[b][0], lut4(d0), f32x4{0.f, 0.f, 0.f, 0.f});
-            tmp = mfma16(xf[b][1], lut4(d1), tmp);
-            const float sc = __int_as_float(
-                __builtin_amdgcn_ds_bpermute((n16 + 16 * (i % 4)) * 4, __float_as_int(sreg[i / 4])));
+        for (int it = 0; it < NI + 3; ++it) {
+            __builtin_amdgcn_sched_barrier(0);  // keep the stages of one step together
+            if (it >= 3) {  // E(it - 3)
+                const int i = it - 3, t = i / DEC_KB;
 #pragma unroll
-            for (int v = 0; v < MV; ++v) acc[t][v] = __builtin_fmaf(sc, tmp[v], acc[t][v]);
+                for (int v = 0; v < MV; ++v) acc[t][v] = __builtin_fmaf(scv[i % 4], tmp[i % 2][v], acc[t][v]);
+            }
+            if (it >= 2 && it - 2 < NI) {  // C(it - 2)
+                const int i = it - 2, b = i % DEC_KB;
+                f32x4 z = mfma16(xf[b][0], wv[i % 2][0], f32x4{0.f, 0.f, 0.f, 0.f});
+                tmp[i % 2] = mfma16(xf[b][1], wv[i % 2][1], z);
+            }
+            if (it >= 1 && it - 1 < NI) {  // B(it - 1)
+                const int i = it - 1, t = i / DEC_KB, b = i % DEC_KB;
+                wv[i % 2][0] = lut4(cd[i % 2][0]);
+                wv[i % 2][1] = lut4(cd[i % 2][1]);
+                scv[i % 4] = __int_as_float(
+                    __builtin_amdgcn_ds_bpermute((n16 + 16 * (t % 4)) * 4, __float_as_int(sq[t / 4][b])));
+            }
+            if (it < NI) {  // A(it)
+                const int i = it;
+                const uint2 c = cw[i % D];
+                if (i + D < NI) cw[i % D] = load_code(i + D);
+                cd[i % 2][0] = (uint32_t)__builtin_amdgcn_ds_bpermute(code_src, (int)c.x);
+                cd[i % 2][1] = (uint32_t)__builtin_amdgcn_ds_bpermute(code_src, (int)c.y);
+            }
         }
     }
 
     // ---- cross-wave sums (fixed order) --------------------------------------
+    // the group counter: read here (after the last load the waves wait on), used
+    // after the partials are out; a fresh workspace gets it tagged
+    unsigned long long ctr0 = 0;
+    if (S > 1 && tid == 0) ctr0 = __hip_atomic_load(p.ctr + grp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
     for (int t = 0; t < TW; ++t) red[wave][t][lane] = acc[t];
     if (u_wave) ured[kpart][lane] = uacc;
@@ -353,44 +420,51 @@ __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, N
         }
     }
     __syncthreads();
-    // s U B^T as an MFMA pair: U split into bf16 hi + lo, lane (m, g) holds U[m][8 g .. + 7]
-    uint4 uhi{0, 0, 0, 0}, ulo{0, 0, 0, 0};
-    if (fuse_u && g < 2) {
-        const f32x4 u0 = *reinterpret_cast<const f32x4 *>(&us[n16][8 * g]);
-        const f32x4 u1 = *reinterpret_cast<const f32x4 *>(&us[n16][8 * g + 4]);
-        const float uu[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
-        uint32_t h2[4], l2[4];
+    // U B^T by MFMA over 32-wide slices of j: U split into bf16 hi + lo, lane
+    // (m, g) holds U[m][32 it + 8 g .. + 7], lane (n, g) holds B[n][same j]
+    f32x4 ad[NTT];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            h2[e] = pack_bf16x2(uu[2 * e], uu[2 * e + 1]);
-            l2[e] = pack_bf16x2(uu[2 * e] - bf16_bits_to_f32(h2[e] & 0xFFFFu),
-                                uu[2 * e + 1] - bf16_bits_to_f32(h2[e] >> 16));
+    for (int h = 0; h < NTT; ++h) ad[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nj = (r + 31) / 32;
+    for (int it = 0; it < nj; ++it) {
+        const int j0 = 32 * it + 8 * g;
+        uint4 uhi{0, 0, 0, 0}, ulo{0, 0, 0, 0};
+        if (j0 < r) {
+            const f32x4 u0 = *reinterpret_cast<const f32x4 *>(&us[n16][j0]);
+            const f32x4 u1 = *reinterpret_cast<const f32x4 *>(&us[n16][j0 + 4]);
+            float uu[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) uu[e] = j0 + e < r ? uu[e] : 0.0f;
+            uint32_t h2[4], l2[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                h2[e] = pack_bf16x2(uu[2 * e], uu[2 * e + 1]);
+                l2[e] = pack_bf16x2(uu[2 * e] - bf16_bits_to_f32(h2[e] & 0xFFFFu),
+                                    uu[2 * e + 1] - bf16_bits_to_f32(h2[e] >> 16));
+            }
+            uhi = uint4{h2[0], h2[1], h2[2], h2[3]};
+            ulo = uint4{l2[0], l2[1], l2[2], l2[3]};
         }
-        uhi = uint4{h2[0], h2[1], h2[2], h2[3]};
-        ulo = uint4{l2[0], l2[1], l2[2], l2[3]};
+#pragma unroll
+        for (int h = 0; h < NTT; ++h) {
+            const int tt = wave + DEC_WAVES * h;
+            if (tt >= T) continue;
+            const uint4 bf = it == 0 ? bfr[h] : load_bfrag(rb, row_g + 16 * tt + n16, j0, r, true);
+            ad[h] = mfma16(uhi, bf, ad[h]);
+            ad[h] = mfma16(ulo, bf, ad[h]);
+        }
     }
+    // all loads are done: the stores below never wait on each other
 #pragma unroll
     for (int h = 0; h < NTT; ++h) {
         const int tt = wave + DEC_WAVES * h;
-        const int64_t row = row_g + 16 * tt + n16;
-        if (tt >= T) continue;
-        f32x4 ad = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (fuse_u) {
-            ad = mfma16(uhi, bfr[h], ad);
-            ad = mfma16(ulo, bfr[h], ad);
-        }
-        if (row >= d) continue;
+        const int row = row_g + 16 * tt + n16;
+        if (tt >= T || row >= d) continue;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int m = 4 * g + v;
             if (m >= M) continue;
-            float a2 = ad[v];
-            if (!fuse_u) {
-                a2 = 0.0f;
-                for (int j = 0; j < r; ++j)
-                    a2 = __builtin_fmaf(p.U[m * r + j], bf16_bits_to_f32(p.B[row * r + j]), a2);
-            }
-            const float out = ysum[h][v] + p.s * a2;
+            const float out = ysum[h][v] + p.s * ad[h][v];
             p.y[(int64_t)m * d + row] = (uint16_t)(pack_bf16x2(out, 0.0f) & 0xFFFFu);
         }
     }
