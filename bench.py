@@ -57,20 +57,23 @@ def source_sha(name: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel: str, source: str, launches_bytes: float | None):
-    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they
-    were taken on the current kernel source (else None)."""
-    path = os.path.join(PROFILES, f"traffic_{kernel}.json")
+def traffic_from_profiles(key: str, source: str):
+    """HBM bytes per launch of one kernel from the committed rocprofv3 --pmc
+    summary (profiles/hbm_traffic.txt): FETCH_SIZE + WRITE_SIZE per dispatch,
+    scaled by the factor a plain copy of known size gives.  None when the
+    summary was taken on another version of the kernel's source."""
+    path = os.path.join(PROFILES, "hbm_traffic.txt")
     if not os.path.exists(path):
         return None
-    try:
-        with open(path) as f:
-            t = json.load(f)
-        if t.get("source_sha") != source_sha(source):
+    for ln in open(path):
+        f = ln.split()
+        if not f or f[0] != key:
+            continue
+        kv = dict(x.split("=", 1) for x in f[1:] if "=" in x)
+        if kv.get("source_sha") != source_sha(source):
             return None
-        return float(t["hbm_bytes_per_launch"])
-    except Exception:
-        return None
+        return round(float(kv["hbm_bytes_per_launch"]))
+    return None
 
 
 class Timer:
@@ -148,7 +151,8 @@ def run_layer_bench(q, torch, steps, warmup):
     phases = {"quantize_ms": tq.total_ms() / steps, "fwd_ms": tf.total_ms() / steps,
               "bwd_ms": tb.total_ms() / steps}
     fb_ms = phases["fwd_ms"] + phases["bwd_ms"]
-    return {
+    ctx = (wq, x, a, b, alpha, y, u, lws, r)
+    return ctx, {
         "m": m, "d": d, "k": k, "r": r, "alpha": alpha, "ms_per_step": ms_step,
         "wall_ms_per_step": wall_ms / steps,
         "tflops_step": flops / (ms_step * 1e-3) / 1e12,
@@ -190,12 +194,90 @@ def run_decode_bench(q, torch, iters=50):
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / iters
             gbs = packed / (us * 1e-6) / 1e9
-            out[f"{p.name}_m{m}"] = {"us_per_call": round(us, 3), "packed_gbs": round(gbs, 1),
-                                     "hbm_frac_packed": round(gbs / HBM_PEAK_GBS, 4)}
+            alg = decode_bytes(m, p.d, p.k, wl.r)
+            out[f"{p.name}_m{m}"] = {"us_per_call": round(us, 3), "kernels_per_call": 1,
+                                     "packed_gbs": round(gbs, 1),
+                                     "hbm_frac_packed": round(gbs / HBM_PEAK_GBS, 4),
+                                     "algorithmic_bytes": alg,
+                                     "algorithmic_gbs": round(alg / (us * 1e-6) / 1e9, 1)}
             log(f"decode {p.name} M={m}: {us:.2f} us/call, {gbs:.0f} GB/s packed")
         del ws
         torch.cuda.empty_cache()
     return out
+
+
+def gemm_flops(m, d, k, r):
+    """Algorithmic flops of the forward dequant-GEMM kernel: X What^T plus the
+    adapter's up-projection (s U) B^T that its epilogue k-columns carry."""
+    return 2 * m * d * k + 2 * m * d * r
+
+
+def time_gemm_only(q, torch, ctx, iters):
+    """The forward's GEMM kernel alone (qlora_linear_gemm_only on the workspace
+    the preceding forward prepared), timed with HIP events on torch's current
+    stream -- the stream the library launches on."""
+    w, x, a, b, alpha, y, u, lws, r = ctx
+    q.qlora_linear_fwd(w, x, a, b, alpha, out=y, u_out=u, workspace=lws)
+    for _ in range(3):
+        q.qlora_linear_gemm_only(w, False, x, r, y, lws)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        q.qlora_linear_gemm_only(w, False, x, r, y, lws)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def decode_bytes(m, d, k, r):
+    """Algorithmic HBM bytes of one decode forward: packed codes, 8-bit block
+    constants, fp32 group constants and mean, x, A, B, Y."""
+    nb = d * k // 64
+    return d * k // 2 + nb + 4 * ((nb + 255) // 256) + 4 + 2 * m * k + 2 * r * k + 2 * d * r + 2 * m * d
+
+
+def decode_roofline(decode):
+    """The decode forward at M = 16 on the 14336 x 4096 projection: one kernel
+    per call, bound by HBM; algorithmic bytes over its event-timed duration."""
+    e = decode.get("14336x4096_m16") or next(iter(decode.values()))
+    return {"bound": "hbm", "achieved": e["algorithmic_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(e["algorithmic_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profiles("nf4_decode_kernel_w14336x4096_m16", "decode.hip"),
+            "kernel": "nf4_decode_kernel (decode forward, 14336 x 4096, M = 16)",
+            "kernel_us": e["us_per_call"], "work_per_launch": f"{e['algorithmic_bytes']} bytes"}
+
+
+def pmc_run(q, torch, which):
+    """A short, fixed sequence of launches for rocprofv3 --pmc counter passes:
+    a plain device copy of 256 MiB (the calibration of FETCH_SIZE/WRITE_SIZE),
+    then three launches of the kernel under study."""
+    from workloads import WORKLOADS, workload_layer
+    from tests.helpers import to_dev_bf16, to_dev_f32
+    n = 256 * 2**20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    if which == "gemm":
+        ctx, _ = run_layer_bench(q, torch, 1, 0)
+        w, x, a, b, alpha, y, u, lws, r = ctx
+        for _ in range(3):
+            q.qlora_linear_gemm_only(w, False, x, r, y, lws)
+    else:
+        wl = WORKLOADS["decode"]
+        for pi, p in enumerate(wl.projections):
+            inp = workload_layer("decode", pi)
+            w = q.qlora_nf4_quantize(to_dev_f32(inp.w0))
+            a, b = to_dev_bf16(inp.a), to_dev_bf16(inp.b)
+            x = to_dev_bf16(inp.x[:16])
+            y = torch.empty((16, p.d), dtype=torch.bfloat16, device="cuda")
+            lws = torch.empty(q.linear_workspace_bytes(16, p.d, p.k, wl.r), dtype=torch.uint8, device="cuda")
+            for _ in range(3):
+                q.qlora_linear_fwd(w, x, a, b, wl.alpha, save_u=False, out=y, workspace=lws)
+    torch.cuda.synchronize()
+    log(f"pmc run ({which}) done")
 
 
 def run_cpu_baseline(target_s=15.0):
@@ -243,6 +325,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-run", choices=["gemm", "decode"],
+                    help="only a short fixed launch sequence for rocprofv3 --pmc passes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -255,17 +339,22 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.pmc_run:
+        pmc_run(q, torch, args.pmc_run)
+        return
 
-    lay = run_layer_bench(q, torch, args.steps, args.warmup)
+    ctx, lay = run_layer_bench(q, torch, args.steps, args.warmup)
     m, d, k, r = lay["m"], lay["d"], lay["k"], lay["r"]
-    # dominant kernel: the forward dequant-GEMM, timed through qlora_linear_fwd
-    fwd_ms = lay["phases"]["fwd_ms"]
-    achieved = fwd_flops(m, d, k, r) / (fwd_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": "qlora_linear_fwd (nf4_gemm_kernel<fwd> + U kernel)",
-                "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic_from_profiles("nf4_gemm_fwd", "gemm.hip", None),
-                "work_per_launch": f"2*M*d*k + 2*M*r*(d+k) = {fwd_flops(m, d, k, r)} flop"}
+    # dominant kernel: the forward dequant-GEMM (nf4_gemm_kernel), launched alone
+    log("layer4096: timing the forward GEMM kernel alone")
+    gemm_ms = time_gemm_only(q, torch, ctx, max(args.steps, 10))
+    achieved = gemm_flops(m, d, k, r) / (gemm_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic_from_profiles("nf4_gemm_kernel_fwd_layer4096", "gemm_nf4.hip"),
+                "kernel": "nf4_gemm_kernel<fwd> (layer4096 forward)",
+                "kernel_us": round(gemm_ms * 1e3, 2),
+                "work_per_launch": f"2*M*d*k + 2*M*d*r = {gemm_flops(m, d, k, r)} flop"}
     decode = None if args.skip_decode else run_decode_bench(q, torch)
     cpu = None
     if not args.skip_cpu_baseline:
@@ -284,6 +373,7 @@ def main():
         "quantize_gbs": round(lay["quantize_gbs"], 1),
         "roofline": roofline,
         "decode_fwd": decode,
+        "decode_roofline": None if decode is None else decode_roofline(decode),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

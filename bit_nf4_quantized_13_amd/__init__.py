@@ -29,7 +29,7 @@ DQ_BLOCK = 256
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m bit_nf4_quantized_13_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python bit_nf4_quantized_13_amd/build.py` "
         "(there is no CPU fallback)")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -61,8 +61,12 @@ _SIGS = {
                                         _SZ, _P]),
     "qlora_linear_bwd": (ctypes.c_int, [_WP, _P, _P, _P, _P, _P, _I64, _I32, ctypes.c_float, _P,
                                         _P, _P, _P, _SZ, _P]),
+    "qlora_linear_gemm_only": (ctypes.c_int, [_WP, _I32, _P, _I64, _I32, _P, _P, _SZ, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
+    if not hasattr(_lib, _name):
+        raise ImportError(f"{LIB_PATH} lacks {_name}: it predates its sources; rebuild it with "
+                          "`python bit_nf4_quantized_13_amd/build.py`")
     _fn = getattr(_lib, _name)
     _fn.restype = _res
     _fn.argtypes = _args
@@ -239,6 +243,20 @@ def qlora_linear_bwd(w: NF4Weight, x: torch.Tensor, dy: torch.Tensor, a: torch.T
     return dx, da, db
 
 
+def qlora_linear_gemm_only(w: NF4Weight, backward: bool, a: torch.Tensor, r: int,
+                           out: torch.Tensor, workspace: torch.Tensor) -> torch.Tensor:
+    """Re-run the dequant-GEMM kernel of the preceding qlora_linear_fwd (a = x,
+    out = Y) or qlora_linear_bwd (a = dY, out = dX) call alone, on the workspace
+    that call prepared (for timing the GEMM in isolation)."""
+    _dev_tensor(a, torch.bfloat16, "a")
+    _dev_tensor(out, torch.bfloat16, "out")
+    cw = w.c_struct()
+    _check(_lib.qlora_linear_gemm_only(ctypes.byref(cw), 1 if backward else 0, a.data_ptr(), a.shape[0], r,
+                                       out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()),
+           "qlora_linear_gemm_only")
+    return out
+
+
 def adapter_scale(alpha: float, r: int) -> float:
     """alpha / r as the library computes it (fp32)."""
     import numpy as np
@@ -247,7 +265,7 @@ def adapter_scale(alpha: float, r: int) -> float:
 
 __all__ = [
     "NF4Weight", "QloraError", "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd",
-    "qlora_linear_bwd", "qlora_nf4_codebook", "qlora_nf4_thresholds", "status_str", "library",
+    "qlora_linear_bwd", "qlora_linear_gemm_only", "qlora_nf4_codebook", "qlora_nf4_thresholds", "status_str", "library",
     "abi_version", "quantize_workspace_bytes", "linear_workspace_bytes", "adapter_scale",
     "BLOCK", "DQ_BLOCK",
 ]

@@ -1,6 +1,6 @@
 """Build libqlora_nf4.so (gfx950) in-tree with hipcc.
 
-    python -m bit_nf4_quantized_13_amd.build        # or build() from Python
+    python bit_nf4_quantized_13_amd/build.py        # or build() from Python
 
 Every translation unit is compiled with:
   --offload-arch=gfx950 -O3           MI355X only

@@ -261,4 +261,21 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const qlora_bf16 *x, const qlora
     return hip_status(e);
 }
 
+int qlora_linear_gemm_only(const qlora_nf4_weight *w, int32_t backward, const qlora_bf16 *a, int64_t M,
+                           int32_t r, qlora_bf16 *out, void *ws, size_t ws_bytes, void *stream) {
+    int st = check_weight(w, true);
+    if (st != QLORA_OK) return st;
+    if (!a || !out || M <= 0 || r <= 0) return QLORA_EINVAL;
+    if (r > QLORA_MAX_RANK || w->d % 8 != 0) return QLORA_ENOTSUP;
+    if (!aligned(a, 16) || !aligned(out, 16)) return QLORA_EALIGN;
+    if (!backward && M <= 16 && w->k <= kDecodeMaxK) return QLORA_EINVAL;  // the decode path has no separate GEMM
+    const LinWs l = lin_ws(M, w->d, w->k, r);
+    if (!ws || ws_bytes < l.total) return QLORA_EWORKSPACE;
+    if (!aligned(ws, 16)) return QLORA_EALIGN;
+    (void)hipGetLastError();
+    const Nf4Weights nw{w->codes, w->absmax_q, w->absmax_scale, w->absmax_mean, w->d, w->k};
+    return hip_status(launch_gemm_core(backward != 0, nw, a, M, r, out, gemm_ws(static_cast<char *>(ws), l),
+                                       static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -660,9 +660,11 @@ __global__ __launch_bounds__(256) void dequant_tile_kernel(const uint8_t *__rest
     }
 }
 
+// core_only: launch the GEMM kernel alone on a workspace that a full launch
+// with the same arguments prepared (block scales, adapter operands, bf16 copy)
 hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, const float *V,
                   const uint16_t *ext_w, int r, float s, uint16_t *out, const GemmWs &ws,
-                  hipStream_t st) {
+                  hipStream_t st, bool core_only = false) {
     GemmArgs p;
     p.a = a;
     p.M = M;
@@ -701,7 +703,7 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
     q.ext_b = ws.ext_b;
     q.Ke = p.Ke;
     const int64_t gs = (q.nb + 255) / 256, ga = (M * (p.Ke / 8) + 255) / 256, gb = (p.N * (p.Ke / 8) + 255) / 256;
-    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(gs + ga + gb)), dim3(256), 0, st, q, gs, ga);
+    if (!core_only) hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(gs + ga + gb)), dim3(256), 0, st, q, gs, ga);
 
     const int64_t tiles_m = (M + BM - 1) / BM, tiles = tiles_m * ((p.N + BN - 1) / BN);
     const dim3 grid((unsigned)tiles), block(NTHREADS);
@@ -712,7 +714,8 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
         // dequantized copy of the weight operand, once per call
         const int64_t rows = dx ? w.k : w.d, cols = dx ? p.ldw : w.k;
         const dim3 tgrid((unsigned)(((w.k + 255) / 256) * ((w.d + 63) / 64)));
-        if (dx)
+        if (core_only) {
+        } else if (dx)
             hipLaunchKernelGGL(dequant_tile_kernel<true>, tgrid, dim3(256), 0, st, w.codes, ws.shat, w.d, w.k, p.ldw,
                                nf4_consts(), ws.wbf);
         else
@@ -744,6 +747,11 @@ hipError_t launch_gemm_dx(const Nf4Weights &w, const uint16_t *dy, int64_t M, co
                           const uint16_t *A, int r, float s, uint16_t *dX, const GemmWs &ws,
                           hipStream_t st) {
     return launch(true, w, dy, M, G, A, r, s, dX, ws, st);
+}
+
+hipError_t launch_gemm_core(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, int r, uint16_t *out,
+                            const GemmWs &ws, hipStream_t st) {
+    return launch(dx, w, a, M, nullptr, nullptr, r, 0.0f, out, ws, st, true);
 }
 
 }  // namespace qnf4

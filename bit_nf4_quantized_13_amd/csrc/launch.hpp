@@ -71,6 +71,11 @@ hipError_t launch_gemm_dx(const Nf4Weights &w, const uint16_t *dy, int64_t M, co
                           const uint16_t *A, int r, float s, uint16_t *dX, const GemmWs &ws,
                           hipStream_t st);
 
+// The GEMM kernel of launch_gemm_fwd (dx = false) or launch_gemm_dx (dx = true)
+// alone, on a workspace that a full launch with the same arguments prepared.
+hipError_t launch_gemm_core(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, int r, uint16_t *out,
+                            const GemmWs &ws, hipStream_t st);
+
 // Decode-shaped forward, M <= 16: Y = X What^T + s U B^T.  U [M x r] fp32 is
 // either given (U != null) or computed in the same kernel from A [r x k]
 // (U == null, r <= 16; written to U_save when that is not null).  part holds

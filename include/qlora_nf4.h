@@ -164,6 +164,23 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const qlora_bf16 *x, const qlora
                      void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * qlora_linear_gemm_only -- the dequant-GEMM kernel of the preceding
+ * qlora_linear_fwd (backward = 0) or qlora_linear_bwd (backward = 1) call,
+ * launched alone, so that its duration can be measured in isolation.  Those
+ * calls first run small preparation kernels (U = X A^T or G = dY B, the
+ * dequantized block scales, the adapter operands laid out as extra k-columns,
+ * a bf16 copy of What when M > 512) into the workspace and then one GEMM
+ * kernel; this call re-runs only the GEMM on that prepared workspace.
+ *   a    the call's x (forward) or dY (backward); M, r, ws as in that call
+ *   out  rewritten with the values the call wrote to Y (forward) or dX
+ *        (backward)
+ * The workspace must not have been used by another call in between.  A
+ * forward with M <= 16 has no separate GEMM (one kernel): QLORA_EINVAL.
+ */
+int qlora_linear_gemm_only(const qlora_nf4_weight *w, int32_t backward, const qlora_bf16 *a, int64_t M,
+                           int32_t r, qlora_bf16 *out, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * qlora_nf4_codebook -- host-only: copies the library's 16 fp32 NF4 levels
  * (chkda, "NF4: Choose the codebook to fit the distribution"; built as in
  * "Building the NF4 codebook" from standard-normal quantiles) into out[16].

@@ -157,3 +157,29 @@ def test_valid_call_without_gpu_reports_hip_error():
         pytest.skip("a GPU is present: this check is for hosts without one")
     w = weight()
     assert quant(w) == q.QLORA_EHIP
+
+
+def gemm_only(w=None, backward=0, a=FAKE, m=64, r=8, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    w = w or weight()
+    return q.library().qlora_linear_gemm_only(ctypes.byref(w), backward, a, m, r, out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(a=None), q.QLORA_EINVAL), (dict(out=None), q.QLORA_EINVAL), (dict(m=0), q.QLORA_EINVAL),
+    (dict(r=0), q.QLORA_EINVAL), (dict(r=129), q.QLORA_ENOTSUP), (dict(w=weight(d=252)), q.QLORA_ENOTSUP),
+    (dict(a=FAKE_MIS), q.QLORA_EALIGN), (dict(out=FAKE_MIS), q.QLORA_EALIGN),
+    (dict(ws=None), q.QLORA_EWORKSPACE), (dict(ws_bytes=64), q.QLORA_EWORKSPACE),
+    (dict(m=16), q.QLORA_EINVAL),                      # decode-sized forward: no separate GEMM
+    (dict(w=weight(codes=None)), q.QLORA_EINVAL),
+])
+def test_gemm_only_rejects_invalid_arguments(kw, status):
+    assert gemm_only(**kw) == status
+
+
+def test_gemm_only_backward_accepts_small_m_shapes():
+    """The backward always runs the GEMM, also for M <= 16: only the missing GPU
+    stops this call."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: this check is for hosts without one")
+    assert gemm_only(backward=1, m=16) == q.QLORA_EHIP

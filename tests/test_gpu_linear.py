@@ -162,3 +162,24 @@ def test_alpha_zero_gives_base_output_and_zero_adapter_grads():
     assert torch.equal(y, y0)
     _, da, db = q.qlora_linear_bwd(w, xd, dyd, ad, bd, 0.0)
     assert torch.count_nonzero(da) == 0 and torch.count_nonzero(db) == 0
+
+
+@pytest.mark.parametrize("m", [200, 600])
+def test_gemm_only_reruns_the_calls_gemm(m):
+    """qlora_linear_gemm_only re-launches just the dequant-GEMM on the workspace
+    the preceding call prepared: the output must be bit-identical."""
+    import bit_nf4_quantized_13_amd as q
+    say(f"gemm_only M={m}")
+    inp = make_layer(44, m, 384, 320, m, 8)
+    w = q.qlora_nf4_quantize(to_dev_f32(inp.w0))
+    xd, ad, bd, dyd = (to_dev_bf16(t) for t in (inp.x, inp.a, inp.b, inp.dy))
+    ws = torch.empty(q.linear_workspace_bytes(m, 384, 320, 8), dtype=torch.uint8, device="cuda")
+    y, u = q.qlora_linear_fwd(w, xd, ad, bd, 16.0, workspace=ws)
+    y2 = torch.full_like(y, 7)
+    q.qlora_linear_gemm_only(w, False, xd, 8, y2, ws)
+    assert torch.equal(y, y2)
+    dx, _, _ = q.qlora_linear_bwd(w, xd, dyd, ad, bd, 16.0, u=u, workspace=ws)
+    dx2 = torch.full_like(dx, 7)
+    q.qlora_linear_gemm_only(w, True, dyd, 8, dx2, ws)
+    assert torch.equal(dx, dx2)
+    torch.cuda.synchronize()
