@@ -68,6 +68,14 @@ def backward(w_hat, x, dy, a, b, alpha: float) -> tuple[np.ndarray, np.ndarray, 
     return dx, da, db
 
 
+def adapter_grads(x, dy, a, b, alpha: float) -> tuple[np.ndarray, np.ndarray]:
+    """(dA, dB) of backward() without its dX product, for shapes whose full dX
+    is too large to form on the host: dA = s (dY B)^T X, dB = s dY^T (X A^T)."""
+    x, dy, a, b = _f64(x), _f64(dy), _f64(a), _f64(b)
+    s = adapter_scale(alpha, a.shape[0])
+    return s * ((dy @ b).T @ x), s * (dy.T @ (x @ a.T))
+
+
 def merged_weight(w_hat, a, b, alpha: float) -> np.ndarray:
     """W_merged = W0 + (alpha/r) B A (chkda "Merging LoRA weights for inference")."""
     a, b = _f64(a), _f64(b)

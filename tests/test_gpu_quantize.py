@@ -89,13 +89,6 @@ def test_wide_dynamic_range_of_scales():
     assert_bit_exact(w, "scales over 9 decades")
 
 
-@pytest.mark.parametrize("proj", [0, 4, 6])
-def test_llama7b_projections_full(proj):
-    wl = WORKLOADS["llama7b"]
-    p = wl.projections[proj]
-    assert_bit_exact(random_weights(100 + proj, (p.d, p.k)), f"llama7b {p.name} {p.d}x{p.k}")
-
-
 def test_determinism():
     w0 = random_weights(15, (512, 1024))
     a, _ = gpu_quantize(w0)

@@ -357,3 +357,26 @@ def test_workload_inputs_are_bf16_and_seeded():
     assert l1.x.dtype == np.uint16 and l1.w0.dtype == np.float32
     xf = bf16_bits_as_f32(l1.x)
     assert np.all(np.isfinite(xf))
+
+
+def test_adapter_grads_central_finite_differences():
+    """The dX-free adapter gradients, pinned like backward(): central finite
+    differences of sum(dY * Y) in fp64."""
+    w, x, a, b, dy = _tiny_layer(4)
+    alpha = 10.0
+    da, db = qlora.adapter_grads(x, dy, a, b, alpha)
+
+    def loss(aa, bb):
+        y, _ = qlora.forward(w, x, aa, bb, alpha)
+        return float(np.sum(dy * y))
+
+    h = 1e-6
+    for arr, grad, which in ((a, da, 0), (b, db, 1)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            p = arr.copy(); p[idx] += h
+            mm = arr.copy(); mm[idx] -= h
+            args_p = (p, b) if which == 0 else (a, p)
+            args_m = (mm, b) if which == 0 else (a, mm)
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        assert np.allclose(grad, num, rtol=1e-6, atol=1e-7)
