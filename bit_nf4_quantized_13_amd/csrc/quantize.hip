@@ -27,11 +27,83 @@ namespace {
 constexpr int kBlock = 64;
 constexpr int kGroup = 256;
 
-__device__ __forceinline__ uint32_t nearest_level(float x, const Nf4Consts &t) {
-    uint32_t q = 0;
-#pragma unroll
-    for (int j = 0; j < 15; ++j) q += (x >= t.thresh[j]) ? 1u : 0u;
-    return q;
+// Nearest level through a bucket table (a compare against each of the 15
+// thresholds costs two instructions per weight; this costs a handful).
+// x = fl32(w / absmax) lies in [-1, 1].  Bucket = sign, exponent and the top
+// three mantissa bits of x: the floats of one bucket form an interval, and no
+// bucket holds more than one threshold (the thresholds are >= 0.08 apart, a
+// bucket at most 0.0625 wide), so code = base + (x >= T) with (base, T) read
+// from the table.  |x| < 2^-5 (exponent <= 121) is one bucket per sign: all of
+// it lies strictly between the two thresholds around zero (code 7).
+// Index: clamp(bits[20..30] - (121 << 3), 0, 55) + 56 * sign.
+//
+// The division is skipped where it cannot matter: x' = w * rcp(absmax) is
+// within a few ulp of x, so the code of x' is the code of x unless a threshold
+// lies within that distance.  Each entry carries a band [lo, hi] around its
+// threshold (2^-20 relative, far wider than the error); an x' inside the band
+// takes the exact path (IEEE division), and so does a whole bucket that has a
+// threshold near one of its edges (band = everything; none does for the NF4
+// table).
+// a lane's value after a DPP lane permutation within its row of 16 lanes
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+constexpr int kLutEntries = 112;
+constexpr float kBand = 0x1p-20f;
+
+struct LutEntry {
+    uint32_t base;
+    float thresh;  // the one threshold inside the bucket, or +inf
+    float lo, hi;  // where x' must go the exact way
+};
+
+__device__ __forceinline__ uint32_t lut_index(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const int k11 = (int)((u >> 20) & 0x7FFu) - (121 << 3);
+    const int c = k11 < 0 ? 0 : (k11 > 55 ? 55 : k11);
+    return (uint32_t)c + 56u * (u >> 31);
+}
+
+// Entry i of the table: the bucket's smallest and largest float decide the
+// base count and the threshold inside it.
+__device__ void lut_entry(int i, const Nf4Consts &t, LutEntry *out) {
+    const uint32_t sign = i >= 56 ? 1u : 0u;
+    const int c = i - 56 * (int)sign;
+    float lo, hi;  // the bucket's smallest and largest value
+    if (c < 8) {   // exponent <= 121 (both signs): all of (-2^-5, 2^-5)
+        lo = -0x1.fffffep-6f;
+        hi = 0x1.fffffep-6f;
+    } else {
+        const uint32_t k = (uint32_t)(c + (121 << 3));  // exponent and mantissa top bits
+        const uint32_t b0 = (sign << 31) | (k << 20), b1 = b0 | 0xFFFFFu;
+        const float f0 = __uint_as_float(b0), f1 = __uint_as_float(b1);
+        lo = sign ? f1 : f0;
+        hi = sign ? f0 : f1;
+    }
+    uint32_t base = 0;
+    float inside = __builtin_inff();
+    bool edge = false;
+    for (int j = 0; j < 15; ++j) {
+        const float tj = t.thresh[j];
+        if (tj <= lo) ++base;
+        else if (tj <= hi) inside = tj;
+        const float m = fabsf(tj) * (4.0f * kBand);
+        if (fabsf(tj - lo) <= m || fabsf(tj - hi) <= m) edge = true;
+    }
+    out->base = base;
+    out->thresh = inside;
+    if (edge) {
+        out->lo = -__builtin_inff();
+        out->hi = __builtin_inff();
+    } else if (inside == __builtin_inff()) {
+        out->lo = __builtin_inff();  // no threshold: an empty band
+        out->hi = -__builtin_inff();
+    } else {
+        out->lo = inside - fabsf(inside) * kBand;
+        out->hi = inside + fabsf(inside) * kBand;
+    }
 }
 
 // Each wave owns 64 consecutive blocks of the group: 8 rounds of 8 blocks.
@@ -42,6 +114,7 @@ __global__ __launch_bounds__(256) void nf4_quantize_groups(
     const float *__restrict__ w, int64_t nb, Nf4Consts tab, uint8_t *__restrict__ codes,
     float *__restrict__ absmax, double *__restrict__ group_sum) {
     __shared__ float s_abs[kGroup];
+    __shared__ LutEntry lut[kLutEntries];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t blk0 = (int64_t)blockIdx.x * kGroup;
     s_abs[tid] = 0.0f;  // missing blocks of a ragged last group count as +0.0
@@ -53,25 +126,55 @@ __global__ __launch_bounds__(256) void nf4_quantize_groups(
         v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (blk < nb) v[i] = *reinterpret_cast<const float4 *>(w + blk * kBlock + (lane & 15) * 4);
     }
-    __syncthreads();  // s_abs cleared before any lane records a block
+    if (tid < kLutEntries) lut_entry(tid, tab, &lut[tid]);
+    __syncthreads();  // s_abs cleared and the table built before any lane uses them
+    // codes of four weights of one block: the four table reads in flight
+    // together, one branch for the (rare) exact path
+    auto code4 = [&](const float4 &wv, float m, float r) {
+        const float w4[4] = {wv.x, wv.y, wv.z, wv.w};
+        float xa[4];
+        LutEntry e[4];
+        uint32_t q[4];
+        bool slow = false;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            xa[c] = w4[c] * r;
+            e[c] = lut[lut_index(xa[c])];
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            q[c] = e[c].base + (xa[c] >= e[c].thresh ? 1u : 0u);
+            // near a threshold (or x' not a number): decide with the exact quotient
+            slow |= !((xa[c] > e[c].hi) | (xa[c] < e[c].lo));
+        }
+        if (__builtin_expect(slow, 0)) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float x = w4[c] / m;
+                const LutEntry ex = lut[lut_index(x)];
+                q[c] = ex.base + (x >= ex.thresh ? 1u : 0u);
+            }
+        }
+        return q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12);
+    };
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int local = wave * 64 + (i >> 1) * 8 + (i & 1) * 4 + (lane >> 4);
         const int64_t blk = blk0 + local;
         float m = fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w)));
-        m = fmaxf(m, __shfl_xor(m, 8, 16));
-        m = fmaxf(m, __shfl_xor(m, 4, 16));
-        m = fmaxf(m, __shfl_xor(m, 2, 16));
-        m = fmaxf(m, __shfl_xor(m, 1, 16));
-        uint32_t q0 = 7, q1 = 7, q2 = 7, q3 = 7;  // exact-zero level for an all-zero block
+        m = fmaxf(m, dpp_f32<0xB1>(m));   // quad_perm [1,0,3,2]
+        m = fmaxf(m, dpp_f32<0x4E>(m));   // quad_perm [2,3,0,1]
+        m = fmaxf(m, dpp_f32<0x141>(m));  // row_half_mirror
+        m = fmaxf(m, dpp_f32<0x140>(m));  // row_mirror: the max of the 16 lanes of the block
+        uint32_t packed4 = 0x7777u;  // exact-zero level for an all-zero block
         if (m != 0.0f) {
-            q0 = nearest_level(v[i].x / m, tab);
-            q1 = nearest_level(v[i].y / m, tab);
-            q2 = nearest_level(v[i].z / m, tab);
-            q3 = nearest_level(v[i].w / m, tab);
+            // an absmax below 2^-100 (reciprocal near overflow, subnormal
+            // operands) takes the exact path for every weight
+            const float r = m >= 0x1p-100f ? __builtin_amdgcn_rcpf(m) : __builtin_nanf("");
+            packed4 = code4(v[i], m, r);
         }
         if (blk < nb) {
-            const uint16_t packed = (uint16_t)(q0 | (q1 << 4) | (q2 << 8) | (q3 << 12));
+            const uint16_t packed = (uint16_t)packed4;
             *reinterpret_cast<uint16_t *>(codes + blk * (kBlock / 2) + (lane & 15) * 2) = packed;
             if ((lane & 15) == 0) {
                 absmax[blk] = m;
