@@ -245,11 +245,14 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const qlora_bf16 *x, const qlora
     }
     if (e == hipSuccess) e = launch_transpose_bf16(B, d, r, Bt, s);             // B^T [r x d]
     if (e == hipSuccess) e = launch_rows_skinny(dY, Bt, M, d, r, G, s);         // G = dY B
+    ColsReduceJob red[2];
+    const ColsReduceJob *pending = nullptr;  // dB, dA reductions not yet run
     if (r <= 16) {                                                              // dB = s dY^T U, dA = s G^T X
         float *part_b = part;
         float *part_a = part + (size_t)cols_valu_splits(M) * round_up(d, 64) * r;
         if (e == hipSuccess)
-            e = launch_cols_valu_pair(dY, Uin, d, scale, part_b, dB, 0, x, G, k, scale, part_a, dA, 1, M, r, s);
+            e = launch_cols_valu_pair(dY, Uin, d, scale, part_b, dB, 0, x, G, k, scale, part_a, dA, 1, M, r, red, s);
+        pending = red;
     } else {
         if (e == hipSuccess)
             e = launch_cols_skinny(dY, Uin, M, d, r, scale, part, cols_skinny_splits(M, d), dB, 0, s);
@@ -257,7 +260,9 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const qlora_bf16 *x, const qlora
             e = launch_cols_skinny(x, G, M, k, r, scale, part, cols_skinny_splits(M, k), dA, 1, s);
     }
     if (e == hipSuccess && dX)                                                  // dX = dY What + s G A
-        e = launch_gemm_dx(nw, dY, M, G, A, r, scale, dX, gemm_ws(base, l), s);
+        e = launch_gemm_dx(nw, dY, M, G, A, r, scale, dX, gemm_ws(base, l), pending, s);
+    else if (e == hipSuccess && pending)
+        e = launch_cols_reduce(pending, s);
     return hip_status(e);
 }
 

@@ -531,74 +531,10 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
     }
 }
 
-// Preparation, one launch over three index ranges:
-//   shat[j] = fp32(c2[j] / c1[j / 256]) + mean                    (j < nb)
-//   ext_a[m][c] = hi(s V[m][c]), lo(s V[m][c - r]) or 0 by column  (M x Ke)
-//   ext_b[n][c] = W'[n][c mod r] for c < 2r, else 0                (N x Ke)
-// where W'[n][j] = B[n][j] (forward, B [d x r]) or A[j][n] (dX, A [r x k]).
-struct PrepArgs {
-    const int8_t *c2;
-    const float *c1;
-    const float *mean;
-    int64_t nb;
-    float *shat;
-    const float *V;
-    int64_t M;
-    int r;
-    float s;
-    uint16_t *ext_a;
-    const uint16_t *W;
-    int64_t N;
-    int dx;
-    uint16_t *ext_b;
-    int64_t Ke;
-};
-
-// Workgroup ranges: [0, gs) block scales, one per thread; [gs, gs + ga) ext_a
-// and then ext_b, 8 columns (one 16-byte store) per thread.
-__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a, int64_t gs, int64_t ga) {
-    const int64_t b = blockIdx.x;
-    if (b < gs) {
-        const int64_t x = b * 256 + threadIdx.x;
-        if (x < a.nb) a.shat[x] = dq_scale(a.c2[x], a.c1[x >> 8], *a.mean);
-        return;
-    }
-    const uint32_t cgs = (uint32_t)(a.Ke / 8);  // 8-column groups per row
-    const bool is_a = b < gs + ga;
-    const int64_t x = (b - (is_a ? gs : gs + ga)) * 256 + threadIdx.x;
-    const int64_t rows = is_a ? a.M : a.N;
-    const int64_t row = x / cgs;
-    if (row >= rows) return;
-    const int c0 = (int)(x - row * cgs) * 8;
-    uint32_t v[4];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-        uint32_t pr = 0;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int c = c0 + 2 * h + q;
-            uint32_t bits = 0;
-            if (c < 2 * a.r) {
-                const int jj = c < a.r ? c : c - a.r;
-                if (is_a) {
-                    const float f = a.s * a.V[row * a.r + jj];
-                    const uint32_t hb = pack_bf16x2(f, 0.0f) & 0xFFFFu;
-                    bits = c < a.r ? hb : (pack_bf16x2(f - bf16_bits_to_f32(hb), 0.0f) & 0xFFFFu);
-                } else {
-                    bits = a.dx ? a.W[(int64_t)jj * a.N + row] : a.W[row * a.r + jj];
-                }
-            }
-            pr |= bits << (16 * q);
-        }
-        v[h] = pr;
-    }
-    uint16_t *dst = (is_a ? a.ext_a : a.ext_b) + row * a.Ke + c0;
-    *reinterpret_cast<uint4 *>(dst) = uint4{v[0], v[1], v[2], v[3]};
-}
-
 // Dequantized weight operand for the non-expanding GEMM: What [d x k]
 // (forward) or What^T [k x ldw] with zero columns d .. ldw-1 (dX), bf16,
-// bit-identical to qlora_nf4_dequantize.  One workgroup per 64 W0 rows x 256
+// bit-identical to qlora_nf4_dequantize (the block scale is doubleDequant's,
+// computed here from c2, c1 and the mean).  One workgroup per 64 W0 rows x 256
 // columns; thread t expands an 8 x 8 block: rows 8 (t % 8) .., columns
 // 8 (t / 8) .. (inside one NF4 block, so one scale per row).  Code reads are
 // 32 contiguous bytes per row for 8 lanes; the transposed form transposes the
@@ -606,12 +542,13 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a, int64_t gs, int64
 // LDS is involved and every store is a contiguous 128-byte row segment per 8
 // lanes.
 template <bool T>
-__global__ __launch_bounds__(256) void dequant_tile_kernel(const uint8_t *__restrict__ codes,
-                                                           const float *__restrict__ shat, int64_t d, int64_t k,
-                                                           int64_t ldw, Nf4Consts tab, uint16_t *__restrict__ out) {
+__device__ __forceinline__ void dequant_tile(int64_t bid, const uint8_t *__restrict__ codes,
+                                             const int8_t *__restrict__ c2, const float *__restrict__ c1, float mean,
+                                             int64_t d, int64_t k, int64_t ldw, const Nf4Consts &tab,
+                                             uint16_t *__restrict__ out) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int64_t ct = (k + 255) / 256;
-    const int64_t tk = blockIdx.x % ct, td = blockIdx.x / ct;
+    const int64_t tk = bid % ct, td = bid / ct;
     const int ng = tid & 7, kg = tid >> 3;
     const int64_t n0 = td * 64 + 8 * ng;   // first of this thread's 8 W0 rows
     const int64_t k0 = tk * 256 + 8 * kg;  // first of its 8 columns
@@ -628,16 +565,17 @@ __global__ __launch_bounds__(256) void dequant_tile_kernel(const uint8_t *__rest
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int64_t n = n0 + e;
+        const int64_t jb = n * kb + k0 / 64;
         cw[e] = n < d ? *reinterpret_cast<const uint32_t *>(codes + n * (k / 2) + k0 / 2) : 0u;
-        sc[e] = n < d ? shat[n * kb + k0 / 64] : 0.0f;
+        sc[e] = n < d ? dq_scale(c2[jb], c1[jb >> 8], mean) : 0.0f;
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
-        for (int c2 = 0; c2 < 4; ++c2) {
-            const uint32_t x = pack_bf16x2(level(code_addr(cw[e], 2 * c2), lv) * sc[e],
-                                           level(code_addr(cw[e], 2 * c2 + 1), lv) * sc[e]);
-            v[e][c2] = n0 + e < d ? x : 0u;  // rows past d: zero columns of What^T
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t x = pack_bf16x2(level(code_addr(cw[e], 2 * q), lv) * sc[e],
+                                           level(code_addr(cw[e], 2 * q + 1), lv) * sc[e]);
+            v[e][q] = n0 + e < d ? x : 0u;  // rows past d: zero columns of What^T
         }
     if constexpr (!T) {
 #pragma unroll
@@ -660,11 +598,109 @@ __global__ __launch_bounds__(256) void dequant_tile_kernel(const uint8_t *__rest
     }
 }
 
+// Preparation of one dequant-GEMM call, one launch over consecutive
+// workgroup ranges (each range may be empty):
+//   shat[j] = fp32(c2[j] / c1[j / 256]) + mean         (j < nb; the expanding GEMM)
+//   ext_a[m][c] = hi(s V[m][c]), lo(s V[m][c - r]) or 0 by column  (M x Ke)
+//   ext_b[n][c] = W'[n][c mod r] for c < 2r, else 0                (N x Ke)
+//   the dequantized weight operand, What or What^T                 (the non-expanding GEMM)
+//   up to two column reductions out = scale sum_splits part        (the dX call's dB, dA)
+// where W'[n][j] = B[n][j] (forward, B [d x r]) or A[j][n] (dX, A [r x k]).
+struct PrepArgs {
+    const int8_t *c2;
+    const float *c1;
+    const float *mean;
+    int64_t nb;
+    float *shat;
+    const float *V;
+    int64_t M;
+    int r;
+    float s;
+    uint16_t *ext_a;
+    const uint16_t *W;
+    int64_t N;
+    uint16_t *ext_b;
+    int64_t Ke;
+    const uint8_t *codes;  // dequantized operand
+    int64_t d, k, ldw;
+    uint16_t *wbf;
+    ColsReduceJob red[2];
+    int64_t g_shat, g_a, g_b, g_t, g_r0;  // workgroups per range (the second reduction takes the rest)
+};
+
+__device__ __forceinline__ void cols_reduce(const ColsReduceJob &jb, int64_t e) {
+    if (e >= jb.N * jb.R) return;
+    float v[64];
+    const int sp = jb.splits;
+#pragma unroll
+    for (int q = 0; q < 64; ++q) v[q] = q < sp ? jb.part[(int64_t)q * jb.N * jb.R + e] : 0.0f;
+    float sum = 0.0f;
+    for (int q = 0; q < sp && q < 64; ++q) sum += v[q];  // split order
+    for (int q = 64; q < sp; ++q) sum += jb.part[(int64_t)q * jb.N * jb.R + e];
+    const int64_t n = e / jb.R;
+    const int j = (int)(e - n * jb.R);
+    if (jb.trans) jb.out[(int64_t)j * jb.N + n] = jb.scale * sum;
+    else jb.out[e] = jb.scale * sum;
+}
+
+template <bool DX>
+__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a, Nf4Consts tab) {
+    int64_t b = blockIdx.x;
+    if (b < a.g_shat) {
+        const int64_t x = b * 256 + threadIdx.x;
+        if (x < a.nb) a.shat[x] = dq_scale(a.c2[x], a.c1[x >> 8], *a.mean);
+        return;
+    }
+    b -= a.g_shat;
+    if (b < a.g_a + a.g_b) {
+        const uint32_t cgs = (uint32_t)(a.Ke / 8);  // 8-column groups per row
+        const bool is_a = b < a.g_a;
+        const int64_t x = (b - (is_a ? 0 : a.g_a)) * 256 + threadIdx.x;
+        const int64_t rows = is_a ? a.M : a.N;
+        const int64_t row = x / cgs;
+        if (row >= rows) return;
+        const int c0 = (int)(x - row * cgs) * 8;
+        uint32_t v[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            uint32_t pr = 0;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int c = c0 + 2 * h + q;
+                uint32_t bits = 0;
+                if (c < 2 * a.r) {
+                    const int jj = c < a.r ? c : c - a.r;
+                    if (is_a) {
+                        const float f = a.s * a.V[row * a.r + jj];
+                        const uint32_t hb = pack_bf16x2(f, 0.0f) & 0xFFFFu;
+                        bits = c < a.r ? hb : (pack_bf16x2(f - bf16_bits_to_f32(hb), 0.0f) & 0xFFFFu);
+                    } else {
+                        bits = DX ? a.W[(int64_t)jj * a.N + row] : a.W[row * a.r + jj];
+                    }
+                }
+                pr |= bits << (16 * q);
+            }
+            v[h] = pr;
+        }
+        uint16_t *dst = (is_a ? a.ext_a : a.ext_b) + row * a.Ke + c0;
+        *reinterpret_cast<uint4 *>(dst) = uint4{v[0], v[1], v[2], v[3]};
+        return;
+    }
+    b -= a.g_a + a.g_b;
+    if (b < a.g_t) {
+        dequant_tile<DX>(b, a.codes, a.c2, a.c1, *a.mean, a.d, a.k, a.ldw, tab, a.wbf);
+        return;
+    }
+    b -= a.g_t;
+    const bool second = b >= a.g_r0;
+    cols_reduce(a.red[second ? 1 : 0], (b - (second ? a.g_r0 : 0)) * 256 + threadIdx.x);
+}
+
 // core_only: launch the GEMM kernel alone on a workspace that a full launch
 // with the same arguments prepared (block scales, adapter operands, bf16 copy)
 hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, const float *V,
                   const uint16_t *ext_w, int r, float s, uint16_t *out, const GemmWs &ws,
-                  hipStream_t st, bool core_only = false) {
+                  const ColsReduceJob *red, hipStream_t st, bool core_only = false) {
     GemmArgs p;
     p.a = a;
     p.M = M;
@@ -686,43 +722,46 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
         (int64_t)BM * p.Ke * 2 >= (int64_t(1) << 31))
         return hipErrorInvalidValue;
 
-    PrepArgs q;
-    q.c2 = w.c2;
-    q.c1 = w.c1;
-    q.mean = w.mean;
-    q.nb = w.d * w.k / 64;
-    q.shat = ws.shat;
-    q.V = V;
-    q.M = M;
-    q.r = r;
-    q.s = s;
-    q.ext_a = ws.ext_a;
-    q.W = ext_w;
-    q.N = p.N;
-    q.dx = dx ? 1 : 0;
-    q.ext_b = ws.ext_b;
-    q.Ke = p.Ke;
-    const int64_t gs = (q.nb + 255) / 256, ga = (M * (p.Ke / 8) + 255) / 256, gb = (p.N * (p.Ke / 8) + 255) / 256;
-    if (!core_only) hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(gs + ga + gb)), dim3(256), 0, st, q, gs, ga);
-
     const int64_t tiles_m = (M + BM - 1) / BM, tiles = tiles_m * ((p.N + BN - 1) / BN);
+    const bool expand = tiles_m == 1;
+    if (!core_only) {
+        PrepArgs q;
+        q.c2 = w.c2;
+        q.c1 = w.c1;
+        q.mean = w.mean;
+        q.nb = w.d * w.k / 64;
+        q.shat = ws.shat;
+        q.V = V;
+        q.M = M;
+        q.r = r;
+        q.s = s;
+        q.ext_a = ws.ext_a;
+        q.W = ext_w;
+        q.N = p.N;
+        q.ext_b = ws.ext_b;
+        q.Ke = p.Ke;
+        q.codes = w.codes;
+        q.d = w.d;
+        q.k = w.k;
+        q.ldw = p.ldw;
+        q.wbf = ws.wbf;
+        q.red[0] = red ? red[0] : ColsReduceJob{nullptr, 0, 1, 0, 0, 0.0f, nullptr};
+        q.red[1] = red ? red[1] : ColsReduceJob{nullptr, 0, 1, 0, 0, 0.0f, nullptr};
+        q.g_shat = expand ? (q.nb + 255) / 256 : 0;  // only the expanding GEMM reads the scales
+        q.g_a = (M * (p.Ke / 8) + 255) / 256;
+        q.g_b = (p.N * (p.Ke / 8) + 255) / 256;
+        q.g_t = expand ? 0 : ((w.k + 255) / 256) * ((w.d + 63) / 64);  // the bf16 copy of What (or What^T)
+        q.g_r0 = (q.red[0].N * q.red[0].R + 255) / 256;
+        const int64_t g_r1 = (q.red[1].N * q.red[1].R + 255) / 256;
+        const dim3 pgrid((unsigned)(q.g_shat + q.g_a + q.g_b + q.g_t + q.g_r0 + g_r1));
+        if (dx) hipLaunchKernelGGL(prep_kernel<true>, pgrid, dim3(256), 0, st, q, nf4_consts());
+        else hipLaunchKernelGGL(prep_kernel<false>, pgrid, dim3(256), 0, st, q, nf4_consts());
+    }
     const dim3 grid((unsigned)tiles), block(NTHREADS);
-    if (tiles_m == 1) {
+    if (expand) {
         if (dx) hipLaunchKernelGGL((nf4_gemm_kernel<true, true>), grid, block, 0, st, p, nf4_consts());
         else hipLaunchKernelGGL((nf4_gemm_kernel<false, true>), grid, block, 0, st, p, nf4_consts());
     } else {
-        // dequantized copy of the weight operand, once per call
-        const int64_t rows = dx ? w.k : w.d, cols = dx ? p.ldw : w.k;
-        const dim3 tgrid((unsigned)(((w.k + 255) / 256) * ((w.d + 63) / 64)));
-        if (core_only) {
-        } else if (dx)
-            hipLaunchKernelGGL(dequant_tile_kernel<true>, tgrid, dim3(256), 0, st, w.codes, ws.shat, w.d, w.k, p.ldw,
-                               nf4_consts(), ws.wbf);
-        else
-            hipLaunchKernelGGL(dequant_tile_kernel<false>, tgrid, dim3(256), 0, st, w.codes, ws.shat, w.d, w.k, p.ldw,
-                               nf4_consts(), ws.wbf);
-        (void)rows;
-        (void)cols;
         if (dx) hipLaunchKernelGGL((nf4_gemm_kernel<true, false>), grid, block, 0, st, p, nf4_consts());
         else hipLaunchKernelGGL((nf4_gemm_kernel<false, false>), grid, block, 0, st, p, nf4_consts());
     }
@@ -740,18 +779,29 @@ int64_t gemm_wbf_elems(int64_t M, int64_t d, int64_t k) {
 hipError_t launch_gemm_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, const float *U,
                            const uint16_t *B, int r, float s, uint16_t *Y, const GemmWs &ws,
                            hipStream_t st) {
-    return launch(false, w, x, M, U, B, r, s, Y, ws, st);
+    return launch(false, w, x, M, U, B, r, s, Y, ws, nullptr, st);
 }
 
 hipError_t launch_gemm_dx(const Nf4Weights &w, const uint16_t *dy, int64_t M, const float *G,
                           const uint16_t *A, int r, float s, uint16_t *dX, const GemmWs &ws,
-                          hipStream_t st) {
-    return launch(true, w, dy, M, G, A, r, s, dX, ws, st);
+                          const ColsReduceJob *red, hipStream_t st) {
+    return launch(true, w, dy, M, G, A, r, s, dX, ws, red, st);
+}
+
+hipError_t launch_cols_reduce(const ColsReduceJob *red, hipStream_t st) {
+    PrepArgs q{};
+    q.red[0] = red[0];
+    q.red[1] = red[1];
+    q.g_r0 = (q.red[0].N * q.red[0].R + 255) / 256;
+    const int64_t g_r1 = (q.red[1].N * q.red[1].R + 255) / 256;
+    if (q.g_r0 + g_r1 == 0) return hipSuccess;
+    hipLaunchKernelGGL(prep_kernel<false>, dim3((unsigned)(q.g_r0 + g_r1)), dim3(256), 0, st, q, nf4_consts());
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm_core(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, int r, uint16_t *out,
                             const GemmWs &ws, hipStream_t st) {
-    return launch(dx, w, a, M, nullptr, nullptr, r, 0.0f, out, ws, st, true);
+    return launch(dx, w, a, M, nullptr, nullptr, r, 0.0f, out, ws, nullptr, st, true);
 }
 
 }  // namespace qnf4

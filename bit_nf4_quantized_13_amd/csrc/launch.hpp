@@ -28,15 +28,24 @@ hipError_t launch_transpose_bf16(const uint16_t *src, int64_t R, int64_t C, uint
 // bf16, V [M x R] fp32; then out = scale * sum over splits of (hi + lo part),
 // written as out[N x R] (transpose_out = 0) or out[R x N] (transpose_out = 1).
 int cols_skinny_splits(int64_t M, int64_t N);
-// Rank R <= 16: the same reductions on the vector ALU in fp32, two at once
-// (job 1 skipped when in1 is null):  out_i = scale_i * In_i^T V_i, stored
-// out_i[N_i x R] (trans_i = 0) or out_i[R x N_i] (trans_i = 1).  part_i holds
-// cols_valu_splits(M) * N_i * R floats.
+// Rank R <= 16: the same reductions on the vector ALU in fp32, two jobs in
+// one launch (job 1 skipped when in1 is null): part_i[S][N_i][R] holds the
+// split-M partial sums In_i^T V_i, S = cols_valu_splits(M).  The reduction
+// out_i = scale_i * sum over splits, stored out_i[N_i x R] (trans_i = 0) or
+// out_i[R x N_i] (trans_i = 1), is described by a ColsReduceJob and run by the
+// next launch that takes one (the dX GEMM's preparation).
 int cols_valu_splits(int64_t M);
+struct ColsReduceJob {
+    const float *part;
+    int64_t N;
+    int R, splits, trans;
+    float scale;
+    float *out;
+};
 hipError_t launch_cols_valu_pair(const uint16_t *in0, const float *v0, int64_t N0, float scale0, float *part0,
                                  float *out0, int trans0, const uint16_t *in1, const float *v1, int64_t N1,
                                  float scale1, float *part1, float *out1, int trans1, int64_t M, int R,
-                                 hipStream_t s);
+                                 ColsReduceJob *jobs, hipStream_t s);
 hipError_t launch_cols_skinny(const uint16_t *in, const float *v, int64_t M, int64_t N, int R,
                               float scale, float *part, int splits, float *out, int transpose_out,
                               hipStream_t s);
@@ -67,9 +76,12 @@ hipError_t launch_gemm_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, co
                            const uint16_t *B, int r, float s, uint16_t *Y, const GemmWs &ws,
                            hipStream_t st);
 // dX[M x k] = bf16( dY[M x d] What + [hi(sG) | lo(sG)] [A ; A] ),  G [M x r] fp32
+// red: null, or two column reductions (ColsReduceJob) to run in the same
+// preparation launch; launch_cols_reduce runs them alone.
+hipError_t launch_cols_reduce(const ColsReduceJob *red, hipStream_t st);
 hipError_t launch_gemm_dx(const Nf4Weights &w, const uint16_t *dy, int64_t M, const float *G,
                           const uint16_t *A, int r, float s, uint16_t *dX, const GemmWs &ws,
-                          hipStream_t st);
+                          const ColsReduceJob *red, hipStream_t st);
 
 // The GEMM kernel of launch_gemm_fwd (dx = false) or launch_gemm_dx (dx = true)
 // alone, on a workspace that a full launch with the same arguments prepared.

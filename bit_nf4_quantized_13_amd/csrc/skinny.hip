@@ -257,24 +257,32 @@ __global__ __launch_bounds__(256) void cols_skinny_reduce_kernel(const float *__
 constexpr int kVColsN = 512;
 constexpr int kVRowsMax = 128;  // rows per split
 
+struct ColsJob {
+    const uint16_t *in;
+    const float *v;
+    int64_t N;
+    float *part;
+};
+
 template <int R>
-__global__ __launch_bounds__(256) void cols_valu_kernel(const uint16_t *__restrict__ in,
-                                                        const float *__restrict__ v, int64_t M, int64_t N,
-                                                        int64_t rows_per_split, float *__restrict__ part) {
+__global__ __launch_bounds__(256) void cols_valu_kernel(ColsJob j0, ColsJob j1, int64_t M, int64_t rows_per_split) {
     __shared__ float sv[kVRowsMax * R];
     __shared__ float red[4][kVColsN * R];
+    const ColsJob &jb = blockIdx.z ? j1 : j0;
+    const int64_t N = jb.N;
+    if ((int64_t)blockIdx.x * kVColsN >= N) return;  // the other job is wider
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t n0 = (int64_t)blockIdx.x * kVColsN + 8 * lane;
     const int sp = blockIdx.y;
     const int64_t mbeg = (int64_t)sp * rows_per_split;
     const int64_t mend = (mbeg + rows_per_split < M) ? mbeg + rows_per_split : M;
     const int rows = (int)(mend > mbeg ? mend - mbeg : 0);
-    for (int e = tid; e < rows * R; e += 256) sv[e] = v[mbeg * R + e];
+    for (int e = tid; e < rows * R; e += 256) sv[e] = jb.v[mbeg * R + e];
     __syncthreads();
     // N % 8 == 0: a lane's 8 columns are all inside or all outside
     const bool col_ok = n0 < N;
     const int64_t nrows_buf = (M - mbeg) > 0 ? (M - mbeg) : 0;
-    const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + mbeg * N, nrows_buf * N * 2);
+    const __amdgpu_buffer_rsrc_t rin = make_rsrc(jb.in + mbeg * N, nrows_buf * N * 2);
     float acc[8][R];
 #pragma unroll
     for (int c = 0; c < 8; ++c)
@@ -310,32 +318,9 @@ __global__ __launch_bounds__(256) void cols_valu_kernel(const uint16_t *__restri
     __syncthreads();
     for (int e = tid; e < kVColsN * R; e += 256) {
         const int64_t n = (int64_t)blockIdx.x * kVColsN + e / R;
-        if (n < N) part[((int64_t)sp * N) * R + (int64_t)blockIdx.x * kVColsN * R + e] =
+        if (n < N) jb.part[((int64_t)sp * N) * R + (int64_t)blockIdx.x * kVColsN * R + e] =
             (red[0][e] + red[1][e]) + (red[2][e] + red[3][e]);
     }
-}
-
-// out = scale * sum over splits of part[sp][n][j]: out[n][j] (trans = 0) or
-// out[j][n] (trans = 1).  Two independent jobs in one launch: workgroups
-// [0, g0) for job 0, the rest for job 1.
-struct ColsReduceJob {
-    const float *part;
-    int64_t N;
-    int R, splits, trans;
-    float scale;
-    float *out;
-};
-__global__ __launch_bounds__(256) void cols_valu_reduce_kernel(ColsReduceJob j0, ColsReduceJob j1, int64_t g0) {
-    const bool second = blockIdx.x >= g0;
-    const ColsReduceJob &jb = second ? j1 : j0;
-    const int64_t e = ((int64_t)blockIdx.x - (second ? g0 : 0)) * 256 + threadIdx.x;
-    if (e >= jb.N * jb.R) return;
-    float sum = 0.0f;
-    for (int sp = 0; sp < jb.splits; ++sp) sum += jb.part[(int64_t)sp * jb.N * jb.R + e];
-    const int64_t n = e / jb.R;
-    const int j = (int)(e - n * jb.R);
-    if (jb.trans) jb.out[(int64_t)j * jb.N + n] = jb.scale * sum;
-    else jb.out[e] = jb.scale * sum;
 }
 
 // ---------------------------------------------------------------------------
@@ -415,26 +400,24 @@ int cols_valu_splits(int64_t M) {
 hipError_t launch_cols_valu_pair(const uint16_t *in0, const float *v0, int64_t N0, float scale0, float *part0,
                                  float *out0, int trans0, const uint16_t *in1, const float *v1, int64_t N1,
                                  float scale1, float *part1, float *out1, int trans1, int64_t M, int R,
-                                 hipStream_t s) {
+                                 ColsReduceJob *jobs, hipStream_t s) {
     const int splits = cols_valu_splits(M);
     const int64_t rps = kVRowsMax;
-    const dim3 g0((unsigned)((N0 + kVColsN - 1) / kVColsN), (unsigned)splits);
-    const dim3 g1((unsigned)((N1 + kVColsN - 1) / kVColsN), (unsigned)splits);
+    const int64_t nmax = in1 && N1 > N0 ? N1 : N0;
+    const dim3 grid((unsigned)((nmax + kVColsN - 1) / kVColsN), (unsigned)splits, in1 ? 2u : 1u);
+    const ColsJob j0{in0, v0, N0, part0}, j1{in1, v1, N1, part1};
     switch (R) {
-#define QNF4_CV(RV)                                                                                       \
-    case RV:                                                                                              \
-        hipLaunchKernelGGL(cols_valu_kernel<RV>, g0, dim3(256), 0, s, in0, v0, M, N0, rps, part0);        \
-        if (in1) hipLaunchKernelGGL(cols_valu_kernel<RV>, g1, dim3(256), 0, s, in1, v1, M, N1, rps, part1); \
+#define QNF4_CV(RV)                                                                     \
+    case RV:                                                                            \
+        hipLaunchKernelGGL(cols_valu_kernel<RV>, grid, dim3(256), 0, s, j0, j1, M, rps); \
         break;
         QNF4_CV(1) QNF4_CV(2) QNF4_CV(3) QNF4_CV(4) QNF4_CV(5) QNF4_CV(6) QNF4_CV(7) QNF4_CV(8)
         QNF4_CV(9) QNF4_CV(10) QNF4_CV(11) QNF4_CV(12) QNF4_CV(13) QNF4_CV(14) QNF4_CV(15) QNF4_CV(16)
 #undef QNF4_CV
         default: return hipErrorInvalidValue;
     }
-    ColsReduceJob j0{part0, N0, R, splits, trans0, scale0, out0};
-    ColsReduceJob j1{part1, N1, R, splits, trans1, scale1, out1};
-    const int64_t b0 = (N0 * R + 255) / 256, b1 = in1 ? (N1 * R + 255) / 256 : 0;
-    hipLaunchKernelGGL(cols_valu_reduce_kernel, dim3((unsigned)(b0 + b1)), dim3(256), 0, s, j0, j1, b0);
+    jobs[0] = ColsReduceJob{part0, N0, R, splits, trans0, scale0, out0};
+    jobs[1] = ColsReduceJob{part1, in1 ? N1 : 0, R, splits, trans1, scale1, out1};
     return hipGetLastError();
 }
 
