@@ -51,7 +51,7 @@ QuantWs quant_ws(int64_t d, int64_t k) {
 }
 
 struct LinWs {
-    size_t ctr, dpart, shat, ext_a, ext_b, wbf, u, bt, g, part, total;
+    size_t ctr, dpart, shat, ext_a, ext_b, wbf, u, bt, g, vt, part, total;
 };
 // The decode counters sit first, at the same offset for every shape, so that no
 // other call's data ever lands on them.
@@ -77,13 +77,10 @@ LinWs lin_ws(int64_t M, int64_t d, int64_t k, int r) {
     off += round_up(sizeof(uint16_t) * d * r, 256);
     l.g = off;
     off += round_up(sizeof(float) * M * r, 256);
+    l.vt = off;  // transposed hi / lo planes of U and of G
+    off += round_up(sizeof(uint16_t) * 2 * 2 * cols_rank_pad(r) * M, 256);
     l.part = off;
-    const size_t pd = sizeof(float) * cols_skinny_splits(M, d) * d * 2 * r;
-    const size_t pk = sizeof(float) * cols_skinny_splits(M, k) * k * 2 * r;
-    const size_t pv = sizeof(float) * cols_valu_splits(M) * (round_up(d, 64) + k) * r;
-    size_t part_bytes = pd > pk ? pd : pk;
-    if (r <= 16 && pv > part_bytes) part_bytes = pv;
-    off += round_up(part_bytes, 256);
+    off += round_up(sizeof(float) * cols_splits(M) * (size_t)r * (round_up(d, 64) + k), 256);
     l.total = off;
     return l;
 }
@@ -203,11 +200,11 @@ int qlora_linear_fwd(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M,
         if (r <= 16) {
             e = launch_decode_fwd(nw, x, M, A, nullptr, B, r, scale, Y, U_save, dpart, ctr, s);
         } else {
-            e = launch_rows_skinny(x, A, M, w->k, r, U, s);
+            e = launch_rows_skinny(x, A, M, w->k, r, U, nullptr, s);
             if (e == hipSuccess) e = launch_decode_fwd(nw, x, M, nullptr, U, B, r, scale, Y, nullptr, dpart, ctr, s);
         }
     } else {
-        e = launch_rows_skinny(x, A, M, w->k, r, U, s);
+        e = launch_rows_skinny(x, A, M, w->k, r, U, nullptr, s);
         if (e == hipSuccess) e = launch_gemm_fwd(nw, x, M, U, B, r, scale, Y, gemm_ws(base, l), s);
     }
     return hip_status(e);
@@ -237,32 +234,25 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const qlora_bf16 *x, const qlora
     float *part = reinterpret_cast<float *>(base + l.part);
     const Nf4Weights nw{w->codes, w->absmax_q, w->absmax_scale, w->absmax_mean, d, k};
 
+    uint16_t *vt_u = reinterpret_cast<uint16_t *>(base + l.vt);
+    uint16_t *vt_g = vt_u + 2 * cols_rank_pad(r) * M;
     hipError_t e = hipSuccess;
     const float *Uin = U;
-    if (!Uin) {
-        e = launch_rows_skinny(x, A, M, k, r, Uw, s);
+    if (!Uin) {  // recompute U = X A^T, with its transposed planes
+        e = launch_rows_skinny(x, A, M, k, r, Uw, vt_u, s);
         Uin = Uw;
     }
-    if (e == hipSuccess) e = launch_transpose_bf16(B, d, r, Bt, s);             // B^T [r x d]
-    if (e == hipSuccess) e = launch_rows_skinny(dY, Bt, M, d, r, G, s);         // G = dY B
+    if (e == hipSuccess) e = launch_bwd_prep(B, d, r, Bt, U, M, vt_u, s);    // B^T [r x d] (and U's planes)
+    if (e == hipSuccess) e = launch_rows_skinny(dY, Bt, M, d, r, G, vt_g, s);  // G = dY B
     ColsReduceJob red[2];
-    const ColsReduceJob *pending = nullptr;  // dB, dA reductions not yet run
-    if (r <= 16) {                                                              // dB = s dY^T U, dA = s G^T X
-        float *part_b = part;
-        float *part_a = part + (size_t)cols_valu_splits(M) * round_up(d, 64) * r;
-        if (e == hipSuccess)
-            e = launch_cols_valu_pair(dY, Uin, d, scale, part_b, dB, 0, x, G, k, scale, part_a, dA, 1, M, r, red, s);
-        pending = red;
-    } else {
-        if (e == hipSuccess)
-            e = launch_cols_skinny(dY, Uin, M, d, r, scale, part, cols_skinny_splits(M, d), dB, 0, s);
-        if (e == hipSuccess)
-            e = launch_cols_skinny(x, G, M, k, r, scale, part, cols_skinny_splits(M, k), dA, 1, s);
-    }
+    float *part_b = part;                                                       // dB = s U^T dY (as [d x r])
+    float *part_a = part + (size_t)cols_splits(M) * r * round_up(d, 64);        // dA = s G^T X
+    if (e == hipSuccess)
+        e = launch_cols_pair(dY, vt_u, d, scale, part_b, dB, 0, x, vt_g, k, scale, part_a, dA, 1, M, r, red, s);
     if (e == hipSuccess && dX)                                                  // dX = dY What + s G A
-        e = launch_gemm_dx(nw, dY, M, G, A, r, scale, dX, gemm_ws(base, l), pending, s);
-    else if (e == hipSuccess && pending)
-        e = launch_cols_reduce(pending, s);
+        e = launch_gemm_dx(nw, dY, M, G, A, r, scale, dX, gemm_ws(base, l), red, s);
+    else if (e == hipSuccess)
+        e = launch_cols_reduce(red, s);
     return hip_status(e);
 }
 

@@ -628,19 +628,24 @@ struct PrepArgs {
     int64_t g_shat, g_a, g_b, g_t, g_r0;  // workgroups per range (the second reduction takes the rest)
 };
 
+// out = scale * sum over splits of part[sp][j][n] (split order), e = (j, n)
+// with n fastest; stored out[n][j] (trans = 0) or out[j][n] (trans = 1)
 __device__ __forceinline__ void cols_reduce(const ColsReduceJob &jb, int64_t e) {
-    if (e >= jb.N * jb.R) return;
-    float v[64];
+    const int64_t RN = (int64_t)jb.R * jb.N;
+    if (e >= RN) return;
+    constexpr int kMax = 32;
+    float v[kMax];
     const int sp = jb.splits;
 #pragma unroll
-    for (int q = 0; q < 64; ++q) v[q] = q < sp ? jb.part[(int64_t)q * jb.N * jb.R + e] : 0.0f;
-    float sum = 0.0f;
-    for (int q = 0; q < sp && q < 64; ++q) sum += v[q];  // split order
-    for (int q = 64; q < sp; ++q) sum += jb.part[(int64_t)q * jb.N * jb.R + e];
-    const int64_t n = e / jb.R;
-    const int j = (int)(e - n * jb.R);
-    if (jb.trans) jb.out[(int64_t)j * jb.N + n] = jb.scale * sum;
-    else jb.out[e] = jb.scale * sum;
+    for (int q = 0; q < kMax; ++q) v[q] = q < sp ? jb.part[(int64_t)q * RN + e] : 0.0f;
+    float sum = v[0];
+#pragma unroll
+    for (int q = 1; q < kMax; ++q)
+        if (q < sp) sum += v[q];
+    for (int q = kMax; q < sp; ++q) sum += jb.part[(int64_t)q * RN + e];
+    const int64_t j = e / jb.N, n = e - j * jb.N;
+    if (jb.trans) jb.out[e] = jb.scale * sum;
+    else jb.out[n * jb.R + j] = jb.scale * sum;
 }
 
 template <bool DX>

@@ -19,22 +19,23 @@ hipError_t launch_dequantize(const uint8_t *codes, const int8_t *c2, const float
                              const float *mean, int64_t n, uint16_t *out, hipStream_t s);
 
 // ---- skinny GEMMs ----------------------------------------------------------
-// out[M x R] (fp32) = In[M x K] (bf16) * W[R x K]^T (bf16), R <= 128.
+// out[M x R] (fp32) = In[M x K] (bf16) * W[R x K]^T (bf16), R <= 128.  vt: null,
+// or [2][Rp][M] bf16 receiving the transposed hi and lo planes of out (rows
+// R..Rp-1 zero), Rp = cols_rank_pad(R).
+int64_t cols_rank_pad(int r);
 hipError_t launch_rows_skinny(const uint16_t *in, const uint16_t *w, int64_t M, int64_t K, int R,
-                              float *out, hipStream_t s);
-// dst[C x R] = transpose(src[R x C]) for bf16.
-hipError_t launch_transpose_bf16(const uint16_t *src, int64_t R, int64_t C, uint16_t *dst, hipStream_t s);
-// part[S][N][2R] = split-M partial sums of In^T * [hi(V) | lo(V)], In [M x N]
-// bf16, V [M x R] fp32; then out = scale * sum over splits of (hi + lo part),
-// written as out[N x R] (transpose_out = 0) or out[R x N] (transpose_out = 1).
-int cols_skinny_splits(int64_t M, int64_t N);
-// Rank R <= 16: the same reductions on the vector ALU in fp32, two jobs in
-// one launch (job 1 skipped when in1 is null): part_i[S][N_i][R] holds the
-// split-M partial sums In_i^T V_i, S = cols_valu_splits(M).  The reduction
-// out_i = scale_i * sum over splits, stored out_i[N_i x R] (trans_i = 0) or
-// out_i[R x N_i] (trans_i = 1), is described by a ColsReduceJob and run by the
-// next launch that takes one (the dX GEMM's preparation).
-int cols_valu_splits(int64_t M);
+                              float *out, uint16_t *vt, hipStream_t s);
+// Backward preparation: Bt[r x d] = B[d x r]^T and, when U is given, the
+// transposed hi / lo planes of U [M x r] into vt [2][Rp][M].
+hipError_t launch_bwd_prep(const uint16_t *B, int64_t d, int r, uint16_t *Bt, const float *U, int64_t M,
+                           uint16_t *vt, hipStream_t s);
+// Two column reductions in one launch (job 1 skipped when in1 is null):
+// part_i[S][R][N_i] = split-M partial sums of V_i^T In_i (V_i given as vt_i),
+// S = cols_splits(M).  The reduction out_i = scale_i * sum over splits, stored
+// out_i[N_i x R] (trans_i = 0) or out_i[R x N_i] (trans_i = 1), is described by
+// a ColsReduceJob and run by the next launch that takes one (the dX GEMM's
+// preparation, or launch_cols_reduce).
+int cols_splits(int64_t M);
 struct ColsReduceJob {
     const float *part;
     int64_t N;
@@ -42,13 +43,10 @@ struct ColsReduceJob {
     float scale;
     float *out;
 };
-hipError_t launch_cols_valu_pair(const uint16_t *in0, const float *v0, int64_t N0, float scale0, float *part0,
-                                 float *out0, int trans0, const uint16_t *in1, const float *v1, int64_t N1,
-                                 float scale1, float *part1, float *out1, int trans1, int64_t M, int R,
-                                 ColsReduceJob *jobs, hipStream_t s);
-hipError_t launch_cols_skinny(const uint16_t *in, const float *v, int64_t M, int64_t N, int R,
-                              float scale, float *part, int splits, float *out, int transpose_out,
-                              hipStream_t s);
+hipError_t launch_cols_pair(const uint16_t *in0, const uint16_t *vt0, int64_t N0, float scale0, float *part0,
+                            float *out0, int trans0, const uint16_t *in1, const uint16_t *vt1, int64_t N1,
+                            float scale1, float *part1, float *out1, int trans1, int64_t M, int R,
+                            ColsReduceJob *jobs, hipStream_t s);
 
 // ---- fused NF4 dequant GEMMs ----------------------------------------------
 struct Nf4Weights {

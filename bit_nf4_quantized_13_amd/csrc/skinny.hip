@@ -53,7 +53,8 @@ template <int NT, int W>  // W waves split K
 __global__ __launch_bounds__(64 * W) void rows_skinny_kernel(const uint16_t *__restrict__ in,
                                                              const uint16_t *__restrict__ w,
                                                              int64_t M, int64_t K, int R,
-                                                             float *__restrict__ out) {
+                                                             float *__restrict__ out, uint16_t *__restrict__ vt,
+                                                             int64_t Rp) {
     __shared__ f32x4 s_acc[W][NT][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i = lane & 15, g = lane >> 4;
@@ -106,19 +107,40 @@ __global__ __launch_bounds__(64 * W) void rows_skinny_kernel(const uint16_t *__r
             for (int r = 0; r < 4; ++r) {
                 const int64_t row = (int64_t)blockIdx.x * 16 + 4 * g + r;
                 if (row < M && j < R) out[row * R + j] = v[r];
+                if (vt && row < M && j < Rp) {  // transposed bf16 hi + lo planes (zero rows past R)
+                    const float f = j < R ? v[r] : 0.0f;
+                    const uint32_t hb = pack_bf16x2(f, 0.0f) & 0xFFFFu;
+                    vt[(int64_t)j * M + row] = (uint16_t)hb;
+                    vt[(Rp + j) * M + row] = (uint16_t)(pack_bf16x2(f - bf16_bits_to_f32(hb), 0.0f) & 0xFFFFu);
+                }
             }
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// dst[C x R] = src[R x C]^T (bf16), 64 x 64 tiles through LDS.
+// Backward preparation, one launch: workgroups [0, gt) transpose src = B
+// [R = d rows x C = r columns] into dst = B^T [r x d] (64 x 64 tiles through
+// LDS); the rest write the transposed bf16 planes of a given U [M x r] fp32:
+// vt[j][m] = hi(U[m][j]), vt[Rp + j][m] = lo(U[m][j]) (zero for r <= j < Rp).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *__restrict__ src,
-                                                             int64_t R, int64_t C,
-                                                             uint16_t *__restrict__ dst) {
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t *__restrict__ src, int64_t R, int64_t C,
+                                                       uint16_t *__restrict__ dst, int64_t gt,
+                                                       const float *__restrict__ U, int64_t M, int64_t Rp,
+                                                       uint16_t *__restrict__ vt) {
     __shared__ uint16_t tile[64][65];
-    const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
+    if ((int64_t)blockIdx.x >= gt) {
+        const int64_t e = ((int64_t)blockIdx.x - gt) * 256 + threadIdx.x;  // (j, m), m fastest
+        if (e >= Rp * M) return;
+        const int64_t j = e / M, m = e - j * M;  // the rank is C (B is [R = d] x [C = r])
+        const float f = j < C ? U[m * C + j] : 0.0f;
+        const uint32_t hb = pack_bf16x2(f, 0.0f) & 0xFFFFu;
+        vt[e] = (uint16_t)hb;
+        vt[Rp * M + e] = (uint16_t)(pack_bf16x2(f - bf16_bits_to_f32(hb), 0.0f) & 0xFFFFu);
+        return;
+    }
+    const int64_t tiles_c = (C + 63) / 64;
+    const int64_t c0 = ((int64_t)blockIdx.x % tiles_c) * 64, r0 = ((int64_t)blockIdx.x / tiles_c) * 64;
     for (int e = threadIdx.x; e < 64 * 64; e += 256) {
         const int rr = e / 64, cc = e % 64;
         const int64_t r = r0 + rr, c = c0 + cc;
@@ -133,193 +155,106 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *__r
 }
 
 // ---------------------------------------------------------------------------
-// Split-M partial sums of In^T [hi(V) | lo(V)]:
-//   part[sp][n][j]     = sum_{m in split sp} In[m][n] hi(V[m][j])
-//   part[sp][n][R + j] = sum_{m in split sp} In[m][n] lo(V[m][j])
-// hi(v) = bf16(v), lo(v) = bf16(v - hi(v)), so hi + lo carries V to about 16
-// significant bits through bf16 MFMA.  A workgroup owns 64 columns n and one
-// split; per round it stages 64 rows of In (transposed, m contiguous) and of
-// V (split, transposed) in LDS and runs two MFMA k-steps.
+// Split-M column reductions on MFMA, two jobs in one launch (blockIdx.z):
+//   part[sp][j][n] = sum_{m in split sp} V[m][j] In[m][n]     (j < R)
+// with V supplied as transposed bf16 hi + lo planes vt [2][Rp][M] (hi + lo
+// carry V to about 16 significant bits).  A workgroup owns 128 columns and
+// one split; its four waves take 32-row steps in turn.  Lane (n, g) loads rows
+// m0 + 8 g .. + 7 of columns 8 n .. 8 n + 7 (16 lanes read a 256-byte row
+// segment), transposes the 8 x 8 block in registers (v_perm) and so holds, for
+// each q = 0..7, column 8 n + q over those 8 rows: the second MFMA operand of
+// tile q, whose column index is n.  The first operand is vt (rows j, k = m),
+// contiguous.  Result lane (n, g) register v of tile q: j = 16 t + 4 g + v,
+// column 8 n + q.
 // ---------------------------------------------------------------------------
-constexpr int kColsTileN = 64;
-constexpr int kColsRows = 64;
-constexpr int kPitch = kColsRows + 8;  // bf16 elements per LDS row (16-byte multiple)
+constexpr int kCColsN = 128;
+constexpr int kCRows = 512;  // rows per split
 
-template <int NT2>  // 16-wide tiles covering 2R
-__global__ __launch_bounds__(256) void cols_skinny_partial_kernel(
-    const uint16_t *__restrict__ in, const float *__restrict__ v, int64_t M, int64_t N, int R,
-    int64_t rows_per_split, float *__restrict__ part) {
-    __shared__ __attribute__((aligned(16))) uint16_t s_in[kColsTileN][kPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t s_v[NT2 * 16][kPitch];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int i = lane & 15, g = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * kColsTileN;
-    const int sp = blockIdx.y;
-    const int64_t mbeg = (int64_t)sp * rows_per_split;
-    const int64_t mend = (mbeg + rows_per_split < M) ? mbeg + rows_per_split : M;
-    const int R2 = 2 * R;
-
-    f32x4 acc[NT2];
-#pragma unroll
-    for (int t = 0; t < NT2; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int64_t m0 = mbeg; m0 < mend; m0 += kColsRows) {
-        // In[m0 .. m0+63][n0 .. n0+63]: each thread loads 2 x 8 columns of one row
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int e = tid + 256 * h;     // 512 pieces of 8 columns
-            const int rr = e >> 3, cc = (e & 7) * 8;
-            const int64_t mm = m0 + rr, nn = n0 + cc;
-            uint4 val = uint4{0, 0, 0, 0};
-            if (mm < mend && nn < N) val = *reinterpret_cast<const uint4 *>(in + mm * N + nn);
-            const uint32_t wv[4] = {val.x, val.y, val.z, val.w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                s_in[cc + 2 * q][rr] = (uint16_t)(wv[q] & 0xFFFF);
-                s_in[cc + 2 * q + 1][rr] = (uint16_t)(wv[q] >> 16);
-            }
-        }
-        // V[m0 .. m0+63][0 .. R) split into hi / lo, stored s_v[j'][m]
-        for (int e = tid; e < kColsRows * NT2 * 16 / 2; e += 256) {
-            const int rr = e % kColsRows, j = e / kColsRows;  // j < NT2*8
-            uint16_t hi = 0, lo = 0;
-            const int64_t mm = m0 + rr;
-            if (j < R && mm < mend) {
-                const float x = v[mm * R + j];
-                const uint32_t hb = pack_bf16x2(x, 0.0f) & 0xFFFFu;
-                hi = (uint16_t)hb;
-                lo = (uint16_t)(pack_bf16x2(x - bf16_bits_to_f32(hb), 0.0f) & 0xFFFFu);
-            }
-            if (j < R) {
-                s_v[j][rr] = hi;
-                s_v[R + j][rr] = lo;
-            }
-        }
-        // zero the pad columns j' in [2R, NT2*16)
-        for (int e = tid; e < kColsRows * (NT2 * 16 - R2); e += 256) {
-            const int rr = e % kColsRows, j = R2 + e / kColsRows;
-            s_v[j][rr] = 0;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int ks = 0; ks < kColsRows / 32; ++ks) {
-            const uint4 a = *reinterpret_cast<const uint4 *>(&s_in[16 * wave + i][32 * ks + 8 * g]);
-#pragma unroll
-            for (int t = 0; t < NT2; ++t) {
-                const uint4 b = *reinterpret_cast<const uint4 *>(&s_v[16 * t + i][32 * ks + 8 * g]);
-                acc[t] = mfma16(a, b, acc[t]);
-            }
-        }
-        __syncthreads();
-    }
-    // D[4g + r][i]: row = column n of In, col = j'
-#pragma unroll
-    for (int t = 0; t < NT2; ++t) {
-        const int j = 16 * t + i;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t nn = n0 + 16 * wave + 4 * g + r;
-            if (nn < N && j < R2) part[((int64_t)sp * N + nn) * R2 + j] = acc[t][r];
-        }
-    }
-}
-
-__global__ __launch_bounds__(256) void cols_skinny_reduce_kernel(const float *__restrict__ part,
-                                                                 int64_t N, int R, int splits,
-                                                                 float scale, float *__restrict__ out,
-                                                                 int transpose_out) {
-    const int64_t total = N * R;
-    const int R2 = 2 * R;
-    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
-         e += (int64_t)gridDim.x * 256) {
-        const int64_t n = e / R;
-        const int j = (int)(e % R);
-        float hi = 0.0f, lo = 0.0f;
-        for (int sp = 0; sp < splits; ++sp) {
-            const float *p = part + ((int64_t)sp * N + n) * R2;
-            hi += p[j];
-            lo += p[R + j];
-        }
-        const float val = scale * (hi + lo);
-        if (transpose_out) out[(int64_t)j * N + n] = val;
-        else out[n * R + j] = val;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Small-rank column reductions on the vector ALU (R <= 16):
-//   part[sp][n][j] = sum over rows m of split sp of In[m][n] V[m][j]   (fp32)
-// A workgroup owns 512 columns and one row split; lane l of every wave owns
-// columns 8 l .. 8 l + 7 (one 16-byte load per row) and the 4 waves take every
-// 4th row.  V of the split is staged in LDS (each row's R values are read as a
-// broadcast); the 4 wave partials are summed in LDS in a fixed order.
-// ---------------------------------------------------------------------------
-constexpr int kVColsN = 512;
-constexpr int kVRowsMax = 128;  // rows per split
-
-struct ColsJob {
-    const uint16_t *in;
-    const float *v;
+struct ColsMJob {
+    const uint16_t *in;   // [M x N] bf16
+    const uint16_t *vt;   // [2][Rp][M] bf16
     int64_t N;
-    float *part;
+    float *part;          // [splits][R][N]
 };
 
-template <int R>
-__global__ __launch_bounds__(256) void cols_valu_kernel(ColsJob j0, ColsJob j1, int64_t M, int64_t rows_per_split) {
-    __shared__ float sv[kVRowsMax * R];
-    __shared__ float red[4][kVColsN * R];
-    const ColsJob &jb = blockIdx.z ? j1 : j0;
+template <int RT>  // 16-row tiles of Rp
+__global__ __launch_bounds__(256) void cols_mfma_kernel(ColsMJob j0, ColsMJob j1, int64_t M, int R) {
+    __shared__ __attribute__((aligned(16))) float red[4][16 * kCColsN];
+    const ColsMJob &jb = blockIdx.z ? j1 : j0;
     const int64_t N = jb.N;
-    if ((int64_t)blockIdx.x * kVColsN >= N) return;  // the other job is wider
+    const int64_t cb = (int64_t)blockIdx.x * kCColsN;
+    if (cb >= N) return;  // the other job is wider
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t n0 = (int64_t)blockIdx.x * kVColsN + 8 * lane;
+    const int n16 = lane & 15, g = lane >> 4;
+    const int64_t Rp = 16 * RT;
     const int sp = blockIdx.y;
-    const int64_t mbeg = (int64_t)sp * rows_per_split;
-    const int64_t mend = (mbeg + rows_per_split < M) ? mbeg + rows_per_split : M;
-    const int rows = (int)(mend > mbeg ? mend - mbeg : 0);
-    for (int e = tid; e < rows * R; e += 256) sv[e] = jb.v[mbeg * R + e];
-    __syncthreads();
-    // N % 8 == 0: a lane's 8 columns are all inside or all outside
-    const bool col_ok = n0 < N;
-    const int64_t nrows_buf = (M - mbeg) > 0 ? (M - mbeg) : 0;
-    const __amdgpu_buffer_rsrc_t rin = make_rsrc(jb.in + mbeg * N, nrows_buf * N * 2);
-    float acc[8][R];
+    const int64_t mbeg = (int64_t)sp * kCRows;
+    const int64_t mend = mbeg + kCRows < M ? mbeg + kCRows : M;
+    const __amdgpu_buffer_rsrc_t rin = make_rsrc(jb.in, M * N * 2);
+    const __amdgpu_buffer_rsrc_t rvt = make_rsrc(jb.vt, 2 * Rp * M * 2);
+    const bool col_ok = cb + 8 * n16 < N;  // N % 8 == 0
+    f32x4 acc[RT][8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+    for (int t = 0; t < RT; ++t)
 #pragma unroll
-        for (int j = 0; j < R; ++j) acc[c][j] = 0.0f;
-    for (int r0 = wave; r0 < rows; r0 += 16) {
-        uint4 x[4];
+        for (int q = 0; q < 8; ++q) acc[t][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int64_t m0 = mbeg + 32 * wave; m0 < mend; m0 += 128) {
+        uint4 rv[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) x[u] = load16(rin, (uint32_t)(((int64_t)(r0 + 4 * u) * N + n0) * 2));
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int rr = r0 + 4 * u;
-            if (rr >= rows || !col_ok) continue;
-            const uint32_t xw[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
-            float xf[8];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                xf[2 * q] = __uint_as_float(xw[q] << 16);
-                xf[2 * q + 1] = __uint_as_float(xw[q] & 0xFFFF0000u);
-            }
-#pragma unroll
-            for (int j = 0; j < R; ++j) {
-                const float vj = sv[rr * R + j];
-#pragma unroll
-                for (int c = 0; c < 8; ++c) acc[c][j] = __builtin_fmaf(xf[c], vj, acc[c][j]);
-            }
+        for (int e = 0; e < 8; ++e) {
+            const int64_t row = m0 + 8 * g + e;
+            rv[e] = load16(rin, row < mend && col_ok ? (uint32_t)((row * N + cb + 8 * n16) * 2) : 0x80000000u);
         }
+        uint4 ph[RT], pl[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            const int64_t off = ((16 * t + n16) * M + m0 + 8 * g) * 2;
+            ph[t] = load16(rvt, (uint32_t)off);
+            pl[t] = load16(rvt, (uint32_t)(off + Rp * M * 2));
+        }
+        // 8 x 8 transpose: word h of column q pairs rows 2 h (low half) and 2 h + 1 (high half)
+        uint4 fr[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint32_t sel = (q & 1) ? 0x07060302u : 0x05040100u;
+            uint32_t w[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const uint4 a = rv[2 * h], b = rv[2 * h + 1];
+                const uint32_t lo = q < 2 ? a.x : q < 4 ? a.y : q < 6 ? a.z : a.w;
+                const uint32_t hi = q < 2 ? b.x : q < 4 ? b.y : q < 6 ? b.z : b.w;
+                w[h] = __builtin_amdgcn_perm(hi, lo, sel);
+            }
+            fr[q] = uint4{w[0], w[1], w[2], w[3]};
+        }
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                acc[t][q] = mfma16(ph[t], fr[q], acc[t][q]);
+                acc[t][q] = mfma16(pl[t], fr[q], acc[t][q]);
+            }
     }
+    // the four waves in a fixed order, one 16-row tile of j at a time
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+    for (int t = 0; t < RT; ++t) {
 #pragma unroll
-        for (int j = 0; j < R; ++j) red[wave][(8 * lane + c) * R + j] = acc[c][j];
-    __syncthreads();
-    for (int e = tid; e < kVColsN * R; e += 256) {
-        const int64_t n = (int64_t)blockIdx.x * kVColsN + e / R;
-        if (n < N) jb.part[((int64_t)sp * N) * R + (int64_t)blockIdx.x * kVColsN * R + e] =
-            (red[0][e] + red[1][e]) + (red[2][e] + red[3][e]);
+        for (int v = 0; v < 4; ++v) {
+            float *dst = &red[wave][(4 * g + v) * kCColsN + 8 * n16];
+            *reinterpret_cast<f32x4 *>(dst) = f32x4{acc[t][0][v], acc[t][1][v], acc[t][2][v], acc[t][3][v]};
+            *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{acc[t][4][v], acc[t][5][v], acc[t][6][v], acc[t][7][v]};
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = tid + 256 * u;  // (j, column), column fastest
+            const int jl = e / kCColsN, c = e % kCColsN;
+            const int j = 16 * t + jl;
+            const int64_t n = cb + c;
+            if (j < R && n < N)
+                jb.part[((int64_t)sp * R + j) * N + n] = (red[0][e] + red[1][e]) + (red[2][e] + red[3][e]);
+        }
+        __syncthreads();
     }
 }
 
@@ -330,21 +265,23 @@ __global__ __launch_bounds__(256) void cols_valu_kernel(ColsJob j0, ColsJob j1, 
 // over the whole chip instead of one workgroup.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void dot_rows_kernel(const uint16_t *__restrict__ in, const uint16_t *__restrict__ w,
-                                                       int64_t M, int64_t K, int R, float *__restrict__ out) {
+                                                       int64_t M, int64_t K, int R, float *__restrict__ out,
+                                                       uint16_t *__restrict__ vt, int64_t Rp) {
     const int lane = threadIdx.x & 63;
-    const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // output element
-    if (e >= M * R) return;
-    const int64_t m = e / R;
-    const int j = (int)(e - m * R);
+    const int64_t Rc = vt ? Rp : R;  // columns computed: Rp when the zero-padded planes are wanted
+    const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // output element (m, j)
+    if (e >= M * Rc) return;
+    const int64_t m = e / Rc;
+    const int j = (int)(e - m * Rc);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(in + m * K, K * 2);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(w + (int64_t)j * K, K * 2);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(w + (int64_t)(j < R ? j : 0) * K, j < R ? K * 2 : 0);
     float acc = 0.0f;
     for (int64_t k0 = 0; k0 < K; k0 += 64 * 8 * 8) {
         uint4 a[8], b[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const uint32_t off = (uint32_t)((k0 + (u * 64 + lane) * 8) * 2);
-            a[u] = load16(ra, off);  // past K: zero
+            a[u] = load16(ra, off);  // past K (and W rows past R): zero
             b[u] = load16(rb, off);
         }
 #pragma unroll
@@ -360,23 +297,33 @@ __global__ __launch_bounds__(256) void dot_rows_kernel(const uint16_t *__restric
     // fixed-order butterfly over the 64 lanes
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) out[e] = acc;
+    if (lane == 0) {
+        if (j < R) out[m * R + j] = acc;
+        if (vt) {  // transposed bf16 hi + lo planes
+            const uint32_t hb = pack_bf16x2(acc, 0.0f) & 0xFFFFu;
+            vt[(int64_t)j * M + m] = (uint16_t)hb;
+            vt[(Rp + j) * M + m] = (uint16_t)(pack_bf16x2(acc - bf16_bits_to_f32(hb), 0.0f) & 0xFFFFu);
+        }
+    }
 }
 
 }  // namespace
 
 hipError_t launch_rows_skinny(const uint16_t *in, const uint16_t *w, int64_t M, int64_t K, int R,
-                              float *out, hipStream_t s) {
+                              float *out, uint16_t *vt, hipStream_t s) {
+    const int64_t Rp = cols_rank_pad(R);
     const dim3 grid((unsigned)((M + 15) / 16));
     const int nt = (R + 15) / 16;
     // decode-sized M: one wave per output element, spread over the chip
-    if (M * R <= 4096) {
-        hipLaunchKernelGGL(dot_rows_kernel, dim3((unsigned)((M * R + 3) / 4)), dim3(256), 0, s, in, w, M, K, R, out);
+    if (M * R <= 4096) {  // (the choice must not depend on vt: U and its recomputation agree bit for bit)
+        const int64_t rc = vt ? Rp : R;
+        hipLaunchKernelGGL(dot_rows_kernel, dim3((unsigned)((M * rc + 3) / 4)), dim3(256), 0, s, in, w, M, K, R, out,
+                           vt, Rp);
         return hipGetLastError();
     }
     switch (nt) {
 #define QNF4_ROWS(NTV) \
-    case NTV: hipLaunchKernelGGL((rows_skinny_kernel<NTV, 4>), grid, dim3(256), 0, s, in, w, M, K, R, out); break;
+    case NTV: hipLaunchKernelGGL((rows_skinny_kernel<NTV, 4>), grid, dim3(256), 0, s, in, w, M, K, R, out, vt, Rp); break;
         QNF4_ROWS(1) QNF4_ROWS(2) QNF4_ROWS(3) QNF4_ROWS(4)
         QNF4_ROWS(5) QNF4_ROWS(6) QNF4_ROWS(7) QNF4_ROWS(8)
 #undef QNF4_ROWS
@@ -385,75 +332,42 @@ hipError_t launch_rows_skinny(const uint16_t *in, const uint16_t *w, int64_t M, 
     return hipGetLastError();
 }
 
-hipError_t launch_transpose_bf16(const uint16_t *src, int64_t R, int64_t C, uint16_t *dst,
-                                 hipStream_t s) {
-    const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
-    hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, src, R, C, dst);
+int64_t cols_rank_pad(int r) { return (r + 15) / 16 * 16; }
+
+hipError_t launch_bwd_prep(const uint16_t *B, int64_t d, int r, uint16_t *Bt, const float *U, int64_t M,
+                           uint16_t *vt, hipStream_t s) {
+    const int64_t Rp = cols_rank_pad(r);
+    const int64_t gt = ((d + 63) / 64) * ((r + 63) / 64);
+    const int64_t gu = U ? (Rp * M + 255) / 256 : 0;
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)(gt + gu)), dim3(256), 0, s, B, d, (int64_t)r, Bt, gt, U, M, Rp,
+                       vt);
     return hipGetLastError();
 }
 
-int cols_valu_splits(int64_t M) {
-    int64_t splits = (M + kVRowsMax - 1) / kVRowsMax;
-    return (int)(splits < 1 ? 1 : splits);
+int cols_splits(int64_t M) {
+    const int64_t sp = (M + kCRows - 1) / kCRows;
+    return (int)(sp < 1 ? 1 : sp);
 }
 
-hipError_t launch_cols_valu_pair(const uint16_t *in0, const float *v0, int64_t N0, float scale0, float *part0,
-                                 float *out0, int trans0, const uint16_t *in1, const float *v1, int64_t N1,
-                                 float scale1, float *part1, float *out1, int trans1, int64_t M, int R,
-                                 ColsReduceJob *jobs, hipStream_t s) {
-    const int splits = cols_valu_splits(M);
-    const int64_t rps = kVRowsMax;
+hipError_t launch_cols_pair(const uint16_t *in0, const uint16_t *vt0, int64_t N0, float scale0, float *part0,
+                            float *out0, int trans0, const uint16_t *in1, const uint16_t *vt1, int64_t N1,
+                            float scale1, float *part1, float *out1, int trans1, int64_t M, int R,
+                            ColsReduceJob *jobs, hipStream_t s) {
+    const int splits = cols_splits(M);
     const int64_t nmax = in1 && N1 > N0 ? N1 : N0;
-    const dim3 grid((unsigned)((nmax + kVColsN - 1) / kVColsN), (unsigned)splits, in1 ? 2u : 1u);
-    const ColsJob j0{in0, v0, N0, part0}, j1{in1, v1, N1, part1};
-    switch (R) {
-#define QNF4_CV(RV)                                                                     \
-    case RV:                                                                            \
-        hipLaunchKernelGGL(cols_valu_kernel<RV>, grid, dim3(256), 0, s, j0, j1, M, rps); \
+    const dim3 grid((unsigned)((nmax + kCColsN - 1) / kCColsN), (unsigned)splits, in1 ? 2u : 1u);
+    const ColsMJob j0{in0, vt0, N0, part0}, j1{in1, vt1, N1, part1};
+    switch ((R + 15) / 16) {
+#define QNF4_CM(RT)                                                                  \
+    case RT:                                                                         \
+        hipLaunchKernelGGL(cols_mfma_kernel<RT>, grid, dim3(256), 0, s, j0, j1, M, R); \
         break;
-        QNF4_CV(1) QNF4_CV(2) QNF4_CV(3) QNF4_CV(4) QNF4_CV(5) QNF4_CV(6) QNF4_CV(7) QNF4_CV(8)
-        QNF4_CV(9) QNF4_CV(10) QNF4_CV(11) QNF4_CV(12) QNF4_CV(13) QNF4_CV(14) QNF4_CV(15) QNF4_CV(16)
-#undef QNF4_CV
+        QNF4_CM(1) QNF4_CM(2) QNF4_CM(3) QNF4_CM(4) QNF4_CM(5) QNF4_CM(6) QNF4_CM(7) QNF4_CM(8)
+#undef QNF4_CM
         default: return hipErrorInvalidValue;
     }
     jobs[0] = ColsReduceJob{part0, N0, R, splits, trans0, scale0, out0};
     jobs[1] = ColsReduceJob{part1, in1 ? N1 : 0, R, splits, trans1, scale1, out1};
-    return hipGetLastError();
-}
-
-int cols_skinny_splits(int64_t M, int64_t N) {
-    const int64_t tiles = (N + kColsTileN - 1) / kColsTileN;
-    int64_t splits = (1024 + tiles - 1) / tiles;  // aim for >= 1024 workgroups
-    const int64_t max_splits = (M + kColsRows - 1) / kColsRows;
-    if (splits > max_splits) splits = max_splits;
-    if (splits > 64) splits = 64;
-    if (splits < 1) splits = 1;
-    return (int)splits;
-}
-
-hipError_t launch_cols_skinny(const uint16_t *in, const float *v, int64_t M, int64_t N, int R,
-                              float scale, float *part, int splits, float *out, int transpose_out,
-                              hipStream_t s) {
-    int64_t rows = (M + splits - 1) / splits;
-    rows = (rows + kColsRows - 1) / kColsRows * kColsRows;
-    const dim3 grid((unsigned)((N + kColsTileN - 1) / kColsTileN), (unsigned)splits);
-    const int nt2 = (2 * R + 15) / 16;
-    switch (nt2) {
-#define QNF4_COLS(NTV)                                                                         \
-    case NTV:                                                                                  \
-        hipLaunchKernelGGL(cols_skinny_partial_kernel<NTV>, grid, dim3(256), 0, s, in, v, M, N, \
-                           R, rows, part);                                                     \
-        break;
-        QNF4_COLS(1) QNF4_COLS(2) QNF4_COLS(3) QNF4_COLS(4) QNF4_COLS(5) QNF4_COLS(6)
-        QNF4_COLS(7) QNF4_COLS(8) QNF4_COLS(9) QNF4_COLS(10) QNF4_COLS(11) QNF4_COLS(12)
-        QNF4_COLS(13) QNF4_COLS(14) QNF4_COLS(15) QNF4_COLS(16)
-#undef QNF4_COLS
-        default: return hipErrorInvalidValue;
-    }
-    int64_t rgrid = (N * R + 255) / 256;
-    if (rgrid > 4096) rgrid = 4096;
-    hipLaunchKernelGGL(cols_skinny_reduce_kernel, dim3((unsigned)rgrid), dim3(256), 0, s, part, N,
-                       R, splits, scale, out, transpose_out);
     return hipGetLastError();
 }
 
