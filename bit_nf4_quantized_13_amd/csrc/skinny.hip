@@ -49,7 +49,7 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff)
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
-template <int NT, int W>  // W waves split K
+template <int NT, int W, int CPI>  // W waves split K; CPI chunks of 128 k in flight per wave
 __global__ __launch_bounds__(64 * W) void rows_skinny_kernel(const uint16_t *__restrict__ in,
                                                              const uint16_t *__restrict__ w,
                                                              int64_t M, int64_t K, int R,
@@ -68,14 +68,14 @@ __global__ __launch_bounds__(64 * W) void rows_skinny_kernel(const uint16_t *__r
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Two chunks of 128 k per iteration, all loads issued before the MFMAs
+    // CPI chunks of 128 k per iteration, all loads issued before the MFMAs
     // (enough bytes in flight per CU to stream the activations from HBM).
     const int64_t chunks = (K + 127) / 128;
-    for (int64_t c = wave; c < chunks; c += 2 * W) {
-        uint4 a[2][4], b[2][NT][4];
-        bool ok[2][4];
+    for (int64_t c = wave; c < chunks; c += CPI * W) {
+        uint4 a[CPI][4], b[CPI][NT][4];
+        bool ok[CPI][4];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < CPI; ++u) {
             const int64_t k0 = (c + W * u) * 128 + 32 * g;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(64 * W) void rows_skinny_kernel(const uint16_t *__r
             }
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < CPI; ++u)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint4 av = ok[u][e] ? a[u][e] : uint4{0, 0, 0, 0};
@@ -323,7 +323,10 @@ hipError_t launch_rows_skinny(const uint16_t *in, const uint16_t *w, int64_t M, 
     }
     switch (nt) {
 #define QNF4_ROWS(NTV) \
-    case NTV: hipLaunchKernelGGL((rows_skinny_kernel<NTV, 4>), grid, dim3(256), 0, s, in, w, M, K, R, out, vt, Rp); break;
+    case NTV:                                                                                          \
+        hipLaunchKernelGGL((rows_skinny_kernel<NTV, 8, (NTV == 1 ? 4 : 2)>), grid, dim3(512), 0, s, in, w, M, K, R, \
+                           out, vt, Rp);                                                                       \
+        break;
         QNF4_ROWS(1) QNF4_ROWS(2) QNF4_ROWS(3) QNF4_ROWS(4)
         QNF4_ROWS(5) QNF4_ROWS(6) QNF4_ROWS(7) QNF4_ROWS(8)
 #undef QNF4_ROWS
