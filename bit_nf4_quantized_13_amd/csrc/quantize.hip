@@ -18,6 +18,9 @@
 //      sums, then mean = fp32(sum / nb).
 //   3. dq_encode: one workgroup per group; a_g = max|s - mean|, c1 = 127/a_g,
 //      c2 = clamp(rint(c1 (s - mean)), +-127).
+// With at most 1024 groups (up to 16.7M weights) every dq_encode workgroup
+// runs the mean's tree itself (the same additions in the same order) and
+// launch 2 is skipped; workgroup 0 stores the mean.
 // The fixed tree order makes the mean, and so every output, bit-reproducible.
 #include "launch.hpp"
 
@@ -233,14 +236,56 @@ __global__ __launch_bounds__(kMeanThreads) void dq_mean(const double *__restrict
     if (t == 0) *mean = (float)(s[0] / (double)nb);
 }
 
+// dq_encode with the mean computed in every workgroup (a few group sums: the
+// same stride-halving tree as dq_mean, so the same bits), which saves the
+// one-workgroup launch.  padded <= 1024: thread t folds its entries t, t + 256,
+// ... (the levels h >= 256), then the levels h < 256 run across threads in LDS.
+constexpr int kMeanInline = 1024;
+
+__device__ __forceinline__ float tree_mean(const double *__restrict__ group_sum, int64_t groups, int64_t padded,
+                                           int64_t nb, double *s) {
+    const int t = threadIdx.x;
+    const int64_t T = padded < 256 ? padded : 256;
+    const int per = (int)(padded / T);
+    double v[kMeanInline / 256];
+#pragma unroll
+    for (int u = 0; u < kMeanInline / 256; ++u) {
+        const int64_t i = t + T * u;
+        v[u] = (t < T && u < per && i < groups) ? group_sum[i] : 0.0;
+    }
+#pragma unroll
+    for (int h = kMeanInline / 512; h >= 1; h >>= 1) {
+        if (2 * h <= per) {
+#pragma unroll
+            for (int u = 0; u < h; ++u) v[u] = v[u] + v[u + h];
+        }
+    }
+    s[t] = v[0];
+    __syncthreads();
+    for (int64_t h = T / 2; h >= 1; h >>= 1) {
+        if (t < h) s[t] = s[t] + s[t + h];
+        __syncthreads();
+    }
+    return (float)(s[0] / (double)nb);
+}
+
+template <bool INLINE_MEAN>
 __global__ __launch_bounds__(256) void dq_encode(const float *__restrict__ absmax, int64_t nb,
-                                                 const float *__restrict__ mean_p,
+                                                 float *__restrict__ mean_p, const double *__restrict__ group_sum,
+                                                 int64_t groups, int64_t padded,
                                                  int8_t *__restrict__ c2, float *__restrict__ c1) {
     __shared__ float s_red[4];
+    __shared__ double s_tree[256];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t j = (int64_t)blockIdx.x * kGroup + tid;
     const bool valid = j < nb;
-    const float mean = *mean_p;
+    float mean;
+    if constexpr (INLINE_MEAN) {
+        mean = tree_mean(group_sum, groups, padded, nb, s_tree);
+        if (blockIdx.x == 0 && tid == 0) *mean_p = mean;
+    } else {
+        mean = *mean_p;
+    }
     const float centred = valid ? absmax[j] - mean : 0.0f;
     float a = fabsf(centred);
 #pragma unroll
@@ -270,10 +315,14 @@ hipError_t launch_quantize(const float *W0, int64_t n, uint8_t *codes, int8_t *c
     if (padded > (int64_t)kMeanThreads * kMeanPerThread) return hipErrorInvalidValue;
     hipLaunchKernelGGL(nf4_quantize_groups, dim3((unsigned)groups), dim3(256), 0, s, W0, nb,
                        nf4_consts(), codes, absmax_ws, group_sum_ws);
-    hipLaunchKernelGGL(dq_mean, dim3(1), dim3(kMeanThreads), 0, s, group_sum_ws, groups, padded, nb,
-                       mean);
-    hipLaunchKernelGGL(dq_encode, dim3((unsigned)groups), dim3(256), 0, s, absmax_ws, nb, mean, c2,
-                       c1);
+    if (padded <= kMeanInline) {
+        hipLaunchKernelGGL(dq_encode<true>, dim3((unsigned)groups), dim3(256), 0, s, absmax_ws, nb, mean, group_sum_ws,
+                           groups, padded, c2, c1);
+    } else {
+        hipLaunchKernelGGL(dq_mean, dim3(1), dim3(kMeanThreads), 0, s, group_sum_ws, groups, padded, nb, mean);
+        hipLaunchKernelGGL(dq_encode<false>, dim3((unsigned)groups), dim3(256), 0, s, absmax_ws, nb, mean, group_sum_ws,
+                           groups, padded, c2, c1);
+    }
     return hipGetLastError();
 }
 
