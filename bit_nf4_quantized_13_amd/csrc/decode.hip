@@ -17,18 +17,29 @@
 //   through a 256-entry table in LDS, replicated once per lane so that every
 //   lane reads its own bank: one v_perm (address) and one ds_read_b32 per two
 //   weights.
-// * Codes are read with 8-byte loads, four lanes per row and 32 bytes (one
-//   block) per row per load; one ds_bpermute per code dword moves them into the
-//   MFMA operand layout.
-// * Work split: a workgroup (8 waves) takes T tiles of 16 rows and one of S
-//   k-slices; its waves split the slice P ways and the tiles 8/P ways.  X and A
-//   fragments of a wave's k-range stay in registers for all of its tiles.
-//   Partial sums are reduced across waves in LDS in a fixed order; with S > 1
-//   every workgroup stores its partial, and the last of the S workgroups of a
-//   tile group (a counter in the workspace) adds the S partials in slice order,
-//   the adapter term, and writes bf16 Y.  Results do not depend on arrival order.
-// * The LoRA down-projection U = X A^T (r <= 16) rides along: X is already in
-//   registers, so each k-range adds one MFMA pair per block on the A rows.
+// * Every global load is coalesced (consecutive lanes read consecutive
+//   bytes: the address path of a CU handles such loads about three times
+//   faster than loads in the MFMA operand layout, whose consecutive lanes sit
+//   on different rows).  Codes: four lanes per row read a row's 64 bytes of a
+//   pair of blocks; X and A: eight lanes per row read a block's 128 bytes.
+//   Each wave then passes the data through a small LDS stage of its own,
+//   padded so that the MFMA-layout reads are free of bank conflicts.
+// * Work split: a workgroup (8 waves) owns up to TW <= 4 consecutive 16-row
+//   tiles and one of S k-slices; the eight waves split the slice's blocks and
+//   each runs all of the workgroup's tiles over its blocks, so an X fragment
+//   is staged once per block per wave.  With enough tiles to occupy the chip
+//   S = 1: a workgroup owns whole rows and writes Y itself.  With few tiles
+//   S > 1: every workgroup stores its partial, and the last of the S
+//   workgroups of a tile group (a counter in the workspace) adds the S
+//   partials in slice order, the adapter term, and writes bf16 Y.  Cross-wave
+//   sums run in a fixed order, so results do not depend on arrival order.
+// * Streaming: a wave keeps the codes of its next blocks in a register ring
+//   (RPC pairs) and the X / A of the next RXB blocks, refilled as each block
+//   is consumed; the block loop is straight-line (blocks past the wave's
+//   range read zero X and add nothing), so the compiler overlaps one block's
+//   lookups and MFMAs with the next block's staging.
+// * The LoRA down-projection U = X A^T (r <= 16) rides along: X is already
+//   staged, so each block adds one MFMA pair on the A rows.
 //
 // MFMA v_mfma_f32_16x16x32_bf16, g = lane / 16: first operand lane (m, g)
 // holds X[m][8 k], second operand lane (n, g) holds What[n][the same 8 k],
@@ -41,8 +52,8 @@ namespace {
 
 constexpr int DEC_WAVES = 8;
 constexpr int DEC_THREADS = 64 * DEC_WAVES;
-constexpr int DEC_KB = 4;                    // 64-deep blocks per wave per chunk
-constexpr int DEC_MAX_TW = 8;                // tiles per wave
+constexpr int DEC_MAX_TW = 4;                // tiles per workgroup
+constexpr int DEC_MAX_S = 8;                 // k-slices
 constexpr int DEC_MAX_GROUPS = 4096;         // counters reserved in the workspace
 constexpr uint32_t DEC_TAG = 0x4E463444u;    // high word of an initialised counter
 constexpr uint32_t DEC_OOB = 0x80000000u;    // buffer offset past every range used here
@@ -79,10 +90,13 @@ struct DecodeArgs {
     float s;
     uint16_t *y;           // [M x d] bf16
     float *u_save;         // [M x r] fp32 or null (fused U only)
-    float *part;           // partials [grid][T + 1][64] f32x4: Y per tile, then U
-    unsigned long long *ctr;  // one per tile group
-    int S, T, P, nbw;      // k-slices, tiles per group, waves per tile subset, blocks per wave
-    int grid_;             // workgroups
+    float *part;           // S > 1: partials [G S][TW + 1][64] f32x4: Y per tile, then U
+    unsigned long long *ctr;  // S > 1: one counter per tile group
+    int S, G;              // k-slices, tile groups (G S workgroups)
+    // balanced splits, precomputed on the host (no wide division in the kernel):
+    // group g has tiles [g tb + min(g, tr), +tb + (g < tr)), slice s has blocks
+    // [s kbs + min(s, kr), +kbs + (s < kr))
+    int tb, tr, kbs, kr;
 };
 
 // Device-coherent 16-byte store / load (sc1: not cached non-coherently in the
@@ -111,29 +125,53 @@ __device__ __forceinline__ uint4 load_bfrag(__amdgpu_buffer_rsrc_t rb, int row, 
     return uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
 }
 
-template <int TW, int MV>  // TW tiles per wave; MV result registers that can hold m < M
+// TW tiles per workgroup; MV result registers that can hold m < M; XR row halves of X
+// loaded (1: M <= 8); FU: U = X A^T computed here
+template <int TW, int MV, int XR, bool FU>
 __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, Nf4Consts tab) {
+    constexpr int RPC = TW <= 2 ? 4 : 2;  // code pairs (two blocks each) in flight per wave
+    constexpr int RXB = 2;                // X / A blocks in flight per wave
+    constexpr int CP = 80;                // code stage row pitch: conflict-free 8-byte fragment reads
+    constexpr int XP = 144;               // X / A stage row pitch: conflict-free 16-byte fragment reads
+    constexpr int CSTAGE = 16 * CP;       // one tile's rows over a pair of blocks
+    constexpr int XSTAGE = 16 * XP;       // one block of X or of A
     __shared__ __attribute__((aligned(16))) uint32_t tbl[256 * 64];  // pair table, one copy per lane
-    __shared__ f32x4 red[DEC_WAVES][TW][64];
-    __shared__ f32x4 ured[DEC_WAVES][64];
-    __shared__ __attribute__((aligned(16))) float us[16][DEC_US_LD];  // U [m][j] for the adapter term
+    __shared__ __attribute__((aligned(16))) unsigned char cst[DEC_WAVES][TW][CSTAGE];
+    __shared__ __attribute__((aligned(16))) unsigned char xst[DEC_WAVES][2][XSTAGE];
     __shared__ int last_flag;
+    // after the block loop the stages hold the cross-wave sums and U
+    static_assert(sizeof(f32x4) * DEC_WAVES * TW * 64 <= sizeof(cst), "red alias");
+    static_assert(sizeof(f32x4) * DEC_WAVES * 64 + sizeof(float) * 16 * DEC_US_LD <= sizeof(xst), "U alias");
+    auto red = reinterpret_cast<f32x4 (*)[TW][64]>(&cst[0][0][0]);
+    auto ured = reinterpret_cast<f32x4 (*)[64]>(&xst[0][0][0]);
+    auto us = reinterpret_cast<float (*)[DEC_US_LD]>(&xst[0][0][0] + sizeof(f32x4) * DEC_WAVES * 64);
 
     // All offsets fit in 31 bits (d k <= 2^30, k <= 2^25): 32-bit index math.
     // Rows past d land past the end of their buffer and read zero.
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g = lane >> 4;
-    const int S = p.S, P = p.P, T = p.T, M = p.M, r = p.r;
+    // the scalar arguments used before the block loop, requested together (one
+    // wait for all of them instead of one per first use)
+    asm volatile("" ::"s"(p.S), "s"(p.G), "s"(p.M), "s"(p.r), "s"(p.d), "s"(p.k), "s"(p.tb), "s"(p.tr),
+                 "s"(p.kbs), "s"(p.kr), "s"(p.codes), "s"(p.c2), "s"(p.c1), "s"(p.mean), "s"(p.x), "s"(p.A));
+    asm volatile("" ::"s"(p.B), "s"(p.U), "s"(p.part), "s"(tab.level[1]), "s"(tab.level[2]), "s"(tab.level[3]),
+                 "s"(tab.level[4]), "s"(tab.level[5]), "s"(tab.level[6]), "s"(tab.level[7]), "s"(tab.level[8]),
+                 "s"(tab.level[9]), "s"(tab.level[10]), "s"(tab.level[11]), "s"(tab.level[12]), "s"(tab.level[13]));
+    asm volatile("" ::"s"(tab.level[14]), "s"(tab.level[15]), "s"(tab.level[0]));
+    const int S = p.S, G = p.G, M = p.M, r = p.r;
     const int wg = blockIdx.x, sl = wg % S, grp = wg / S;
-    const int kpart = wave % P, tsub = wave / P;
     const int d = (int)p.d, k = (int)p.k, kb = k / 64, hk = k / 2;
-    const int wblk0 = (sl * P + kpart) * p.nbw;                  // this wave's blocks [wblk0, wblk1)
-    const int wblk1 = wblk0 + p.nbw < kb ? wblk0 + p.nbw : kb;
-    const int row_g = grp * T * 16;                               // first row of the tile group
-    const int row_w = row_g + tsub * TW * 16;                     // first row of this wave's tiles
-    const bool fuse_u = p.U == nullptr;
-    const bool u_wave = fuse_u && tsub == 0;
+    // this group's tiles [t0, t0 + ntl), 1 <= ntl <= TW
+    const int t0 = grp * p.tb + (grp < p.tr ? grp : p.tr);
+    const int ntl = p.tb + (grp < p.tr ? 1 : 0);
+    const int row_g = 16 * t0;
+    // this wave's blocks [wb0, wb0 + nbw): the slice's blocks split eight ways (nbw may be 0)
+    const int sb0 = sl * p.kbs + (sl < p.kr ? sl : p.kr);
+    const int nsb = p.kbs + (sl < p.kr ? 1 : 0);
+    const int wb0 = sb0 + nsb * wave / DEC_WAVES;
+    const int nbw = nsb * (wave + 1) / DEC_WAVES - nsb * wave / DEC_WAVES;
+    constexpr bool fuse_u = FU;
 
     const __amdgpu_buffer_rsrc_t rcode = make_rsrc(p.codes, (int64_t)d * hk);
     const __amdgpu_buffer_rsrc_t rc2 = make_rsrc(p.c2, (int64_t)d * kb);
@@ -142,38 +180,119 @@ __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, N
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, fuse_u ? (int64_t)r * k * 2 : 0);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, (int64_t)d * r * 2);
     const __amdgpu_buffer_rsrc_t rmean = make_rsrc(p.mean, 4);
-    const int64_t part_f4 = p.S > 1 ? (int64_t)p.grid_ * (T + 1) * 64 : 0;  // f32x4 slots
+    const int64_t part_f4 = S > 1 ? (int64_t)G * S * (TW + 1) * 64 : 0;  // f32x4 slots
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.part, part_f4 * 16);
 
-    // thread (tile tt of the group, lane): tt = wave, wave + 8; B fragments for the adapter
-    constexpr int NTT = (2 * DEC_MAX_TW + DEC_WAVES - 1) / DEC_WAVES;
-    uint4 bfr[NTT];
-#pragma unroll
-    for (int h = 0; h < NTT; ++h) {
-        const int tt = wave + DEC_WAVES * h;
-        bfr[h] = load_bfrag(rb, row_g + 16 * tt + n16, 8 * g, r, tt < T);
-    }
-
-    // a given U [M x r] (r > 16): prefetched, parked in LDS with the table
+    // wave w < ntl finishes tile w: its B fragments for the adapter term
+    uint4 bfr = uint4{0, 0, 0, 0};
+    if (wave < ntl) bfr = load_bfrag(rb, row_g + 16 * wave + n16, 8 * g, r, true);
+    // a given U [M x r] (r > 16): prefetched, parked in LDS after the block loop
     constexpr int NUV = 16 * 128 / DEC_THREADS;
     float uvv[NUV];
-    const __amdgpu_buffer_rsrc_t ru = make_rsrc(p.U, fuse_u ? 0 : (int64_t)M * r * 4);
+    if (!fuse_u) {
+        const __amdgpu_buffer_rsrc_t ru = make_rsrc(p.U, (int64_t)M * r * 4);
 #pragma unroll
-    for (int u = 0; u < NUV; ++u) {
-        const int e = tid + DEC_THREADS * u;
-        uvv[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ru, e < M * r ? (uint32_t)e * 4 : DEC_OOB, 0, 0));
+        for (int u = 0; u < NUV; ++u) {
+            const int e = tid + DEC_THREADS * u;
+            uvv[u] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(ru, e < M * r ? (uint32_t)e * 4 : DEC_OOB, 0, 0));
+        }
     }
+    // the DQ mean through the vector memory path (a scalar load would make the
+    // wave wait for it before issuing anything else)
+    const float mean = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rmean, 0, 0, 0));
 
-    f32x4 acc[TW];
+    // ---- coalesced loads into register rings -----------------------------------
+    // Block b of the wave (0 <= b < nbw) is k-block wb0 + b.  Loads past the
+    // wave's blocks or the group's tiles go to an offset past every buffer
+    // (zero, no memory traffic), so every trip issues the same loads.
+    // codes, pair q = blocks 2q, 2q+1 of tile t: lane 4 n + c holds bytes
+    // 16 c .. 16 c + 15 of row n's 64 bytes (four lanes per row)
+    uint4 cr[RPC][TW];
+    const uint32_t code_lane = (uint32_t)((row_g + (lane >> 2)) * hk + 32 * wb0 + 16 * (lane & 3));
+    const uint32_t tile_bytes = 16u * (uint32_t)hk;
+    auto issue_codes = [&](int q, int j) __attribute__((always_inline)) {
+        const bool ok = 2 * q < nbw;
 #pragma unroll
-    for (int t = 0; t < TW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 uacc = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < TW; ++t) {
+            const uint32_t off = ok && t < ntl ? code_lane + (uint32_t)t * tile_bytes + 64u * (uint32_t)q : DEC_OOB;
+            cr[j][t] = load16(rcode, off);
+        }
+    };
+    // X and A block b: lane l holds row 8 i + l / 8, bytes 16 (l % 8) .. + 15 of the
+    // block's 128 (eight lanes per row); rows past M (X) or r (A) read zero.
+    // With M <= 8 only X rows 0..7 are loaded: stage rows 8..15 keep stale
+    // values, which reach only result rows m >= M (each MFMA result row depends
+    // on its own X row alone) and those are never stored.
+    uint4 xr[RXB][2], ar[RXB][2];
+    const uint32_t xa_lane = (uint32_t)(((lane >> 3) * k + 64 * wb0 + 8 * (lane & 7)) * 2);
+    auto issue_xa = [&](int b, int j) __attribute__((always_inline)) {
+        const bool ok = b < nbw;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t off = ok ? xa_lane + (uint32_t)(16 * i * k) + 128u * (uint32_t)b : DEC_OOB;
+            if (i < XR) xr[j][i] = load16(rx, off);
+            if (fuse_u) ar[j][i] = load16(ra, off);
+        }
+    };
+    // block constants of an octet (8 blocks from o): lane (n, g) takes row n of
+    // tile g (g < ntl): its 8 c2 bytes from three aligned dwords, and the c1 of
+    // the first and of the last block (8 blocks span at most two groups of 256).
+    // Single-dword loads: each one is range-checked on its own.
+    const int srow = row_g + 16 * g + n16;
+    const bool srow_ok = g < ntl && srow < d;
+    const uint32_t c2_lane = (uint32_t)(srow * kb + wb0);
+    uint32_t c2w[3];
+    float c1a, c1b;
+    auto issue_c2 = [&](int o) __attribute__((always_inline)) {
+        const bool ok = srow_ok && o < nbw;
+        const uint32_t o8 = c2_lane + (uint32_t)o, a0 = o8 & ~3u;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) c2w[i] = __builtin_amdgcn_raw_buffer_load_b32(rc2, ok ? a0 + 4u * i : DEC_OOB, 0, 0);
+        c1a = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc1, ok ? (o8 >> 8) * 4 : DEC_OOB, 0, 0));
+        c1b = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc1, ok ? ((o8 + 7) >> 8) * 4 : DEC_OOB, 0, 0));
+    };
+
+    // The first block's loads go out before the table is built (the barrier
+    // after it then waits only for a few issued loads per wave); the rest of
+    // the ring follows: codes (from HBM, the longest wait), then X / A.  The
+    // block loop refills one X / A block per block consumed.
+    issue_codes(0, 0);
+    issue_c2(0);
+    issue_xa(0, 0);
+    // pair table, while the first block's loads are under way: entry e = bf16(C[e & 15]) |
+    // bf16(C[e >> 4]) << 16 at dword 64 e + lane
+    {
+        // the levels pass through scalar registers: left to itself the compiler
+        // turns this select into an indexed load from the argument segment
+        float lvf = tab.level[0];
+#pragma unroll
+        for (int j = 1; j < 16; ++j) {
+            float cj;
+            asm("s_mov_b32 %0, %1" : "=s"(cj) : "s"(tab.level[j]));
+            lvf = n16 == j ? cj : lvf;
+        }
+        const int lv = __float_as_int(lvf);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int flat = tid + DEC_THREADS * i;
+            const int e = flat >> 4;
+            const float lo = __int_as_float(__builtin_amdgcn_ds_bpermute((e & 15) << 2, lv));
+            const float hi = __int_as_float(__builtin_amdgcn_ds_bpermute((e >> 4) << 2, lv));
+            const uint32_t v = pack_bf16x2(lo, hi);
+            reinterpret_cast<uint4 *>(tbl)[flat] = uint4{v, v, v, v};
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 1; j < RPC; ++j) issue_codes(j, j);
+#pragma unroll
+    for (int j = 1; j < RXB; ++j) issue_xa(j, j);
 
     const uint32_t lane4 = (uint32_t)lane * 4;
-    const int code_src = (4 * n16 + g) * 4;  // lane holding dwords 2 g, 2 g + 1 of row n16
     const char *tbl_b = reinterpret_cast<const char *>(tbl);
     // byte i of a code dword -> LDS byte address (byte << 8) | (lane << 2)
-    auto lut4 = [&](uint32_t cd) {
+    auto lut4 = [&](uint32_t cd) __attribute__((always_inline)) {
         uint4 o;
         o.x = *reinterpret_cast<const uint32_t *>(tbl_b + __builtin_amdgcn_perm(cd, lane4, 0x0C0C0400u));
         o.y = *reinterpret_cast<const uint32_t *>(tbl_b + __builtin_amdgcn_perm(cd, lane4, 0x0C0C0500u));
@@ -181,185 +300,113 @@ __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, N
         o.w = *reinterpret_cast<const uint32_t *>(tbl_b + __builtin_amdgcn_perm(cd, lane4, 0x0C0C0700u));
         return o;
     };
+    // stage addresses of this lane: ring writes (coalesced layout) and MFMA
+    // fragment reads.  Fragment k order inside a block: MFMA jj gives lane
+    // group g the k = 16 g + 8 jj .. + 7, i.e. code bytes 8 g + 4 jj .. + 3.
+    unsigned char *const cst_w = &cst[wave][0][0];
+    unsigned char *const xst_w = &xst[wave][0][0];
+    const int cst_wr = (lane >> 2) * CP + 16 * (lane & 3);
+    const int cst_rd = n16 * CP + 8 * g;             // + 32 h for block h of the pair
+    const int xst_wr = (lane >> 3) * XP + 16 * (lane & 7);  // + 8 XP i
+    const int xst_rd = n16 * XP + 32 * g;            // + 16 jj
 
-    constexpr int NI = TW * DEC_KB;          // (tile, block) items per chunk, tile-major
-    constexpr int NQ = (TW + 3) / 4;         // tiles whose block constants this lane loads
-    constexpr int D = NI;                    // code loads in flight per wave: all of the chunk's
-    const uint32_t tstride = 16u * (uint32_t)hk;  // bytes of codes per 16-row tile
-    const int nchunks = (p.nbw + DEC_KB - 1) / DEC_KB;
-    for (int ch = 0; ch < nchunks; ++ch) {
-        const int cb = wblk0 + ch * DEC_KB;
-        const int nval = wblk1 - cb;  // blocks of this chunk in range (uniform; may be <= 0)
-        // codes of item i: lane 4 n + q reads bytes 8 q .. 8 q + 7 of row n's block
-        const uint32_t code0 = (uint32_t)((row_w + (lane >> 2)) * hk + 32 * cb + 8 * (lane & 3));
-        auto load_code = [&](int i) {
-            const int t = i / DEC_KB, b = i % DEC_KB;
-            const uint32_t off = b < nval ? code0 + (uint32_t)t * tstride + 32u * b : DEC_OOB;
-            return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rcode, off, 0, 0));
-        };
-        // X (and A) fragments of the chunk's blocks
-        const uint32_t x0 = (uint32_t)((n16 * k + 64 * cb + 16 * g) * 2);
-        uint4 xf[DEC_KB][2], af[DEC_KB][2];
+    f32x4 acc[TW];
 #pragma unroll
-        for (int b = 0; b < DEC_KB; ++b) {
+    for (int t = 0; t < TW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 uacc = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int o = 0; o < nbw; o += 8) {
+        // block scales of the octet (zero for rows past d and tiles past ntl)
+        float sc[8];
+        {
+            const uint32_t sh = 8 * ((c2_lane + (uint32_t)o) & 3u);
+            const uint32_t lo = (uint32_t)(((uint64_t)c2w[1] << 32 | c2w[0]) >> sh);
+            const uint32_t hi = (uint32_t)(((uint64_t)c2w[2] << 32 | c2w[1]) >> sh);
+            const uint32_t ga = (c2_lane + (uint32_t)o) >> 8;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const uint32_t off = b < nval ? x0 + 128u * b + 16u * j : DEC_OOB;
-                xf[b][j] = load16(rx, off);
-                af[b][j] = u_wave ? load16(ra, off) : uint4{0, 0, 0, 0};
+            for (int e = 0; e < 8; ++e) {
+                const int8_t c2 = (int8_t)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xFFu);
+                // blocks past nbw and rows past d get scale 0 from a finite
+                // quotient (c1 = 1), so no NaN meets their zero products
+                const bool ok = srow_ok && o + e < nbw;
+                const float c1 = ok ? (((c2_lane + (uint32_t)(o + e)) >> 8) == ga ? c1a : c1b) : 1.0f;
+                sc[e] = dq_scale(c2, c1, mean) * (ok ? 1.0f : 0.0f);  // exact: x * 1 = x
             }
         }
-        // block constants: lane (n, g) loads tiles t = g + 4 u of row n: the chunk's
-        // four c2 bytes as one dword and their one c1 (four blocks at a multiple of
-        // four never straddle a 256-block group)
-        const bool c2vec = (kb % 4 == 0) && (cb % 4 == 0);  // uniform
-        uint32_t c2w[NQ];
-        float c1q[NQ][DEC_KB];
+        issue_c2(o + 8);
+        // Straight-line over the octet: blocks past nbw have zero X (their loads
+        // read past the buffer) and so add nothing; tiles past ntl are computed
+        // from zero codes and never stored.
 #pragma unroll
-        for (int u = 0; u < NQ; ++u) {
-            const int row = row_w + 16 * (g + 4 * u) + n16;
-            const uint32_t jb = (uint32_t)(row * kb + cb);
-            const bool tile_ok = g + 4 * u < TW && nval > 0;
-            if (c2vec) {
-                c2w[u] = __builtin_amdgcn_raw_buffer_load_b32(rc2, tile_ok ? jb : DEC_OOB, 0, 0);
-                const float c1 = __uint_as_float(
-                    __builtin_amdgcn_raw_buffer_load_b32(rc1, tile_ok ? (jb >> 8) * 4 : DEC_OOB, 0, 0));
+        for (int j = 0; j < 4; ++j) {  // pairs of the octet
+            const int q = o / 2 + j;
 #pragma unroll
-                for (int b = 0; b < DEC_KB; ++b) c1q[u][b] = c1;
-            } else {
-                uint32_t w = 0;
+            for (int t = 0; t < TW; ++t) *reinterpret_cast<uint4 *>(cst_w + t * CSTAGE + cst_wr) = cr[j % RPC][t];
+            issue_codes(q + RPC, j % RPC);
 #pragma unroll
-                for (int b = 0; b < DEC_KB; ++b) {
-                    const bool ok = tile_ok && b < nval;
-                    w |= __builtin_amdgcn_raw_buffer_load_b8(rc2, ok ? jb + b : DEC_OOB, 0, 0) << (8 * b);
-                    c1q[u][b] = __uint_as_float(
-                        __builtin_amdgcn_raw_buffer_load_b32(rc1, ok ? ((jb + b) >> 8) * 4 : DEC_OOB, 0, 0));
+            for (int h = 0; h < 2; ++h) {
+                const int b = o + 2 * j + h;
+                const int jx = (2 * j + h) % RXB;
+                *reinterpret_cast<uint4 *>(xst_w + xst_wr) = xr[jx][0];
+                if (XR == 2) *reinterpret_cast<uint4 *>(xst_w + xst_wr + 8 * XP) = xr[jx][1];
+                if (fuse_u) {
+                    *reinterpret_cast<uint4 *>(xst_w + XSTAGE + xst_wr) = ar[jx][0];
+                    *reinterpret_cast<uint4 *>(xst_w + XSTAGE + xst_wr + 8 * XP) = ar[jx][1];
                 }
-                c2w[u] = w;
-            }
-        }
-        // the DQ mean through the vector memory path (a scalar load would make the
-        // wave wait for it before issuing anything else)
-        const float mean = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rmean, 0, 0, 0));
-        uint2 cw[D];
+                issue_xa(b + RXB, jx);
+                const uint4 xf0 = *reinterpret_cast<const uint4 *>(xst_w + xst_rd);
+                const uint4 xf1 = *reinterpret_cast<const uint4 *>(xst_w + xst_rd + 16);
 #pragma unroll
-        for (int i = 0; i < D; ++i) cw[i] = load_code(i);
-        if (ch == 0) {
-            // pair table: entry e = bf16(C[e & 15]) | bf16(C[e >> 4]) << 16 at dword 64 e + lane
-            float lvf = tab.level[0];
+                for (int t = 0; t < TW; ++t) {
+                    const uint2 cd = *reinterpret_cast<const uint2 *>(cst_w + t * CSTAGE + cst_rd + 32 * h);
+                    const uint4 w0 = lut4(cd.x), w1 = lut4(cd.y);
+                    f32x4 z = mfma16(xf0, w0, f32x4{0.f, 0.f, 0.f, 0.f});
+                    z = mfma16(xf1, w1, z);
+                    // the scale of (tile t, row n): computed by lane (n, t)
+                    const float st =
+                        __int_as_float(__builtin_amdgcn_ds_bpermute((n16 + 16 * t) * 4, __float_as_int(sc[2 * j + h])));
 #pragma unroll
-            for (int j = 1; j < 16; ++j) lvf = n16 == j ? tab.level[j] : lvf;
-            const int lv = __float_as_int(lvf);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int flat = tid + DEC_THREADS * i;
-                const int e = flat >> 4;
-                const float lo = __int_as_float(__builtin_amdgcn_ds_bpermute((e & 15) << 2, lv));
-                const float hi = __int_as_float(__builtin_amdgcn_ds_bpermute((e >> 4) << 2, lv));
-                const uint32_t v = pack_bf16x2(lo, hi);
-                reinterpret_cast<uint4 *>(tbl)[flat] = uint4{v, v, v, v};
-            }
-            if (!fuse_u) {
-#pragma unroll
-                for (int u = 0; u < NUV; ++u) {
-                    const int e = tid + DEC_THREADS * u;
-                    if (e < M * r) us[e / r][e % r] = uvv[u];
+                    for (int v = 0; v < MV; ++v) acc[t][v] = __builtin_fmaf(st, z[v], acc[t][v]);
+                }
+                if (fuse_u) {
+                    const uint4 af0 = *reinterpret_cast<const uint4 *>(xst_w + XSTAGE + xst_rd);
+                    const uint4 af1 = *reinterpret_cast<const uint4 *>(xst_w + XSTAGE + xst_rd + 16);
+                    uacc = mfma16(xf0, af0, uacc);
+                    uacc = mfma16(xf1, af1, uacc);
                 }
             }
-            __syncthreads();
-        }
-        if (u_wave) {  // U partial while the codes are in flight
-#pragma unroll
-            for (int b = 0; b < DEC_KB; ++b) {
-                uacc = mfma16(xf[b][0], af[b][0], uacc);
-                uacc = mfma16(xf[b][1], af[b][1], uacc);
-            }
-        }
-        // scales of the loaded constants (zero for blocks out of range and rows past d)
-        float sq[NQ][DEC_KB];
-#pragma unroll
-        for (int u = 0; u < NQ; ++u) {
-            const bool row_ok = row_w + 16 * (g + 4 * u) + n16 < d;
-#pragma unroll
-            for (int b = 0; b < DEC_KB; ++b) {
-                const int8_t c2 = (int8_t)((c2w[u] >> (8 * b)) & 0xFFu);
-                sq[u][b] = row_ok && b < nval ? dq_scale(c2, c1q[u][b], mean) : 0.0f;
-            }
-        }
-
-        // four-stage software pipeline over the items, so that the LDS round
-        // trips of one item overlap the MFMAs of the previous ones:
-        //   A(i): code dwords into MFMA layout (ds_bpermute)
-        //   B(i): NF4 pair lookups (v_perm + ds_read_b32) and the item's scale
-        //   C(i): MFMA pair on the block
-        //   E(i): scaled accumulation into the tile's sum
-        uint32_t cd[2][2];
-        uint4 wv[2][2];
-        float scv[4];
-        f32x4 tmp[2];
-#pragma unroll
-        for (int it = 0; it < NI + 3; ++it) {
-            __builtin_amdgcn_sched_barrier(0);  // keep the stages of one step together
-            if (it >= 3) {  // E(it - 3)
-                const int i = it - 3, t = i / DEC_KB;
-#pragma unroll
-                for (int v = 0; v < MV; ++v) acc[t][v] = __builtin_fmaf(scv[i % 4], tmp[i % 2][v], acc[t][v]);
-            }
-            if (it >= 2 && it - 2 < NI) {  // C(it - 2)
-                const int i = it - 2, b = i % DEC_KB;
-                f32x4 z = mfma16(xf[b][0], wv[i % 2][0], f32x4{0.f, 0.f, 0.f, 0.f});
-                tmp[i % 2] = mfma16(xf[b][1], wv[i % 2][1], z);
-            }
-            if (it >= 1 && it - 1 < NI) {  // B(it - 1)
-                const int i = it - 1, t = i / DEC_KB, b = i % DEC_KB;
-                wv[i % 2][0] = lut4(cd[i % 2][0]);
-                wv[i % 2][1] = lut4(cd[i % 2][1]);
-                scv[i % 4] = __int_as_float(
-                    __builtin_amdgcn_ds_bpermute((n16 + 16 * (t % 4)) * 4, __float_as_int(sq[t / 4][b])));
-            }
-            if (it < NI) {  // A(it)
-                const int i = it;
-                const uint2 c = cw[i % D];
-                if (i + D < NI) cw[i % D] = load_code(i + D);
-                cd[i % 2][0] = (uint32_t)__builtin_amdgcn_ds_bpermute(code_src, (int)c.x);
-                cd[i % 2][1] = (uint32_t)__builtin_amdgcn_ds_bpermute(code_src, (int)c.y);
-            }
+            __builtin_amdgcn_sched_barrier(0);  // bounds the scheduling window (register pressure)
         }
     }
 
     // ---- cross-wave sums (fixed order) --------------------------------------
-    // the group counter: read here (after the last load the waves wait on), used
-    // after the partials are out; a fresh workspace gets it tagged
+    // the group counter: read here, used after the partials are out; a fresh
+    // workspace gets it tagged
     unsigned long long ctr0 = 0;
     if (S > 1 && tid == 0) ctr0 = __hip_atomic_load(p.ctr + grp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();  // every wave is done with its stages
 #pragma unroll
     for (int t = 0; t < TW; ++t) red[wave][t][lane] = acc[t];
-    if (u_wave) ured[kpart][lane] = uacc;
+    if (fuse_u) ured[wave][lane] = uacc;
     __syncthreads();
-    f32x4 ysum[NTT];
+    // wave w < TW: tile w, the eight waves' sums in wave order
+    f32x4 ysum = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (wave < TW) {
 #pragma unroll
-    for (int h = 0; h < NTT; ++h) {
-        const int tt = wave + DEC_WAVES * h;
-        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (tt < T) {
-            const int ts = tt / TW, t = tt % TW;
-            for (int q = 0; q < P; ++q) a += red[ts * P + q][t][lane];
-        }
-        ysum[h] = a;
+        for (int q = 0; q < DEC_WAVES; ++q) ysum += red[q][wave][lane];
     }
+    // with U fused, every wave that finishes a tile forms U itself
     f32x4 usum = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (fuse_u && wave == 0)
-        for (int q = 0; q < P; ++q) usum += ured[q][lane];
+    if (fuse_u && wave < ntl) {
+#pragma unroll
+        for (int q = 0; q < DEC_WAVES; ++q) usum += ured[q][lane];
+    }
 
     if (S > 1) {
-        // publish this slice's partials (slots [wg][tt][lane], then U at [wg][T][lane]);
+        // publish this slice's partials (slots [wg][t][lane], then U at [wg][TW][lane]);
         // the last workgroup of the group to arrive adds all S in slice order
-#pragma unroll
-        for (int h = 0; h < NTT; ++h) {
-            const int tt = wave + DEC_WAVES * h;
-            if (tt < T) store16_sc1(rp, (uint32_t)((((int64_t)wg * (T + 1) + tt) * 64 + lane) * 16), ysum[h]);
-        }
-        if (fuse_u && wave == 0) store16_sc1(rp, (uint32_t)((((int64_t)wg * (T + 1) + T) * 64 + lane) * 16), usum);
+        if (wave < ntl) store16_sc1(rp, (uint32_t)((((int64_t)wg * (TW + 1) + wave) * 64 + lane) * 16), ysum);
+        if (fuse_u && wave == 0) store16_sc1(rp, (uint32_t)((((int64_t)wg * (TW + 1) + TW) * 64 + lane) * 16), usum);
         __builtin_amdgcn_s_waitcnt(0);  // stores acknowledged before the count
         __syncthreads();
         if (tid == 0) {
@@ -377,61 +424,64 @@ __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, N
         }
         __syncthreads();
         if (!last_flag) return;
-        f32x4 pv[NTT][8];
+        f32x4 pv[DEC_MAX_S], uv[DEC_MAX_S];
 #pragma unroll
-        for (int h = 0; h < NTT; ++h) {
-            const int tt = wave + DEC_WAVES * h;
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                pv[h][q] = q < S && tt < T
-                               ? load16_sc1(rp, (uint32_t)((((int64_t)(grp * S + q) * (T + 1) + tt) * 64 + lane) * 16))
-                               : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < DEC_MAX_S; ++q) {
+            const int64_t slot = (int64_t)(grp * S + q) * (TW + 1);
+            pv[q] = q < S && wave < ntl ? load16_sc1(rp, (uint32_t)(((slot + wave) * 64 + lane) * 16))
+                                        : f32x4{0.f, 0.f, 0.f, 0.f};
+            uv[q] = q < S && fuse_u && wave < ntl ? load16_sc1(rp, (uint32_t)(((slot + TW) * 64 + lane) * 16))
+                                                  : f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        f32x4 uv[8];
+        f32x4 a = pv[0], u = uv[0];
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-            uv[q] = fuse_u && wave == 0 && q < S
-                        ? load16_sc1(rp, (uint32_t)((((int64_t)(grp * S + q) * (T + 1) + T) * 64 + lane) * 16))
-                        : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int h = 0; h < NTT; ++h) {
-            f32x4 a = pv[h][0];
-#pragma unroll
-            for (int q = 1; q < 8; ++q)
-                if (q < S) a += pv[h][q];
-            ysum[h] = a;
-        }
-        f32x4 a = uv[0];
-#pragma unroll
-        for (int q = 1; q < 8; ++q)
-            if (q < S) a += uv[q];
-        usum = a;
+        for (int q = 1; q < DEC_MAX_S; ++q)
+            if (q < S) {
+                a += pv[q];
+                u += uv[q];
+            }
+        ysum = a;
+        usum = u;
     }
 
     // ---- adapter term and bf16 store ------------------------------------------
-    if (fuse_u && wave == 0) {
+    // U [m][j] in LDS, read back in the first-operand layout: a given U (any
+    // r <= 128) in the shared array behind a barrier; a fused U (r <= 16) in
+    // this wave's own small array (same-wave LDS accesses stay in order)
+    constexpr int UWP = 20;  // row pitch of the per-wave U (r <= 16)
+    static_assert(sizeof(f32x4) * DEC_WAVES * 64 + sizeof(float) * 16 * UWP * DEC_MAX_TW <= sizeof(xst), "U alias");
+    float *const usw = reinterpret_cast<float *>(&xst[0][0][0] + sizeof(f32x4) * DEC_WAVES * 64) + wave * 16 * UWP;
+    if (!fuse_u) {
+#pragma unroll
+        for (int u = 0; u < NUV; ++u) {
+            const int e = tid + DEC_THREADS * u;
+            if (e < M * r) us[e / r][e % r] = uvv[u];
+        }
+        __syncthreads();
+    }
+    if (wave >= ntl) return;
+    if (fuse_u) {
         // lane (j, g) holds U[4 g + v][j]
 #pragma unroll
-        for (int v = 0; v < 4; ++v) us[4 * g + v][n16] = usum[v];
-        if (p.u_save && grp == 0 && n16 < r) {
+        for (int v = 0; v < 4; ++v) usw[(4 * g + v) * UWP + n16] = usum[v];
+        if (p.u_save && grp == 0 && wave == 0 && n16 < r) {
 #pragma unroll
             for (int v = 0; v < 4; ++v)
                 if (4 * g + v < M) p.u_save[(4 * g + v) * r + n16] = usum[v];
         }
     }
-    __syncthreads();
     // U B^T by MFMA over 32-wide slices of j: U split into bf16 hi + lo, lane
     // (m, g) holds U[m][32 it + 8 g .. + 7], lane (n, g) holds B[n][same j]
-    f32x4 ad[NTT];
-#pragma unroll
-    for (int h = 0; h < NTT; ++h) ad[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int row = row_g + 16 * wave + n16;
+    f32x4 ad = f32x4{0.f, 0.f, 0.f, 0.f};
     const int nj = (r + 31) / 32;
     for (int it = 0; it < nj; ++it) {
         const int j0 = 32 * it + 8 * g;
         uint4 uhi{0, 0, 0, 0}, ulo{0, 0, 0, 0};
         if (j0 < r) {
-            const f32x4 u0 = *reinterpret_cast<const f32x4 *>(&us[n16][j0]);
-            const f32x4 u1 = *reinterpret_cast<const f32x4 *>(&us[n16][j0 + 4]);
+            const float *const ur = fuse_u ? usw + n16 * UWP + j0 : &us[n16][j0];
+            const f32x4 u0 = *reinterpret_cast<const f32x4 *>(ur);
+            const f32x4 u1 = *reinterpret_cast<const f32x4 *>(ur + 4);
             float uu[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
 #pragma unroll
             for (int e = 0; e < 8; ++e) uu[e] = j0 + e < r ? uu[e] : 0.0f;
@@ -445,64 +495,62 @@ __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, N
             uhi = uint4{h2[0], h2[1], h2[2], h2[3]};
             ulo = uint4{l2[0], l2[1], l2[2], l2[3]};
         }
-#pragma unroll
-        for (int h = 0; h < NTT; ++h) {
-            const int tt = wave + DEC_WAVES * h;
-            if (tt >= T) continue;
-            const uint4 bf = it == 0 ? bfr[h] : load_bfrag(rb, row_g + 16 * tt + n16, j0, r, true);
-            ad[h] = mfma16(uhi, bf, ad[h]);
-            ad[h] = mfma16(ulo, bf, ad[h]);
-        }
+        const uint4 bf = it == 0 ? bfr : load_bfrag(rb, row, j0, r, true);
+        ad = mfma16(uhi, bf, ad);
+        ad = mfma16(ulo, bf, ad);
     }
     // all loads are done: the stores below never wait on each other
+    if (row >= d) return;
 #pragma unroll
-    for (int h = 0; h < NTT; ++h) {
-        const int tt = wave + DEC_WAVES * h;
-        const int row = row_g + 16 * tt + n16;
-        if (tt >= T || row >= d) continue;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int m = 4 * g + v;
-            if (m >= M) continue;
-            const float out = ysum[h][v] + p.s * ad[h][v];
-            p.y[(int64_t)m * d + row] = (uint16_t)(pack_bf16x2(out, 0.0f) & 0xFFFFu);
-        }
+    for (int v = 0; v < 4; ++v) {
+        const int m = 4 * g + v;
+        if (m >= M) continue;
+        const float out = ysum[v] + p.s * ad[v];
+        p.y[(int64_t)m * d + row] = (uint16_t)(pack_bf16x2(out, 0.0f) & 0xFFFFu);
     }
 }
 
 struct DecodePlan {
-    int S, T, TW, P, nbw, groups, grid;
+    int S, G, TW, grid;
 };
 
+// Enough 16-row tiles to occupy the chip (>= 128): one k-slice, up to 256
+// tile groups of up to four tiles (more groups only past 1024 tiles).
+// Fewer tiles: one tile per group and up to eight k-slices, each wave of a
+// slice keeping at least one block.
 DecodePlan decode_plan(int64_t d, int64_t k) {
-    const int64_t kb = k / 64, ntiles = (d + 15) / 16;
+    const int64_t kb = k / 64, nt = (d + 15) / 16;
     DecodePlan pl;
-    pl.P = 4;  // two tile subsets of four k-ranges each
-    const int ts = DEC_WAVES / pl.P;
-    int64_t S = (kb + pl.P * DEC_KB - 1) / (pl.P * DEC_KB);  // one chunk per wave
-    if (S > 8) S = 8;
-    pl.S = (int)S;
-    pl.nbw = (int)((kb + S * pl.P - 1) / (S * pl.P));
-    // about one workgroup per compute unit
-    const int64_t t_need = (ntiles * S + 255) / 256;
-    int64_t tw = (t_need + ts - 1) / ts;
-    tw = tw < 1 ? 1 : (tw > DEC_MAX_TW ? DEC_MAX_TW : tw);
-    pl.TW = (int)tw;
-    pl.T = ts * pl.TW;
-    pl.groups = (int)((ntiles + pl.T - 1) / pl.T);
-    if (pl.S > 1 && pl.groups > DEC_MAX_GROUPS) {  // too many counters: one slice
+    if (nt >= 128) {
+        int64_t tw = (nt + 255) / 256;
+        tw = tw > DEC_MAX_TW ? DEC_MAX_TW : tw;
+        pl.TW = (int)tw;
+        pl.G = (int)(nt > 256 * DEC_MAX_TW ? (nt + DEC_MAX_TW - 1) / DEC_MAX_TW : (nt < 256 ? nt : 256));
         pl.S = 1;
-        pl.nbw = (int)((kb + pl.P - 1) / pl.P);
+    } else {
+        int64_t S = 256 / nt;
+        const int64_t smax = kb / DEC_WAVES;
+        S = S > smax ? smax : S;
+        S = S > DEC_MAX_S ? DEC_MAX_S : (S < 1 ? 1 : S);
+        pl.TW = 1;
+        pl.G = (int)nt;
+        pl.S = (int)S;
     }
-    pl.grid = pl.groups * pl.S;
+    pl.grid = pl.G * pl.S;
     return pl;
 }
 
-template <int TW>
-hipError_t launch_tw(const DecodeArgs &a, int mv, int grid, hipStream_t st) {
-    if (mv == 1) hipLaunchKernelGGL((nf4_decode_kernel<TW, 1>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
-    else hipLaunchKernelGGL((nf4_decode_kernel<TW, 4>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
+template <int TW, bool FU>
+hipError_t launch_fu(const DecodeArgs &a, int grid, hipStream_t st) {
+    if (a.M == 1) hipLaunchKernelGGL((nf4_decode_kernel<TW, 1, 1, FU>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
+    else if (a.M <= 8) hipLaunchKernelGGL((nf4_decode_kernel<TW, 4, 1, FU>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
+    else hipLaunchKernelGGL((nf4_decode_kernel<TW, 4, 2, FU>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
     return hipGetLastError();
+}
+
+template <int TW>
+hipError_t launch_tw(const DecodeArgs &a, int grid, hipStream_t st) {
+    return a.U ? launch_fu<TW, false>(a, grid, st) : launch_fu<TW, true>(a, grid, st);
 }
 
 }  // namespace
@@ -513,7 +561,7 @@ size_t decode_part_bytes(int64_t M, int64_t d, int64_t k) {
     if (M < 1 || M > 16) return 0;
     const DecodePlan pl = decode_plan(d, k);
     if (pl.S == 1) return 0;
-    return sizeof(f32x4) * (size_t)pl.grid * 64 * ((size_t)pl.T + 1);
+    return sizeof(f32x4) * (size_t)pl.grid * 64 * ((size_t)pl.TW + 1);
 }
 
 hipError_t launch_decode_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, const uint16_t *A, const float *U,
@@ -521,7 +569,7 @@ hipError_t launch_decode_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, 
                              unsigned long long *ctr, hipStream_t st) {
     if (M < 1 || M > 16 || (!U && (!A || r > 16)) || w.k > (int64_t(1) << 25)) return hipErrorInvalidValue;
     const DecodePlan pl = decode_plan(w.d, w.k);
-    if (pl.S > 1 && (!part || !ctr)) return hipErrorInvalidValue;
+    if (pl.S > 1 && (!part || !ctr || pl.G > DEC_MAX_GROUPS)) return hipErrorInvalidValue;
     DecodeArgs a;
     a.codes = w.codes;
     a.c2 = w.c2;
@@ -539,22 +587,19 @@ hipError_t launch_decode_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, 
     a.y = Y;
     a.u_save = U ? nullptr : U_save;
     a.part = part;
-    a.grid_ = pl.grid;
     a.ctr = ctr;
     a.S = pl.S;
-    a.T = pl.T;
-    a.P = pl.P;
-    a.nbw = pl.nbw;
-    const int mv = M == 1 ? 1 : 4;
+    a.G = pl.G;
+    const int64_t nt = (w.d + 15) / 16, kb = w.k / 64;
+    a.tb = (int)(nt / pl.G);
+    a.tr = (int)(nt % pl.G);
+    a.kbs = (int)(kb / pl.S);
+    a.kr = (int)(kb % pl.S);
     switch (pl.TW) {
-        case 1: return launch_tw<1>(a, mv, pl.grid, st);
-        case 2: return launch_tw<2>(a, mv, pl.grid, st);
-        case 3: return launch_tw<3>(a, mv, pl.grid, st);
-        case 4: return launch_tw<4>(a, mv, pl.grid, st);
-        case 5: return launch_tw<5>(a, mv, pl.grid, st);
-        case 6: return launch_tw<6>(a, mv, pl.grid, st);
-        case 7: return launch_tw<7>(a, mv, pl.grid, st);
-        default: return launch_tw<8>(a, mv, pl.grid, st);
+        case 1: return launch_tw<1>(a, pl.grid, st);
+        case 2: return launch_tw<2>(a, pl.grid, st);
+        case 3: return launch_tw<3>(a, pl.grid, st);
+        default: return launch_tw<4>(a, pl.grid, st);
     }
 }
 

@@ -55,7 +55,8 @@ def test_single_layer_workload():
 @pytest.mark.parametrize("m,d,k,r", [(1, 256, 512, 8), (300, 320, 192, 8), (257, 512, 320, 1),
                                      (64, 264, 128, 7), (130, 256, 256, 33), (33, 512, 1024, 64),
                                      (20, 128, 256, 128), (16, 200, 448, 33), (3, 136, 1088, 16),
-                                     (5, 4104, 4096, 16), (16, 64, 64, 1)])
+                                     (5, 4104, 4096, 16), (16, 64, 64, 1), (16, 1000, 2048, 16),
+                                     (2, 4104, 256, 16)])
 def test_shapes_ranks_and_ragged_tiles(m, d, k, r):
     inp = make_layer(21, m * 7 + r, d, k, m, r)
     check_layer(inp, 16.0, f"shape m={m} d={d} k={k} r={r}", bf16_rounding_allowance=True)
@@ -75,15 +76,21 @@ def test_decode_shapes_forward(proj, m):
 
 
 def test_decode_workspace_reuse_and_garbage():
-    """The one-kernel decode path keeps per-group counters in the workspace:
-    a workspace full of garbage, reused across calls and shapes, must give the
+    """The one-kernel decode path keeps per-group counters in the workspace
+    when it splits k over workgroups (few row tiles, here d = 512): a
+    workspace full of garbage, reused across calls and shapes, must give the
     same bits as a fresh zeroed one every time."""
+    for d in (512, 4096):
+        check_decode_workspace(d)
+
+
+def check_decode_workspace(d):
     import bit_nf4_quantized_13_amd as q
-    say("decode workspace garbage / reuse")
-    inp = make_layer(43, 0, 4096, 4096, 64, 16)
+    say(f"decode workspace garbage / reuse, d={d}")
+    inp = make_layer(43, 0, d, 4096, 64, 16)
     w = q.qlora_nf4_quantize(to_dev_f32(inp.w0))
     xd, ad, bd = (to_dev_bf16(t) for t in (inp.x, inp.a, inp.b))
-    nbytes = max(q.linear_workspace_bytes(m, 4096, 4096, 16) for m in (1, 4, 16, 64))
+    nbytes = max(q.linear_workspace_bytes(m, d, 4096, 16) for m in (1, 4, 16, 64))
     clean = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     dirty = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
     for m in (16, 1, 4, 16):
