@@ -236,6 +236,33 @@ def time_gemm_only(q, torch, ctx, iters):
     return e0.elapsed_time(e1) / iters
 
 
+def run_merge_bench(q, torch, ctx, iters=20):
+    """qlora_adapter_merge on the layer4096 weight (4096 x 4096, r = 8): the
+    merged bf16 weight What + (alpha/r) B A, r fp64 FMAs per weight.  Reported
+    with its algorithmic HBM bytes (codes, c2, c1, A, B read; bf16 written) and
+    fp64 flops."""
+    w, x, a, b, alpha, y, u, lws, r = ctx
+    d, k = w.d, w.k
+    out = torch.empty((d, k), dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        q.qlora_adapter_merge(w, a, b, alpha, out=out)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        q.qlora_adapter_merge(w, a, b, alpha, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    nb = d * k // 64
+    nbytes = d * k // 2 + nb + 4 * ((nb + 255) // 256) + 4 + 2 * r * k + 2 * d * r + 2 * d * k
+    return {"us_per_call": round(ms * 1e3, 3), "algorithmic_bytes": nbytes,
+            "algorithmic_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "fp64_tflops": round(2 * r * d * k / (ms * 1e-3) / 1e12, 2),
+            "workload": f"layer4096 weight {d}x{k}, r={r}"}
+
+
 def decode_bytes(m, d, k, r):
     """Algorithmic HBM bytes of one decode forward: packed codes, 8-bit block
     constants, fp32 group constants and mean, x, A, B, Y."""
@@ -361,6 +388,8 @@ def main():
                 "kernel": "nf4_gemm_kernel<fwd> (layer4096 forward)",
                 "kernel_us": round(gemm_ms * 1e3, 2),
                 "work_per_launch": f"2*M*d*k + 2*M*d*r = {gemm_flops(m, d, k, r)} flop"}
+    log("layer4096: timing the adapter merge")
+    merge = run_merge_bench(q, torch, ctx)
     decode = None if args.skip_decode else run_decode_bench(q, torch)
     cpu = None
     if not args.skip_cpu_baseline:
@@ -380,6 +409,7 @@ def main():
         "roofline": roofline,
         "decode_fwd": decode,
         "decode_roofline": None if decode is None else decode_roofline(decode),
+        "adapter_merge": merge,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -62,6 +62,8 @@ _SIGS = {
     "qlora_linear_bwd": (ctypes.c_int, [_WP, _P, _P, _P, _P, _P, _I64, _I32, ctypes.c_float, _P,
                                         _P, _P, _P, _SZ, _P]),
     "qlora_linear_gemm_only": (ctypes.c_int, [_WP, _I32, _P, _I64, _I32, _P, _P, _SZ, _P]),
+    "qlora_adapter_merge": (ctypes.c_int, [_WP, _P, _P, _I32, ctypes.c_float, _P, _P]),
+    "qlora_adapter_unmerge": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, ctypes.c_float, _P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     if not hasattr(_lib, _name):
@@ -257,6 +259,33 @@ def qlora_linear_gemm_only(w: NF4Weight, backward: bool, a: torch.Tensor, r: int
     return out
 
 
+def qlora_adapter_merge(w: NF4Weight, a: torch.Tensor, b: torch.Tensor, alpha: float,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 [d, k] = What + (alpha/r) B A (qlora_adapter_merge's fixed rounding)."""
+    _dev_tensor(a, torch.bfloat16, "A")
+    _dev_tensor(b, torch.bfloat16, "B")
+    y = out if out is not None else torch.empty((w.d, w.k), dtype=torch.bfloat16, device=a.device)
+    _dev_tensor(y, torch.bfloat16, "out")
+    cw = w.c_struct()
+    _check(_lib.qlora_adapter_merge(ctypes.byref(cw), a.data_ptr(), b.data_ptr(), a.shape[0], float(alpha),
+                                    y.data_ptr(), _stream()), "qlora_adapter_merge")
+    return y
+
+
+def qlora_adapter_unmerge(w_in: torch.Tensor, a: torch.Tensor, b: torch.Tensor, alpha: float,
+                          out: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 [d, k] = W_in - (alpha/r) B A; out may be w_in (in place)."""
+    _dev_tensor(w_in, torch.bfloat16, "W_in")
+    _dev_tensor(a, torch.bfloat16, "A")
+    _dev_tensor(b, torch.bfloat16, "B")
+    d, k = w_in.shape
+    y = out if out is not None else torch.empty_like(w_in)
+    _dev_tensor(y, torch.bfloat16, "out")
+    _check(_lib.qlora_adapter_unmerge(w_in.data_ptr(), d, k, a.data_ptr(), b.data_ptr(), a.shape[0],
+                                      float(alpha), y.data_ptr(), _stream()), "qlora_adapter_unmerge")
+    return y
+
+
 def adapter_scale(alpha: float, r: int) -> float:
     """alpha / r as the library computes it (fp32)."""
     import numpy as np
@@ -265,7 +294,8 @@ def adapter_scale(alpha: float, r: int) -> float:
 
 __all__ = [
     "NF4Weight", "QloraError", "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd",
-    "qlora_linear_bwd", "qlora_linear_gemm_only", "qlora_nf4_codebook", "qlora_nf4_thresholds", "status_str", "library",
+    "qlora_linear_bwd", "qlora_linear_gemm_only", "qlora_adapter_merge", "qlora_adapter_unmerge",
+    "qlora_nf4_codebook", "qlora_nf4_thresholds", "status_str", "library",
     "abi_version", "quantize_workspace_bytes", "linear_workspace_bytes", "adapter_scale",
     "BLOCK", "DQ_BLOCK",
 ]

@@ -256,6 +256,32 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const qlora_bf16 *x, const qlora
     return hip_status(e);
 }
 
+int qlora_adapter_merge(const qlora_nf4_weight *w, const qlora_bf16 *A, const qlora_bf16 *B, int32_t r,
+                        float alpha, qlora_bf16 *W_out, void *stream) {
+    int st = check_weight(w, true);
+    if (st != QLORA_OK) return st;
+    if (!A || !B || !W_out || r <= 0 || !std::isfinite(alpha)) return QLORA_EINVAL;
+    if (r > QLORA_MAX_RANK) return QLORA_ENOTSUP;
+    if (!aligned(A, 16) || !aligned(B, 2) || !aligned(W_out, 16)) return QLORA_EALIGN;
+    (void)hipGetLastError();
+    const Nf4Weights nw{w->codes, w->absmax_q, w->absmax_scale, w->absmax_mean, w->d, w->k};
+    const float scale = alpha / static_cast<float>(r);
+    return hip_status(launch_adapter_merge(&nw, nullptr, w->d, w->k, A, B, r, (double)scale, W_out,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int qlora_adapter_unmerge(const qlora_bf16 *W_in, int64_t d, int64_t k, const qlora_bf16 *A, const qlora_bf16 *B,
+                          int32_t r, float alpha, qlora_bf16 *W_out, void *stream) {
+    if (!W_in || !A || !B || !W_out || d <= 0 || k <= 0 || r <= 0 || !std::isfinite(alpha)) return QLORA_EINVAL;
+    if (k % 8 != 0) return QLORA_EINVAL;
+    if (r > QLORA_MAX_RANK || d > kMaxWeights / k) return QLORA_ENOTSUP;
+    if (!aligned(W_in, 16) || !aligned(A, 16) || !aligned(B, 2) || !aligned(W_out, 16)) return QLORA_EALIGN;
+    (void)hipGetLastError();
+    const float scale = alpha / static_cast<float>(r);
+    return hip_status(launch_adapter_merge(nullptr, W_in, d, k, A, B, r, -(double)scale, W_out,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int qlora_linear_gemm_only(const qlora_nf4_weight *w, int32_t backward, const qlora_bf16 *a, int64_t M,
                            int32_t r, qlora_bf16 *out, void *ws, size_t ws_bytes, void *stream) {
     int st = check_weight(w, true);

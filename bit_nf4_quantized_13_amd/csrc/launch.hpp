@@ -86,6 +86,13 @@ hipError_t launch_gemm_dx(const Nf4Weights &w, const uint16_t *dy, int64_t M, co
 hipError_t launch_gemm_core(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, int r, uint16_t *out,
                             const GemmWs &ws, hipStream_t st);
 
+// Adapter merge / unmerge: w_out[d x k] = bf16(fp32(base + s * (B A))) with the
+// sum over ranks in fp64, j ascending; base = doubleDequant(w) when w is not
+// null (merge), else w_in (unmerge, s negated by the caller; w_in may be w_out).
+// k % 8 == 0; no workspace.
+hipError_t launch_adapter_merge(const Nf4Weights *w, const uint16_t *w_in, int64_t d, int64_t k, const uint16_t *A,
+                                const uint16_t *B, int r, double s, uint16_t *w_out, hipStream_t st);
+
 // Decode-shaped forward, M <= 16: Y = X What^T + s U B^T.  U [M x r] fp32 is
 // either given (U != null) or computed in the same kernel from A [r x k]
 // (U == null, r <= 16; written to U_save when that is not null).  part holds

@@ -181,6 +181,41 @@ int qlora_linear_gemm_only(const qlora_nf4_weight *w, int32_t backward, const ql
                            int32_t r, qlora_bf16 *out, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * qlora_adapter_merge -- fold the adapter into a dense bf16 weight.
+ * chkda, "Merging LoRA weights for inference": W_merged = W0 + (alpha/r) B A,
+ * with W0 the double-dequantized What of the NF4 weight ("Double quantization
+ * and double dequantization").  The arithmetic is fixed so that the result is
+ * reproducible bit for bit:
+ *   S[n][k]      = sum over j = 0 .. r-1, ascending, of B[n][j] * A[j][k], in
+ *                  fp64 (each product of two bf16 values is exact in fp64)
+ *   W_out[n][k]  = BF16( fp32( What[n][k] + s * S[n][k] ) ),  s = fp32(alpha / r)
+ * where s * S and the sum are separate fp64 roundings and both narrowings
+ * round to nearest even.  To requantize the merged weight, widen W_out to fp32
+ * and call qlora_nf4_quantize.
+ *   w      the NF4 weight (as for qlora_nf4_dequantize).
+ *   A      device bf16 [r x k], 16-byte aligned;  B  device bf16 [d x r].
+ *   W_out  device bf16 [d x k], 16-byte aligned, written.  No workspace.
+ * Errors: QLORA_EINVAL (null pointer, r <= 0, non-finite alpha), QLORA_ENOTSUP
+ * (r > 128, weight format), QLORA_EALIGN.
+ */
+int qlora_adapter_merge(const qlora_nf4_weight *w, const qlora_bf16 *A, const qlora_bf16 *B, int32_t r,
+                        float alpha, qlora_bf16 *W_out, void *stream);
+
+/*
+ * qlora_adapter_unmerge -- take an adapter back out of a merged bf16 weight
+ * (chkda, "Merging LoRA weights for inference": keeping base and adapters apart
+ * lets one switch adapters):
+ *   W_out[n][k] = BF16( fp32( W_in[n][k] - s * S[n][k] ) )
+ * with S and s as in qlora_adapter_merge.  unmerge(merge(What)) recovers What
+ * up to the two bf16 roundings: half an ulp of the merged value plus half an
+ * ulp of the result, per element.
+ *   W_in   device bf16 [d x k], 16-byte aligned; may equal W_out (in place).
+ *   k % 8 == 0.  Errors as for qlora_adapter_merge.
+ */
+int qlora_adapter_unmerge(const qlora_bf16 *W_in, int64_t d, int64_t k, const qlora_bf16 *A, const qlora_bf16 *B,
+                          int32_t r, float alpha, qlora_bf16 *W_out, void *stream);
+
+/*
  * qlora_nf4_codebook -- host-only: copies the library's 16 fp32 NF4 levels
  * (chkda, "NF4: Choose the codebook to fit the distribution"; built as in
  * "Building the NF4 codebook" from standard-normal quantiles) into out[16].

@@ -27,6 +27,11 @@ upstream gradient dY [M x d] of a loss L(Y):
 
 There is no dW.  These are the closed-form derivatives of Y above; the tests
 pin them with central finite differences.
+
+Merge (chkda "Merging LoRA weights for inference"): W_merged = W0 + s B A,
+in fp64 (merged_weight) and as bf16 under the library's fixed rounding
+(merged_weight_bf16, reading R14: the sum over ranks in fp64 in ascending
+order, two fp64 roundings, then fp32 and bf16 to nearest even).
 """
 from __future__ import annotations
 
@@ -80,6 +85,30 @@ def merged_weight(w_hat, a, b, alpha: float) -> np.ndarray:
     """W_merged = W0 + (alpha/r) B A (chkda "Merging LoRA weights for inference")."""
     a, b = _f64(a), _f64(b)
     return _f64(w_hat) + adapter_scale(alpha, a.shape[0]) * (b @ a)
+
+
+def merged_weight_bf16(base_bits, a, b, alpha: float, sign: float = 1.0) -> np.ndarray:
+    """bf16 bits of base + sign (alpha/r) B A with the merge's fixed rounding
+    (chkda "Merging LoRA weights for inference" gives W0 + (alpha/r) B A and
+    leaves the arithmetic open; reading R14):
+
+        S = sum over j = 0 .. r-1, ascending, of B[:, j] A[j, :]   (fp64; each
+            product of two bf16 values is exact, so each step is one rounding)
+        t = s S,  m = base + t                                       (fp64, two roundings)
+        out = bf16(fp32(m))                                          (nearest even, twice)
+
+    with s = fp32(alpha / r) as the library computes it.  base_bits: uint16 bf16
+    patterns [d x k] -- What for a merge (sign = +1), the merged weight for an
+    unmerge (sign = -1)."""
+    from .nf4 import bf16_bits_to_f32, bf16_rne_bits
+    a, b = _f64(a), _f64(b)
+    r = a.shape[0]
+    s = np.float64(np.float32(np.float32(alpha) / np.float32(r))) * np.float64(sign)
+    acc = np.zeros((b.shape[0], a.shape[1]), dtype=np.float64)
+    for j in range(r):
+        acc += np.outer(b[:, j], a[j, :])
+    m = bf16_bits_to_f32(base_bits).astype(np.float64) + s * acc
+    return bf16_rne_bits(m.astype(np.float32))
 
 
 def trainable_parameters(d: int, k: int, r: int) -> int:

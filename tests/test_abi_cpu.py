@@ -183,3 +183,34 @@ def test_gemm_only_backward_accepts_small_m_shapes():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present: this check is for hosts without one")
     assert gemm_only(backward=1, m=16) == q.QLORA_EHIP
+
+
+def merge(w=None, a=FAKE, b=FAKE, r=8, alpha=16.0, out=FAKE):
+    w = w or weight()
+    return q.library().qlora_adapter_merge(ctypes.byref(w), a, b, r, alpha, out, None)
+
+
+def unmerge(w_in=FAKE, d=256, k=512, a=FAKE, b=FAKE, r=8, alpha=16.0, out=FAKE):
+    return q.library().qlora_adapter_unmerge(w_in, d, k, a, b, r, alpha, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(a=None), q.QLORA_EINVAL), (dict(b=None), q.QLORA_EINVAL), (dict(out=None), q.QLORA_EINVAL),
+    (dict(r=0), q.QLORA_EINVAL), (dict(r=129), q.QLORA_ENOTSUP), (dict(alpha=float("nan")), q.QLORA_EINVAL),
+    (dict(a=FAKE + 8), q.QLORA_EALIGN), (dict(b=FAKE + 1), q.QLORA_EALIGN), (dict(out=FAKE_MIS), q.QLORA_EALIGN),
+    (dict(w=weight(codes=None)), q.QLORA_EINVAL), (dict(w=weight(block=32)), q.QLORA_ENOTSUP),
+    (dict(w=weight(k=100)), q.QLORA_EINVAL),
+])
+def test_merge_rejects_invalid_arguments(kw, status):
+    assert merge(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w_in=None), q.QLORA_EINVAL), (dict(a=None), q.QLORA_EINVAL), (dict(out=None), q.QLORA_EINVAL),
+    (dict(d=0), q.QLORA_EINVAL), (dict(k=-8), q.QLORA_EINVAL), (dict(k=100), q.QLORA_EINVAL),
+    (dict(r=0), q.QLORA_EINVAL), (dict(r=200), q.QLORA_ENOTSUP), (dict(alpha=float("inf")), q.QLORA_EINVAL),
+    (dict(d=1 << 20, k=1 << 12), q.QLORA_ENOTSUP),
+    (dict(w_in=FAKE_MIS), q.QLORA_EALIGN), (dict(a=FAKE + 4), q.QLORA_EALIGN), (dict(out=FAKE + 8), q.QLORA_EALIGN),
+])
+def test_unmerge_rejects_invalid_arguments(kw, status):
+    assert unmerge(**kw) == status

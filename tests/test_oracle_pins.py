@@ -380,3 +380,60 @@ def test_adapter_grads_central_finite_differences():
             args_m = (mm, b) if which == 0 else (a, mm)
             num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
         assert np.allclose(grad, num, rtol=1e-6, atol=1e-7)
+
+
+def _bf16_vals(rng, shape, scale):
+    return nf4.bf16_bits_to_f32(nf4.bf16_rne_bits((rng.standard_normal(shape) * scale).astype(np.float32)))
+
+
+def test_merged_bf16_rank_one_by_brute_force():
+    """r = 1: every element by hand in Python floats (IEEE binary64), then the
+    two narrowings; the oracle's vectorised accumulation must agree bit for bit."""
+    rng = np.random.default_rng(11)
+    d, k, alpha = 5, 7, 3.0
+    base = nf4.bf16_rne_bits((rng.standard_normal((d, k)) * 0.02).astype(np.float32))
+    a, b = _bf16_vals(rng, (1, k), 1.0), _bf16_vals(rng, (d, 1), 0.01)
+    got = qlora.merged_weight_bf16(base, a, b, alpha)
+    s = float(np.float32(np.float32(alpha) / np.float32(1)))
+    basef = nf4.bf16_bits_to_f32(base)
+    for n in range(d):
+        for c in range(k):
+            prod = float(b[n, 0]) * float(a[0, c])          # exact
+            m = float(basef[n, c]) + s * prod
+            want = nf4.bf16_rne_bits(np.array([m], dtype=np.float32))[0]
+            assert got[n, c] == want
+
+
+def test_merged_bf16_is_the_rounded_exact_merge():
+    """Against the plain fp64 merge (BLAS product): within half a bf16 ulp, and
+    equal to that merge's own rounding wherever it is not within 2^-40 of a
+    rounding boundary."""
+    rng = np.random.default_rng(12)
+    d, k, r, alpha = 48, 64, 16, 32.0
+    base = nf4.bf16_rne_bits((rng.standard_normal((d, k)) * 0.02).astype(np.float32))
+    a, b = _bf16_vals(rng, (r, k), 1.0 / np.sqrt(r)), _bf16_vals(rng, (d, r), 0.01)
+    got = nf4.bf16_bits_to_f32(qlora.merged_weight_bf16(base, a, b, alpha)).astype(np.float64)
+    ref = qlora.merged_weight(nf4.bf16_bits_to_f32(base), a, b, alpha)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
+    direct = nf4.bf16_bits_to_f32(nf4.bf16_rne_bits(ref.astype(np.float32))).astype(np.float64)
+    assert np.mean(got == direct) > 0.999
+
+
+def test_merge_of_a_zero_adapter_and_exact_unmerge():
+    rng = np.random.default_rng(13)
+    d, k, r = 8, 16, 4
+    base = nf4.bf16_rne_bits((rng.standard_normal((d, k)) * 0.02).astype(np.float32))
+    a = _bf16_vals(rng, (r, k), 1.0)
+    # B = 0: the merge returns the base (signed zeros become +0: -0 + +0 = +0)
+    m0 = qlora.merged_weight_bf16(base, a, np.zeros((d, r)), 16.0)
+    canon = np.where(base == 0x8000, np.uint16(0), base)
+    assert np.array_equal(m0, canon)
+    # an adapter whose products and sums are exact in bf16 (powers of two on a
+    # coarse grid): merge then unmerge gives the base back bit for bit
+    base2 = nf4.bf16_rne_bits(np.round(rng.standard_normal((d, k)) * 8).astype(np.float32) / 8)
+    a2 = np.where(rng.random((r, k)) < 0.5, 0.5, -0.25)
+    b2 = np.where(rng.random((d, r)) < 0.5, 1.0, 0.0)
+    m = qlora.merged_weight_bf16(base2, a2, b2, float(r))  # s = 1
+    back = qlora.merged_weight_bf16(m, a2, b2, float(r), sign=-1.0)
+    assert np.array_equal(np.where(back == 0x8000, np.uint16(0), back),
+                          np.where(base2 == 0x8000, np.uint16(0), base2))
