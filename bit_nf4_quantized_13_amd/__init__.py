@@ -26,6 +26,7 @@ from .build import LIB_PATH
 QLORA_OK, QLORA_EINVAL, QLORA_ENOTSUP, QLORA_EALIGN, QLORA_EWORKSPACE, QLORA_EHIP = range(6)
 BLOCK = 64
 DQ_BLOCK = 256
+NO_DQ = 0  # dq_block of the format without double quantization (fp32 absmax per block)
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -130,41 +131,55 @@ def _dev_tensor(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
 
 @dataclass
 class NF4Weight:
-    """Device buffers of one quantized W0 [d x k] (see qlora_nf4_weight)."""
-    codes: torch.Tensor          # uint8 [d*k/2]
-    absmax_q: torch.Tensor       # int8 [nb]
-    absmax_scale: torch.Tensor   # float32 [G]
-    absmax_mean: torch.Tensor    # float32 [1]
+    """Device buffers of one quantized W0 [d x k] (see qlora_nf4_weight).
+
+    Double-quantized (dq_block == DQ_BLOCK): absmax_q holds c2, absmax_scale
+    c1 per group of 256 blocks and absmax_mean the mean.  Without double
+    quantization (dq_block == NO_DQ): absmax_scale holds the fp32 absmax of
+    every block and absmax_q / absmax_mean are None.
+    """
+    codes: torch.Tensor                  # uint8 [d*k/2]
+    absmax_q: torch.Tensor | None        # int8 [nb] (double-quantized only)
+    absmax_scale: torch.Tensor           # float32 [G] (double-quantized) or [nb]
+    absmax_mean: torch.Tensor | None     # float32 [1] (double-quantized only)
     d: int
     k: int
     block: int = BLOCK
     dq_block: int = DQ_BLOCK
 
     @staticmethod
-    def empty(d: int, k: int, device="cuda") -> "NF4Weight":
+    def empty(d: int, k: int, device="cuda", double_quant: bool = True) -> "NF4Weight":
         nb = (d * k) // BLOCK
+        codes = torch.empty(d * k // 2, dtype=torch.uint8, device=device)
+        if not double_quant:
+            return NF4Weight(codes, None, torch.empty(nb, dtype=torch.float32, device=device), None,
+                             d, k, dq_block=NO_DQ)
         g = -(-nb // DQ_BLOCK)
-        return NF4Weight(torch.empty(d * k // 2, dtype=torch.uint8, device=device),
-                         torch.empty(nb, dtype=torch.int8, device=device),
+        return NF4Weight(codes, torch.empty(nb, dtype=torch.int8, device=device),
                          torch.empty(g, dtype=torch.float32, device=device),
                          torch.empty(1, dtype=torch.float32, device=device), d, k)
 
+    @property
+    def double_quant(self) -> bool:
+        return self.dq_block != NO_DQ
+
     def c_struct(self) -> _CWeight:
-        return _CWeight(self.codes.data_ptr(), self.absmax_q.data_ptr(),
-                        self.absmax_scale.data_ptr(), self.absmax_mean.data_ptr(),
+        return _CWeight(self.codes.data_ptr(), _ptr(self.absmax_q),
+                        self.absmax_scale.data_ptr(), _ptr(self.absmax_mean),
                         self.d, self.k, self.block, self.dq_block)
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size()
-                   for t in (self.codes, self.absmax_q, self.absmax_scale, self.absmax_mean))
+                   for t in (self.codes, self.absmax_q, self.absmax_scale, self.absmax_mean)
+                   if t is not None)
 
 
 def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
-def quantize_workspace_bytes(d: int, k: int) -> int:
-    return int(_lib.qlora_nf4_quantize_workspace(d, k, BLOCK, DQ_BLOCK))
+def quantize_workspace_bytes(d: int, k: int, dq_block: int = DQ_BLOCK) -> int:
+    return int(_lib.qlora_nf4_quantize_workspace(d, k, BLOCK, dq_block))
 
 
 def linear_workspace_bytes(m: int, d: int, k: int, r: int) -> int:
@@ -172,12 +187,14 @@ def linear_workspace_bytes(m: int, d: int, k: int, r: int) -> int:
 
 
 def qlora_nf4_quantize(w0: torch.Tensor, out: NF4Weight | None = None,
-                       workspace: torch.Tensor | None = None) -> NF4Weight:
-    """NF4 + double quantization of fp32 W0 [d, k] on the current stream."""
+                       workspace: torch.Tensor | None = None,
+                       double_quant: bool = True) -> NF4Weight:
+    """NF4 (+ double quantization of the block absmax) of fp32 W0 [d, k] on the
+    current stream.  With `out` given, its dq_block decides the format."""
     _dev_tensor(w0, torch.float32, "W0")
     d, k = w0.shape
-    w = out if out is not None else NF4Weight.empty(d, k, w0.device)
-    ws_bytes = quantize_workspace_bytes(d, k)
+    w = out if out is not None else NF4Weight.empty(d, k, w0.device, double_quant)
+    ws_bytes = quantize_workspace_bytes(d, k, w.dq_block)
     ws = workspace if workspace is not None else _workspace(ws_bytes, w0.device)
     cw = w.c_struct()
     _check(_lib.qlora_nf4_quantize(w0.data_ptr(), ctypes.byref(cw), ws.data_ptr(),
@@ -297,5 +314,5 @@ __all__ = [
     "qlora_linear_bwd", "qlora_linear_gemm_only", "qlora_adapter_merge", "qlora_adapter_unmerge",
     "qlora_nf4_codebook", "qlora_nf4_thresholds", "status_str", "library",
     "abi_version", "quantize_workspace_bytes", "linear_workspace_bytes", "adapter_scale",
-    "BLOCK", "DQ_BLOCK",
+    "BLOCK", "DQ_BLOCK", "NO_DQ",
 ]

@@ -23,15 +23,25 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 int check_weight(const qlora_nf4_weight *w, bool need_data) {
     if (!w) return QLORA_EINVAL;
     if (w->d <= 0 || w->k <= 0) return QLORA_EINVAL;
-    if (w->block != QLORA_NF4_BLOCK || w->dq_block != QLORA_NF4_DQ_BLOCK) return QLORA_ENOTSUP;
+    if (w->block != QLORA_NF4_BLOCK) return QLORA_ENOTSUP;
+    if (w->dq_block != QLORA_NF4_DQ_BLOCK && w->dq_block != QLORA_NF4_NO_DQ) return QLORA_ENOTSUP;
     if (w->k % QLORA_NF4_BLOCK != 0) return QLORA_EINVAL;
     if (w->d > kMaxWeights / w->k) return QLORA_ENOTSUP;
     if (need_data) {
-        if (!w->codes || !w->absmax_q || !w->absmax_scale || !w->absmax_mean) return QLORA_EINVAL;
-        if (!aligned(w->codes, 16) || !aligned(w->absmax_scale, 4) || !aligned(w->absmax_mean, 4))
+        const bool dq = w->dq_block != QLORA_NF4_NO_DQ;
+        if (!w->codes || !w->absmax_scale) return QLORA_EINVAL;
+        if (dq && (!w->absmax_q || !w->absmax_mean)) return QLORA_EINVAL;
+        if (!aligned(w->codes, 16) || !aligned(w->absmax_scale, 4) || (dq && !aligned(w->absmax_mean, 4)))
             return QLORA_EALIGN;
     }
     return QLORA_OK;
+}
+
+// The kernels' view of a checked weight.
+Nf4Weights nf4_view(const qlora_nf4_weight *w) {
+    const int dq = w->dq_block != QLORA_NF4_NO_DQ;
+    return Nf4Weights{w->codes, dq ? w->absmax_q : nullptr, w->absmax_scale, dq ? w->absmax_mean : nullptr,
+                      w->d, w->k, dq};
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_EHIP; }
@@ -113,7 +123,7 @@ const char *qlora_status_str(int status) {
     switch (status) {
         case QLORA_OK: return "QLORA_OK: success";
         case QLORA_EINVAL: return "QLORA_EINVAL: invalid argument (null pointer, size <= 0, k % block != 0, non-finite alpha)";
-        case QLORA_ENOTSUP: return "QLORA_ENOTSUP: unsupported configuration (block != 64, dq_block != 256, r > 128, d % 8 != 0, tensor too large)";
+        case QLORA_ENOTSUP: return "QLORA_ENOTSUP: unsupported configuration (block != 64, dq_block not 256 or 0, r > 128, d % 8 != 0, tensor too large)";
         case QLORA_EALIGN: return "QLORA_EALIGN: misaligned pointer (16-byte alignment required)";
         case QLORA_EWORKSPACE: return "QLORA_EWORKSPACE: workspace missing or too small";
         case QLORA_EHIP: return "QLORA_EHIP: HIP launch or runtime error";
@@ -154,9 +164,10 @@ int qlora_nf4_quantize(const float *W0, const qlora_nf4_weight *w, void *ws, siz
     if (!aligned(ws, 16)) return QLORA_EALIGN;
     (void)hipGetLastError();
     char *base = static_cast<char *>(ws);
-    return hip_status(launch_quantize(W0, w->d * w->k, w->codes, w->absmax_q, w->absmax_scale,
-                                      w->absmax_mean, reinterpret_cast<float *>(base + q.absmax),
-                                      reinterpret_cast<double *>(base + q.group_sum),
+    const bool dq = w->dq_block != QLORA_NF4_NO_DQ;
+    return hip_status(launch_quantize(W0, w->d * w->k, w->codes, dq ? w->absmax_q : nullptr, w->absmax_scale,
+                                      dq ? w->absmax_mean : nullptr, reinterpret_cast<float *>(base + q.absmax),
+                                      reinterpret_cast<double *>(base + q.group_sum), dq ? 1 : 0,
                                       static_cast<hipStream_t>(stream)));
 }
 
@@ -166,8 +177,9 @@ int qlora_nf4_dequantize(const qlora_nf4_weight *w, qlora_bf16 *W_out, void *str
     if (!W_out) return QLORA_EINVAL;
     if (!aligned(W_out, 16)) return QLORA_EALIGN;
     (void)hipGetLastError();
-    return hip_status(launch_dequantize(w->codes, w->absmax_q, w->absmax_scale, w->absmax_mean,
-                                        w->d * w->k, W_out, static_cast<hipStream_t>(stream)));
+    const Nf4Weights nw = nf4_view(w);
+    return hip_status(launch_dequantize(nw.codes, nw.c2, nw.c1, nw.mean, nw.dq, w->d * w->k, W_out,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 size_t qlora_linear_workspace(int64_t M, int64_t d, int64_t k, int32_t r) {
@@ -191,7 +203,7 @@ int qlora_linear_fwd(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M,
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const float scale = alpha / static_cast<float>(r);
     float *U = U_save ? U_save : reinterpret_cast<float *>(base + l.u);
-    const Nf4Weights nw{w->codes, w->absmax_q, w->absmax_scale, w->absmax_mean, w->d, w->k};
+    const Nf4Weights nw = nf4_view(w);
     float *dpart = reinterpret_cast<float *>(base + l.dpart);
     unsigned long long *ctr = reinterpret_cast<unsigned long long *>(base + l.ctr);
     hipError_t e = hipSuccess;
@@ -232,7 +244,7 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const qlora_bf16 *x, const qlora
     uint16_t *Bt = reinterpret_cast<uint16_t *>(base + l.bt);
     float *G = reinterpret_cast<float *>(base + l.g);
     float *part = reinterpret_cast<float *>(base + l.part);
-    const Nf4Weights nw{w->codes, w->absmax_q, w->absmax_scale, w->absmax_mean, d, k};
+    const Nf4Weights nw = nf4_view(w);
 
     uint16_t *vt_u = reinterpret_cast<uint16_t *>(base + l.vt);
     uint16_t *vt_g = vt_u + 2 * cols_rank_pad(r) * M;
@@ -264,7 +276,7 @@ int qlora_adapter_merge(const qlora_nf4_weight *w, const qlora_bf16 *A, const ql
     if (r > QLORA_MAX_RANK) return QLORA_ENOTSUP;
     if (!aligned(A, 16) || !aligned(B, 2) || !aligned(W_out, 16)) return QLORA_EALIGN;
     (void)hipGetLastError();
-    const Nf4Weights nw{w->codes, w->absmax_q, w->absmax_scale, w->absmax_mean, w->d, w->k};
+    const Nf4Weights nw = nf4_view(w);
     const float scale = alpha / static_cast<float>(r);
     return hip_status(launch_adapter_merge(&nw, nullptr, w->d, w->k, A, B, r, (double)scale, W_out,
                                            static_cast<hipStream_t>(stream)));
@@ -294,7 +306,7 @@ int qlora_linear_gemm_only(const qlora_nf4_weight *w, int32_t backward, const ql
     if (!ws || ws_bytes < l.total) return QLORA_EWORKSPACE;
     if (!aligned(ws, 16)) return QLORA_EALIGN;
     (void)hipGetLastError();
-    const Nf4Weights nw{w->codes, w->absmax_q, w->absmax_scale, w->absmax_mean, w->d, w->k};
+    const Nf4Weights nw = nf4_view(w);
     return hip_status(launch_gemm_core(backward != 0, nw, a, M, r, out, gemm_ws(static_cast<char *>(ws), l),
                                        static_cast<hipStream_t>(stream)));
 }

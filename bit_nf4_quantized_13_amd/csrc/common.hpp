@@ -42,4 +42,11 @@ __device__ __forceinline__ float dq_scale(int8_t c2, float c1, float mean) {
     return (float)c2 / c1 + mean;
 }
 
+// The scale of block blk of a stored weight: doubleDequant's dq_scale, or,
+// for a weight stored without double quantization, the fp32 block absmax
+// itself, kept one per block in the c1 array (c2 and the mean unused).
+__device__ __forceinline__ float block_scale(bool dq, const int8_t *c2, const float *c1, float mean, int64_t blk) {
+    return dq ? dq_scale(c2[blk], c1[blk >> 8], mean) : c1[blk];
+}
+
 }  // namespace qnf4

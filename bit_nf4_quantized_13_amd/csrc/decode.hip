@@ -40,6 +40,10 @@
 //   lookups and MFMAs with the next block's staging.
 // * The LoRA down-projection U = X A^T (r <= 16) rides along: X is already
 //   staged, so each block adds one MFMA pair on the A rows.
+// * A weight stored without double quantization (one fp32 absmax per block)
+//   takes the same path; each lane then loads the aligned 16-byte span that
+//   holds its row's 8 block scales of an octet (three loads) instead of the
+//   c2 bytes and the group's c1.
 //
 // MFMA v_mfma_f32_16x16x32_bf16, g = lane / 16: first operand lane (m, g)
 // holds X[m][8 k], second operand lane (n, g) holds What[n][the same 8 k],
@@ -126,8 +130,9 @@ __device__ __forceinline__ uint4 load_bfrag(__amdgpu_buffer_rsrc_t rb, int row, 
 }
 
 // TW tiles per workgroup; MV result registers that can hold m < M; XR row halves of X
-// loaded (1: M <= 8); FU: U = X A^T computed here
-template <int TW, int MV, int XR, bool FU>
+// loaded (1: M <= 8); FU: U = X A^T computed here; DQ: double-quantized block
+// constants (else c1 holds the fp32 absmax of every block)
+template <int TW, int MV, int XR, bool FU, bool DQ>
 __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, Nf4Consts tab) {
     constexpr int RPC = TW <= 2 ? 4 : 2;  // code pairs (two blocks each) in flight per wave
     constexpr int RXB = 2;                // X / A blocks in flight per wave
@@ -174,12 +179,12 @@ __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, N
     constexpr bool fuse_u = FU;
 
     const __amdgpu_buffer_rsrc_t rcode = make_rsrc(p.codes, (int64_t)d * hk);
-    const __amdgpu_buffer_rsrc_t rc2 = make_rsrc(p.c2, (int64_t)d * kb);
-    const __amdgpu_buffer_rsrc_t rc1 = make_rsrc(p.c1, (((int64_t)d * kb + 255) / 256) * 4);
+    const __amdgpu_buffer_rsrc_t rc2 = make_rsrc(p.c2, DQ ? (int64_t)d * kb : 0);
+    const __amdgpu_buffer_rsrc_t rc1 = make_rsrc(p.c1, (DQ ? ((int64_t)d * kb + 255) / 256 : (int64_t)d * kb) * 4);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (int64_t)M * k * 2);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, fuse_u ? (int64_t)r * k * 2 : 0);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, (int64_t)d * r * 2);
-    const __amdgpu_buffer_rsrc_t rmean = make_rsrc(p.mean, 4);
+    const __amdgpu_buffer_rsrc_t rmean = make_rsrc(p.mean, DQ ? 4 : 0);
     const int64_t part_f4 = S > 1 ? (int64_t)G * S * (TW + 1) * 64 : 0;  // f32x4 slots
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.part, part_f4 * 16);
 
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, N
     }
     // the DQ mean through the vector memory path (a scalar load would make the
     // wave wait for it before issuing anything else)
-    const float mean = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rmean, 0, 0, 0));
+    const float mean = DQ ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rmean, 0, 0, 0)) : 0.0f;
 
     // ---- coalesced loads into register rings -----------------------------------
     // Block b of the wave (0 <= b < nbw) is k-block wb0 + b.  Loads past the
@@ -238,19 +243,32 @@ __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, N
     // block constants of an octet (8 blocks from o): lane (n, g) takes row n of
     // tile g (g < ntl): its 8 c2 bytes from three aligned dwords, and the c1 of
     // the first and of the last block (8 blocks span at most two groups of 256).
-    // Single-dword loads: each one is range-checked on its own.
+    // Single-dword loads: each one is range-checked on its own.  Without double
     const int srow = row_g + 16 * g + n16;
     const bool srow_ok = g < ntl && srow < d;
     const uint32_t c2_lane = (uint32_t)(srow * kb + wb0);
-    uint32_t c2w[3];
+    // quantization the lane loads the 16-byte aligned span of fp32 absmax
+    // values that holds the octet's 8 (three 16-byte loads; d % 8 == 0 makes
+    // every aligned 4-value group wholly inside or wholly past the buffer) and
+    // picks its 8 by the offset inside the span.
+    constexpr int NCW = DQ ? 3 : 1;
+    constexpr int NCS = DQ ? 1 : 3;
+    uint32_t c2w[NCW];
     float c1a, c1b;
+    uint4 absv[NCS];
     auto issue_c2 = [&](int o) __attribute__((always_inline)) {
-        const bool ok = srow_ok && o < nbw;
         const uint32_t o8 = c2_lane + (uint32_t)o, a0 = o8 & ~3u;
+        const bool ok = srow_ok && o < nbw;
+        if constexpr (DQ) {
 #pragma unroll
-        for (int i = 0; i < 3; ++i) c2w[i] = __builtin_amdgcn_raw_buffer_load_b32(rc2, ok ? a0 + 4u * i : DEC_OOB, 0, 0);
-        c1a = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc1, ok ? (o8 >> 8) * 4 : DEC_OOB, 0, 0));
-        c1b = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc1, ok ? ((o8 + 7) >> 8) * 4 : DEC_OOB, 0, 0));
+            for (int i = 0; i < NCW; ++i)
+                c2w[i] = __builtin_amdgcn_raw_buffer_load_b32(rc2, ok ? a0 + 4u * i : DEC_OOB, 0, 0);
+            c1a = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc1, ok ? (o8 >> 8) * 4 : DEC_OOB, 0, 0));
+            c1b = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc1, ok ? ((o8 + 7) >> 8) * 4 : DEC_OOB, 0, 0));
+        } else {
+#pragma unroll
+            for (int i = 0; i < NCS; ++i) absv[i] = load16(rc1, ok ? (a0 + 4u * i) * 4 : DEC_OOB);
+        }
     };
 
     // The first block's loads go out before the table is built (the barrier
@@ -318,7 +336,17 @@ __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, N
     for (int o = 0; o < nbw; o += 8) {
         // block scales of the octet (zero for rows past d and tiles past ntl)
         float sc[8];
-        {
+        if constexpr (!DQ) {
+            const uint32_t sh = (c2_lane + (uint32_t)o) & 3u;
+            const uint32_t f[12] = {absv[0].x, absv[0].y, absv[0].z, absv[0].w, absv[1].x, absv[1].y,
+                                    absv[1].z, absv[1].w, absv[2].x, absv[2].y, absv[2].z, absv[2].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t v = sh == 0 ? f[e] : sh == 1 ? f[e + 1] : sh == 2 ? f[e + 2] : f[e + 3];
+                // blocks past nbw (another wave's, or the next row's) and rows past d add nothing
+                sc[e] = srow_ok && o + e < nbw ? __uint_as_float(v) : 0.0f;
+            }
+        } else {
             const uint32_t sh = 8 * ((c2_lane + (uint32_t)o) & 3u);
             const uint32_t lo = (uint32_t)(((uint64_t)c2w[1] << 32 | c2w[0]) >> sh);
             const uint32_t hi = (uint32_t)(((uint64_t)c2w[2] << 32 | c2w[1]) >> sh);
@@ -540,17 +568,18 @@ DecodePlan decode_plan(int64_t d, int64_t k) {
     return pl;
 }
 
-template <int TW, bool FU>
+template <int TW, bool FU, bool DQ>
 hipError_t launch_fu(const DecodeArgs &a, int grid, hipStream_t st) {
-    if (a.M == 1) hipLaunchKernelGGL((nf4_decode_kernel<TW, 1, 1, FU>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
-    else if (a.M <= 8) hipLaunchKernelGGL((nf4_decode_kernel<TW, 4, 1, FU>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
-    else hipLaunchKernelGGL((nf4_decode_kernel<TW, 4, 2, FU>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
+    if (a.M == 1) hipLaunchKernelGGL((nf4_decode_kernel<TW, 1, 1, FU, DQ>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
+    else if (a.M <= 8) hipLaunchKernelGGL((nf4_decode_kernel<TW, 4, 1, FU, DQ>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
+    else hipLaunchKernelGGL((nf4_decode_kernel<TW, 4, 2, FU, DQ>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
     return hipGetLastError();
 }
 
 template <int TW>
-hipError_t launch_tw(const DecodeArgs &a, int grid, hipStream_t st) {
-    return a.U ? launch_fu<TW, false>(a, grid, st) : launch_fu<TW, true>(a, grid, st);
+hipError_t launch_tw(const DecodeArgs &a, bool dq, int grid, hipStream_t st) {
+    if (dq) return a.U ? launch_fu<TW, false, true>(a, grid, st) : launch_fu<TW, true, true>(a, grid, st);
+    return a.U ? launch_fu<TW, false, false>(a, grid, st) : launch_fu<TW, true, false>(a, grid, st);
 }
 
 }  // namespace
@@ -595,11 +624,12 @@ hipError_t launch_decode_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, 
     a.tr = (int)(nt % pl.G);
     a.kbs = (int)(kb / pl.S);
     a.kr = (int)(kb % pl.S);
+    const bool dq = w.dq != 0;
     switch (pl.TW) {
-        case 1: return launch_tw<1>(a, pl.grid, st);
-        case 2: return launch_tw<2>(a, pl.grid, st);
-        case 3: return launch_tw<3>(a, pl.grid, st);
-        default: return launch_tw<4>(a, pl.grid, st);
+        case 1: return launch_tw<1>(a, dq, pl.grid, st);
+        case 2: return launch_tw<2>(a, dq, pl.grid, st);
+        case 3: return launch_tw<3>(a, dq, pl.grid, st);
+        default: return launch_tw<4>(a, dq, pl.grid, st);
     }
 }
 

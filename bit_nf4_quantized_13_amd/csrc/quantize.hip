@@ -307,14 +307,16 @@ __global__ __launch_bounds__(256) void dq_encode(const float *__restrict__ absma
 }  // namespace
 
 hipError_t launch_quantize(const float *W0, int64_t n, uint8_t *codes, int8_t *c2, float *c1,
-                           float *mean, float *absmax_ws, double *group_sum_ws, hipStream_t s) {
+                           float *mean, float *absmax_ws, double *group_sum_ws, int dq, hipStream_t s) {
     const int64_t nb = n / kBlock;
     const int64_t groups = (nb + kGroup - 1) / kGroup;
     int64_t padded = 1;
     while (padded < groups) padded *= 2;
-    if (padded > (int64_t)kMeanThreads * kMeanPerThread) return hipErrorInvalidValue;
+    if (dq && padded > (int64_t)kMeanThreads * kMeanPerThread) return hipErrorInvalidValue;
+    // without double quantization the block absmax is the stored scale: no encode
     hipLaunchKernelGGL(nf4_quantize_groups, dim3((unsigned)groups), dim3(256), 0, s, W0, nb,
-                       nf4_consts(), codes, absmax_ws, group_sum_ws);
+                       nf4_consts(), codes, dq ? absmax_ws : c1, group_sum_ws);
+    if (!dq) return hipGetLastError();
     if (padded <= kMeanInline) {
         hipLaunchKernelGGL(dq_encode<true>, dim3((unsigned)groups), dim3(256), 0, s, absmax_ws, nb, mean, group_sum_ws,
                            groups, padded, c2, c1);

@@ -45,13 +45,16 @@ extern "C" {
 /* ---- status codes ------------------------------------------------------ */
 #define QLORA_OK          0  /* success                                                  */
 #define QLORA_EINVAL      1  /* null pointer, size <= 0, k % block != 0, non-finite alpha */
-#define QLORA_ENOTSUP     2  /* block != 64, dq_block != 256, r > 128, tensor too large   */
+#define QLORA_ENOTSUP     2  /* block != 64, dq_block not 256 or 0, r > 128, too large   */
 #define QLORA_EALIGN      3  /* a pointer read/written with 128-bit accesses is not 16-byte aligned */
 #define QLORA_EWORKSPACE  4  /* workspace NULL or smaller than the *_workspace() size     */
 #define QLORA_EHIP        5  /* a HIP launch or runtime error (hipGetLastError)          */
 
 #define QLORA_NF4_BLOCK     64   /* weights per NF4 block (chkda, "Quantizing and dequantizing with the codebook") */
 #define QLORA_NF4_DQ_BLOCK  256  /* block constants per second-level group (chkda, "Double quantization ...")   */
+#define QLORA_NF4_NO_DQ     0    /* dq_block value of the format without double quantization: one fp32
+                                    absmax per block (chkda, the bits-per-weight accounting after
+                                    "Double quantization and double dequantization": 4.5 bits/weight) */
 #define QLORA_MAX_RANK      128
 
 typedef uint16_t qlora_bf16; /* raw bfloat16 bits */
@@ -69,7 +72,12 @@ typedef uint16_t qlora_bf16; /* raw bfloat16 bits */
  *   absmax_scale float [G]    c1 (4-byte aligned)
  *   absmax_mean  float [1]    the mean of the nb block absmax values
  *   d, k                      W0 shape, d >= 1, k >= 1, k % block == 0
- *   block, dq_block           must be 64 and 256
+ *   block, dq_block           64, and 256 (or QLORA_NF4_NO_DQ, below)
+ * With dq_block == QLORA_NF4_NO_DQ the block constants are not double
+ * quantized (the "before" format of the same page's bits-per-weight
+ * accounting): absmax_scale holds the fp32 absmax of each block, [nb]
+ * entries, the block's own scale; absmax_q and absmax_mean are neither read
+ * nor written and may be NULL.  Every call below takes either format.
  */
 typedef struct {
     uint8_t *codes;
@@ -94,7 +102,8 @@ size_t qlora_nf4_quantize_workspace(int64_t d, int64_t k, int32_t block, int32_t
  * scales minus their mean are quantized to int8 per group of 256 with
  * c1 = 127 / max|s - mean| (a zero group stores zeros and c1 = 127).
  *   W0  device fp32 [d x k], 16-byte aligned, read only.
- *   w   host struct: shape fields and the four output arrays (all written).
+ *   w   host struct: shape fields and the four output arrays (all written;
+ *       without double quantization only codes and the per-block absmax).
  *   ws  device workspace of >= qlora_nf4_quantize_workspace(...) bytes,
  *       16-byte aligned; its contents on entry are ignored.
  * The result is bit-identical on every run (fixed-order fp64 mean).
@@ -107,6 +116,7 @@ int qlora_nf4_quantize(const float *W0, const qlora_nf4_weight *w,
  * chkda, "Double quantization and double dequantization":
  *   scale[j] = fp32(c2[j] / c1[j/256]) + mean          (IEEE fp32 ops)
  *   W[i]     = BF16(C[code[i]] * scale[i/64])          (one RNE rounding)
+ * (without double quantization scale[j] is the stored fp32 absmax of block j).
  *   W_out  device bf16 [d x k], 16-byte aligned, written.
  */
 int qlora_nf4_dequantize(const qlora_nf4_weight *w, qlora_bf16 *W_out, void *stream);

@@ -16,6 +16,9 @@ Everything here follows chkda.github.io "Why do we need LoRA and QLoRA?":
   int8_absmax_*      "First, how does k-bit quantization work?": c = 127/absmax
                      (stored in fp32), q = round(c*X), Xhat = q / c; an
                      all-zero input stores zeros and a nonzero scale.
+  quantize_single    the same page's bits-per-weight accounting ("before" double
+  dequantize_single  quantization): one fp32 absmax per block, stored as is,
+                     W[i] = BF16(C[W[i]] * absmax[i//64]).
   double_quantize    "Double quantization and double dequantization": the block
   double_dequantize  scales are quantized to 8 bits in groups of 256 with one
                      fp32 second-level scale per group, after subtracting a
@@ -303,6 +306,25 @@ def quantize(w0: np.ndarray, block: int = BLOCK, dq_block: int = DQ_BLOCK) -> di
 def dequantize(q: dict, shape=None, block: int = BLOCK, dq_block: int = DQ_BLOCK) -> np.ndarray:
     """bf16 bits of the double-dequantized weights, optionally reshaped."""
     bits = double_dequantize(q["packed"], q["c2"], q["c1"], q["mean"], q["n"], block, dq_block)
+    return bits.reshape(shape) if shape is not None else bits
+
+
+def quantize_single(w0: np.ndarray, block: int = BLOCK) -> dict:
+    """NF4 without double quantization: the block absmax itself is stored (fp32).
+
+    chkda "Double quantization and double dequantization", its bits-per-weight
+    accounting: before double quantization one fp32 scale serves each block of
+    64 weights.  Returns packed codes, codes, the fp32 absmax per block and n.
+    """
+    codes, scale = quantize_blocks(w0, block)
+    return {"codes": codes, "packed": pack_codes(codes), "absmax": scale,
+            "n": int(np.asarray(w0).size)}
+
+
+def dequantize_single(q: dict, shape=None, block: int = BLOCK) -> np.ndarray:
+    """bf16 bits of W[i] = BF16(C[code[i]] * absmax[i // block]) (R8), no DQ."""
+    codes = unpack_codes(q["packed"], q["n"])
+    bits = bf16_rne_bits(dequantize_blocks(codes, q["absmax"], block))
     return bits.reshape(shape) if shape is not None else bits
 
 

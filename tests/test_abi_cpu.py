@@ -159,6 +159,25 @@ def test_valid_call_without_gpu_reports_hip_error():
     assert quant(w) == q.QLORA_EHIP
 
 
+def test_no_double_quant_format_validation():
+    """dq_block 0: codes and the per-block absmax are required, c2 and the mean
+    are not read (NULL or misaligned is fine); other dq_block values are refused."""
+    import torch
+    lib = q.library()
+    assert lib.qlora_nf4_quantize_workspace(4096, 4096, 64, q.NO_DQ) > 0
+    assert lib.qlora_nf4_quantize_workspace(4096, 4096, 64, 128) == 0
+    assert quant(weight(dq=q.NO_DQ, c1=None, c2=None, mean=None)) == q.QLORA_EINVAL
+    assert quant(weight(dq=q.NO_DQ, codes=None, c2=None, mean=None)) == q.QLORA_EINVAL
+    assert quant(weight(dq=q.NO_DQ, c1=FAKE + 2, c2=None, mean=None)) == q.QLORA_EALIGN
+    assert quant(weight(dq=1, c2=None, mean=None)) == q.QLORA_ENOTSUP
+    assert quant(weight(dq=q.DQ_BLOCK, c2=None)) == q.QLORA_EINVAL    # double-quantized: c2 needed
+    assert fwd(w=weight(dq=q.NO_DQ, c1=None, c2=None, mean=None)) == q.QLORA_EINVAL
+    assert lib.qlora_nf4_dequantize(ctypes.byref(weight(dq=q.NO_DQ, c2=None, mean=None)), FAKE_MIS,
+                                    None) == q.QLORA_EALIGN
+    if not torch.cuda.is_available():  # valid: gets as far as the launch
+        assert quant(weight(dq=q.NO_DQ, c2=None, mean=FAKE + 1)) == q.QLORA_EHIP
+
+
 def gemm_only(w=None, backward=0, a=FAKE, m=64, r=8, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
     w = w or weight()
     return q.library().qlora_linear_gemm_only(ctypes.byref(w), backward, a, m, r, out, ws, ws_bytes, None)

@@ -282,6 +282,66 @@ def test_double_dequant_error_bound():
 
 
 # ----------------------------------------------------------------------------
+# the format without double quantization -- chkda "Double quantization and
+# double dequantization", the bits-per-weight accounting ("before")
+# ----------------------------------------------------------------------------
+def test_single_level_worked_example():
+    kv = golden_kv("worked_examples.txt")
+    s = np.float32(float(kv["nf4.scale"][0]))
+    block = np.zeros(64, np.float32)
+    block[0], block[1] = s, np.float32(float(kv["nf4.weight"][0]))
+    q = nf4.quantize_single(block)
+    assert q["absmax"].dtype == np.float32 and q["absmax"][0] == s
+    what = nf4.bf16_bits_to_f32(nf4.dequantize_single(q)).astype(np.float64)
+    assert what[0] == float(s) and np.all(what[2:] == 0)
+    # the printed 0.32186 (5-decimal level times the scale), plus bf16's half ulp
+    assert abs(what[1] - float(kv["nf4.reconstructed_5dp"][0])) <= float(s) * 5e-6 + 2.0 ** -9 * 0.33
+
+
+def test_single_level_storage_is_four_and_a_half_bits():
+    kv = golden_kv("worked_examples.txt")
+    for shape in ((256, 512), (64, 4096)):
+        q = nf4.quantize_single(random_weights(21, shape))
+        n = q["n"]
+        bits = 8.0 * (q["packed"].nbytes + q["absmax"].nbytes) / n
+        assert bits == float(kv["dq.total_before"][0])
+        assert q["absmax"].nbytes * 8.0 / n == float(kv["dq.before"][0])
+    b = nf4.storage_bits_per_weight(4096 * 4096)
+    assert round(b["codes"] + b["scales_after"], 3) == float(kv["dq.total_after_approx"][0])
+
+
+def test_single_level_error_bound():
+    w = random_weights(22, (64, 64 * 64))
+    q = nf4.quantize_single(w)
+    what = nf4.bf16_bits_to_f32(nf4.dequantize_single(q)).astype(np.float64)
+    s = q["absmax"].astype(np.float64)[np.arange(w.size) // 64]
+    c = nf4.nf4_codebook().astype(np.float64)[q["codes"]]
+    # half the widest codebook gap of the level, then one bf16 rounding
+    bound = 0.1520 * s + 2.0 ** -8 * np.abs(c * s) + 1e-12
+    assert np.all(np.abs(w.reshape(-1) - what) <= bound)
+    # and per element: the nearest level, found by exact brute force
+    rng = np.random.default_rng(23)
+    for i in rng.integers(0, w.size, 200):
+        x = np.float32(np.float32(w.reshape(-1)[i]) / np.float32(s[i]))
+        assert q["codes"][i] == nf4.nearest_level_bruteforce(float(x))
+
+
+def test_single_level_equals_double_quant_when_dq_is_exact():
+    # every block has absmax 0.75: the mean is 0.75 exactly, the centred scales
+    # are 0, so c2 = 0, c1 = 127 and the recovered scale is exactly 0.75 --
+    # both formats must then give the same bf16 weights
+    w = random_weights(24, (48, 64 * 48), std=0.1)
+    blk = w.reshape(-1, 64)
+    blk[:] = np.clip(blk, -0.7, 0.7)
+    blk[:, 5] = np.where(np.arange(blk.shape[0]) % 2 == 0, 0.75, -0.75)
+    dq = nf4.quantize(w)
+    assert np.all(dq["c2"] == 0) and dq["mean"] == np.float32(0.75)
+    single = nf4.quantize_single(w)
+    assert np.array_equal(nf4.dequantize(dq), nf4.dequantize_single(single))
+    assert np.array_equal(dq["packed"], single["packed"])
+
+
+# ----------------------------------------------------------------------------
 # the linear layer -- chkda "How does it work?", "Merging LoRA weights ...";
 # fromzero2ai "Why Does This Save Memory?"
 # ----------------------------------------------------------------------------
