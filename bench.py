@@ -278,23 +278,25 @@ def time_calls(torch, fn, iters):
     return e0.elapsed_time(e1) / iters
 
 
-def run_no_dq_bench(q, torch, ctx, iters=20):
-    """The format without double quantization (one fp32 absmax per block):
+def run_format_bench(q, torch, ctx, fmt, iters=20):
+    """A further storage format of the block constants -- "no_dq" (one fp32
+    absmax per block) or "fp8" (double quantization with c2 in OCP FP8 e4m3):
     quantize, forward + backward on the layer4096 inputs, and the decode
     forward of the 14336 x 4096 projection at M = 16."""
     from workloads import WORKLOADS, workload_layer
     from tests.helpers import to_dev_bf16, to_dev_f32
+    kw = {"double_quant": False} if fmt == "no_dq" else {"c2_fp8": True}
     _, x, a, b, alpha, y, u, lws, r = ctx
     inp = workload_layer("layer4096")
     m, d, k = inp.x.shape[0], inp.w0.shape[0], inp.w0.shape[1]
     w0 = to_dev_f32(inp.w0)
     dy = to_dev_bf16(inp.dy)
-    wq = q.NF4Weight.empty(d, k, double_quant=False)
-    qws = torch.empty(q.quantize_workspace_bytes(d, k, q.NO_DQ), dtype=torch.uint8, device="cuda")
+    wq = q.NF4Weight.empty(d, k, **kw)
+    qws = torch.empty(q.quantize_workspace_bytes(d, k, wq.dq_block), dtype=torch.uint8, device="cuda")
     dx = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
     da = torch.empty((r, k), dtype=torch.float32, device="cuda")
     db = torch.empty((d, r), dtype=torch.float32, device="cuda")
-    log("no-DQ: layer4096 quantize / fwd+bwd")
+    log(f"{fmt}: layer4096 quantize / fwd+bwd")
     q_ms = time_calls(torch, lambda: q.qlora_nf4_quantize(w0, out=wq, workspace=qws), iters)
 
     def fwd_bwd():
@@ -302,6 +304,7 @@ def run_no_dq_bench(q, torch, ctx, iters=20):
         q.qlora_linear_bwd(wq, x, dy, a, b, alpha, u=u, workspace=lws, outs=(dx, da, db))
     fb_ms = time_calls(torch, fwd_bwd, iters)
     flops = fwd_flops(m, d, k, r) + bwd_flops(m, d, k, r)
+    const_bytes = wq.nbytes() - d * k // 2   # block constants of the stored weight
     del w0, wq, qws
     wl = WORKLOADS["decode"]
     pi = max(range(len(wl.projections)), key=lambda i: wl.projections[i].d * wl.projections[i].k)
@@ -310,9 +313,10 @@ def run_no_dq_bench(q, torch, ctx, iters=20):
     dm = max(wl.m)
     packed = p.d * p.k // 2
     copies = max(2, -(-512 * 2**20 // packed) + 1)
-    log(f"no-DQ: decode {p.name} M={dm} over {copies} weight copies")
+    log(f"{fmt}: decode {p.name} M={dm} over {copies} weight copies")
     dw0 = to_dev_f32(dinp.w0)
-    ws = [q.qlora_nf4_quantize(dw0, double_quant=False) for _ in range(copies)]
+    ws = [q.qlora_nf4_quantize(dw0, **kw) for _ in range(copies)]
+    dconst = ws[0].nbytes() - packed
     del dw0
     da_, db_, dx_ = to_dev_bf16(dinp.a), to_dev_bf16(dinp.b), to_dev_bf16(dinp.x[:dm])
     dy_ = torch.empty((dm, p.d), dtype=torch.bfloat16, device="cuda")
@@ -323,13 +327,14 @@ def run_no_dq_bench(q, torch, ctx, iters=20):
         q.qlora_linear_fwd(ws[it[0] % copies], dx_, da_, db_, wl.alpha, save_u=False, out=dy_, workspace=dws)
         it[0] += 1
     dec_us = time_calls(torch, dec, 50) * 1e3
-    nb = p.d * p.k // 64
-    alg = p.d * p.k // 2 + 4 * nb + 2 * dm * p.k + 2 * wl.r * p.k + 2 * p.d * wl.r + 2 * dm * p.d
+    alg = packed + dconst + 2 * dm * p.k + 2 * wl.r * p.k + 2 * p.d * wl.r + 2 * dm * p.d
     del ws
     torch.cuda.empty_cache()
-    return {"format": "NF4 codes + fp32 absmax per 64-block (4.5 bits/weight)",
+    desc = {"no_dq": "NF4 codes + fp32 absmax per 64-block (4.5 bits/weight)",
+            "fp8": "NF4 codes + double quantization with c2 in OCP FP8 e4m3 (4.127 bits/weight)"}[fmt]
+    return {"format": desc,
             "quantize_us": round(q_ms * 1e3, 2),
-            "quantize_gbs": round((d * k * 4 + d * k // 2 + 4 * (d * k // 64)) / (q_ms * 1e-3) / 1e9, 1),
+            "quantize_gbs": round((d * k * 4 + d * k // 2 + const_bytes) / (q_ms * 1e-3) / 1e9, 1),
             "fwd_bwd_ms": round(fb_ms, 4), "fwd_bwd_tflops": round(flops / (fb_ms * 1e-3) / 1e12, 3),
             f"decode_{p.name}_m{dm}": {"us_per_call": round(dec_us, 3), "algorithmic_bytes": alg,
                                         "algorithmic_gbs": round(alg / (dec_us * 1e-6) / 1e9, 1),
@@ -464,7 +469,7 @@ def main():
     log("layer4096: timing the adapter merge")
     merge = run_merge_bench(q, torch, ctx)
     decode = None if args.skip_decode else run_decode_bench(q, torch)
-    no_dq = None if args.skip_decode else run_no_dq_bench(q, torch, ctx)
+    formats = None if args.skip_decode else {f: run_format_bench(q, torch, ctx, f) for f in ("no_dq", "fp8")}
     cpu = None
     if not args.skip_cpu_baseline:
         log("cpu baseline: timing the oracle on a bounded sample")
@@ -484,7 +489,7 @@ def main():
         "decode_fwd": decode,
         "decode_roofline": None if decode is None else decode_roofline(decode),
         "adapter_merge": merge,
-        "no_double_quant": no_dq,
+        "other_formats": formats,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -27,6 +27,7 @@ QLORA_OK, QLORA_EINVAL, QLORA_ENOTSUP, QLORA_EALIGN, QLORA_EWORKSPACE, QLORA_EHI
 BLOCK = 64
 DQ_BLOCK = 256
 NO_DQ = 0  # dq_block of the format without double quantization (fp32 absmax per block)
+C2_INT8, C2_FP8_E4M3 = 0, 1  # c2_format: how the c2 bytes of a double-quantized weight encode values
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -40,7 +41,8 @@ class _CWeight(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("absmax_q", ctypes.c_void_p),
                 ("absmax_scale", ctypes.c_void_p), ("absmax_mean", ctypes.c_void_p),
                 ("d", ctypes.c_int64), ("k", ctypes.c_int64),
-                ("block", ctypes.c_int32), ("dq_block", ctypes.c_int32)]
+                ("block", ctypes.c_int32), ("dq_block", ctypes.c_int32),
+                ("c2_format", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -134,30 +136,35 @@ class NF4Weight:
     """Device buffers of one quantized W0 [d x k] (see qlora_nf4_weight).
 
     Double-quantized (dq_block == DQ_BLOCK): absmax_q holds c2, absmax_scale
-    c1 per group of 256 blocks and absmax_mean the mean.  Without double
-    quantization (dq_block == NO_DQ): absmax_scale holds the fp32 absmax of
-    every block and absmax_q / absmax_mean are None.
+    c1 per group of 256 blocks and absmax_mean the mean; c2_format says
+    whether the c2 bytes are int8 values or OCP FP8 e4m3 bit patterns
+    (absmax_q is then uint8; `.view(torch.float8_e4m3fn)` reads them).
+    Without double quantization (dq_block == NO_DQ): absmax_scale holds the
+    fp32 absmax of every block and absmax_q / absmax_mean are None.
     """
     codes: torch.Tensor                  # uint8 [d*k/2]
-    absmax_q: torch.Tensor | None        # int8 [nb] (double-quantized only)
+    absmax_q: torch.Tensor | None        # int8 or uint8 (e4m3 bits) [nb] (double-quantized only)
     absmax_scale: torch.Tensor           # float32 [G] (double-quantized) or [nb]
     absmax_mean: torch.Tensor | None     # float32 [1] (double-quantized only)
     d: int
     k: int
     block: int = BLOCK
     dq_block: int = DQ_BLOCK
+    c2_format: int = C2_INT8
 
     @staticmethod
-    def empty(d: int, k: int, device="cuda", double_quant: bool = True) -> "NF4Weight":
+    def empty(d: int, k: int, device="cuda", double_quant: bool = True,
+              c2_fp8: bool = False) -> "NF4Weight":
         nb = (d * k) // BLOCK
         codes = torch.empty(d * k // 2, dtype=torch.uint8, device=device)
         if not double_quant:
             return NF4Weight(codes, None, torch.empty(nb, dtype=torch.float32, device=device), None,
                              d, k, dq_block=NO_DQ)
         g = -(-nb // DQ_BLOCK)
-        return NF4Weight(codes, torch.empty(nb, dtype=torch.int8, device=device),
+        return NF4Weight(codes, torch.empty(nb, dtype=torch.uint8 if c2_fp8 else torch.int8, device=device),
                          torch.empty(g, dtype=torch.float32, device=device),
-                         torch.empty(1, dtype=torch.float32, device=device), d, k)
+                         torch.empty(1, dtype=torch.float32, device=device), d, k,
+                         c2_format=C2_FP8_E4M3 if c2_fp8 else C2_INT8)
 
     @property
     def double_quant(self) -> bool:
@@ -166,7 +173,7 @@ class NF4Weight:
     def c_struct(self) -> _CWeight:
         return _CWeight(self.codes.data_ptr(), _ptr(self.absmax_q),
                         self.absmax_scale.data_ptr(), _ptr(self.absmax_mean),
-                        self.d, self.k, self.block, self.dq_block)
+                        self.d, self.k, self.block, self.dq_block, self.c2_format)
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size()
@@ -188,12 +195,13 @@ def linear_workspace_bytes(m: int, d: int, k: int, r: int) -> int:
 
 def qlora_nf4_quantize(w0: torch.Tensor, out: NF4Weight | None = None,
                        workspace: torch.Tensor | None = None,
-                       double_quant: bool = True) -> NF4Weight:
-    """NF4 (+ double quantization of the block absmax) of fp32 W0 [d, k] on the
-    current stream.  With `out` given, its dq_block decides the format."""
+                       double_quant: bool = True, c2_fp8: bool = False) -> NF4Weight:
+    """NF4 (+ double quantization of the block absmax, c2 in int8 or, with
+    c2_fp8, OCP FP8 e4m3) of fp32 W0 [d, k] on the current stream.  With `out`
+    given, its dq_block and c2_format decide the format."""
     _dev_tensor(w0, torch.float32, "W0")
     d, k = w0.shape
-    w = out if out is not None else NF4Weight.empty(d, k, w0.device, double_quant)
+    w = out if out is not None else NF4Weight.empty(d, k, w0.device, double_quant, c2_fp8)
     ws_bytes = quantize_workspace_bytes(d, k, w.dq_block)
     ws = workspace if workspace is not None else _workspace(ws_bytes, w0.device)
     cw = w.c_struct()
@@ -314,5 +322,5 @@ __all__ = [
     "qlora_linear_bwd", "qlora_linear_gemm_only", "qlora_adapter_merge", "qlora_adapter_unmerge",
     "qlora_nf4_codebook", "qlora_nf4_thresholds", "status_str", "library",
     "abi_version", "quantize_workspace_bytes", "linear_workspace_bytes", "adapter_scale",
-    "BLOCK", "DQ_BLOCK", "NO_DQ",
+    "BLOCK", "DQ_BLOCK", "NO_DQ", "C2_INT8", "C2_FP8_E4M3",
 ]

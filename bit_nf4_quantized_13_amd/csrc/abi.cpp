@@ -25,6 +25,7 @@ int check_weight(const qlora_nf4_weight *w, bool need_data) {
     if (w->d <= 0 || w->k <= 0) return QLORA_EINVAL;
     if (w->block != QLORA_NF4_BLOCK) return QLORA_ENOTSUP;
     if (w->dq_block != QLORA_NF4_DQ_BLOCK && w->dq_block != QLORA_NF4_NO_DQ) return QLORA_ENOTSUP;
+    if (w->c2_format != QLORA_C2_INT8 && w->c2_format != QLORA_C2_FP8_E4M3) return QLORA_ENOTSUP;
     if (w->k % QLORA_NF4_BLOCK != 0) return QLORA_EINVAL;
     if (w->d > kMaxWeights / w->k) return QLORA_ENOTSUP;
     if (need_data) {
@@ -39,9 +40,10 @@ int check_weight(const qlora_nf4_weight *w, bool need_data) {
 
 // The kernels' view of a checked weight.
 Nf4Weights nf4_view(const qlora_nf4_weight *w) {
-    const int dq = w->dq_block != QLORA_NF4_NO_DQ;
+    const bool dq = w->dq_block != QLORA_NF4_NO_DQ;
+    const int fmt = !dq ? kNoDq : w->c2_format == QLORA_C2_FP8_E4M3 ? kDqFp8 : kDqInt8;
     return Nf4Weights{w->codes, dq ? w->absmax_q : nullptr, w->absmax_scale, dq ? w->absmax_mean : nullptr,
-                      w->d, w->k, dq};
+                      w->d, w->k, fmt};
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_EHIP; }
@@ -123,7 +125,7 @@ const char *qlora_status_str(int status) {
     switch (status) {
         case QLORA_OK: return "QLORA_OK: success";
         case QLORA_EINVAL: return "QLORA_EINVAL: invalid argument (null pointer, size <= 0, k % block != 0, non-finite alpha)";
-        case QLORA_ENOTSUP: return "QLORA_ENOTSUP: unsupported configuration (block != 64, dq_block not 256 or 0, r > 128, d % 8 != 0, tensor too large)";
+        case QLORA_ENOTSUP: return "QLORA_ENOTSUP: unsupported configuration (block != 64, dq_block not 256 or 0, unknown c2_format, r > 128, d % 8 != 0, tensor too large)";
         case QLORA_EALIGN: return "QLORA_EALIGN: misaligned pointer (16-byte alignment required)";
         case QLORA_EWORKSPACE: return "QLORA_EWORKSPACE: workspace missing or too small";
         case QLORA_EHIP: return "QLORA_EHIP: HIP launch or runtime error";
@@ -167,7 +169,7 @@ int qlora_nf4_quantize(const float *W0, const qlora_nf4_weight *w, void *ws, siz
     const bool dq = w->dq_block != QLORA_NF4_NO_DQ;
     return hip_status(launch_quantize(W0, w->d * w->k, w->codes, dq ? w->absmax_q : nullptr, w->absmax_scale,
                                       dq ? w->absmax_mean : nullptr, reinterpret_cast<float *>(base + q.absmax),
-                                      reinterpret_cast<double *>(base + q.group_sum), dq ? 1 : 0,
+                                      reinterpret_cast<double *>(base + q.group_sum), nf4_view(w).fmt,
                                       static_cast<hipStream_t>(stream)));
 }
 
@@ -178,7 +180,7 @@ int qlora_nf4_dequantize(const qlora_nf4_weight *w, qlora_bf16 *W_out, void *str
     if (!aligned(W_out, 16)) return QLORA_EALIGN;
     (void)hipGetLastError();
     const Nf4Weights nw = nf4_view(w);
-    return hip_status(launch_dequantize(nw.codes, nw.c2, nw.c1, nw.mean, nw.dq, w->d * w->k, W_out,
+    return hip_status(launch_dequantize(nw.codes, nw.c2, nw.c1, nw.mean, nw.fmt, w->d * w->k, W_out,
                                         static_cast<hipStream_t>(stream)));
 }
 

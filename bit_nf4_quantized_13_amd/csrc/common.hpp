@@ -36,17 +36,61 @@ __device__ __forceinline__ float bf16_round(float f) {
     return bf16_bits_to_f32(pack_bf16x2(f, 0.0f) & 0xFFFFu);
 }
 
+// How the block constants of a weight are stored.
+enum ScaleFormat : int {
+    kNoDq = 0,    // one fp32 absmax per block, in the c1 array
+    kDqInt8 = 1,  // double quantization, c2 as int8
+    kDqFp8 = 2,   // double quantization, c2 as OCP FP8 e4m3 (raw bytes)
+};
+
+// OCP FP8 e4m3 (sign, 4 exponent bits with bias 7, 3 mantissa bits, the
+// exponent field 0 holding the subnormals m * 2^-9, S.1111.111 = NaN, no
+// infinities) -> fp32: v_cvt_f32_fp8 reads this format on gfx950, exactly, for
+// byte SEL of a dword (every one of the 256 codes was checked against the
+// format's definition; the library's tests read all finite codes back).
+template <int SEL>
+__device__ __forceinline__ float e4m3_byte_to_f32(uint32_t word) {
+    return __builtin_amdgcn_cvt_f32_fp8((int)word, SEL);
+}
+
+// fp32 -> OCP FP8 e4m3, round to nearest, ties to the even code, for finite
+// |x| <= 448 (the largest finite e4m3 value; callers clamp first).  Below
+// 2^-6 the grid is the multiples of 2^-9 (code = the multiple, 8 being the
+// smallest normal); above it the 3 leading mantissa bits are kept and the
+// carry of the rounding runs into the exponent field.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+    const uint32_t bits = __float_as_uint(x), sign = (bits >> 24) & 0x80u;
+    const float a = fabsf(x);
+    uint32_t code;
+    if (a < 0.015625f) {
+        code = (uint32_t)rintf(a * 512.0f);  // exact scaling, round half to even
+    } else {
+        const uint32_t ab = bits & 0x7FFFFFFFu;
+        const uint32_t t = (((ab >> 23) - 120u) << 3) | ((ab >> 20) & 7u);
+        const uint32_t rem = ab & 0xFFFFFu;
+        code = t + ((rem > 0x80000u || (rem == 0x80000u && (t & 1u))) ? 1u : 0u);
+    }
+    return code | sign;
+}
+
+// The value of a stored c2 byte (byte SEL of a dword).
+template <int SEL = 0>
+__device__ __forceinline__ float c2_value(uint32_t word, bool fp8) {
+    return fp8 ? e4m3_byte_to_f32<SEL>(word) : (float)(int8_t)((word >> (8 * SEL)) & 0xFFu);
+}
+
 // Dequantized block scale (doubleDequant): fp32(c2 / c1) + mean, two IEEE
 // fp32 operations (the library is compiled with -ffp-contract=off).
-__device__ __forceinline__ float dq_scale(int8_t c2, float c1, float mean) {
-    return (float)c2 / c1 + mean;
+__device__ __forceinline__ float dq_scale(float c2, float c1, float mean) {
+    return c2 / c1 + mean;
 }
 
 // The scale of block blk of a stored weight: doubleDequant's dq_scale, or,
 // for a weight stored without double quantization, the fp32 block absmax
 // itself, kept one per block in the c1 array (c2 and the mean unused).
-__device__ __forceinline__ float block_scale(bool dq, const int8_t *c2, const float *c1, float mean, int64_t blk) {
-    return dq ? dq_scale(c2[blk], c1[blk >> 8], mean) : c1[blk];
+__device__ __forceinline__ float block_scale(int fmt, const int8_t *c2, const float *c1, float mean, int64_t blk) {
+    if (fmt == kNoDq) return c1[blk];
+    return dq_scale(c2_value((uint8_t)c2[blk], fmt == kDqFp8), c1[blk >> 8], mean);
 }
 
 }  // namespace qnf4

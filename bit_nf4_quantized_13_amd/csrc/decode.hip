@@ -130,10 +130,11 @@ __device__ __forceinline__ uint4 load_bfrag(__amdgpu_buffer_rsrc_t rb, int row, 
 }
 
 // TW tiles per workgroup; MV result registers that can hold m < M; XR row halves of X
-// loaded (1: M <= 8); FU: U = X A^T computed here; DQ: double-quantized block
-// constants (else c1 holds the fp32 absmax of every block)
-template <int TW, int MV, int XR, bool FU, bool DQ>
+// loaded (1: M <= 8); FU: U = X A^T computed here; F: the ScaleFormat of the block
+// constants (double-quantized with int8 or FP8 c2, or the fp32 absmax of every block)
+template <int TW, int MV, int XR, bool FU, int F>
 __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, Nf4Consts tab) {
+    constexpr bool DQ = F != kNoDq;
     constexpr int RPC = TW <= 2 ? 4 : 2;  // code pairs (two blocks each) in flight per wave
     constexpr int RXB = 2;                // X / A blocks in flight per wave
     constexpr int CP = 80;                // code stage row pitch: conflict-free 8-byte fragment reads
@@ -351,9 +352,13 @@ __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, N
             const uint32_t lo = (uint32_t)(((uint64_t)c2w[1] << 32 | c2w[0]) >> sh);
             const uint32_t hi = (uint32_t)(((uint64_t)c2w[2] << 32 | c2w[1]) >> sh);
             const uint32_t ga = (c2_lane + (uint32_t)o) >> 8;
+            constexpr bool fp8 = F == kDqFp8;
+            const float c2v[8] = {c2_value<0>(lo, fp8), c2_value<1>(lo, fp8), c2_value<2>(lo, fp8),
+                                  c2_value<3>(lo, fp8), c2_value<0>(hi, fp8), c2_value<1>(hi, fp8),
+                                  c2_value<2>(hi, fp8), c2_value<3>(hi, fp8)};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int8_t c2 = (int8_t)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xFFu);
+                const float c2 = c2v[e];
                 // blocks past nbw and rows past d get scale 0 from a finite
                 // quotient (c1 = 1), so no NaN meets their zero products
                 const bool ok = srow_ok && o + e < nbw;
@@ -568,18 +573,24 @@ DecodePlan decode_plan(int64_t d, int64_t k) {
     return pl;
 }
 
-template <int TW, bool FU, bool DQ>
+template <int TW, bool FU, int F>
 hipError_t launch_fu(const DecodeArgs &a, int grid, hipStream_t st) {
-    if (a.M == 1) hipLaunchKernelGGL((nf4_decode_kernel<TW, 1, 1, FU, DQ>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
-    else if (a.M <= 8) hipLaunchKernelGGL((nf4_decode_kernel<TW, 4, 1, FU, DQ>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
-    else hipLaunchKernelGGL((nf4_decode_kernel<TW, 4, 2, FU, DQ>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
+    if (a.M == 1) hipLaunchKernelGGL((nf4_decode_kernel<TW, 1, 1, FU, F>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
+    else if (a.M <= 8) hipLaunchKernelGGL((nf4_decode_kernel<TW, 4, 1, FU, F>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
+    else hipLaunchKernelGGL((nf4_decode_kernel<TW, 4, 2, FU, F>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
     return hipGetLastError();
 }
 
+template <int TW, int F>
+hipError_t launch_f(const DecodeArgs &a, int grid, hipStream_t st) {
+    return a.U ? launch_fu<TW, false, F>(a, grid, st) : launch_fu<TW, true, F>(a, grid, st);
+}
+
 template <int TW>
-hipError_t launch_tw(const DecodeArgs &a, bool dq, int grid, hipStream_t st) {
-    if (dq) return a.U ? launch_fu<TW, false, true>(a, grid, st) : launch_fu<TW, true, true>(a, grid, st);
-    return a.U ? launch_fu<TW, false, false>(a, grid, st) : launch_fu<TW, true, false>(a, grid, st);
+hipError_t launch_tw(const DecodeArgs &a, int fmt, int grid, hipStream_t st) {
+    if (fmt == kDqInt8) return launch_f<TW, kDqInt8>(a, grid, st);
+    if (fmt == kDqFp8) return launch_f<TW, kDqFp8>(a, grid, st);
+    return launch_f<TW, kNoDq>(a, grid, st);
 }
 
 }  // namespace
@@ -624,12 +635,11 @@ hipError_t launch_decode_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, 
     a.tr = (int)(nt % pl.G);
     a.kbs = (int)(kb / pl.S);
     a.kr = (int)(kb % pl.S);
-    const bool dq = w.dq != 0;
     switch (pl.TW) {
-        case 1: return launch_tw<1>(a, dq, pl.grid, st);
-        case 2: return launch_tw<2>(a, dq, pl.grid, st);
-        case 3: return launch_tw<3>(a, dq, pl.grid, st);
-        default: return launch_tw<4>(a, dq, pl.grid, st);
+        case 1: return launch_tw<1>(a, w.fmt, pl.grid, st);
+        case 2: return launch_tw<2>(a, w.fmt, pl.grid, st);
+        case 3: return launch_tw<3>(a, w.fmt, pl.grid, st);
+        default: return launch_tw<4>(a, w.fmt, pl.grid, st);
     }
 }
 

@@ -542,7 +542,7 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
 // LDS is involved and every store is a contiguous 128-byte row segment per 8
 // lanes.
 template <bool T>
-__device__ __forceinline__ void dequant_tile(int64_t bid, const uint8_t *__restrict__ codes, bool dq,
+__device__ __forceinline__ void dequant_tile(int64_t bid, const uint8_t *__restrict__ codes, int fmt,
                                              const int8_t *__restrict__ c2, const float *__restrict__ c1, float mean,
                                              int64_t d, int64_t k, int64_t ldw, const Nf4Consts &tab,
                                              uint16_t *__restrict__ out) {
@@ -567,7 +567,7 @@ __device__ __forceinline__ void dequant_tile(int64_t bid, const uint8_t *__restr
         const int64_t n = n0 + e;
         const int64_t jb = n * kb + k0 / 64;
         cw[e] = n < d ? *reinterpret_cast<const uint32_t *>(codes + n * (k / 2) + k0 / 2) : 0u;
-        sc[e] = n < d ? block_scale(dq, c2, c1, mean, jb) : 0.0f;
+        sc[e] = n < d ? block_scale(fmt, c2, c1, mean, jb) : 0.0f;
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -607,7 +607,7 @@ __device__ __forceinline__ void dequant_tile(int64_t bid, const uint8_t *__restr
 //   up to two column reductions out = scale sum_splits part        (the dX call's dB, dA)
 // where W'[n][j] = B[n][j] (forward, B [d x r]) or A[j][n] (dX, A [r x k]).
 struct PrepArgs {
-    bool dq;  // double-quantized block constants (else c1 = fp32 absmax per block)
+    int fmt;  // ScaleFormat of the block constants
     const int8_t *c2;
     const float *c1;
     const float *mean;
@@ -654,7 +654,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a, Nf4Consts tab) {
     int64_t b = blockIdx.x;
     if (b < a.g_shat) {
         const int64_t x = b * 256 + threadIdx.x;
-        if (x < a.nb) a.shat[x] = block_scale(a.dq, a.c2, a.c1, a.dq ? *a.mean : 0.0f, x);
+        if (x < a.nb) a.shat[x] = block_scale(a.fmt, a.c2, a.c1, a.fmt != kNoDq ? *a.mean : 0.0f, x);
         return;
     }
     b -= a.g_shat;
@@ -694,7 +694,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a, Nf4Consts tab) {
     }
     b -= a.g_a + a.g_b;
     if (b < a.g_t) {
-        dequant_tile<DX>(b, a.codes, a.dq, a.c2, a.c1, a.dq ? *a.mean : 0.0f, a.d, a.k, a.ldw, tab, a.wbf);
+        dequant_tile<DX>(b, a.codes, a.fmt, a.c2, a.c1, a.fmt != kNoDq ? *a.mean : 0.0f, a.d, a.k, a.ldw, tab, a.wbf);
         return;
     }
     b -= a.g_t;
@@ -732,7 +732,7 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
     const bool expand = tiles_m == 1;
     if (!core_only) {
         PrepArgs q;
-        q.dq = w.dq != 0;
+        q.fmt = w.fmt;
         q.c2 = w.c2;
         q.c1 = w.c1;
         q.mean = w.mean;

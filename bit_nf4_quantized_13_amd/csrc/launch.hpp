@@ -11,13 +11,13 @@ namespace qnf4 {
 const Nf4Consts &nf4_consts();  // built once on the host (nf4_table.cpp)
 
 // ---- quantize (three kernels) --------------------------------------------
-// dq = 0: the fp32 block absmax goes to c1 (one per block); c2 and mean are unused.
+// fmt = kNoDq: the fp32 block absmax goes to c1 (one per block); c2 and mean are unused.
 hipError_t launch_quantize(const float *W0, int64_t n, uint8_t *codes, int8_t *c2, float *c1,
-                           float *mean, float *absmax_ws, double *group_sum_ws, int dq, hipStream_t s);
+                           float *mean, float *absmax_ws, double *group_sum_ws, int fmt, hipStream_t s);
 
 // ---- standalone double dequant --------------------------------------------
 hipError_t launch_dequantize(const uint8_t *codes, const int8_t *c2, const float *c1,
-                             const float *mean, int dq, int64_t n, uint16_t *out, hipStream_t s);
+                             const float *mean, int fmt, int64_t n, uint16_t *out, hipStream_t s);
 
 // ---- skinny GEMMs ----------------------------------------------------------
 // out[M x R] (fp32) = In[M x K] (bf16) * W[R x K]^T (bf16), R <= 128.  vt: null,
@@ -53,10 +53,10 @@ hipError_t launch_cols_pair(const uint16_t *in0, const uint16_t *vt0, int64_t N0
 struct Nf4Weights {
     const uint8_t *codes;
     const int8_t *c2;
-    const float *c1;    // dq: c1 per group of 256 blocks; else the fp32 absmax per block
-    const float *mean;  // dq only
+    const float *c1;    // double-quantized: c1 per group of 256 blocks; else the fp32 absmax per block
+    const float *mean;  // double-quantized only
     int64_t d, k;
-    int dq;             // 1: double-quantized block constants (c2, c1, mean); 0: fp32 absmax
+    int fmt;            // ScaleFormat (common.hpp): kNoDq, kDqInt8 or kDqFp8
 };
 // Workspace of one dequant-GEMM call: the dequantized block scales
 // (d*k/64 floats) and the adapter operands laid out as extra k-columns,

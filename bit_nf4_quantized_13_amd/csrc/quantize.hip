@@ -17,7 +17,12 @@
 //   2. dq_mean: one workgroup; the same stride-halving tree over the group
 //      sums, then mean = fp32(sum / nb).
 //   3. dq_encode: one workgroup per group; a_g = max|s - mean|, c1 = 127/a_g,
-//      c2 = clamp(rint(c1 (s - mean)), +-127).
+//      c2 = clamp(rint(c1 (s - mean)), +-127).  With c2 in FP8 (the pages
+//      label c2 as FP8; the OCP e4m3 format) the same rule maps a_g to the
+//      largest finite e4m3 value: c1 = 448/a_g, c2 = e4m3(c1 (s - mean)),
+//      round to nearest even.
+// Without double quantization only launch 1 runs, writing the block absmax
+// as the stored scale.
 // With at most 1024 groups (up to 16.7M weights) every dq_encode workgroup
 // runs the mean's tree itself (the same additions in the same order) and
 // launch 2 is skipped; workgroup 0 stores the mean.
@@ -272,7 +277,7 @@ __device__ __forceinline__ float tree_mean(const double *__restrict__ group_sum,
 template <bool INLINE_MEAN>
 __global__ __launch_bounds__(256) void dq_encode(const float *__restrict__ absmax, int64_t nb,
                                                  float *__restrict__ mean_p, const double *__restrict__ group_sum,
-                                                 int64_t groups, int64_t padded,
+                                                 int64_t groups, int64_t padded, int fp8,
                                                  int8_t *__restrict__ c2, float *__restrict__ c1) {
     __shared__ float s_red[4];
     __shared__ double s_tree[256];
@@ -293,13 +298,21 @@ __global__ __launch_bounds__(256) void dq_encode(const float *__restrict__ absma
     if (lane == 0) s_red[wave] = a;
     __syncthreads();
     const float ag = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    float c = 127.0f / ag;
+    // the largest code magnitude: 127 (int8), 448 (the largest finite e4m3 value)
+    const float qmax = fp8 ? 448.0f : 127.0f;
+    float c = qmax / ag;
     const bool zero = (ag == 0.0f) || !__builtin_isfinite(c);
-    if (zero) c = 127.0f;  // an all-zero group stores zeros and a nonzero scale
+    if (zero) c = qmax;  // an all-zero group stores zeros and a nonzero scale
     if (valid) {
-        float q = rintf(c * centred);  // round half to even
-        q = fminf(fmaxf(q, -127.0f), 127.0f);
-        c2[j] = zero ? (int8_t)0 : (int8_t)(int)q;
+        const float p = c * centred;  // one fp32 rounding
+        int8_t code;
+        if (fp8) {
+            code = (int8_t)f32_to_e4m3(fminf(fmaxf(p, -448.0f), 448.0f));
+        } else {
+            const float q = fminf(fmaxf(rintf(p), -127.0f), 127.0f);  // round half to even
+            code = (int8_t)(int)q;
+        }
+        c2[j] = zero ? (int8_t)0 : code;
     }
     if (tid == 0) c1[blockIdx.x] = c;
 }
@@ -307,7 +320,9 @@ __global__ __launch_bounds__(256) void dq_encode(const float *__restrict__ absma
 }  // namespace
 
 hipError_t launch_quantize(const float *W0, int64_t n, uint8_t *codes, int8_t *c2, float *c1,
-                           float *mean, float *absmax_ws, double *group_sum_ws, int dq, hipStream_t s) {
+                           float *mean, float *absmax_ws, double *group_sum_ws, int fmt, hipStream_t s) {
+    const bool dq = fmt != kNoDq;
+    const int fp8 = fmt == kDqFp8 ? 1 : 0;
     const int64_t nb = n / kBlock;
     const int64_t groups = (nb + kGroup - 1) / kGroup;
     int64_t padded = 1;
@@ -319,11 +334,11 @@ hipError_t launch_quantize(const float *W0, int64_t n, uint8_t *codes, int8_t *c
     if (!dq) return hipGetLastError();
     if (padded <= kMeanInline) {
         hipLaunchKernelGGL(dq_encode<true>, dim3((unsigned)groups), dim3(256), 0, s, absmax_ws, nb, mean, group_sum_ws,
-                           groups, padded, c2, c1);
+                           groups, padded, fp8, c2, c1);
     } else {
         hipLaunchKernelGGL(dq_mean, dim3(1), dim3(kMeanThreads), 0, s, group_sum_ws, groups, padded, nb, mean);
         hipLaunchKernelGGL(dq_encode<false>, dim3((unsigned)groups), dim3(256), 0, s, absmax_ws, nb, mean, group_sum_ws,
-                           groups, padded, c2, c1);
+                           groups, padded, fp8, c2, c1);
     }
     return hipGetLastError();
 }

@@ -45,7 +45,8 @@ extern "C" {
 /* ---- status codes ------------------------------------------------------ */
 #define QLORA_OK          0  /* success                                                  */
 #define QLORA_EINVAL      1  /* null pointer, size <= 0, k % block != 0, non-finite alpha */
-#define QLORA_ENOTSUP     2  /* block != 64, dq_block not 256 or 0, r > 128, too large   */
+#define QLORA_ENOTSUP     2  /* block != 64, dq_block not 256 or 0, unknown c2_format,
+                                r > 128, tensor too large                                */
 #define QLORA_EALIGN      3  /* a pointer read/written with 128-bit accesses is not 16-byte aligned */
 #define QLORA_EWORKSPACE  4  /* workspace NULL or smaller than the *_workspace() size     */
 #define QLORA_EHIP        5  /* a HIP launch or runtime error (hipGetLastError)          */
@@ -55,6 +56,9 @@ extern "C" {
 #define QLORA_NF4_NO_DQ     0    /* dq_block value of the format without double quantization: one fp32
                                     absmax per block (chkda, the bits-per-weight accounting after
                                     "Double quantization and double dequantization": 4.5 bits/weight) */
+#define QLORA_C2_INT8       0    /* c2_format: c2 as int8, Int8 absmax rule (127)                        */
+#define QLORA_C2_FP8_E4M3   1    /* c2_format: c2 as OCP FP8 e4m3 bytes (the "c2_FP8" of chkda's
+                                    doubleDequant(c1_FP32, c2_FP8, W_NF4)), absmax rule with 448    */
 #define QLORA_MAX_RANK      128
 
 typedef uint16_t qlora_bf16; /* raw bfloat16 bits */
@@ -73,6 +77,12 @@ typedef uint16_t qlora_bf16; /* raw bfloat16 bits */
  *   absmax_mean  float [1]    the mean of the nb block absmax values
  *   d, k                      W0 shape, d >= 1, k >= 1, k % block == 0
  *   block, dq_block           64, and 256 (or QLORA_NF4_NO_DQ, below)
+ *   c2_format                 QLORA_C2_INT8 (0) or QLORA_C2_FP8_E4M3: how the
+ *                             c2 bytes encode their values (ignored without
+ *                             double quantization)
+ * With QLORA_C2_FP8_E4M3 each c2 byte is an OCP FP8 e4m3 value (sign, 4
+ * exponent bits with bias 7, 3 mantissa bits; largest finite 448) read
+ * exactly as fp32, and c1 = 448 / max|s - mean| per group.
  * With dq_block == QLORA_NF4_NO_DQ the block constants are not double
  * quantized (the "before" format of the same page's bits-per-weight
  * accounting): absmax_scale holds the fp32 absmax of each block, [nb]
@@ -86,6 +96,7 @@ typedef struct {
     float   *absmax_mean;
     int64_t  d, k;
     int32_t  block, dq_block;
+    int32_t  c2_format;
 } qlora_nf4_weight;
 
 /* Bytes of device workspace qlora_nf4_quantize needs for this shape
@@ -100,7 +111,10 @@ size_t qlora_nf4_quantize_workspace(int64_t d, int64_t k, int32_t block, int32_t
  * exact-zero level); "Double quantization and double dequantization" with the
  * Int8 absmax rule of "First, how does k-bit quantization work?": the block
  * scales minus their mean are quantized to int8 per group of 256 with
- * c1 = 127 / max|s - mean| (a zero group stores zeros and c1 = 127).
+ * c1 = 127 / max|s - mean| (a zero group stores zeros and c1 = 127).  With
+ * c2_format == QLORA_C2_FP8_E4M3: c1 = 448 / max|s - mean| (448 for a zero
+ * group) and c2 = e4m3(fp32(c1 (s - mean))), round to nearest, ties to the
+ * even code.
  *   W0  device fp32 [d x k], 16-byte aligned, read only.
  *   w   host struct: shape fields and the four output arrays (all written;
  *       without double quantization only codes and the per-block absmax).
@@ -114,7 +128,8 @@ int qlora_nf4_quantize(const float *W0, const qlora_nf4_weight *w,
 /*
  * qlora_nf4_dequantize -- doubleDequant into a dense bf16 matrix.
  * chkda, "Double quantization and double dequantization":
- *   scale[j] = fp32(c2[j] / c1[j/256]) + mean          (IEEE fp32 ops)
+ *   scale[j] = fp32(c2[j] / c1[j/256]) + mean          (IEEE fp32 ops; c2[j]
+ *                                                       its int8 or e4m3 value)
  *   W[i]     = BF16(C[code[i]] * scale[i/64])          (one RNE rounding)
  * (without double quantization scale[j] is the stored fp32 absmax of block j).
  *   W_out  device bf16 [d x k], 16-byte aligned, written.
@@ -246,7 +261,7 @@ const char *qlora_status_str(int status);
 
 /* ABI version of this header/library pair. */
 int qlora_abi_version(void);
-#define QLORA_ABI_VERSION 1
+#define QLORA_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

@@ -19,6 +19,8 @@ Everything here follows chkda.github.io "Why do we need LoRA and QLoRA?":
   quantize_single    the same page's bits-per-weight accounting ("before" double
   dequantize_single  quantization): one fp32 absmax per block, stored as is,
                      W[i] = BF16(C[W[i]] * absmax[i//64]).
+  e4m3_*, fp8_*      the same section's c2_FP8 label, as a second c2 format
+                     (reading R16).
   double_quantize    "Double quantization and double dequantization": the block
   double_dequantize  scales are quantized to 8 bits in groups of 256 with one
                      fp32 second-level scale per group, after subtracting a
@@ -51,6 +53,13 @@ notes):
      -> c1 = 127 and c2 = 0 for the group.
   R7 dequantized scale: fl32(fl32(c2 / c1) + mean) with IEEE division.
   R8 BF16(.) is one round-to-nearest-even of the fp32 product.
+  R16 c2 in FP8: the pages write doubleDequant(c1_FP32, c2_FP8, W_NF4); as a
+     second format c2 is stored as OCP FP8 e4m3 (1 sign, 4 exponent bits with
+     bias 7, 3 mantissa bits, subnormals, no infinities, S.1111.111 = NaN,
+     largest finite 448).  The absmax rule of R6 with 448 in place of 127:
+     c1 = fl32(448 / a_g), c2 = the e4m3 value nearest fl32(c1 (s - mean))
+     (clamped to +-448), ties to the even code; a_g = 0 or a non-finite c1 ->
+     c1 = 448, c2 = +0.  Its value enters R7 exactly.
 """
 from __future__ import annotations
 
@@ -63,6 +72,8 @@ P_MAX = 0.967705          # reading R1
 BLOCK = 64                # chkda "Quantizing and dequantizing with the codebook"
 DQ_BLOCK = 256            # chkda "Double quantization and double dequantization"
 INT8_Q = 127              # chkda "First, how does k-bit quantization work?"
+FP8_MAX = 448.0           # largest finite OCP e4m3 value (reading R16)
+C2_FORMATS = ("int8", "fp8")
 
 
 # ----------------------------------------------------------------------------
@@ -219,6 +230,64 @@ def int8_dequantize(q: np.ndarray, c: np.float32) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# OCP FP8 e4m3 (reading R16)
+# ----------------------------------------------------------------------------
+def e4m3_values() -> np.ndarray:
+    """The value of each of the 256 e4m3 codes (float64; NaN for S.1111.111).
+
+    Code = sign << 7 | E << 3 | m: E = 0 gives (m / 8) 2^-6, else (1 + m/8) 2^(E - 7).
+    """
+    out = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        sign = -1.0 if code & 0x80 else 1.0
+        e, m = (code >> 3) & 15, code & 7
+        if e == 15 and m == 7:
+            out[code] = np.nan
+        elif e == 0:
+            out[code] = sign * (m / 8.0) * 2.0 ** -6
+        else:
+            out[code] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return out
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """Nearest e4m3 code of each fp32 value, ties to the even code; magnitudes
+    above 448 become 448 first.  The sign bit is the sign of x (-0 -> 0x80)."""
+    x = np.asarray(x, dtype=np.float32)
+    a = np.minimum(np.abs(x).astype(np.float64), FP8_MAX)
+    vals = e4m3_values()[:127]                      # codes 0 .. 126: 0 .. 448, increasing
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    d_lo, d_hi = a - vals[lo], vals[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return (code | (np.signbit(x).astype(np.uint8) << np.uint8(7))).astype(np.uint8)
+
+
+def fp8_absmax_quantize(x: np.ndarray) -> tuple[np.ndarray, np.float32]:
+    """The absmax rule with FP8's 448: c = fl32(448 / absmax), q = e4m3(fl32(c x)).
+
+    An all-zero input (or a non-finite c) stores +0 codes and c = 448 (R16).
+    Returns (uint8 e4m3 codes, c).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    a = np.float32(np.abs(x).max()) if x.size else np.float32(0)
+    with np.errstate(divide="ignore", over="ignore"):
+        c = np.float32(FP8_MAX) / a if a != 0 else np.float32(np.inf)
+    if a == 0 or not np.isfinite(c):
+        return np.zeros(x.shape, dtype=np.uint8), np.float32(FP8_MAX)
+    return e4m3_encode((c * x).astype(np.float32)), np.float32(c)
+
+
+def c2_values(c2: np.ndarray, c2_format: str = "int8") -> np.ndarray:
+    """The fp32 value of stored c2 bytes (int8, or e4m3 bit patterns)."""
+    c2 = np.asarray(c2)
+    if c2_format == "fp8":
+        return e4m3_values()[c2.view(np.uint8).astype(np.int64)].astype(np.float32)
+    return c2.astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
 # double quantization (chkda "Double quantization and double dequantization")
 # ----------------------------------------------------------------------------
 def tree_sum_f64(values: np.ndarray) -> np.float64:
@@ -250,39 +319,44 @@ def scales_mean(scale: np.ndarray, dq_block: int = DQ_BLOCK) -> np.float32:
     return np.float32(total / np.float64(nb))
 
 
-def double_quantize(scale: np.ndarray, dq_block: int = DQ_BLOCK):
-    """Quantize the block scales: returns (c2 int8[nb], c1 float32[G], mean float32).
+def double_quantize(scale: np.ndarray, dq_block: int = DQ_BLOCK, c2_format: str = "int8"):
+    """Quantize the block scales: returns (c2 [nb], c1 float32[G], mean float32).
 
-    Each group of ``dq_block`` centred scales (fl32(s - mean)) is Int8-absmax
-    quantized with its own fp32 second-level scale c1 (reading R6).
+    Each group of ``dq_block`` centred scales (fl32(s - mean)) is absmax
+    quantized with its own fp32 second-level scale c1: Int8 (reading R6, c2
+    int8) or FP8 e4m3 (reading R16, c2 uint8 bit patterns).
     """
+    assert c2_format in C2_FORMATS
     s = np.asarray(scale, dtype=np.float32).reshape(-1)
     nb = s.size
     mean = scales_mean(s, dq_block)
     centred = (s - mean).astype(np.float32)
     g = -(-nb // dq_block)
-    c2 = np.zeros(nb, dtype=np.int8)
+    fp8 = c2_format == "fp8"
+    c2 = np.zeros(nb, dtype=np.uint8 if fp8 else np.int8)
     c1 = np.zeros(g, dtype=np.float32)
+    quant = fp8_absmax_quantize if fp8 else int8_absmax_quantize
     for i in range(g):
-        q, c = int8_absmax_quantize(centred[i * dq_block:(i + 1) * dq_block])
+        q, c = quant(centred[i * dq_block:(i + 1) * dq_block])
         c2[i * dq_block:(i + 1) * dq_block] = q
         c1[i] = c
     return c2, c1, mean
 
 
-def double_dequantize_scales(c2: np.ndarray, c1: np.ndarray, mean, dq_block: int = DQ_BLOCK) -> np.ndarray:
+def double_dequantize_scales(c2: np.ndarray, c1: np.ndarray, mean, dq_block: int = DQ_BLOCK,
+                             c2_format: str = "int8") -> np.ndarray:
     """scales[j] = dequant(c2[j], c1[j // dq_block]) + mean, all in fp32 (R7)."""
     c2 = np.asarray(c2).reshape(-1)
     group = np.arange(c2.size) // dq_block
-    q = (c2.astype(np.float32) / np.asarray(c1, dtype=np.float32)[group]).astype(np.float32)
+    q = (c2_values(c2, c2_format) / np.asarray(c1, dtype=np.float32)[group]).astype(np.float32)
     return (q + np.float32(mean)).astype(np.float32)
 
 
 def double_dequantize(packed: np.ndarray, c2: np.ndarray, c1: np.ndarray, mean, n: int,
-                      block: int = BLOCK, dq_block: int = DQ_BLOCK) -> np.ndarray:
+                      block: int = BLOCK, dq_block: int = DQ_BLOCK, c2_format: str = "int8") -> np.ndarray:
     """doubleDequant: W[i] = BF16(C[W[i]] * scales[i // block]); uint16 bits [n]."""
     codes = unpack_codes(packed, n)
-    shat = double_dequantize_scales(c2, c1, mean, dq_block)
+    shat = double_dequantize_scales(c2, c1, mean, dq_block, c2_format)
     blk = np.arange(n) // block
     prod = (nf4_codebook()[codes] * shat[blk]).astype(np.float32)  # one fp32 multiply
     return bf16_rne_bits(prod)
@@ -291,21 +365,24 @@ def double_dequantize(packed: np.ndarray, c2: np.ndarray, c1: np.ndarray, mean, 
 # ----------------------------------------------------------------------------
 # the whole storage format
 # ----------------------------------------------------------------------------
-def quantize(w0: np.ndarray, block: int = BLOCK, dq_block: int = DQ_BLOCK) -> dict:
+def quantize(w0: np.ndarray, block: int = BLOCK, dq_block: int = DQ_BLOCK, c2_format: str = "int8") -> dict:
     """NF4 + double quantization of W0 [d x k] (fp32).
 
     Returns a dict with packed codes (uint8[N/2]), codes (uint8[N]), the exact
-    block scales (float32[nb]), c2 (int8[nb]), c1 (float32[G]), mean (float32).
+    block scales (float32[nb]), c2 ([nb]: int8, or uint8 e4m3 bit patterns),
+    c1 (float32[G]), mean (float32) and the c2 format.
     """
     codes, scale = quantize_blocks(w0, block)
-    c2, c1, mean = double_quantize(scale, dq_block)
+    c2, c1, mean = double_quantize(scale, dq_block, c2_format)
     return {"codes": codes, "packed": pack_codes(codes), "absmax": scale,
-            "c2": c2, "c1": c1, "mean": np.float32(mean), "n": int(np.asarray(w0).size)}
+            "c2": c2, "c1": c1, "mean": np.float32(mean), "n": int(np.asarray(w0).size),
+            "c2_format": c2_format}
 
 
 def dequantize(q: dict, shape=None, block: int = BLOCK, dq_block: int = DQ_BLOCK) -> np.ndarray:
     """bf16 bits of the double-dequantized weights, optionally reshaped."""
-    bits = double_dequantize(q["packed"], q["c2"], q["c1"], q["mean"], q["n"], block, dq_block)
+    bits = double_dequantize(q["packed"], q["c2"], q["c1"], q["mean"], q["n"], block, dq_block,
+                             q.get("c2_format", "int8"))
     return bits.reshape(shape) if shape is not None else bits
 
 

@@ -178,6 +178,41 @@ def test_no_double_quant_format_validation():
         assert quant(weight(dq=q.NO_DQ, c2=None, mean=FAKE + 1)) == q.QLORA_EHIP
 
 
+def test_c2_format_validation():
+    lib = q.library()
+    assert quant(weight(dq=q.DQ_BLOCK)) != q.QLORA_ENOTSUP
+    w = weight()
+    w.c2_format = 2
+    assert quant(w) == q.QLORA_ENOTSUP
+    w.c2_format = -1
+    assert fwd(w=w) == q.QLORA_ENOTSUP
+    assert lib.qlora_nf4_dequantize(ctypes.byref(w), FAKE, None) == q.QLORA_ENOTSUP
+    w.c2_format = q.C2_FP8_E4M3
+    assert lib.qlora_nf4_dequantize(ctypes.byref(w), FAKE_MIS, None) == q.QLORA_EALIGN
+
+
+def test_weight_struct_layout_matches_the_header(tmp_path):
+    """The binding's ctypes struct has the header's size and field offsets
+    (compiled with the host C compiler)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    inc = os.path.join(ROOT, "include")
+    fields = [f[0] for f in q._CWeight._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"qlora_nf4.h\"\nint main(void){\n"
+                   + f'printf("%zu\\n", sizeof(qlora_nf4_weight));\n'
+                   + "".join(f'printf("%zu\\n", offsetof(qlora_nf4_weight, {f}));\n' for f in fields)
+                   + "return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(q._CWeight)
+    assert got[1:] == [getattr(q._CWeight, f).offset for f in fields]
+
+
 def gemm_only(w=None, backward=0, a=FAKE, m=64, r=8, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
     w = w or weight()
     return q.library().qlora_linear_gemm_only(ctypes.byref(w), backward, a, m, r, out, ws, ws_bytes, None)

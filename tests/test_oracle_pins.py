@@ -282,6 +282,79 @@ def test_double_dequant_error_bound():
 
 
 # ----------------------------------------------------------------------------
+# c2 in FP8 (OCP e4m3) -- chkda "Double quantization and double
+# dequantization" labels c2 as FP8 (reading R16)
+# ----------------------------------------------------------------------------
+def test_e4m3_closed_form_values():
+    v = nf4.e4m3_values()
+    assert v[0x00] == 0.0 and np.signbit(v[0x80])
+    assert v[0x01] == 2.0 ** -9 and v[0x07] == 7 * 2.0 ** -9        # subnormals m 2^-9
+    assert v[0x08] == 2.0 ** -6                                      # smallest normal
+    assert v[0x38] == 1.0 and v[0x40] == 2.0 and v[0x3C] == 1.5
+    assert v[0x7E] == 448.0 == nf4.FP8_MAX and np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+    assert np.all(np.diff(v[:127]) > 0)                              # codes 0..126 increasing
+    assert np.array_equal(v[0x80:0xFF], -v[:127])
+
+
+def test_e4m3_against_torch_float8_e4m3fn():
+    # torch's CPU float8_e4m3fn is an independent implementation of the same
+    # OCP format: decoding of all 256 codes, and round-to-nearest-even encoding
+    # of in-range values (torch does not saturate above 448, the oracle clamps)
+    v = nf4.e4m3_values()
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(v), np.isnan(t)) and np.array_equal(v[~np.isnan(v)], t[~np.isnan(t)])
+    rng = np.random.default_rng(25)
+    x = (rng.standard_normal(100000) * np.exp(rng.uniform(-14, 6.5, 100000))).astype(np.float32)
+    vals = v[:127]
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)           # exact ties
+    x = np.concatenate([x, mids, -mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e4)),
+                        vals.astype(np.float32), np.float32([0.0, -0.0, 448.0, -448.0])])
+    x = x[np.abs(x) <= 448]
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(nf4.e4m3_encode(x), want)
+    assert np.all(nf4.e4m3_encode(np.float32([460.0, 1e6, -1e6])) == [0x7E, 0x7E, 0xFE])
+
+
+def test_fp8_double_quant_largest_maps_to_448_and_error_bound():
+    w = random_weights(26, (64, 64 * 64))
+    q = nf4.quantize(w, c2_format="fp8")
+    assert q["c2"].dtype == np.uint8
+    s = q["absmax"].astype(np.float64)
+    x = (q["absmax"] - q["mean"]).astype(np.float32)
+    vals = nf4.c2_values(q["c2"], "fp8").astype(np.float64)
+    for g in range(q["c1"].size):
+        sl = slice(256 * g, 256 * (g + 1))
+        a = np.abs(x[sl]).max()
+        assert q["c1"][g] == np.float32(448.0) / np.float32(a)        # the absmax rule with 448
+        assert np.abs(vals[sl]).max() == 448.0                        # the largest maps to 448
+    shat = nf4.double_dequantize_scales(q["c2"], q["c1"], q["mean"], c2_format="fp8").astype(np.float64)
+    c1 = q["c1"].astype(np.float64)[np.arange(s.size) // 256]
+    eps = 2.0 ** -23
+    # 3 mantissa bits: half an ulp is 2^-4 relative (2^-10 absolute below 2^-6)
+    bound = (2.0 ** -4 * np.abs(x) * (1 + 4 * eps) + 2.0 ** -10 / c1
+             + 4 * eps * (np.abs(s) + np.abs(float(q["mean"]))))
+    assert np.all(np.abs(shat - s) <= bound)
+    # the Int8 format on the same scales has a uniform step 1/c1: FP8 is finer near the mean
+    q8 = nf4.quantize(w)
+    e8 = np.abs(nf4.double_dequantize_scales(q8["c2"], q8["c1"], q8["mean"]).astype(np.float64) - s)
+    small = np.abs(x) < np.abs(x).max() / 16
+    assert np.abs(shat - s)[small].mean() < e8[small].mean()
+
+
+def test_fp8_zero_group_and_dequant_path():
+    c2, c1, mean = nf4.double_quantize(np.full(300, 0.5, np.float32), c2_format="fp8")
+    assert np.all(c2 == 0) and np.all(c1 == np.float32(448)) and mean == np.float32(0.5)
+    w = random_weights(27, (8, 64 * 40))
+    q = nf4.quantize(w, c2_format="fp8")
+    bits = nf4.dequantize(q)
+    # the same doubleDequant with the c2 values written out as fp32 by hand
+    sh = ((nf4.e4m3_values()[q["c2"].astype(np.int64)].astype(np.float32)
+           / q["c1"][np.arange(q["c2"].size) // 256]).astype(np.float32) + q["mean"]).astype(np.float32)
+    prod = (nf4.nf4_codebook()[q["codes"]] * sh[np.arange(w.size) // 64]).astype(np.float32)
+    assert np.array_equal(bits, nf4.bf16_rne_bits(prod))
+
+
+# ----------------------------------------------------------------------------
 # the format without double quantization -- chkda "Double quantization and
 # double dequantization", the bits-per-weight accounting ("before")
 # ----------------------------------------------------------------------------
