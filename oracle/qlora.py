@@ -28,6 +28,21 @@ upstream gradient dY [M x d] of a loss L(Y):
 There is no dW.  These are the closed-form derivatives of Y above; the tests
 pin them with central finite differences.
 
+Adapter dropout (fromzero2ai "Python Implementation: Fine-Tuning with PEFT
+and BitsAndBytes" trains with a LoRA dropout rate of 0.05; chkda "Merging LoRA
+weights for inference" notes the two-path form equals the merged one only with
+dropout disabled).  Reading R17: dropout acts on the adapter's input only,
+
+    Xd = drop(X)                   [M x k]  (bf16: x c kept, +0 dropped)
+    U  = Xd A^T,   Y = X What^T + s U B^T
+    dA = s G^T Xd, dB = s dY^T U,  dX = dY What + c (M o (s G A))
+
+with c = fl32(1 / fl32(1 - p)) and the keep mask M drawn by Philox4x32-10
+(Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3",
+SC 2011) from a 64-bit seed: element i = m k + col uses word i mod 4 of the
+block for counter (i div 4 as two 32-bit words, 0, 0) and key (seed low, seed
+high); it is dropped iff that word < floor(p 2^32).
+
 Merge (chkda "Merging LoRA weights for inference"): W_merged = W0 + s B A,
 in fp64 (merged_weight) and as bf16 under the library's fixed rounding
 (merged_weight_bf16, reading R14: the sum over ranks in fp64 in ascending
@@ -125,3 +140,85 @@ def forward_flops(m: int, d: int, k: int, r: int) -> int:
 def backward_flops(m: int, d: int, k: int, r: int) -> int:
     """dX base GEMM plus G, s G A, dA and dB (U is saved by the forward)."""
     return 2 * m * d * k + 4 * m * r * (d + k)
+
+
+# ----------------------------------------------------------------------------
+# adapter dropout (reading R17)
+# ----------------------------------------------------------------------------
+PHILOX_M = (0xD2511F53, 0xCD9E8D57)   # Philox4x32 round multipliers
+PHILOX_W = (0x9E3779B9, 0xBB67AE85)   # Philox4x32 key increments (Weyl sequence)
+
+
+def philox4x32_10(ctr: np.ndarray, key: tuple[int, int]) -> np.ndarray:
+    """Philox4x32 with 10 rounds on an array of counters [n x 4] (uint32).
+
+    A round multiplies counter words 0 and 2 by the two constants (64-bit
+    products), and the new counter is (hi(w2 M1) ^ c1 ^ k0, lo(w2 M1),
+    hi(w0 M0) ^ c3 ^ k1, lo(w0 M0)); the key gains the Weyl increments
+    between rounds.  Returns [n x 4] uint32.
+    """
+    c = [np.asarray(ctr, dtype=np.uint64)[:, i].copy() for i in range(4)]
+    k0, k1 = int(key[0]) & 0xFFFFFFFF, int(key[1]) & 0xFFFFFFFF
+    lo32 = np.uint64(0xFFFFFFFF)
+    for rnd in range(10):
+        if rnd:
+            k0 = (k0 + PHILOX_W[0]) & 0xFFFFFFFF
+            k1 = (k1 + PHILOX_W[1]) & 0xFFFFFFFF
+        p0 = c[0] * np.uint64(PHILOX_M[0])
+        p1 = c[2] * np.uint64(PHILOX_M[1])
+        c = [(p1 >> np.uint64(32)) ^ c[1] ^ np.uint64(k0), p1 & lo32,
+             (p0 >> np.uint64(32)) ^ c[3] ^ np.uint64(k1), p0 & lo32]
+    return np.stack(c, axis=1).astype(np.uint32)
+
+
+def dropout_threshold(p: float) -> int:
+    """floor(p 2^32) for the fp32 value of p in [0, 1)."""
+    p = float(np.float32(p))
+    assert 0.0 <= p < 1.0
+    return int(np.floor(p * 2.0 ** 32))
+
+
+def dropout_scale(p: float) -> np.float32:
+    """c = fl32(1 / fl32(1 - p)), the inverse keep probability."""
+    return np.float32(np.float32(1.0) / np.float32(np.float32(1.0) - np.float32(p)))
+
+
+def dropout_keep_mask(m: int, k: int, p: float, seed: int) -> np.ndarray:
+    """Keep mask [m x k] (bool) of reading R17."""
+    n = m * k
+    blocks = np.arange((n + 3) // 4, dtype=np.uint64)
+    ctr = np.zeros((blocks.size, 4), dtype=np.uint64)
+    ctr[:, 0] = blocks & np.uint64(0xFFFFFFFF)
+    ctr[:, 1] = blocks >> np.uint64(32)
+    words = philox4x32_10(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)).reshape(-1)[:n]
+    return (words.astype(np.uint64) >= np.uint64(dropout_threshold(p))).reshape(m, k)
+
+
+def lora_dropout_bits(x_bits: np.ndarray, p: float, seed: int) -> tuple[np.ndarray, np.ndarray]:
+    """Xd as bf16 bits: bf16(fl32(x c)) where kept, +0 where dropped; and the mask."""
+    from .nf4 import bf16_bits_to_f32, bf16_rne_bits
+    m, k = x_bits.shape
+    keep = dropout_keep_mask(m, k, p, seed)
+    xs = (bf16_bits_to_f32(x_bits) * dropout_scale(p)).astype(np.float32)   # one fp32 rounding
+    out = bf16_rne_bits(xs)
+    out[~keep] = 0
+    return out, keep
+
+
+def forward_dropout(w_hat, x, xd, a, b, alpha: float) -> tuple[np.ndarray, np.ndarray]:
+    """(Y, U) with dropout on the adapter input: U = Xd A^T, Y = X What^T + s U B^T."""
+    w_hat, x, xd, a, b = _f64(w_hat), _f64(x), _f64(xd), _f64(a), _f64(b)
+    s = adapter_scale(alpha, a.shape[0])
+    u = xd @ a.T
+    return x @ w_hat.T + s * (u @ b.T), u
+
+
+def backward_dropout(w_hat, xd, keep, dy, a, b, alpha: float, p: float):
+    """(dX, dA, dB) of forward_dropout (keep: the mask, c = dropout_scale(p))."""
+    w_hat, xd, dy, a, b = _f64(w_hat), _f64(xd), _f64(dy), _f64(a), _f64(b)
+    s = adapter_scale(alpha, a.shape[0])
+    c = float(dropout_scale(p))
+    u = xd @ a.T
+    g = dy @ b
+    dx = dy @ w_hat + c * np.where(keep, s * (g @ a), 0.0)
+    return dx, s * (g.T @ xd), s * (dy.T @ u)

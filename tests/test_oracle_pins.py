@@ -355,6 +355,108 @@ def test_fp8_zero_group_and_dequant_path():
 
 
 # ----------------------------------------------------------------------------
+# adapter dropout (reading R17): Philox4x32-10 and the dropout layer
+# ----------------------------------------------------------------------------
+def _philox_scalar(ctr, key, width):
+    """Philox4xW-10 on Python ints, for W = 32 (the dropout generator) and
+    W = 64 (numpy's Philox): one counter at a time, written from the round
+    definition independently of the vectorized oracle."""
+    mask = (1 << width) - 1
+    mult = {32: (0xD2511F53, 0xCD9E8D57), 64: (0xD2E7470EE14C6C93, 0xCA5A826395121157)}[width]
+    weyl = {32: (0x9E3779B9, 0xBB67AE85), 64: (0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B)}[width]
+    c, k = list(ctr), list(key)
+    for rnd in range(10):
+        if rnd:
+            k = [(k[0] + weyl[0]) & mask, (k[1] + weyl[1]) & mask]
+        p0, p1 = mult[0] * c[0], mult[1] * c[2]
+        c = [(p1 >> width) ^ c[1] ^ k[0], p1 & mask, (p0 >> width) ^ c[3] ^ k[1], p0 & mask]
+    return c
+
+
+def test_philox4x32_known_answers():
+    for name, *words in (line.split() for line in read_golden("philox_kat.txt")):
+        v = [int(w, 16) for w in words]
+        got = qlora.philox4x32_10(np.array([v[:4]], np.uint64), (v[4], v[5]))[0]
+        assert [int(g) for g in got] == v[6:], name
+        assert _philox_scalar(v[:4], v[4:6], 32) == v[6:], name
+
+
+def test_philox_rounds_match_numpy_philox4x64():
+    # numpy's Philox bit generator is Philox4x64-10; it advances its counter
+    # before each block, so its block j comes from counter + j + 1
+    for key, ctr0 in (((0, 0), 0), ((0x0123456789ABCDEF, 42), 7), ((2**64 - 1, 5), 2**64 - 3)):
+        bg = np.random.Philox(key=np.array(key, dtype=np.uint64),
+                              counter=np.array([ctr0, 0, 0, 0], dtype=np.uint64))
+        raw = [int(v) for v in bg.random_raw(12)]
+        for j in range(3):
+            c = ctr0 + j + 1
+            ctr = [c & (2**64 - 1), c >> 64, 0, 0]
+            assert _philox_scalar(ctr, list(key), 64) == raw[4 * j:4 * j + 4]
+
+
+def test_philox4x32_vectorized_equals_scalar():
+    rng = np.random.default_rng(28)
+    ctr = rng.integers(0, 2**32, (64, 4), dtype=np.uint64)
+    key = (int(rng.integers(0, 2**32)), int(rng.integers(0, 2**32)))
+    got = qlora.philox4x32_10(ctr, key)
+    for i in range(64):
+        assert [int(g) for g in got[i]] == _philox_scalar([int(c) for c in ctr[i]], list(key), 32)
+
+
+def test_dropout_mask_layout_rate_and_edges():
+    m, k, seed = 48, 1024, 0x1234_5678_9ABC
+    keep = qlora.dropout_keep_mask(m, k, 0.05, seed)
+    # element i uses word i % 4 of the block for counter i // 4 (low, high words)
+    for i in (0, 1, 2, 3, 4, 4097, m * k - 1):
+        blk = i // 4
+        w = _philox_scalar([blk & 0xFFFFFFFF, blk >> 32, 0, 0], [seed & 0xFFFFFFFF, seed >> 32], 32)[i % 4]
+        assert keep.reshape(-1)[i] == (w >= qlora.dropout_threshold(0.05))
+    for p in (0.05, 0.3, 0.5):
+        frac = 1.0 - qlora.dropout_keep_mask(m, k, p, seed + 1).mean()
+        assert abs(frac - p) < 5 * np.sqrt(p * (1 - p) / (m * k))
+    assert qlora.dropout_keep_mask(m, k, 0.0, seed).all()
+    assert qlora.dropout_threshold(0.5) == 2**31 and qlora.dropout_threshold(0.0) == 0
+    assert qlora.dropout_scale(0.5) == np.float32(2.0) and qlora.dropout_scale(0.0) == np.float32(1.0)
+    assert not np.array_equal(keep, qlora.dropout_keep_mask(m, k, 0.05, seed + 1))
+
+
+def test_lora_dropout_values():
+    x = make_layer(29, 0, 8, 512, 32, 4).x
+    xd, keep = qlora.lora_dropout_bits(x, 0.0, 5)
+    assert keep.all() and np.array_equal(xd, x)                    # p = 0: the identity
+    xd, keep = qlora.lora_dropout_bits(x, 0.1, 5)
+    assert np.all(xd[~keep] == 0)
+    xs, ref = bf16_bits_as_f32(xd)[keep].astype(np.float64), bf16_bits_as_f32(x)[keep].astype(np.float64) / 0.9
+    assert np.all(np.abs(xs - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)  # one bf16 rounding of x / (1 - p)
+
+
+def test_dropout_backward_central_finite_differences():
+    rng = np.random.default_rng(30)
+    m, d, k, r, alpha, p = 5, 6, 8, 3, 12.0, 0.25
+    w = rng.standard_normal((d, k))
+    a, b, x, dy = (rng.standard_normal(sh) for sh in ((r, k), (d, r), (m, k), (m, d)))
+    keep = qlora.dropout_keep_mask(m, k, p, 77)
+    c = float(qlora.dropout_scale(p))
+
+    def loss(x_, a_, b_):
+        y, _ = qlora.forward_dropout(w, x_, c * keep * x_, a_, b_, alpha)
+        return float(np.sum(y * dy))
+    dx, da, db = qlora.backward_dropout(w, c * keep * x, keep, dy, a, b, alpha, p)
+    h = 1e-6
+    for arr, grad, f in ((x, dx, lambda t: loss(t, a, b)), (a, da, lambda t: loss(x, t, b)),
+                         (b, db, lambda t: loss(x, a, t))):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            e = np.zeros_like(arr)
+            e[idx] = h
+            num[idx] = (f(arr + e) - f(arr - e)) / (2 * h)
+        assert np.allclose(grad, num, rtol=1e-6, atol=1e-6)
+    y0, u0 = qlora.forward_dropout(w, x, x, a, b, alpha)               # p = 0 reduces to the plain layer
+    y1, u1 = qlora.forward(w, x, a, b, alpha)
+    assert np.allclose(y0, y1, rtol=1e-13, atol=1e-12) and np.allclose(u0, u1, rtol=1e-13, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
 # the format without double quantization -- chkda "Double quantization and
 # double dequantization", the bits-per-weight accounting ("before")
 # ----------------------------------------------------------------------------
