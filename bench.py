@@ -341,6 +341,34 @@ def run_format_bench(q, torch, ctx, fmt, iters=20):
                                         "hbm_frac": round(alg / (dec_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
 
 
+def run_dropout_bench(q, torch, ctx, p=0.05, iters=20):
+    """Forward + backward of the layer4096 inputs with adapter dropout (rate p,
+    as in the pages' training configuration), and qlora_lora_dropout alone."""
+    from workloads import workload_layer
+    from tests.helpers import to_dev_bf16
+    w, x, a, b, alpha, y, u, lws, r = ctx
+    inp = workload_layer("layer4096")
+    m, d, k = inp.x.shape[0], w.d, w.k
+    dy = to_dev_bf16(inp.dy)
+    ws = torch.empty(q.linear_workspace_bytes(m, d, k, r, dropout=True), dtype=torch.uint8, device="cuda")
+    dx = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
+    da = torch.empty((r, k), dtype=torch.float32, device="cuda")
+    db = torch.empty((d, r), dtype=torch.float32, device="cuda")
+    xd = torch.empty_like(x)
+    log(f"dropout p={p}: layer4096 fwd+bwd")
+
+    def fwd_bwd():
+        q.qlora_linear_fwd(w, x, a, b, alpha, out=y, u_out=u, workspace=ws, dropout=p, seed=1234)
+        q.qlora_linear_bwd(w, x, dy, a, b, alpha, u=u, workspace=ws, outs=(dx, da, db), dropout=p, seed=1234)
+    fb_ms = time_calls(torch, fwd_bwd, iters)
+    drop_ms = time_calls(torch, lambda: q.qlora_lora_dropout(x, p, 1234, out=xd), iters)
+    flops = fwd_flops(m, d, k, r) + bwd_flops(m, d, k, r)
+    return {"p": p, "fwd_bwd_ms": round(fb_ms, 4), "fwd_bwd_tflops": round(flops / (fb_ms * 1e-3) / 1e12, 3),
+            "lora_dropout_us": round(drop_ms * 1e3, 2),
+            "lora_dropout_gbs": round(4 * m * k / (drop_ms * 1e-3) / 1e9, 1),
+            "workload": f"layer4096, M={m}, r={r}"}
+
+
 def decode_bytes(m, d, k, r):
     """Algorithmic HBM bytes of one decode forward: packed codes, 8-bit block
     constants, fp32 group constants and mean, x, A, B, Y."""
@@ -470,6 +498,7 @@ def main():
     merge = run_merge_bench(q, torch, ctx)
     decode = None if args.skip_decode else run_decode_bench(q, torch)
     formats = None if args.skip_decode else {f: run_format_bench(q, torch, ctx, f) for f in ("no_dq", "fp8")}
+    dropout = None if args.skip_decode else run_dropout_bench(q, torch, ctx)
     cpu = None
     if not args.skip_cpu_baseline:
         log("cpu baseline: timing the oracle on a bounded sample")
@@ -490,6 +519,7 @@ def main():
         "decode_roofline": None if decode is None else decode_roofline(decode),
         "adapter_merge": merge,
         "other_formats": formats,
+        "adapter_dropout": dropout,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -67,6 +67,12 @@ _SIGS = {
     "qlora_linear_gemm_only": (ctypes.c_int, [_WP, _I32, _P, _I64, _I32, _P, _P, _SZ, _P]),
     "qlora_adapter_merge": (ctypes.c_int, [_WP, _P, _P, _I32, ctypes.c_float, _P, _P]),
     "qlora_adapter_unmerge": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, ctypes.c_float, _P, _P]),
+    "qlora_lora_dropout": (ctypes.c_int, [_P, _I64, _I64, ctypes.c_float, ctypes.c_uint64, _P, _P]),
+    "qlora_linear_dropout_workspace": (_SZ, [_I64, _I64, _I64, _I32]),
+    "qlora_linear_fwd_dropout": (ctypes.c_int, [_WP, _P, _I64, _P, _P, _I32, ctypes.c_float, ctypes.c_float,
+                                                ctypes.c_uint64, _P, _P, _P, _SZ, _P]),
+    "qlora_linear_bwd_dropout": (ctypes.c_int, [_WP, _P, _P, _P, _P, _P, _I64, _I32, ctypes.c_float,
+                                                ctypes.c_float, ctypes.c_uint64, _P, _P, _P, _P, _SZ, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     if not hasattr(_lib, _name):
@@ -189,8 +195,21 @@ def quantize_workspace_bytes(d: int, k: int, dq_block: int = DQ_BLOCK) -> int:
     return int(_lib.qlora_nf4_quantize_workspace(d, k, BLOCK, dq_block))
 
 
-def linear_workspace_bytes(m: int, d: int, k: int, r: int) -> int:
+def linear_workspace_bytes(m: int, d: int, k: int, r: int, dropout: bool = False) -> int:
+    if dropout:
+        return int(_lib.qlora_linear_dropout_workspace(m, d, k, r))
     return int(_lib.qlora_linear_workspace(m, d, k, r))
+
+
+def qlora_lora_dropout(x: torch.Tensor, p: float, seed: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Xd = dropout of bf16 x [M, k] on the adapter input (Philox keep mask of
+    (p, seed); kept values x / (1 - p) rounded to bf16, dropped +0)."""
+    _dev_tensor(x, torch.bfloat16, "x")
+    m, k = x.shape
+    xd = out if out is not None else torch.empty_like(x)
+    _check(_lib.qlora_lora_dropout(x.data_ptr(), m, k, float(p), int(seed) & (2**64 - 1), xd.data_ptr(),
+                                   _stream()), "qlora_lora_dropout")
+    return xd
 
 
 def qlora_nf4_quantize(w0: torch.Tensor, out: NF4Weight | None = None,
@@ -222,8 +241,12 @@ def qlora_nf4_dequantize(w: NF4Weight, out: torch.Tensor | None = None) -> torch
 
 def qlora_linear_fwd(w: NF4Weight, x: torch.Tensor, a: torch.Tensor, b: torch.Tensor,
                      alpha: float, save_u: bool = True, out: torch.Tensor | None = None,
-                     u_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
-    """Y = x What^T + (alpha/r) (x A^T) B^T.  Returns (Y bf16 [M, d], U fp32 [M, r] or None)."""
+                     u_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                     dropout: float = 0.0, seed: int = 0):
+    """Y = x What^T + (alpha/r) (x A^T) B^T.  Returns (Y bf16 [M, d], U fp32 [M, r] or None).
+
+    dropout > 0: the adapter's input is Xd = drop(x) (qlora_lora_dropout with
+    this seed), U = Xd A^T; the backward takes the same dropout and seed."""
     _dev_tensor(x, torch.bfloat16, "x")
     _dev_tensor(a, torch.bfloat16, "A")
     _dev_tensor(b, torch.bfloat16, "B")
@@ -234,8 +257,14 @@ def qlora_linear_fwd(w: NF4Weight, x: torch.Tensor, a: torch.Tensor, b: torch.Te
     else:
         u = torch.empty((m, r), dtype=torch.float32, device=x.device) if save_u else None
     ws = workspace if workspace is not None else _workspace(
-        linear_workspace_bytes(m, w.d, w.k, r), x.device)
+        linear_workspace_bytes(m, w.d, w.k, r, dropout > 0), x.device)
     cw = w.c_struct()
+    if dropout > 0:
+        _check(_lib.qlora_linear_fwd_dropout(ctypes.byref(cw), x.data_ptr(), m, a.data_ptr(), b.data_ptr(), r,
+                                             float(alpha), float(dropout), int(seed) & (2**64 - 1), y.data_ptr(),
+                                             _ptr(u), ws.data_ptr(), ws.numel(), _stream()),
+               "qlora_linear_fwd_dropout")
+        return y, u
     _check(_lib.qlora_linear_fwd(ctypes.byref(cw), x.data_ptr(), m, a.data_ptr(), b.data_ptr(), r,
                                  float(alpha), y.data_ptr(), _ptr(u), ws.data_ptr(), ws.numel(),
                                  _stream()), "qlora_linear_fwd")
@@ -245,8 +274,9 @@ def qlora_linear_fwd(w: NF4Weight, x: torch.Tensor, a: torch.Tensor, b: torch.Te
 def qlora_linear_bwd(w: NF4Weight, x: torch.Tensor, dy: torch.Tensor, a: torch.Tensor,
                      b: torch.Tensor, alpha: float, u: torch.Tensor | None = None,
                      need_dx: bool = True, workspace: torch.Tensor | None = None,
-                     outs: tuple | None = None):
-    """Returns (dX bf16 [M, k] or None, dA fp32 [r, k], dB fp32 [d, r])."""
+                     outs: tuple | None = None, dropout: float = 0.0, seed: int = 0):
+    """Returns (dX bf16 [M, k] or None, dA fp32 [r, k], dB fp32 [d, r]).  dropout and
+    seed: those of the forward."""
     _dev_tensor(x, torch.bfloat16, "x")
     _dev_tensor(dy, torch.bfloat16, "dY")
     _dev_tensor(a, torch.bfloat16, "A")
@@ -261,8 +291,14 @@ def qlora_linear_bwd(w: NF4Weight, x: torch.Tensor, dy: torch.Tensor, a: torch.T
         da = torch.empty((r, w.k), dtype=torch.float32, device=x.device)
         db = torch.empty((w.d, r), dtype=torch.float32, device=x.device)
     ws = workspace if workspace is not None else _workspace(
-        linear_workspace_bytes(m, w.d, w.k, r), x.device)
+        linear_workspace_bytes(m, w.d, w.k, r, dropout > 0), x.device)
     cw = w.c_struct()
+    if dropout > 0:
+        _check(_lib.qlora_linear_bwd_dropout(ctypes.byref(cw), x.data_ptr(), dy.data_ptr(), a.data_ptr(),
+                                             b.data_ptr(), _ptr(u), m, r, float(alpha), float(dropout),
+                                             int(seed) & (2**64 - 1), _ptr(dx), da.data_ptr(), db.data_ptr(),
+                                             ws.data_ptr(), ws.numel(), _stream()), "qlora_linear_bwd_dropout")
+        return dx, da, db
     _check(_lib.qlora_linear_bwd(ctypes.byref(cw), x.data_ptr(), dy.data_ptr(), a.data_ptr(),
                                  b.data_ptr(), _ptr(u), m, r, float(alpha), _ptr(dx), da.data_ptr(),
                                  db.data_ptr(), ws.data_ptr(), ws.numel(), _stream()),
@@ -320,6 +356,7 @@ def adapter_scale(alpha: float, r: int) -> float:
 __all__ = [
     "NF4Weight", "QloraError", "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd",
     "qlora_linear_bwd", "qlora_linear_gemm_only", "qlora_adapter_merge", "qlora_adapter_unmerge",
+    "qlora_lora_dropout",
     "qlora_nf4_codebook", "qlora_nf4_thresholds", "status_str", "library",
     "abi_version", "quantize_workspace_bytes", "linear_workspace_bytes", "adapter_scale",
     "BLOCK", "DQ_BLOCK", "NO_DQ", "C2_INT8", "C2_FP8_E4M3",

@@ -102,6 +102,14 @@ GemmWs gemm_ws(char *base, const LinWs &l) {
                   reinterpret_cast<uint16_t *>(base + l.ext_b), reinterpret_cast<uint16_t *>(base + l.wbf)};
 }
 
+// Dropout parameters: the keep threshold floor(p 2^16) and c = fp32(1 / fp32(1 - p)).
+bool dropout_params(float p, uint32_t *thr, float *c) {
+    if (!(p >= 0.0f && p < 1.0f)) return false;  // also rejects NaN
+    *thr = (uint32_t)std::floor((double)p * 65536.0);
+    *c = 1.0f / (1.0f - p);
+    return true;
+}
+
 int check_linear(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M, const qlora_bf16 *A,
                  const qlora_bf16 *B, int32_t r, float alpha) {
     int st = check_weight(w, true);
@@ -294,6 +302,103 @@ int qlora_adapter_unmerge(const qlora_bf16 *W_in, int64_t d, int64_t k, const ql
     const float scale = alpha / static_cast<float>(r);
     return hip_status(launch_adapter_merge(nullptr, W_in, d, k, A, B, r, -(double)scale, W_out,
                                            static_cast<hipStream_t>(stream)));
+}
+
+int qlora_lora_dropout(const qlora_bf16 *x, int64_t M, int64_t k, float p, uint64_t seed, qlora_bf16 *xd,
+                       void *stream) {
+    uint32_t thr;
+    float c;
+    if (!x || !xd || M <= 0 || k <= 0 || k % 8 != 0 || !dropout_params(p, &thr, &c)) return QLORA_EINVAL;
+    if (M > kMaxWeights / k) return QLORA_ENOTSUP;
+    if (!aligned(x, 16) || !aligned(xd, 16)) return QLORA_EALIGN;
+    (void)hipGetLastError();
+    return hip_status(launch_lora_dropout(x, M, k, thr, c, seed, xd, static_cast<hipStream_t>(stream)));
+}
+
+size_t qlora_linear_dropout_workspace(int64_t M, int64_t d, int64_t k, int32_t r) {
+    const size_t base = qlora_linear_workspace(M, d, k, r);
+    if (base == 0 || M > kMaxWeights / k) return 0;
+    return base + round_up(sizeof(uint16_t) * M * k, 256);
+}
+
+int qlora_linear_fwd_dropout(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M, const qlora_bf16 *A,
+                             const qlora_bf16 *B, int32_t r, float alpha, float p, uint64_t seed, qlora_bf16 *Y,
+                             float *U_save, void *ws, size_t ws_bytes, void *stream) {
+    int st = check_linear(w, x, M, A, B, r, alpha);
+    if (st != QLORA_OK) return st;
+    uint32_t thr;
+    float c;
+    if (!Y || !dropout_params(p, &thr, &c)) return QLORA_EINVAL;
+    if (M > kMaxWeights / w->k) return QLORA_ENOTSUP;
+    if (!aligned(Y, 16) || (U_save && !aligned(U_save, 4))) return QLORA_EALIGN;
+    const LinWs l = lin_ws(M, w->d, w->k, r);
+    if (!ws || ws_bytes < qlora_linear_dropout_workspace(M, w->d, w->k, r)) return QLORA_EWORKSPACE;
+    if (!aligned(ws, 16)) return QLORA_EALIGN;
+    (void)hipGetLastError();
+    char *base = static_cast<char *>(ws);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const float scale = alpha / static_cast<float>(r);
+    uint16_t *xd = reinterpret_cast<uint16_t *>(base + l.total);
+    float *U = U_save ? U_save : reinterpret_cast<float *>(base + l.u);
+    const Nf4Weights nw = nf4_view(w);
+    hipError_t e = launch_lora_dropout(x, M, w->k, thr, c, seed, xd, s);
+    if (e == hipSuccess) e = launch_rows_skinny(xd, A, M, w->k, r, U, nullptr, s);   // U = Xd A^T
+    if (e == hipSuccess) {
+        if (M <= 16 && w->k <= kDecodeMaxK)
+            e = launch_decode_fwd(nw, x, M, nullptr, U, B, r, scale, Y, nullptr, reinterpret_cast<float *>(base + l.dpart),
+                                  reinterpret_cast<unsigned long long *>(base + l.ctr), s);
+        else
+            e = launch_gemm_fwd(nw, x, M, U, B, r, scale, Y, gemm_ws(base, l), s);
+    }
+    return hip_status(e);
+}
+
+int qlora_linear_bwd_dropout(const qlora_nf4_weight *w, const qlora_bf16 *x, const qlora_bf16 *dY,
+                             const qlora_bf16 *A, const qlora_bf16 *B, const float *U, int64_t M, int32_t r,
+                             float alpha, float p, uint64_t seed, qlora_bf16 *dX, float *dA, float *dB, void *ws,
+                             size_t ws_bytes, void *stream) {
+    int st = check_linear(w, x, M, A, B, r, alpha);
+    if (st != QLORA_OK) return st;
+    uint32_t thr;
+    float c;
+    if (!dY || !dA || !dB || !dropout_params(p, &thr, &c)) return QLORA_EINVAL;
+    if (M > kMaxWeights / w->k) return QLORA_ENOTSUP;
+    if (!aligned(dY, 16) || (dX && !aligned(dX, 16)) || !aligned(dA, 4) || !aligned(dB, 4) ||
+        (U && !aligned(U, 4)))
+        return QLORA_EALIGN;
+    const LinWs l = lin_ws(M, w->d, w->k, r);
+    if (!ws || ws_bytes < qlora_linear_dropout_workspace(M, w->d, w->k, r)) return QLORA_EWORKSPACE;
+    if (!aligned(ws, 16)) return QLORA_EALIGN;
+    (void)hipGetLastError();
+    char *base = static_cast<char *>(ws);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const float scale = alpha / static_cast<float>(r);
+    const int64_t d = w->d, k = w->k;
+    uint16_t *xd = reinterpret_cast<uint16_t *>(base + l.total);
+    float *Uw = reinterpret_cast<float *>(base + l.u);
+    uint16_t *Bt = reinterpret_cast<uint16_t *>(base + l.bt);
+    float *G = reinterpret_cast<float *>(base + l.g);
+    float *part = reinterpret_cast<float *>(base + l.part);
+    const Nf4Weights nw = nf4_view(w);
+    uint16_t *vt_u = reinterpret_cast<uint16_t *>(base + l.vt);
+    uint16_t *vt_g = vt_u + 2 * cols_rank_pad(r) * M;
+    hipError_t e = launch_lora_dropout(x, M, k, thr, c, seed, xd, s);           // the forward's Xd again
+    if (e == hipSuccess && !U) e = launch_rows_skinny(xd, A, M, k, r, Uw, vt_u, s);
+    if (e == hipSuccess) e = launch_bwd_prep(B, d, r, Bt, U, M, vt_u, s);
+    if (e == hipSuccess) e = launch_rows_skinny(dY, Bt, M, d, r, G, vt_g, s);   // G = dY B
+    ColsReduceJob red[2];
+    float *part_b = part;                                                       // dB = s U^T dY
+    float *part_a = part + (size_t)cols_splits(M) * r * round_up(d, 64);        // dA = s G^T Xd
+    if (e == hipSuccess)
+        e = launch_cols_pair(dY, vt_u, d, scale, part_b, dB, 0, xd, vt_g, k, scale, part_a, dA, 1, M, r, red, s);
+    if (e == hipSuccess && dX) {
+        // the base term dY What (the GEMM's adapter columns get scale 0), then the masked adapter term
+        e = launch_gemm_dx(nw, dY, M, G, A, r, 0.0f, dX, gemm_ws(base, l), red, s);
+        if (e == hipSuccess) e = launch_dropout_dx_add(dX, M, k, G, r, A, scale * c, thr, seed, s);
+    } else if (e == hipSuccess) {
+        e = launch_cols_reduce(red, s);
+    }
+    return hip_status(e);
 }
 
 int qlora_linear_gemm_only(const qlora_nf4_weight *w, int32_t backward, const qlora_bf16 *a, int64_t M,

@@ -19,6 +19,15 @@ hipError_t launch_quantize(const float *W0, int64_t n, uint8_t *codes, int8_t *c
 hipError_t launch_dequantize(const uint8_t *codes, const int8_t *c2, const float *c1,
                              const float *mean, int fmt, int64_t n, uint16_t *out, hipStream_t s);
 
+// ---- adapter dropout (dropout.hip) ----------------------------------------
+// xd[M x k] = bf16(x c) where the Philox keep mask (threshold thr, 64-bit seed)
+// keeps the element, +0 where it drops it; M k % 8 == 0, 16-byte aligned rows.
+hipError_t launch_lora_dropout(const uint16_t *x, int64_t M, int64_t k, uint32_t thr, float c, uint64_t seed,
+                               uint16_t *xd, hipStream_t st);
+// dx[M x k] (bf16, in place) += kept ? sc (G A)[m][n] : 0, with G [M x r] fp32 and A [r x k] bf16.
+hipError_t launch_dropout_dx_add(uint16_t *dx, int64_t M, int64_t k, const float *G, int r, const uint16_t *A,
+                                 float sc, uint32_t thr, uint64_t seed, hipStream_t st);
+
 // ---- skinny GEMMs ----------------------------------------------------------
 // out[M x R] (fp32) = In[M x K] (bf16) * W[R x K]^T (bf16), R <= 128.  vt: null,
 // or [2][Rp][M] bf16 receiving the transposed hi and lo planes of out (rows

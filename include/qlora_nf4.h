@@ -189,6 +189,61 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const qlora_bf16 *x, const qlora
                      void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Adapter dropout (fromzero2ai "LoRA and QLoRA", "Python Implementation:
+ * Fine-Tuning with PEFT and BitsAndBytes": training with a LoRA dropout rate;
+ * chkda "Merging LoRA weights for inference": the two-path layer equals the
+ * merged one only with dropout disabled).  Dropout acts on the adapter's input
+ * only:  Xd = drop(X),  U = Xd A^T,  Y = X What^T + s U B^T,
+ *        dA = s G^T Xd,  dB = s dY^T U,  dX = dY What + c (Mask o (s G A)),
+ * with c = fp32(1 / fp32(1 - p)).  The keep mask is Philox4x32-10 (Salmon et
+ * al., "Parallel random numbers: as easy as 1, 2, 3", SC 2011): element
+ * i = m k + col of X [M x k] uses the 16-bit half i mod 2 (0: low) of word
+ * (i mod 8) div 2 of the block for counter (i div 8 low word, i div 8 high
+ * word, 0, 0) and key (seed low, seed high), and is dropped iff that half
+ * < floor(p 2^16).  The same (p, seed) in the
+ * forward and the backward gives the same mask; nothing is stored.
+ *   p     dropout probability, 0 <= p < 1 (p = 0: the calls without dropout
+ *         give the same results); seed any 64-bit value.
+ */
+
+/*
+ * qlora_lora_dropout -- Xd = drop(X) alone:  Xd[m][c] = BF16(fp32(x c))
+ * (round to nearest even) where kept, +0 where dropped.
+ *   x, xd  device bf16 [M x k], 16-byte aligned, k % 8 == 0; may not overlap.
+ */
+int qlora_lora_dropout(const qlora_bf16 *x, int64_t M, int64_t k, float p, uint64_t seed,
+                       qlora_bf16 *xd, void *stream);
+
+/* Bytes of device workspace the two dropout calls need (a linear workspace
+ * plus room for Xd); 0 for invalid arguments. */
+size_t qlora_linear_dropout_workspace(int64_t M, int64_t d, int64_t k, int32_t r);
+
+/*
+ * qlora_linear_fwd_dropout -- qlora_linear_fwd with dropout on the adapter
+ * input.  Arguments as qlora_linear_fwd plus p and seed; U_save receives
+ * U = Xd A^T, the value qlora_linear_bwd_dropout takes as U.
+ *   ws  >= qlora_linear_dropout_workspace(M, d, k, r) bytes.
+ */
+int qlora_linear_fwd_dropout(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M,
+                             const qlora_bf16 *A, const qlora_bf16 *B, int32_t r, float alpha,
+                             float p, uint64_t seed, qlora_bf16 *Y, float *U_save,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * qlora_linear_bwd_dropout -- qlora_linear_bwd with dropout on the adapter
+ * input, for the forward with the same p and seed.  Arguments as
+ * qlora_linear_bwd plus p and seed (U: that forward's U_save, or NULL to
+ * recompute it).  dX: the base term is rounded to bf16 first, then the
+ * masked adapter term is added and the sum rounded again.
+ *   ws  >= qlora_linear_dropout_workspace(M, d, k, r) bytes.
+ */
+int qlora_linear_bwd_dropout(const qlora_nf4_weight *w, const qlora_bf16 *x, const qlora_bf16 *dY,
+                             const qlora_bf16 *A, const qlora_bf16 *B, const float *U,
+                             int64_t M, int32_t r, float alpha, float p, uint64_t seed,
+                             qlora_bf16 *dX, float *dA, float *dB,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/*
  * qlora_linear_gemm_only -- the dequant-GEMM kernel of the preceding
  * qlora_linear_fwd (backward = 0) or qlora_linear_bwd (backward = 1) call,
  * launched alone, so that its duration can be measured in isolation.  Those

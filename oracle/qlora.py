@@ -39,9 +39,10 @@ dropout disabled).  Reading R17: dropout acts on the adapter's input only,
 
 with c = fl32(1 / fl32(1 - p)) and the keep mask M drawn by Philox4x32-10
 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3",
-SC 2011) from a 64-bit seed: element i = m k + col uses word i mod 4 of the
-block for counter (i div 4 as two 32-bit words, 0, 0) and key (seed low, seed
-high); it is dropped iff that word < floor(p 2^32).
+SC 2011) from a 64-bit seed: element i = m k + col takes the 16-bit half
+i mod 2 (0: low) of word (i mod 8) div 2 of the block for counter (i div 8 as
+two 32-bit words, 0, 0) and key (seed low, seed high); it is dropped iff that
+half < floor(p 2^16).
 
 Merge (chkda "Merging LoRA weights for inference"): W_merged = W0 + s B A,
 in fp64 (merged_weight) and as bf16 under the library's fixed rounding
@@ -172,10 +173,10 @@ def philox4x32_10(ctr: np.ndarray, key: tuple[int, int]) -> np.ndarray:
 
 
 def dropout_threshold(p: float) -> int:
-    """floor(p 2^32) for the fp32 value of p in [0, 1)."""
+    """floor(p 2^16) for the fp32 value of p in [0, 1)."""
     p = float(np.float32(p))
     assert 0.0 <= p < 1.0
-    return int(np.floor(p * 2.0 ** 32))
+    return int(np.floor(p * 2.0 ** 16))
 
 
 def dropout_scale(p: float) -> np.float32:
@@ -186,12 +187,13 @@ def dropout_scale(p: float) -> np.float32:
 def dropout_keep_mask(m: int, k: int, p: float, seed: int) -> np.ndarray:
     """Keep mask [m x k] (bool) of reading R17."""
     n = m * k
-    blocks = np.arange((n + 3) // 4, dtype=np.uint64)
+    blocks = np.arange((n + 7) // 8, dtype=np.uint64)
     ctr = np.zeros((blocks.size, 4), dtype=np.uint64)
     ctr[:, 0] = blocks & np.uint64(0xFFFFFFFF)
     ctr[:, 1] = blocks >> np.uint64(32)
-    words = philox4x32_10(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)).reshape(-1)[:n]
-    return (words.astype(np.uint64) >= np.uint64(dropout_threshold(p))).reshape(m, k)
+    words = philox4x32_10(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)).reshape(-1)
+    halves = np.stack([words & 0xFFFF, words >> 16], axis=1).reshape(-1)[:n]   # element 2j: low half of word j
+    return (halves.astype(np.int64) >= dropout_threshold(p)).reshape(m, k)
 
 
 def lora_dropout_bits(x_bits: np.ndarray, p: float, seed: int) -> tuple[np.ndarray, np.ndarray]:

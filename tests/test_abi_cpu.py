@@ -268,3 +268,24 @@ def test_merge_rejects_invalid_arguments(kw, status):
 ])
 def test_unmerge_rejects_invalid_arguments(kw, status):
     assert unmerge(**kw) == status
+
+
+def test_dropout_calls_reject_invalid_arguments():
+    lib = q.library()
+    assert lib.qlora_linear_dropout_workspace(64, 256, 512, 8) > lib.qlora_linear_workspace(64, 256, 512, 8)
+    assert lib.qlora_linear_dropout_workspace(64, 256, 500, 8) == 0
+    for p in (-0.1, 1.0, 1.5, float("nan"), float("inf")):
+        assert lib.qlora_lora_dropout(FAKE, 16, 512, p, 1, FAKE, None) == q.QLORA_EINVAL, p
+    assert lib.qlora_lora_dropout(None, 16, 512, 0.1, 1, FAKE, None) == q.QLORA_EINVAL
+    assert lib.qlora_lora_dropout(FAKE, 16, 500, 0.1, 1, FAKE, None) == q.QLORA_EINVAL
+    assert lib.qlora_lora_dropout(FAKE_MIS, 16, 512, 0.1, 1, FAKE, None) == q.QLORA_EALIGN
+    w = weight()
+    fwd_d = lambda p=0.1, ws_bytes=1 << 30, y=FAKE: lib.qlora_linear_fwd_dropout(
+        ctypes.byref(w), FAKE, 16, FAKE, FAKE, 8, 16.0, p, 7, y, None, FAKE, ws_bytes, None)
+    bwd_d = lambda p=0.1, ws_bytes=1 << 30, da=FAKE: lib.qlora_linear_bwd_dropout(
+        ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, None, 16, 8, 16.0, p, 7, FAKE, da, FAKE, FAKE, ws_bytes, None)
+    assert fwd_d(p=1.0) == q.QLORA_EINVAL and bwd_d(p=-1.0) == q.QLORA_EINVAL
+    assert fwd_d(y=None) == q.QLORA_EINVAL and bwd_d(da=None) == q.QLORA_EINVAL
+    need = lib.qlora_linear_dropout_workspace(16, 256, 512, 8)
+    assert fwd_d(ws_bytes=need - 1) == q.QLORA_EWORKSPACE and bwd_d(ws_bytes=need - 1) == q.QLORA_EWORKSPACE
+    assert fwd_d(y=FAKE_MIS) == q.QLORA_EALIGN

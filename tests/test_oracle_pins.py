@@ -406,16 +406,19 @@ def test_philox4x32_vectorized_equals_scalar():
 def test_dropout_mask_layout_rate_and_edges():
     m, k, seed = 48, 1024, 0x1234_5678_9ABC
     keep = qlora.dropout_keep_mask(m, k, 0.05, seed)
-    # element i uses word i % 4 of the block for counter i // 4 (low, high words)
-    for i in (0, 1, 2, 3, 4, 4097, m * k - 1):
-        blk = i // 4
-        w = _philox_scalar([blk & 0xFFFFFFFF, blk >> 32, 0, 0], [seed & 0xFFFFFFFF, seed >> 32], 32)[i % 4]
-        assert keep.reshape(-1)[i] == (w >= qlora.dropout_threshold(0.05))
+    # element i uses 16-bit half i % 2 of word (i % 8) // 2 of the block for
+    # counter i // 8 (low, high words)
+    for i in (0, 1, 2, 3, 4, 7, 8, 4097, m * k - 1):
+        blk = i // 8
+        w = _philox_scalar([blk & 0xFFFFFFFF, blk >> 32, 0, 0], [seed & 0xFFFFFFFF, seed >> 32], 32)[(i % 8) // 2]
+        half = (w >> (16 * (i % 2))) & 0xFFFF
+        assert keep.reshape(-1)[i] == (half >= qlora.dropout_threshold(0.05))
     for p in (0.05, 0.3, 0.5):
         frac = 1.0 - qlora.dropout_keep_mask(m, k, p, seed + 1).mean()
         assert abs(frac - p) < 5 * np.sqrt(p * (1 - p) / (m * k))
     assert qlora.dropout_keep_mask(m, k, 0.0, seed).all()
-    assert qlora.dropout_threshold(0.5) == 2**31 and qlora.dropout_threshold(0.0) == 0
+    assert qlora.dropout_threshold(0.5) == 2**15 and qlora.dropout_threshold(0.0) == 0
+    assert qlora.dropout_threshold(0.05) == 3276
     assert qlora.dropout_scale(0.5) == np.float32(2.0) and qlora.dropout_scale(0.0) == np.float32(1.0)
     assert not np.array_equal(keep, qlora.dropout_keep_mask(m, k, 0.05, seed + 1))
 
