@@ -531,21 +531,22 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
     }
 }
 
-// Dequantized weight operand for the non-expanding GEMM: What [d x k]
-// (forward) or What^T [k x ldw] with zero columns d .. ldw-1 (dX), bf16,
-// bit-identical to qlora_nf4_dequantize (the block scale is doubleDequant's,
-// computed here from c2, c1 and the mean).  One workgroup per 64 W0 rows x 256
-// columns; thread t expands an 8 x 8 block: rows 8 (t % 8) .., columns
-// 8 (t / 8) .. (inside one NF4 block, so one scale per row).  Code reads are
-// 32 contiguous bytes per row for 8 lanes; the transposed form transposes the
-// 8 x 8 block in registers (v_perm) and stores 16-byte column pieces, so no
-// LDS is involved and every store is a contiguous 128-byte row segment per 8
-// lanes.
-template <bool T>
-__device__ __forceinline__ void dequant_tile(int64_t bid, const uint8_t *__restrict__ codes, int fmt,
-                                             const int8_t *__restrict__ c2, const float *__restrict__ c1, float mean,
-                                             int64_t d, int64_t k, int64_t ldw, const Nf4Consts &tab,
-                                             uint16_t *__restrict__ out) {
+// Transposed dequantized weight operand for the non-expanding dX GEMM: What^T
+// [k x ldw] with zero columns d .. ldw-1, bf16, bit-identical to
+// qlora_nf4_dequantize (the block scale is doubleDequant's, computed here from
+// c2, c1 and the mean).  One workgroup per 64 W0 rows x 256 columns; thread t
+// expands an 8 x 8 block: rows 8 (t % 8) .., columns 8 (t / 8) .. (inside one
+// NF4 block, so one scale per row).  Code reads are 32 contiguous bytes per
+// row for 8 lanes; the 8 x 8 block is transposed in registers (v_perm) and
+// stored as 16-byte column pieces, so no LDS is involved and every store is a
+// contiguous 128-byte row segment per 8 lanes.  (The forward's What, laid out
+// like the codes, is written by a plain stride loop in prep_kernel.)  Narrower
+// blocks (8 x 4) and two tiles per workgroup with the next one's loads
+// overlapping were both slower.
+__device__ __forceinline__ void dequant_tile_t(int64_t bid, const uint8_t *__restrict__ codes, int fmt,
+                                               const int8_t *__restrict__ c2, const float *__restrict__ c1,
+                                               float mean, int64_t d, int64_t k, int64_t ldw, const Nf4Consts &tab,
+                                               uint16_t *__restrict__ out) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int64_t ct = (k + 255) / 256;
     const int64_t tk = bid % ct, td = bid / ct;
@@ -558,8 +559,6 @@ __device__ __forceinline__ void dequant_tile(int64_t bid, const uint8_t *__restr
     for (int j = 1; j < 16; ++j) lvf = (lane & 15) == j ? tab.level[j] : lvf;
     const int lv = __float_as_int(lvf);
     const int64_t kb = k / 64;
-    // v[e][c2]: row e, columns 2 c2, 2 c2 + 1 (bf16 pair)
-    uint32_t v[8][4];
     uint32_t cw[8];
     float sc[8];
 #pragma unroll
@@ -569,6 +568,8 @@ __device__ __forceinline__ void dequant_tile(int64_t bid, const uint8_t *__restr
         cw[e] = n < d ? *reinterpret_cast<const uint32_t *>(codes + n * (k / 2) + k0 / 2) : 0u;
         sc[e] = n < d ? block_scale(fmt, c2, c1, mean, jb) : 0.0f;
     }
+    // v[e][q]: row e, columns 2 q, 2 q + 1 (bf16 pair)
+    uint32_t v[8][4];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
@@ -577,24 +578,17 @@ __device__ __forceinline__ void dequant_tile(int64_t bid, const uint8_t *__restr
                                            level(code_addr(cw[e], 2 * q + 1), lv) * sc[e]);
             v[e][q] = n0 + e < d ? x : 0u;  // rows past d: zero columns of What^T
         }
-    if constexpr (!T) {
+    // column c of the block: rows 0..7 packed as 4 bf16 pairs
+    // (rows 2 e2, 2 e2 + 1) = low halves (c even) or high halves (c odd)
+    // of v[2 e2][c / 2] and v[2 e2 + 1][c / 2]
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            if (n0 + e < d)
-                *reinterpret_cast<uint4 *>(out + (n0 + e) * k + k0) = uint4{v[e][0], v[e][1], v[e][2], v[e][3]};
-    } else {
-        // column c of the block: rows 0..7 packed as 4 bf16 pairs
-        // (rows 2 e2, 2 e2 + 1) = low halves (c even) or high halves (c odd)
-        // of v[2 e2][c / 2] and v[2 e2 + 1][c / 2]
+    for (int c = 0; c < 8; ++c) {
+        uint32_t o[4];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            uint32_t o[4];
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2)
-                o[e2] = (c & 1) ? __builtin_amdgcn_perm(v[2 * e2 + 1][c >> 1], v[2 * e2][c >> 1], 0x07060302u)
-                                : __builtin_amdgcn_perm(v[2 * e2 + 1][c >> 1], v[2 * e2][c >> 1], 0x05040100u);
-            *reinterpret_cast<uint4 *>(out + (k0 + c) * ldw + n0) = uint4{o[0], o[1], o[2], o[3]};
-        }
+        for (int e2 = 0; e2 < 4; ++e2)
+            o[e2] = (c & 1) ? __builtin_amdgcn_perm(v[2 * e2 + 1][c >> 1], v[2 * e2][c >> 1], 0x07060302u)
+                            : __builtin_amdgcn_perm(v[2 * e2 + 1][c >> 1], v[2 * e2][c >> 1], 0x05040100u);
+        *reinterpret_cast<uint4 *>(out + (k0 + c) * ldw + n0) = uint4{o[0], o[1], o[2], o[3]};
     }
 }
 
@@ -694,7 +688,29 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a, Nf4Consts tab) {
     }
     b -= a.g_a + a.g_b;
     if (b < a.g_t) {
-        dequant_tile<DX>(b, a.codes, a.fmt, a.c2, a.c1, a.fmt != kNoDq ? *a.mean : 0.0f, a.d, a.k, a.ldw, tab, a.wbf);
+        const float mean = a.fmt != kNoDq ? *a.mean : 0.0f;
+        if constexpr (DX) {
+            dequant_tile_t(b, a.codes, a.fmt, a.c2, a.c1, mean, a.d, a.k, a.ldw, tab, a.wbf);
+        } else {
+            // What [d x k], row-major like the codes: a stride loop over 8-weight
+            // items (one code dword -> one 16-byte store), the levels in LDS
+            __shared__ float lut[16];
+            if (threadIdx.x < 16) lut[threadIdx.x] = tab.level[threadIdx.x];
+            __syncthreads();
+            const int64_t items = a.d * a.k / 8;
+            const uint32_t *codes4 = reinterpret_cast<const uint32_t *>(a.codes);
+            uint4 *out = reinterpret_cast<uint4 *>(a.wbf);
+            for (int64_t i = b * 256 + threadIdx.x; i < items; i += a.g_t * 256) {
+                const uint32_t c = codes4[i];
+                const float sh = block_scale(a.fmt, a.c2, a.c1, mean, i >> 3);  // 8 items per 64-block
+                uint4 o;
+                o.x = pack_bf16x2(lut[c & 15] * sh, lut[(c >> 4) & 15] * sh);
+                o.y = pack_bf16x2(lut[(c >> 8) & 15] * sh, lut[(c >> 12) & 15] * sh);
+                o.z = pack_bf16x2(lut[(c >> 16) & 15] * sh, lut[(c >> 20) & 15] * sh);
+                o.w = pack_bf16x2(lut[(c >> 24) & 15] * sh, lut[c >> 28] * sh);
+                out[i] = o;
+            }
+        }
         return;
     }
     b -= a.g_t;
@@ -757,7 +773,8 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
         q.g_shat = expand ? (q.nb + 255) / 256 : 0;  // only the expanding GEMM reads the scales
         q.g_a = (M * (p.Ke / 8) + 255) / 256;
         q.g_b = (p.N * (p.Ke / 8) + 255) / 256;
-        q.g_t = expand ? 0 : ((w.k + 255) / 256) * ((w.d + 63) / 64);  // the bf16 copy of What (or What^T)
+        // the bf16 copy of What (forward: a stride loop over 8-weight items) or What^T (dX: 64 x 256 tiles)
+        q.g_t = expand ? 0 : ((w.k + 255) / 256) * ((w.d + 63) / 64);
         q.g_r0 = (q.red[0].N * q.red[0].R + 255) / 256;
         const int64_t g_r1 = (q.red[1].N * q.red[1].R + 255) / 256;
         const dim3 pgrid((unsigned)(q.g_shat + q.g_a + q.g_b + q.g_t + q.g_r0 + g_r1));

@@ -35,70 +35,55 @@ namespace {
 constexpr int kBlock = 64;
 constexpr int kGroup = 256;
 
-// Nearest level through a bucket table (a compare against each of the 15
-// thresholds costs two instructions per weight; this costs a handful).
-// x = fl32(w / absmax) lies in [-1, 1].  Bucket = sign, exponent and the top
-// three mantissa bits of x: the floats of one bucket form an interval, and no
-// bucket holds more than one threshold (the thresholds are >= 0.08 apart, a
-// bucket at most 0.0625 wide), so code = base + (x >= T) with (base, T) read
-// from the table.  |x| < 2^-5 (exponent <= 121) is one bucket per sign: all of
-// it lies strictly between the two thresholds around zero (code 7).
-// Index: clamp(bits[20..30] - (121 << 3), 0, 55) + 56 * sign.
-//
-// The division is skipped where it cannot matter: x' = w * rcp(absmax) is
-// within a few ulp of x, so the code of x' is the code of x unless a threshold
-// lies within that distance.  Each entry carries a band [lo, hi] around its
-// threshold (2^-20 relative, far wider than the error); an x' inside the band
-// takes the exact path (IEEE division), and so does a whole bucket that has a
-// threshold near one of its edges (band = everything; none does for the NF4
-// table).
+// Nearest level through a bucket table.  The exact rule is code = #{j : x >=
+// T_j} for x = fl32(w / absmax) in [-1, 1] and the 15 thresholds T_j (the
+// smallest fp32 above each midpoint).  Fast path: y = fma(w, 64 rcp(absmax),
+// 64) approximates 64 x + 64 in [0, 128] to within 2.5e-5 (rcp and the two
+// roundings), so bucket i = (uint) y covers x in about [(i - 64)/64, (i -
+// 63)/64): 129 buckets of width 1/64, and the thresholds (at least 0.08 apart)
+// put at most one in each.  Entry i holds the count of thresholds below the
+// bucket and the one inside it (in y units), so code = base + (y >= t).  A y
+// within kBandY (2^-13, five times the error) of that threshold, or not a
+// number (an absmax below 2^-100 or zero reciprocal), takes the exact path:
+// the IEEE quotient compared with all 15 thresholds.  A threshold within kBandY
+// of a bucket edge would make both buckets exact-path-only; no NF4 threshold is
+// (all lie 0.015 or more from an edge in y units).  Two instructions form the
+// index where the previous exponent-and-mantissa bucketing took five.
 // a lane's value after a DPP lane permutation within its row of 16 lanes
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-constexpr int kLutEntries = 112;
-constexpr float kBand = 0x1p-20f;
+constexpr int kLutEntries = 129;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const int n = (int)__builtin_amdgcn_readfirstlane((uint32_t)bytes);
+    void *p = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, n, 0x00020000);
+}
+constexpr float kBandY = 0x1p-13f;
 
 struct LutEntry {
     uint32_t base;
-    float thresh;  // the one threshold inside the bucket, or +inf
-    float lo, hi;  // where x' must go the exact way
+    float thresh;  // the one threshold inside the bucket (y units), or +inf
+    float lo, hi;  // where y must go the exact way
 };
 
-__device__ __forceinline__ uint32_t lut_index(float x) {
-    const uint32_t u = __float_as_uint(x);
-    const int k11 = (int)((u >> 20) & 0x7FFu) - (121 << 3);
-    const int c = k11 < 0 ? 0 : (k11 > 55 ? 55 : k11);
-    return (uint32_t)c + 56u * (u >> 31);
-}
-
-// Entry i of the table: the bucket's smallest and largest float decide the
-// base count and the threshold inside it.
+// Entry i (bucket [i, i + 1) of y): its base count and the threshold inside it.
 __device__ void lut_entry(int i, const Nf4Consts &t, LutEntry *out) {
-    const uint32_t sign = i >= 56 ? 1u : 0u;
-    const int c = i - 56 * (int)sign;
-    float lo, hi;  // the bucket's smallest and largest value
-    if (c < 8) {   // exponent <= 121 (both signs): all of (-2^-5, 2^-5)
-        lo = -0x1.fffffep-6f;
-        hi = 0x1.fffffep-6f;
-    } else {
-        const uint32_t k = (uint32_t)(c + (121 << 3));  // exponent and mantissa top bits
-        const uint32_t b0 = (sign << 31) | (k << 20), b1 = b0 | 0xFFFFFu;
-        const float f0 = __uint_as_float(b0), f1 = __uint_as_float(b1);
-        lo = sign ? f1 : f0;
-        hi = sign ? f0 : f1;
-    }
+    const float lo = (float)i, hi = (float)(i + 1);
     uint32_t base = 0;
     float inside = __builtin_inff();
     bool edge = false;
     for (int j = 0; j < 15; ++j) {
-        const float tj = t.thresh[j];
-        if (tj <= lo) ++base;
-        else if (tj <= hi) inside = tj;
-        const float m = fabsf(tj) * (4.0f * kBand);
-        if (fabsf(tj - lo) <= m || fabsf(tj - hi) <= m) edge = true;
+        const float ty = t.thresh[j] * 64.0f + 64.0f;  // one rounding (< 2^-16), far inside the band
+        if (ty < lo) ++base;
+        else if (ty < hi) inside = ty;
+        if (fabsf(ty - lo) <= 2.0f * kBandY || fabsf(ty - hi) <= 2.0f * kBandY) edge = true;
     }
     out->base = base;
     out->thresh = inside;
@@ -109,8 +94,8 @@ __device__ void lut_entry(int i, const Nf4Consts &t, LutEntry *out) {
         out->lo = __builtin_inff();  // no threshold: an empty band
         out->hi = -__builtin_inff();
     } else {
-        out->lo = inside - fabsf(inside) * kBand;
-        out->hi = inside + fabsf(inside) * kBand;
+        out->lo = inside - kBandY;
+        out->hi = inside + kBandY;
     }
 }
 
@@ -127,40 +112,52 @@ __global__ __launch_bounds__(256) void nf4_quantize_groups(
     const int64_t blk0 = (int64_t)blockIdx.x * kGroup;
     s_abs[tid] = 0.0f;  // missing blocks of a ragged last group count as +0.0
 
+    // Unconditional loads through a buffer resource over this group's blocks
+    // (past the last block they read zero): no branch between them, so each
+    // block's codes are computed as soon as its own data is in.
+    const int64_t nloc = nb - blk0 < kGroup ? nb - blk0 : kGroup;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + blk0 * kBlock, nloc * kBlock * 4);
     float4 v[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const int64_t blk = blk0 + wave * 64 + (i >> 1) * 8 + (i & 1) * 4 + (lane >> 4);
-        v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (blk < nb) v[i] = *reinterpret_cast<const float4 *>(w + blk * kBlock + (lane & 15) * 4);
+        const int local = wave * 64 + (i >> 1) * 8 + (i & 1) * 4 + (lane >> 4);
+        v[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rw, (uint32_t)(local * kBlock * 4 + (lane & 15) * 16), 0, 0));
     }
     if (tid < kLutEntries) lut_entry(tid, tab, &lut[tid]);
-    __syncthreads();  // s_abs cleared and the table built before any lane uses them
+    // s_abs cleared and the table built before any lane uses them; an LDS-only
+    // fence, so the barrier does not wait for the loads above
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     // codes of four weights of one block: the four table reads in flight
     // together, one branch for the (rare) exact path
-    auto code4 = [&](const float4 &wv, float m, float r) {
+    auto code4 = [&](const float4 &wv, float m, float r64) {
         const float w4[4] = {wv.x, wv.y, wv.z, wv.w};
-        float xa[4];
+        float y[4];
         LutEntry e[4];
         uint32_t q[4];
         bool slow = false;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            xa[c] = w4[c] * r;
-            e[c] = lut[lut_index(xa[c])];
+            y[c] = __builtin_fmaf(w4[c], r64, 64.0f);
+            const uint32_t i = (uint32_t)fminf(fmaxf(y[c], 0.0f), 128.0f);  // NaN -> 0
+            e[c] = lut[i];
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            q[c] = e[c].base + (xa[c] >= e[c].thresh ? 1u : 0u);
-            // near a threshold (or x' not a number): decide with the exact quotient
-            slow |= !((xa[c] > e[c].hi) | (xa[c] < e[c].lo));
+            q[c] = e[c].base + (y[c] >= e[c].thresh ? 1u : 0u);
+            // near a threshold (or y not a number): decide with the exact quotient
+            slow |= !((y[c] > e[c].hi) | (y[c] < e[c].lo));
         }
         if (__builtin_expect(slow, 0)) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const float x = w4[c] / m;
-                const LutEntry ex = lut[lut_index(x)];
-                q[c] = ex.base + (x >= ex.thresh ? 1u : 0u);
+                uint32_t n = 0;
+#pragma unroll
+                for (int j = 0; j < 15; ++j) n += x >= tab.thresh[j] ? 1u : 0u;
+                q[c] = n;
             }
         }
         return q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12);
@@ -178,8 +175,8 @@ __global__ __launch_bounds__(256) void nf4_quantize_groups(
         if (m != 0.0f) {
             // an absmax below 2^-100 (reciprocal near overflow, subnormal
             // operands) takes the exact path for every weight
-            const float r = m >= 0x1p-100f ? __builtin_amdgcn_rcpf(m) : __builtin_nanf("");
-            packed4 = code4(v[i], m, r);
+            const float r64 = m >= 0x1p-100f ? __builtin_amdgcn_rcpf(m) * 64.0f : __builtin_nanf("");
+            packed4 = code4(v[i], m, r64);
         }
         if (blk < nb) {
             const uint16_t packed = (uint16_t)packed4;

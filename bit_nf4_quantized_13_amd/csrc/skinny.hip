@@ -119,39 +119,31 @@ __global__ __launch_bounds__(64 * W) void rows_skinny_kernel(const uint16_t *__r
 }
 
 // ---------------------------------------------------------------------------
-// Backward preparation, one launch: workgroups [0, gt) transpose src = B
-// [R = d rows x C = r columns] into dst = B^T [r x d] (64 x 64 tiles through
-// LDS); the rest write the transposed bf16 planes of a given U [M x r] fp32:
+// Backward preparation, one launch, one thread per row: workgroups [0, gt)
+// transpose src = B [R = d rows x C = r columns] into dst = B^T [r x d] (thread
+// = row of B: its C values in, one column of B^T out); the rest write the
+// transposed bf16 planes of a given U [M x r] fp32 (thread = row m of U):
 // vt[j][m] = hi(U[m][j]), vt[Rp + j][m] = lo(U[m][j]) (zero for r <= j < Rp).
+// Stores of consecutive threads are consecutive; no LDS, no barrier.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t *__restrict__ src, int64_t R, int64_t C,
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t *__restrict__ src, int64_t R, int C,
                                                        uint16_t *__restrict__ dst, int64_t gt,
-                                                       const float *__restrict__ U, int64_t M, int64_t Rp,
+                                                       const float *__restrict__ U, int64_t M, int Rp,
                                                        uint16_t *__restrict__ vt) {
-    __shared__ uint16_t tile[64][65];
     if ((int64_t)blockIdx.x >= gt) {
-        const int64_t e = ((int64_t)blockIdx.x - gt) * 256 + threadIdx.x;  // (j, m), m fastest
-        if (e >= Rp * M) return;
-        const int64_t j = e / M, m = e - j * M;  // the rank is C (B is [R = d] x [C = r])
-        const float f = j < C ? U[m * C + j] : 0.0f;
-        const uint32_t hb = pack_bf16x2(f, 0.0f) & 0xFFFFu;
-        vt[e] = (uint16_t)hb;
-        vt[Rp * M + e] = (uint16_t)(pack_bf16x2(f - bf16_bits_to_f32(hb), 0.0f) & 0xFFFFu);
+        const int64_t m = ((int64_t)blockIdx.x - gt) * 256 + threadIdx.x;
+        if (m >= M) return;
+        for (int j = 0; j < Rp; ++j) {
+            const float f = j < C ? U[m * C + j] : 0.0f;
+            const uint32_t hb = pack_bf16x2(f, 0.0f) & 0xFFFFu;
+            vt[(int64_t)j * M + m] = (uint16_t)hb;
+            vt[(int64_t)(Rp + j) * M + m] = (uint16_t)(pack_bf16x2(f - bf16_bits_to_f32(hb), 0.0f) & 0xFFFFu);
+        }
         return;
     }
-    const int64_t tiles_c = (C + 63) / 64;
-    const int64_t c0 = ((int64_t)blockIdx.x % tiles_c) * 64, r0 = ((int64_t)blockIdx.x / tiles_c) * 64;
-    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-        const int rr = e / 64, cc = e % 64;
-        const int64_t r = r0 + rr, c = c0 + cc;
-        tile[rr][cc] = (r < R && c < C) ? src[r * C + c] : (uint16_t)0;
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-        const int cc = e / 64, rr = e % 64;
-        const int64_t r = r0 + rr, c = c0 + cc;
-        if (r < R && c < C) dst[c * R + r] = tile[rr][cc];
-    }
+    const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (row >= R) return;
+    for (int c = 0; c < C; ++c) dst[(int64_t)c * R + row] = src[row * C + c];
 }
 
 // ---------------------------------------------------------------------------
@@ -339,11 +331,10 @@ int64_t cols_rank_pad(int r) { return (r + 15) / 16 * 16; }
 
 hipError_t launch_bwd_prep(const uint16_t *B, int64_t d, int r, uint16_t *Bt, const float *U, int64_t M,
                            uint16_t *vt, hipStream_t s) {
-    const int64_t Rp = cols_rank_pad(r);
-    const int64_t gt = ((d + 63) / 64) * ((r + 63) / 64);
-    const int64_t gu = U ? (Rp * M + 255) / 256 : 0;
-    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)(gt + gu)), dim3(256), 0, s, B, d, (int64_t)r, Bt, gt, U, M, Rp,
-                       vt);
+    const int Rp = (int)cols_rank_pad(r);
+    const int64_t gt = (d + 255) / 256;
+    const int64_t gu = U ? (M + 255) / 256 : 0;
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)(gt + gu)), dim3(256), 0, s, B, d, r, Bt, gt, U, M, Rp, vt);
     return hipGetLastError();
 }
 
