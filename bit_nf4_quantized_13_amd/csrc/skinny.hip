@@ -16,9 +16,11 @@
 //   A (16 x 32): lane l holds A[l % 16][8 (l / 16) .. +7]
 //   B (32 x 16): lane l holds B[8 (l / 16) .. +7][l % 16]
 //   D (16 x 16): lane l, register v holds D[4 (l / 16) + v][l % 16]
-// Since the k-order of a reduction is free, a lane may take 32 contiguous k
-// values (64 bytes) and feed them to four consecutive MFMAs, provided both
-// operands use the same k-assignment.
+// Since the k-order of a reduction is free, any assignment of k to the MFMAs
+// of a chunk works if both operands use it; rows_skinny gives MFMA e of a
+// 128-wide chunk the standard 32-wide slab 32 e .., so that the four lane
+// groups of a row load 64 contiguous bytes per instruction (16-byte pieces 64
+// bytes apart ran the activation stream at about half the rate).
 #include "launch.hpp"
 
 namespace qnf4 {
@@ -76,13 +78,15 @@ __global__ __launch_bounds__(64 * W) void rows_skinny_kernel(const uint16_t *__r
         bool ok[CPI][4];
 #pragma unroll
         for (int u = 0; u < CPI; ++u) {
-            const int64_t k0 = (c + W * u) * 128 + 32 * g;
+            // MFMA e of the chunk takes k = 32 e .. 32 e + 31, lane group g its 8 k at 32 e + 8 g:
+            // the four lanes of a row read 64 contiguous bytes per load
+            const int64_t k0 = (c + W * u) * 128 + 8 * g;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                ok[u][e] = k0 + 8 * e < K;  // K % 8 == 0: pieces are entirely inside or outside
-                a[u][e] = load16(rin, (uint32_t)((i * K + k0 + 8 * e) * 2));
+                ok[u][e] = k0 + 32 * e < K;  // K % 8 == 0: pieces are entirely inside or outside
+                a[u][e] = load16(rin, (uint32_t)((i * K + k0 + 32 * e) * 2));
 #pragma unroll
-                for (int t = 0; t < NT; ++t) b[u][t][e] = load16(rw, (uint32_t)(((t * 16 + i) * K + k0 + 8 * e) * 2));
+                for (int t = 0; t < NT; ++t) b[u][t][e] = load16(rw, (uint32_t)(((t * 16 + i) * K + k0 + 32 * e) * 2));
             }
         }
 #pragma unroll
