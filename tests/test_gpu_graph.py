@@ -77,3 +77,32 @@ def test_graph_replay_of_decode(d):
         q.qlora_linear_fwd(w, x, a, b, 32.0, out=y, u_out=u, workspace=lws)
 
     capture_and_check(step, [y, u])
+
+
+@pytest.mark.parametrize("fmt", ["no_dq", "fp8"])
+def test_graph_replay_of_a_dropout_step_in_other_formats(fmt):
+    """The further weight formats and adapter dropout under capture: quantize,
+    dropout forward and dropout backward (the mask regenerated from the seed in
+    each replay) give the eager outputs bit for bit."""
+    import bit_nf4_quantized_13_amd as q
+    say(f"graph capture: {fmt} quantize + dropout fwd + bwd, M=600 d=512 k=1024 r=8")
+    inp = make_layer(53, 0, 512, 1024, 600, 8)
+    m, d, k, r, alpha, p, seed = 600, 512, 1024, 8, 16.0, 0.1, 77
+    w0 = to_dev_f32(inp.w0)
+    x, a, b, dy = (to_dev_bf16(t) for t in (inp.x, inp.a, inp.b, inp.dy))
+    wq = q.NF4Weight.empty(d, k, double_quant=fmt != "no_dq", c2_fp8=fmt == "fp8")
+    qws = torch.empty(q.quantize_workspace_bytes(d, k, wq.dq_block), dtype=torch.uint8, device="cuda")
+    lws = torch.empty(q.linear_workspace_bytes(m, d, k, r, dropout=True), dtype=torch.uint8, device="cuda")
+    y = torch.empty((m, d), dtype=torch.bfloat16, device="cuda")
+    u = torch.empty((m, r), dtype=torch.float32, device="cuda")
+    dx = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
+    da = torch.empty((r, k), dtype=torch.float32, device="cuda")
+    db = torch.empty((d, r), dtype=torch.float32, device="cuda")
+
+    def step():
+        q.qlora_nf4_quantize(w0, out=wq, workspace=qws)
+        q.qlora_linear_fwd(wq, x, a, b, alpha, out=y, u_out=u, workspace=lws, dropout=p, seed=seed)
+        q.qlora_linear_bwd(wq, x, dy, a, b, alpha, u=u, workspace=lws, outs=(dx, da, db), dropout=p, seed=seed)
+
+    outs = [wq.codes, wq.absmax_scale, y, u, dx, da, db] + ([wq.absmax_q, wq.absmax_mean] if fmt == "fp8" else [])
+    capture_and_check(step, outs)
