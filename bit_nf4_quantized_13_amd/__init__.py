@@ -160,16 +160,17 @@ class NF4Weight:
 
     @staticmethod
     def empty(d: int, k: int, device="cuda", double_quant: bool = True,
-              c2_fp8: bool = False) -> "NF4Weight":
-        nb = (d * k) // BLOCK
+              c2_fp8: bool = False, block: int = BLOCK) -> "NF4Weight":
+        """Uninitialised buffers for W0 [d, k] in blocks of `block` (64, 128 or 256) weights."""
+        nb = (d * k) // block
         codes = torch.empty(d * k // 2, dtype=torch.uint8, device=device)
         if not double_quant:
             return NF4Weight(codes, None, torch.empty(nb, dtype=torch.float32, device=device), None,
-                             d, k, dq_block=NO_DQ)
+                             d, k, block=block, dq_block=NO_DQ)
         g = -(-nb // DQ_BLOCK)
         return NF4Weight(codes, torch.empty(nb, dtype=torch.uint8 if c2_fp8 else torch.int8, device=device),
                          torch.empty(g, dtype=torch.float32, device=device),
-                         torch.empty(1, dtype=torch.float32, device=device), d, k,
+                         torch.empty(1, dtype=torch.float32, device=device), d, k, block=block,
                          c2_format=C2_FP8_E4M3 if c2_fp8 else C2_INT8)
 
     @property
@@ -191,8 +192,8 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
-def quantize_workspace_bytes(d: int, k: int, dq_block: int = DQ_BLOCK) -> int:
-    return int(_lib.qlora_nf4_quantize_workspace(d, k, BLOCK, dq_block))
+def quantize_workspace_bytes(d: int, k: int, dq_block: int = DQ_BLOCK, block: int = BLOCK) -> int:
+    return int(_lib.qlora_nf4_quantize_workspace(d, k, block, dq_block))
 
 
 def linear_workspace_bytes(m: int, d: int, k: int, r: int, dropout: bool = False) -> int:
@@ -214,14 +215,15 @@ def qlora_lora_dropout(x: torch.Tensor, p: float, seed: int, out: torch.Tensor |
 
 def qlora_nf4_quantize(w0: torch.Tensor, out: NF4Weight | None = None,
                        workspace: torch.Tensor | None = None,
-                       double_quant: bool = True, c2_fp8: bool = False) -> NF4Weight:
-    """NF4 (+ double quantization of the block absmax, c2 in int8 or, with
-    c2_fp8, OCP FP8 e4m3) of fp32 W0 [d, k] on the current stream.  With `out`
-    given, its dq_block and c2_format decide the format."""
+                       double_quant: bool = True, c2_fp8: bool = False, block: int = BLOCK) -> NF4Weight:
+    """NF4 in blocks of `block` weights (64, 128 or 256) (+ double quantization
+    of the block absmax, c2 in int8 or, with c2_fp8, OCP FP8 e4m3) of fp32 W0
+    [d, k] on the current stream.  With `out` given, its block, dq_block and
+    c2_format decide the format."""
     _dev_tensor(w0, torch.float32, "W0")
     d, k = w0.shape
-    w = out if out is not None else NF4Weight.empty(d, k, w0.device, double_quant, c2_fp8)
-    ws_bytes = quantize_workspace_bytes(d, k, w.dq_block)
+    w = out if out is not None else NF4Weight.empty(d, k, w0.device, double_quant, c2_fp8, block)
+    ws_bytes = quantize_workspace_bytes(d, k, w.dq_block, w.block)
     ws = workspace if workspace is not None else _workspace(ws_bytes, w0.device)
     cw = w.c_struct()
     _check(_lib.qlora_nf4_quantize(w0.data_ptr(), ctypes.byref(cw), ws.data_ptr(),

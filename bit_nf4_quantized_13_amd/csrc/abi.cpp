@@ -23,10 +23,10 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 int check_weight(const qlora_nf4_weight *w, bool need_data) {
     if (!w) return QLORA_EINVAL;
     if (w->d <= 0 || w->k <= 0) return QLORA_EINVAL;
-    if (w->block != QLORA_NF4_BLOCK) return QLORA_ENOTSUP;
+    if (w->block != 64 && w->block != 128 && w->block != 256) return QLORA_ENOTSUP;
     if (w->dq_block != QLORA_NF4_DQ_BLOCK && w->dq_block != QLORA_NF4_NO_DQ) return QLORA_ENOTSUP;
     if (w->c2_format != QLORA_C2_INT8 && w->c2_format != QLORA_C2_FP8_E4M3) return QLORA_ENOTSUP;
-    if (w->k % QLORA_NF4_BLOCK != 0) return QLORA_EINVAL;
+    if (w->k % w->block != 0) return QLORA_EINVAL;
     if (w->d > kMaxWeights / w->k) return QLORA_ENOTSUP;
     if (need_data) {
         const bool dq = w->dq_block != QLORA_NF4_NO_DQ;
@@ -42,8 +42,9 @@ int check_weight(const qlora_nf4_weight *w, bool need_data) {
 Nf4Weights nf4_view(const qlora_nf4_weight *w) {
     const bool dq = w->dq_block != QLORA_NF4_NO_DQ;
     const int fmt = !dq ? kNoDq : w->c2_format == QLORA_C2_FP8_E4M3 ? kDqFp8 : kDqInt8;
+    const int bshift = w->block == 256 ? 2 : w->block == 128 ? 1 : 0;
     return Nf4Weights{w->codes, dq ? w->absmax_q : nullptr, w->absmax_scale, dq ? w->absmax_mean : nullptr,
-                      w->d, w->k, fmt};
+                      w->d, w->k, fmt, bshift};
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_EHIP; }
@@ -52,8 +53,8 @@ int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_EHIP; }
 struct QuantWs {
     size_t absmax, group_sum, total;
 };
-QuantWs quant_ws(int64_t d, int64_t k) {
-    const int64_t nb = d * k / QLORA_NF4_BLOCK;
+QuantWs quant_ws(int64_t d, int64_t k, int block) {
+    const int64_t nb = d * k / block;
     const int64_t g = (nb + QLORA_NF4_DQ_BLOCK - 1) / QLORA_NF4_DQ_BLOCK;
     QuantWs q;
     q.absmax = 0;
@@ -133,7 +134,7 @@ const char *qlora_status_str(int status) {
     switch (status) {
         case QLORA_OK: return "QLORA_OK: success";
         case QLORA_EINVAL: return "QLORA_EINVAL: invalid argument (null pointer, size <= 0, k % block != 0, non-finite alpha)";
-        case QLORA_ENOTSUP: return "QLORA_ENOTSUP: unsupported configuration (block != 64, dq_block not 256 or 0, unknown c2_format, r > 128, d % 8 != 0, tensor too large)";
+        case QLORA_ENOTSUP: return "QLORA_ENOTSUP: unsupported configuration (block not 64, 128 or 256, dq_block not 256 or 0, unknown c2_format, r > 128, d % 8 != 0, tensor too large)";
         case QLORA_EALIGN: return "QLORA_EALIGN: misaligned pointer (16-byte alignment required)";
         case QLORA_EWORKSPACE: return "QLORA_EWORKSPACE: workspace missing or too small";
         case QLORA_EHIP: return "QLORA_EHIP: HIP launch or runtime error";
@@ -160,7 +161,7 @@ size_t qlora_nf4_quantize_workspace(int64_t d, int64_t k, int32_t block, int32_t
     w.block = block;
     w.dq_block = dq_block;
     if (check_weight(&w, false) != QLORA_OK) return 0;
-    return quant_ws(d, k).total;
+    return quant_ws(d, k, block).total;
 }
 
 int qlora_nf4_quantize(const float *W0, const qlora_nf4_weight *w, void *ws, size_t ws_bytes,
@@ -169,13 +170,13 @@ int qlora_nf4_quantize(const float *W0, const qlora_nf4_weight *w, void *ws, siz
     if (st != QLORA_OK) return st;
     if (!W0) return QLORA_EINVAL;
     if (!aligned(W0, 16)) return QLORA_EALIGN;
-    const QuantWs q = quant_ws(w->d, w->k);
+    const QuantWs q = quant_ws(w->d, w->k, w->block);
     if (!ws || ws_bytes < q.total) return QLORA_EWORKSPACE;
     if (!aligned(ws, 16)) return QLORA_EALIGN;
     (void)hipGetLastError();
     char *base = static_cast<char *>(ws);
     const bool dq = w->dq_block != QLORA_NF4_NO_DQ;
-    return hip_status(launch_quantize(W0, w->d * w->k, w->codes, dq ? w->absmax_q : nullptr, w->absmax_scale,
+    return hip_status(launch_quantize(W0, w->d * w->k, w->block, w->codes, dq ? w->absmax_q : nullptr, w->absmax_scale,
                                       dq ? w->absmax_mean : nullptr, reinterpret_cast<float *>(base + q.absmax),
                                       reinterpret_cast<double *>(base + q.group_sum), nf4_view(w).fmt,
                                       static_cast<hipStream_t>(stream)));
@@ -188,7 +189,7 @@ int qlora_nf4_dequantize(const qlora_nf4_weight *w, qlora_bf16 *W_out, void *str
     if (!aligned(W_out, 16)) return QLORA_EALIGN;
     (void)hipGetLastError();
     const Nf4Weights nw = nf4_view(w);
-    return hip_status(launch_dequantize(nw.codes, nw.c2, nw.c1, nw.mean, nw.fmt, w->d * w->k, W_out,
+    return hip_status(launch_dequantize(nw.codes, nw.c2, nw.c1, nw.mean, nw.fmt, nw.bshift, w->d * w->k, W_out,
                                         static_cast<hipStream_t>(stream)));
 }
 

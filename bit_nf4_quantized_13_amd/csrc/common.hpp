@@ -85,10 +85,13 @@ __device__ __forceinline__ float dq_scale(float c2, float c1, float mean) {
     return c2 / c1 + mean;
 }
 
-// The scale of block blk of a stored weight: doubleDequant's dq_scale, or,
-// for a weight stored without double quantization, the fp32 block absmax
+// The scale of the 64-weight sub-block j64 of a stored weight whose blocks
+// hold 64 << bshift weights (block j64 >> bshift): doubleDequant's dq_scale,
+// or, for a weight stored without double quantization, the fp32 block absmax
 // itself, kept one per block in the c1 array (c2 and the mean unused).
-__device__ __forceinline__ float block_scale(int fmt, const int8_t *c2, const float *c1, float mean, int64_t blk) {
+__device__ __forceinline__ float block_scale(int fmt, const int8_t *c2, const float *c1, float mean, int64_t j64,
+                                             int bshift = 0) {
+    const int64_t blk = j64 >> bshift;
     if (fmt == kNoDq) return c1[blk];
     return dq_scale(c2_value((uint8_t)c2[blk], fmt == kDqFp8), c1[blk >> 8], mean);
 }

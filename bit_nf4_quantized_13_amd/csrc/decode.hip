@@ -101,6 +101,7 @@ struct DecodeArgs {
     // group g has tiles [g tb + min(g, tr), +tb + (g < tr)), slice s has blocks
     // [s kbs + min(s, kr), +kbs + (s < kr))
     int tb, tr, kbs, kr;
+    int bs;                // blocks of 64 << bs weights
 };
 
 // Device-coherent 16-byte store / load (sc1: not cached non-coherently in the
@@ -180,8 +181,9 @@ __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, N
     constexpr bool fuse_u = FU;
 
     const __amdgpu_buffer_rsrc_t rcode = make_rsrc(p.codes, (int64_t)d * hk);
-    const __amdgpu_buffer_rsrc_t rc2 = make_rsrc(p.c2, DQ ? (int64_t)d * kb : 0);
-    const __amdgpu_buffer_rsrc_t rc1 = make_rsrc(p.c1, (DQ ? ((int64_t)d * kb + 255) / 256 : (int64_t)d * kb) * 4);
+    const int64_t nblk = ((int64_t)d * kb) >> p.bs;  // stored blocks
+    const __amdgpu_buffer_rsrc_t rc2 = make_rsrc(p.c2, DQ ? nblk : 0);
+    const __amdgpu_buffer_rsrc_t rc1 = make_rsrc(p.c1, (DQ ? (nblk + 255) / 256 : nblk) * 4);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (int64_t)M * k * 2);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, fuse_u ? (int64_t)r * k * 2 : 0);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, (int64_t)d * r * 2);
@@ -257,15 +259,20 @@ __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, N
     uint32_t c2w[NCW];
     float c1a, c1b;
     uint4 absv[NCS];
+    // Blocks of 64 << bs weights: sub-block j (64 weights) takes block j >> bs, so
+    // an octet spans at most 8 blocks from b0 = (c2_lane + o) >> bs; the same
+    // windows from the aligned a0 = b0 & ~3 cover them.
+    const int bs = p.bs;
     auto issue_c2 = [&](int o) __attribute__((always_inline)) {
-        const uint32_t o8 = c2_lane + (uint32_t)o, a0 = o8 & ~3u;
+        const uint32_t o8 = c2_lane + (uint32_t)o, b0 = o8 >> bs, a0 = b0 & ~3u;
         const bool ok = srow_ok && o < nbw;
         if constexpr (DQ) {
 #pragma unroll
             for (int i = 0; i < NCW; ++i)
                 c2w[i] = __builtin_amdgcn_raw_buffer_load_b32(rc2, ok ? a0 + 4u * i : DEC_OOB, 0, 0);
-            c1a = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc1, ok ? (o8 >> 8) * 4 : DEC_OOB, 0, 0));
-            c1b = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc1, ok ? ((o8 + 7) >> 8) * 4 : DEC_OOB, 0, 0));
+            c1a = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc1, ok ? (b0 >> 8) * 4 : DEC_OOB, 0, 0));
+            c1b = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(rc1, ok ? (((o8 + 7) >> bs) >> 8) * 4 : DEC_OOB, 0, 0));
         } else {
 #pragma unroll
             for (int i = 0; i < NCS; ++i) absv[i] = load16(rc1, ok ? (a0 + 4u * i) * 4 : DEC_OOB);
@@ -338,14 +345,38 @@ __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, N
         // block scales of the octet (zero for rows past d and tiles past ntl)
         float sc[8];
         if constexpr (!DQ) {
-            const uint32_t sh = (c2_lane + (uint32_t)o) & 3u;
             const uint32_t f[12] = {absv[0].x, absv[0].y, absv[0].z, absv[0].w, absv[1].x, absv[1].y,
                                     absv[1].z, absv[1].w, absv[2].x, absv[2].y, absv[2].z, absv[2].w};
+            if (bs == 0) {
+                const uint32_t sh = (c2_lane + (uint32_t)o) & 3u;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t v = sh == 0 ? f[e] : sh == 1 ? f[e + 1] : sh == 2 ? f[e + 2] : f[e + 3];
+                    // blocks past nbw (another wave's, or the next row's) and rows past d add nothing
+                    sc[e] = srow_ok && o + e < nbw ? __uint_as_float(v) : 0.0f;
+                }
+            } else {
+                const uint32_t o8 = c2_lane + (uint32_t)o, a0 = (o8 >> bs) & ~3u;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t off = ((o8 + (uint32_t)e) >> bs) - a0;  // 0 .. 6
+                    uint32_t v = f[0];
+#pragma unroll
+                    for (int c = 1; c < 12; ++c) v = off == (uint32_t)c ? f[c] : v;
+                    sc[e] = srow_ok && o + e < nbw ? __uint_as_float(v) : 0.0f;
+                }
+            }
+        } else if (bs != 0) {
+            const uint32_t o8 = c2_lane + (uint32_t)o, b0 = o8 >> bs, a0 = b0 & ~3u, ga = b0 >> 8;
+            const uint64_t lo64 = (uint64_t)c2w[1] << 32 | c2w[0], hi64 = (uint64_t)c2w[2] << 32 | c2w[1];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const uint32_t v = sh == 0 ? f[e] : sh == 1 ? f[e + 1] : sh == 2 ? f[e + 2] : f[e + 3];
-                // blocks past nbw (another wave's, or the next row's) and rows past d add nothing
-                sc[e] = srow_ok && o + e < nbw ? __uint_as_float(v) : 0.0f;
+                const uint32_t idx = (o8 + (uint32_t)e) >> bs, off = idx - a0;  // 0 .. 6
+                const uint32_t byte = (uint32_t)(off < 8 ? lo64 >> (8 * off) : hi64 >> (8 * (off - 4)));
+                const float c2 = c2_value<0>(byte, F == kDqFp8);
+                const bool ok = srow_ok && o + e < nbw;
+                const float c1 = ok ? ((idx >> 8) == ga ? c1a : c1b) : 1.0f;
+                sc[e] = dq_scale(c2, c1, mean) * (ok ? 1.0f : 0.0f);
             }
         } else {
             const uint32_t sh = 8 * ((c2_lane + (uint32_t)o) & 3u);
@@ -635,6 +666,7 @@ hipError_t launch_decode_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, 
     a.tr = (int)(nt % pl.G);
     a.kbs = (int)(kb / pl.S);
     a.kr = (int)(kb % pl.S);
+    a.bs = w.bshift;
     switch (pl.TW) {
         case 1: return launch_tw<1>(a, w.fmt, pl.grid, st);
         case 2: return launch_tw<2>(a, w.fmt, pl.grid, st);

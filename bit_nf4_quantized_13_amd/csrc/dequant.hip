@@ -17,7 +17,7 @@ namespace {
 
 __global__ __launch_bounds__(256) void nf4_dequantize_kernel(
     const uint32_t *__restrict__ codes4, const int8_t *__restrict__ c2,
-    const float *__restrict__ c1, const float *__restrict__ mean_p, int fmt, int64_t items,
+    const float *__restrict__ c1, const float *__restrict__ mean_p, int fmt, int bshift, int64_t items,
     Nf4Consts tab, uint4 *__restrict__ out) {
     __shared__ float lut[16];
     if (threadIdx.x < 16) lut[threadIdx.x] = tab.level[threadIdx.x];
@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void nf4_dequantize_kernel(
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < items; i += stride) {
         const uint32_t c = codes4[i];
         const int64_t blk = i >> 3;  // 8 items per 64-weight block
-        const float sh = block_scale(fmt, c2, c1, mean, blk);
+        const float sh = block_scale(fmt, c2, c1, mean, blk, bshift);
         uint4 o;
         o.x = pack_bf16x2(lut[c & 15] * sh, lut[(c >> 4) & 15] * sh);
         o.y = pack_bf16x2(lut[(c >> 8) & 15] * sh, lut[(c >> 12) & 15] * sh);
@@ -40,12 +40,12 @@ __global__ __launch_bounds__(256) void nf4_dequantize_kernel(
 }  // namespace
 
 hipError_t launch_dequantize(const uint8_t *codes, const int8_t *c2, const float *c1,
-                             const float *mean, int fmt, int64_t n, uint16_t *out, hipStream_t s) {
+                             const float *mean, int fmt, int bshift, int64_t n, uint16_t *out, hipStream_t s) {
     const int64_t items = n / 8;
     int64_t grid = (items + 255) / 256;
     if (grid > 256 * 64) grid = 256 * 64;
     hipLaunchKernelGGL(nf4_dequantize_kernel, dim3((unsigned)grid), dim3(256), 0, s,
-                       reinterpret_cast<const uint32_t *>(codes), c2, c1, mean, fmt, items, nf4_consts(),
+                       reinterpret_cast<const uint32_t *>(codes), c2, c1, mean, fmt, bshift, items, nf4_consts(),
                        reinterpret_cast<uint4 *>(out));
     return hipGetLastError();
 }

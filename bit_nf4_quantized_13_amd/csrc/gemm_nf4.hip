@@ -543,7 +543,7 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
 // like the codes, is written by a plain stride loop in prep_kernel.)  Narrower
 // blocks (8 x 4) and two tiles per workgroup with the next one's loads
 // overlapping were both slower.
-__device__ __forceinline__ void dequant_tile_t(int64_t bid, const uint8_t *__restrict__ codes, int fmt,
+__device__ __forceinline__ void dequant_tile_t(int64_t bid, const uint8_t *__restrict__ codes, int fmt, int bshift,
                                                const int8_t *__restrict__ c2, const float *__restrict__ c1,
                                                float mean, int64_t d, int64_t k, int64_t ldw, const Nf4Consts &tab,
                                                uint16_t *__restrict__ out) {
@@ -566,7 +566,7 @@ __device__ __forceinline__ void dequant_tile_t(int64_t bid, const uint8_t *__res
         const int64_t n = n0 + e;
         const int64_t jb = n * kb + k0 / 64;
         cw[e] = n < d ? *reinterpret_cast<const uint32_t *>(codes + n * (k / 2) + k0 / 2) : 0u;
-        sc[e] = n < d ? block_scale(fmt, c2, c1, mean, jb) : 0.0f;
+        sc[e] = n < d ? block_scale(fmt, c2, c1, mean, jb, bshift) : 0.0f;
     }
     // v[e][q]: row e, columns 2 q, 2 q + 1 (bf16 pair)
     uint32_t v[8][4];
@@ -601,7 +601,8 @@ __device__ __forceinline__ void dequant_tile_t(int64_t bid, const uint8_t *__res
 //   up to two column reductions out = scale sum_splits part        (the dX call's dB, dA)
 // where W'[n][j] = B[n][j] (forward, B [d x r]) or A[j][n] (dX, A [r x k]).
 struct PrepArgs {
-    int fmt;  // ScaleFormat of the block constants
+    int fmt;     // ScaleFormat of the block constants
+    int bshift;  // blocks of 64 << bshift weights
     const int8_t *c2;
     const float *c1;
     const float *mean;
@@ -648,7 +649,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a, Nf4Consts tab) {
     int64_t b = blockIdx.x;
     if (b < a.g_shat) {
         const int64_t x = b * 256 + threadIdx.x;
-        if (x < a.nb) a.shat[x] = block_scale(a.fmt, a.c2, a.c1, a.fmt != kNoDq ? *a.mean : 0.0f, x);
+        if (x < a.nb) a.shat[x] = block_scale(a.fmt, a.c2, a.c1, a.fmt != kNoDq ? *a.mean : 0.0f, x, a.bshift);
         return;
     }
     b -= a.g_shat;
@@ -690,7 +691,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a, Nf4Consts tab) {
     if (b < a.g_t) {
         const float mean = a.fmt != kNoDq ? *a.mean : 0.0f;
         if constexpr (DX) {
-            dequant_tile_t(b, a.codes, a.fmt, a.c2, a.c1, mean, a.d, a.k, a.ldw, tab, a.wbf);
+            dequant_tile_t(b, a.codes, a.fmt, a.bshift, a.c2, a.c1, mean, a.d, a.k, a.ldw, tab, a.wbf);
         } else {
             // What [d x k], row-major like the codes: a stride loop over 8-weight
             // items (one code dword -> one 16-byte store), the levels in LDS
@@ -702,7 +703,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a, Nf4Consts tab) {
             uint4 *out = reinterpret_cast<uint4 *>(a.wbf);
             for (int64_t i = b * 256 + threadIdx.x; i < items; i += a.g_t * 256) {
                 const uint32_t c = codes4[i];
-                const float sh = block_scale(a.fmt, a.c2, a.c1, mean, i >> 3);  // 8 items per 64-block
+                const float sh = block_scale(a.fmt, a.c2, a.c1, mean, i >> 3, a.bshift);  // 8 items per 64 weights
                 uint4 o;
                 o.x = pack_bf16x2(lut[c & 15] * sh, lut[(c >> 4) & 15] * sh);
                 o.y = pack_bf16x2(lut[(c >> 8) & 15] * sh, lut[(c >> 12) & 15] * sh);
@@ -749,6 +750,7 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
     if (!core_only) {
         PrepArgs q;
         q.fmt = w.fmt;
+        q.bshift = w.bshift;
         q.c2 = w.c2;
         q.c1 = w.c1;
         q.mean = w.mean;

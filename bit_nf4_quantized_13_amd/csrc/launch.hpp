@@ -12,12 +12,13 @@ const Nf4Consts &nf4_consts();  // built once on the host (nf4_table.cpp)
 
 // ---- quantize (three kernels) --------------------------------------------
 // fmt = kNoDq: the fp32 block absmax goes to c1 (one per block); c2 and mean are unused.
-hipError_t launch_quantize(const float *W0, int64_t n, uint8_t *codes, int8_t *c2, float *c1,
+// block: 64, 128 or 256 weights (the blocks of 128 and 256 take a plain per-block kernel)
+hipError_t launch_quantize(const float *W0, int64_t n, int block, uint8_t *codes, int8_t *c2, float *c1,
                            float *mean, float *absmax_ws, double *group_sum_ws, int fmt, hipStream_t s);
 
 // ---- standalone double dequant --------------------------------------------
 hipError_t launch_dequantize(const uint8_t *codes, const int8_t *c2, const float *c1,
-                             const float *mean, int fmt, int64_t n, uint16_t *out, hipStream_t s);
+                             const float *mean, int fmt, int bshift, int64_t n, uint16_t *out, hipStream_t s);
 
 // ---- adapter dropout (dropout.hip) ----------------------------------------
 // xd[M x k] = bf16(x c) where the Philox keep mask (threshold thr, 64-bit seed)
@@ -66,6 +67,7 @@ struct Nf4Weights {
     const float *mean;  // double-quantized only
     int64_t d, k;
     int fmt;            // ScaleFormat (common.hpp): kNoDq, kDqInt8 or kDqFp8
+    int bshift;         // blocks of 64 << bshift weights (0, 1, 2: 64, 128, 256)
 };
 // Workspace of one dequant-GEMM call: the dequantized block scales
 // (d*k/64 floats) and the adapter operands laid out as extra k-columns,

@@ -30,7 +30,7 @@ template <bool NF4>  // NF4: merge from the packed weight; else unmerge from bf1
 __global__ __launch_bounds__(256) void adapter_merge_kernel(const uint8_t *__restrict__ codes,
                                                             const int8_t *__restrict__ c2,
                                                             const float *__restrict__ c1,
-                                                            const float *__restrict__ mean_p, int fmt,
+                                                            const float *__restrict__ mean_p, int fmt, int bshift,
                                                             const uint16_t *__restrict__ w_in,
                                                             const uint16_t *__restrict__ A,
                                                             const uint16_t *__restrict__ B, int64_t d,
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void adapter_merge_kernel(const uint8_t *__res
         if constexpr (NF4) {  // What: doubleDequant, bit-identical to qlora_nf4_dequantize
             const uint32_t cw = *reinterpret_cast<const uint32_t *>(codes + (n * k + k0) / 2);
             const int64_t blk = (n * k + k0) / 64;
-            const float sh = block_scale(fmt, c2, c1, mean, blk);
+            const float sh = block_scale(fmt, c2, c1, mean, blk, bshift);
 #pragma unroll
             for (int c = 0; c < 8; ++c) base[c] = bf16_round(lut[(cw >> (4 * c)) & 15u] * sh);
         } else {
@@ -140,10 +140,10 @@ hipError_t launch_adapter_merge(const Nf4Weights *w, const uint16_t *w_in, int64
     const int64_t tiles = ((d + kMRows - 1) / kMRows) * ((k + kMCols - 1) / kMCols);
     if (w)
         hipLaunchKernelGGL(adapter_merge_kernel<true>, dim3((unsigned)tiles), dim3(256), 0, st, w->codes, w->c2, w->c1,
-                           w->mean, w->fmt, nullptr, A, B, d, k, r, s, nf4_consts(), w_out);
+                           w->mean, w->fmt, w->bshift, nullptr, A, B, d, k, r, s, nf4_consts(), w_out);
     else
         hipLaunchKernelGGL(adapter_merge_kernel<false>, dim3((unsigned)tiles), dim3(256), 0, st, nullptr, nullptr,
-                           nullptr, nullptr, 0, w_in, A, B, d, k, r, s, nf4_consts(), w_out);
+                           nullptr, nullptr, 0, 0, w_in, A, B, d, k, r, s, nf4_consts(), w_out);
     return hipGetLastError();
 }
 

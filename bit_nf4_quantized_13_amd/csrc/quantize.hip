@@ -202,6 +202,57 @@ __global__ __launch_bounds__(256) void nf4_quantize_groups(
     }
 }
 
+// Blocks of B = 128 or 256 weights (the path for block sizes other than 64):
+// one workgroup per group of 256 blocks, thread t owns block blk0 + t: its
+// absmax (a max over B weights), then each weight's code by the definition --
+// the IEEE quotient x = w / absmax counted against the 15 thresholds -- two
+// codes per byte, and the group's fp64 partial sum by the stride-halving tree
+// in LDS (a[i] += a[i + h], h = 128 .. 1), the same additions as the 64-weight
+// kernel's.  A plain kernel: each thread streams its own block.
+template <int B>
+__global__ __launch_bounds__(256) void nf4_quantize_wide(const float *__restrict__ w, int64_t nb, Nf4Consts tab,
+                                                         uint8_t *__restrict__ codes, float *__restrict__ absmax,
+                                                         double *__restrict__ group_sum) {
+    __shared__ double s_tree[kGroup];
+    const int t = threadIdx.x;
+    const int64_t blk = (int64_t)blockIdx.x * kGroup + t;
+    const bool valid = blk < nb;
+    const float4 *src = reinterpret_cast<const float4 *>(w + (valid ? blk : 0) * B);
+    float m = 0.0f;
+    if (valid) {
+        for (int i = 0; i < B / 4; ++i) {
+            const float4 v = src[i];
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        }
+        absmax[blk] = m;
+        uint32_t *dst = reinterpret_cast<uint32_t *>(codes + blk * (B / 2));
+        for (int i = 0; i < B / 8; ++i) {
+            const float4 v0 = src[2 * i], v1 = src[2 * i + 1];
+            const float x8[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            uint32_t word = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                uint32_t q = 7u;  // an all-zero block: the exact-zero level
+                if (m != 0.0f) {
+                    const float x = x8[e] / m;
+                    q = 0;
+#pragma unroll
+                    for (int j = 0; j < 15; ++j) q += x >= tab.thresh[j] ? 1u : 0u;
+                }
+                word |= q << (4 * e);
+            }
+            dst[i] = word;
+        }
+    }
+    s_tree[t] = valid ? (double)m : 0.0;  // missing blocks of a ragged last group count as +0.0
+    __syncthreads();
+    for (int h = kGroup / 2; h >= 1; h >>= 1) {
+        if (t < h) s_tree[t] = s_tree[t] + s_tree[t + h];
+        __syncthreads();
+    }
+    if (t == 0) group_sum[blockIdx.x] = s_tree[0];
+}
+
 constexpr int kMeanThreads = 1024;
 constexpr int kMeanPerThread = 64;  // supports up to 65536 groups
 
@@ -316,18 +367,25 @@ __global__ __launch_bounds__(256) void dq_encode(const float *__restrict__ absma
 
 }  // namespace
 
-hipError_t launch_quantize(const float *W0, int64_t n, uint8_t *codes, int8_t *c2, float *c1,
+hipError_t launch_quantize(const float *W0, int64_t n, int block, uint8_t *codes, int8_t *c2, float *c1,
                            float *mean, float *absmax_ws, double *group_sum_ws, int fmt, hipStream_t s) {
     const bool dq = fmt != kNoDq;
     const int fp8 = fmt == kDqFp8 ? 1 : 0;
-    const int64_t nb = n / kBlock;
+    const int64_t nb = n / block;
     const int64_t groups = (nb + kGroup - 1) / kGroup;
     int64_t padded = 1;
     while (padded < groups) padded *= 2;
     if (dq && padded > (int64_t)kMeanThreads * kMeanPerThread) return hipErrorInvalidValue;
     // without double quantization the block absmax is the stored scale: no encode
-    hipLaunchKernelGGL(nf4_quantize_groups, dim3((unsigned)groups), dim3(256), 0, s, W0, nb,
-                       nf4_consts(), codes, dq ? absmax_ws : c1, group_sum_ws);
+    if (block == 128)
+        hipLaunchKernelGGL(nf4_quantize_wide<128>, dim3((unsigned)groups), dim3(256), 0, s, W0, nb, nf4_consts(), codes,
+                           dq ? absmax_ws : c1, group_sum_ws);
+    else if (block == 256)
+        hipLaunchKernelGGL(nf4_quantize_wide<256>, dim3((unsigned)groups), dim3(256), 0, s, W0, nb, nf4_consts(), codes,
+                           dq ? absmax_ws : c1, group_sum_ws);
+    else
+        hipLaunchKernelGGL(nf4_quantize_groups, dim3((unsigned)groups), dim3(256), 0, s, W0, nb,
+                           nf4_consts(), codes, dq ? absmax_ws : c1, group_sum_ws);
     if (!dq) return hipGetLastError();
     if (padded <= kMeanInline) {
         hipLaunchKernelGGL(dq_encode<true>, dim3((unsigned)groups), dim3(256), 0, s, absmax_ws, nb, mean, group_sum_ws,

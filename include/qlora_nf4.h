@@ -45,7 +45,7 @@ extern "C" {
 /* ---- status codes ------------------------------------------------------ */
 #define QLORA_OK          0  /* success                                                  */
 #define QLORA_EINVAL      1  /* null pointer, size <= 0, k % block != 0, non-finite alpha */
-#define QLORA_ENOTSUP     2  /* block != 64, dq_block not 256 or 0, unknown c2_format,
+#define QLORA_ENOTSUP     2  /* block not 64/128/256, dq_block not 256 or 0, c2_format,
                                 r > 128, tensor too large                                */
 #define QLORA_EALIGN      3  /* a pointer read/written with 128-bit accesses is not 16-byte aligned */
 #define QLORA_EWORKSPACE  4  /* workspace NULL or smaller than the *_workspace() size     */
@@ -76,7 +76,11 @@ typedef uint16_t qlora_bf16; /* raw bfloat16 bits */
  *   absmax_scale float [G]    c1 (4-byte aligned)
  *   absmax_mean  float [1]    the mean of the nb block absmax values
  *   d, k                      W0 shape, d >= 1, k >= 1, k % block == 0
- *   block, dq_block           64, and 256 (or QLORA_NF4_NO_DQ, below)
+ *   block, dq_block           block: 64 (the pages' size), 128 or 256 weights,
+ *                             nb = N / block, k % block == 0; dq_block: 256
+ *                             (or QLORA_NF4_NO_DQ, below).  The kernels work
+ *                             on 64-weight sub-blocks; sub-block j takes the
+ *                             constants of block j / (block / 64)
  *   c2_format                 QLORA_C2_INT8 (0) or QLORA_C2_FP8_E4M3: how the
  *                             c2 bytes encode their values (ignored without
  *                             double quantization)

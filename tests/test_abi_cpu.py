@@ -110,7 +110,7 @@ def test_dequantize_rejects_invalid_arguments():
     lib = q.library()
     assert lib.qlora_nf4_dequantize(ctypes.byref(weight()), None, None) == q.QLORA_EINVAL
     assert lib.qlora_nf4_dequantize(ctypes.byref(weight()), FAKE_MIS, None) == q.QLORA_EALIGN
-    assert lib.qlora_nf4_dequantize(ctypes.byref(weight(block=128)), FAKE, None) == q.QLORA_ENOTSUP
+    assert lib.qlora_nf4_dequantize(ctypes.byref(weight(block=96)), FAKE, None) == q.QLORA_ENOTSUP
 
 
 def fwd(w=None, x=FAKE, m=16, a=FAKE, b=FAKE, r=8, alpha=16.0, y=FAKE, u=None, ws=FAKE,
@@ -176,6 +176,19 @@ def test_no_double_quant_format_validation():
                                     None) == q.QLORA_EALIGN
     if not torch.cuda.is_available():  # valid: gets as far as the launch
         assert quant(weight(dq=q.NO_DQ, c2=None, mean=FAKE + 1)) == q.QLORA_EHIP
+
+
+def test_block_size_validation():
+    lib = q.library()
+    for blk in (64, 128, 256):
+        assert lib.qlora_nf4_quantize_workspace(256, 512, blk, 256) > 0
+        assert lib.qlora_nf4_quantize_workspace(256, 512, blk, q.NO_DQ) > 0
+    for blk in (32, 96, 512, 0):
+        assert lib.qlora_nf4_quantize_workspace(256, 512, blk, 256) == 0
+        assert quant(weight(block=blk)) == q.QLORA_ENOTSUP
+    assert quant(weight(k=576, block=256)) == q.QLORA_EINVAL      # k % block != 0
+    assert quant(weight(k=640, block=128)) != q.QLORA_EINVAL      # 640 = 5 x 128
+    assert fwd(w=weight(k=576, block=128)) == q.QLORA_EINVAL
 
 
 def test_c2_format_validation():

@@ -212,3 +212,58 @@ def test_fp8_every_finite_code_reads_back_exactly():
         got = bf16_to_host_f64(y)
         assert np.array_equal(got, np.repeat(want[None, :], m, axis=0)), m
     torch.cuda.synchronize()
+
+
+BLOCK_CASES = [(fmt, blk) for blk in (128, 256) for fmt in ("int8", "no_dq", "fp8")]
+
+
+@pytest.mark.parametrize("fmt,block", BLOCK_CASES, ids=[f"{f}-b{b}" for f, b in BLOCK_CASES])
+def test_block_sizes(fmt, block):
+    """Blocks of 128 and 256 weights in every format: quantize and dequantize
+    bit-exact (ragged groups and an all-zero block included), the linear
+    forward and backward on the decode and GEMM paths, and the merge."""
+    import bit_nf4_quantized_13_amd as q
+    say(f"block {block}, format {fmt}")
+    kw = {"double_quant": fmt != "no_dq", "c2_fp8": fmt == "fp8", "block": block}
+    w0 = random_weights(64 + block, (40, 4 * block * 9))
+    w0[3, :block] = 0.0
+    w = q.qlora_nf4_quantize(to_dev_f32(w0), **kw)
+    assert w.block == block
+    what = bf16_to_host_bits(q.qlora_nf4_dequantize(w))
+    torch.cuda.synchronize()
+    if fmt == "no_dq":
+        ref = nf4.quantize_single(w0, block)
+        assert np.array_equal(w.absmax_scale.cpu().numpy().view(np.uint32), ref["absmax"].view(np.uint32))
+        want = nf4.dequantize_single(ref, w0.shape, block)
+    else:
+        ref = nf4.quantize(w0, block, c2_format=fmt)
+        assert np.array_equal(w.absmax_q.cpu().numpy().view(np.uint8), ref["c2"].view(np.uint8))
+        assert np.array_equal(w.absmax_scale.cpu().numpy().view(np.uint32), ref["c1"].view(np.uint32))
+        assert np.float32(w.absmax_mean.cpu().numpy()[0]).view(np.uint32) == np.float32(ref["mean"]).view(np.uint32)
+        want = nf4.dequantize(ref, w0.shape, block)
+    assert np.array_equal(w.codes.cpu().numpy(), ref["packed"])
+    assert np.array_equal(what, want)
+
+    for m, d, k, r in ((16, 4104, 2048, 16), (3, 512, 4096, 33), (600, 320, 4 * block, 8)):
+        say(f"block {block} {fmt} linear m={m} d={d} k={k} r={r}")
+        inp = make_layer(65, m + r + block, d, k, m, r)
+        wq = q.qlora_nf4_quantize(to_dev_f32(inp.w0), **kw)
+        xd, ad, bd, dyd = (to_dev_bf16(t) for t in (inp.x, inp.a, inp.b, inp.dy))
+        y, u = q.qlora_linear_fwd(wq, xd, ad, bd, 16.0)
+        dx, da, db = q.qlora_linear_bwd(wq, xd, dyd, ad, bd, 16.0, u=u)
+        merged = bf16_to_host_bits(q.qlora_adapter_merge(wq, ad, bd, 16.0))
+        torch.cuda.synchronize()
+        rq = nf4.quantize_single(inp.w0, block) if fmt == "no_dq" else nf4.quantize(inp.w0, block, c2_format=fmt)
+        hat_bits = (nf4.dequantize_single(rq, inp.w0.shape, block) if fmt == "no_dq"
+                    else nf4.dequantize(rq, inp.w0.shape, block))
+        w_hat = nf4.bf16_bits_to_f32(hat_bits).astype(np.float64)
+        x, a, b, dy = (bf16_bits_as_f32(t) for t in (inp.x, inp.a, inp.b, inp.dy))
+        y_ref, u_ref = qlora.forward(w_hat, x, a, b, 16.0)
+        dx_ref, da_ref, db_ref = qlora.backward(w_hat, x, dy, a, b, 16.0)
+        name = f"block {block} {fmt} m={m} d={d} k={k}"
+        assert_close(u.cpu().numpy(), u_ref, f"{name} U")
+        assert_close(bf16_to_host_f64(y), y_ref, f"{name} Y", bf16_output=True)
+        assert_close(bf16_to_host_f64(dx), dx_ref, f"{name} dX", bf16_output=True)
+        assert_close(da.cpu().numpy(), da_ref, f"{name} dA")
+        assert_close(db.cpu().numpy(), db_ref, f"{name} dB")
+        assert np.array_equal(merged, qlora.merged_weight_bf16(hat_bits, a, b, 16.0)), f"{name} merge"

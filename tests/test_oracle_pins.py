@@ -504,6 +504,29 @@ def test_single_level_error_bound():
         assert q["codes"][i] == nf4.nearest_level_bruteforce(float(x))
 
 
+@pytest.mark.parametrize("block", [128, 256])
+def test_larger_blocks_nearest_level_and_reduction_to_64(block):
+    # each element: the exact brute-force nearest level of w / absmax(its block)
+    w = random_weights(31, (8, 2 * block * 4))
+    q = nf4.quantize_single(w, block)
+    s = q["absmax"][np.arange(w.size) // block]
+    assert np.all(s == np.abs(w.reshape(-1, block)).max(axis=1).repeat(block))
+    rng = np.random.default_rng(32)
+    for i in rng.integers(0, w.size, 200):
+        x = np.float32(np.float32(w.reshape(-1)[i]) / np.float32(s[i]))
+        assert q["codes"][i] == nf4.nearest_level_bruteforce(float(x))
+    # a tensor whose 64-weight pieces all share their block's absmax quantizes the
+    # same with blocks of 64 and of `block` (no double quantization)
+    v = np.clip(random_weights(33, (4, 4 * block)), -0.5, 0.5).reshape(-1, 64)
+    v[:, 3] = np.repeat(np.linspace(0.6, 0.9, v.shape[0] // (block // 64)), block // 64).astype(np.float32)
+    v = v.reshape(4, 4 * block)
+    q64, qb = nf4.quantize_single(v, 64), nf4.quantize_single(v, block)
+    assert np.array_equal(q64["packed"], qb["packed"])
+    assert np.array_equal(nf4.dequantize_single(q64, v.shape, 64), nf4.dequantize_single(qb, v.shape, block))
+    bits = nf4.storage_bits_per_weight(4096 * 4096, block)
+    assert bits["scales_before"] == 32.0 / block and bits["scales_after"] == 8.0 / block + 32.0 / (256 * block)
+
+
 def test_single_level_equals_double_quant_when_dq_is_exact():
     # every block has absmax 0.75: the mean is 0.75 exactly, the centred scales
     # are 0, so c2 = 0, c1 = 127 and the recovered scale is exactly 0.75 --
