@@ -468,7 +468,7 @@ def main():
                     help="only a short fixed launch sequence for rocprofv3 --pmc passes")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
               "(the layer's multi-GPU sharding is a design note only)", file=sys.stderr)
         sys.exit(2)
 

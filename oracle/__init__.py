@@ -2,7 +2,7 @@
 
 TEST INFRASTRUCTURE ONLY.  This package is the plain, slow, obviously
 correct definition that the HIP library is checked against.  Only the test
-suite, the graft smoke entry point and the benchmark's CPU-baseline leg may
+suite, the ``smoke()`` entry point and the benchmark's CPU-baseline leg may
 import it; the product path (``bit_nf4_quantized_13_amd``) never does, and
 this package imports nothing from it.
 
