@@ -14,6 +14,8 @@ namespace {
 
 constexpr int64_t kMaxWeights = int64_t(1) << 30;  // 2^24 NF4 blocks: 65536 DQ groups
 constexpr int64_t kDecodeMaxK = int64_t(1) << 25;  // 32-bit buffer offsets of X and A rows
+constexpr int64_t kMaxDim = int64_t(1) << 20;      // d, k of a linear call: 32-bit offsets in GEMM tiles
+constexpr int64_t kMaxPlanes = int64_t(1) << 29;   // M * r16: U and G as transposed bf16 hi / lo planes
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -111,6 +113,16 @@ bool dropout_params(float p, uint32_t *thr, float *c) {
     return true;
 }
 
+// Shapes the linear calls support.  The kernels address each operand (or
+// each tile of one) through buffer resources with 32-bit byte offsets:
+// d, k <= 2^20; M k (X, dX), M d (Y, dY) and d k (W0) <= 2^30 elements; and
+// M r16 <= 2^29 (r16 = r rounded up to 16) for the bf16 planes of U and G.
+bool linear_shape_ok(int64_t M, int64_t d, int64_t k, int32_t r) {
+    if (d > kMaxDim || k > kMaxDim || d > kMaxWeights / k) return false;
+    if (M > kMaxWeights / k || M > kMaxWeights / d) return false;
+    return M <= kMaxPlanes / cols_rank_pad(r);
+}
+
 int check_linear(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M, const qlora_bf16 *A,
                  const qlora_bf16 *B, int32_t r, float alpha) {
     int st = check_weight(w, true);
@@ -120,6 +132,7 @@ int check_linear(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M, cons
     if (!std::isfinite(alpha)) return QLORA_EINVAL;
     if (r > QLORA_MAX_RANK) return QLORA_ENOTSUP;
     if (w->d % 8 != 0) return QLORA_ENOTSUP;  // bf16 rows of [M x d] must be 16-byte aligned
+    if (!linear_shape_ok(M, w->d, w->k, r)) return QLORA_ENOTSUP;
     if (!aligned(x, 16) || !aligned(A, 16) || !aligned(B, 2)) return QLORA_EALIGN;
     return QLORA_OK;
 }
@@ -195,7 +208,7 @@ int qlora_nf4_dequantize(const qlora_nf4_weight *w, qlora_bf16 *W_out, void *str
 
 size_t qlora_linear_workspace(int64_t M, int64_t d, int64_t k, int32_t r) {
     if (M <= 0 || d <= 0 || k <= 0 || r <= 0 || r > QLORA_MAX_RANK) return 0;
-    if (k % QLORA_NF4_BLOCK != 0 || d > kMaxWeights / k) return 0;
+    if (k % QLORA_NF4_BLOCK != 0 || !linear_shape_ok(M, d, k, r)) return 0;
     return lin_ws(M, d, k, r).total;
 }
 
@@ -318,7 +331,7 @@ int qlora_lora_dropout(const qlora_bf16 *x, int64_t M, int64_t k, float p, uint6
 
 size_t qlora_linear_dropout_workspace(int64_t M, int64_t d, int64_t k, int32_t r) {
     const size_t base = qlora_linear_workspace(M, d, k, r);
-    if (base == 0 || M > kMaxWeights / k) return 0;
+    if (base == 0) return 0;
     return base + round_up(sizeof(uint16_t) * M * k, 256);
 }
 
@@ -330,7 +343,6 @@ int qlora_linear_fwd_dropout(const qlora_nf4_weight *w, const qlora_bf16 *x, int
     uint32_t thr;
     float c;
     if (!Y || !dropout_params(p, &thr, &c)) return QLORA_EINVAL;
-    if (M > kMaxWeights / w->k) return QLORA_ENOTSUP;
     if (!aligned(Y, 16) || (U_save && !aligned(U_save, 4))) return QLORA_EALIGN;
     const LinWs l = lin_ws(M, w->d, w->k, r);
     if (!ws || ws_bytes < qlora_linear_dropout_workspace(M, w->d, w->k, r)) return QLORA_EWORKSPACE;
@@ -363,7 +375,6 @@ int qlora_linear_bwd_dropout(const qlora_nf4_weight *w, const qlora_bf16 *x, con
     uint32_t thr;
     float c;
     if (!dY || !dA || !dB || !dropout_params(p, &thr, &c)) return QLORA_EINVAL;
-    if (M > kMaxWeights / w->k) return QLORA_ENOTSUP;
     if (!aligned(dY, 16) || (dX && !aligned(dX, 16)) || !aligned(dA, 4) || !aligned(dB, 4) ||
         (U && !aligned(U, 4)))
         return QLORA_EALIGN;
@@ -408,6 +419,7 @@ int qlora_linear_gemm_only(const qlora_nf4_weight *w, int32_t backward, const ql
     if (st != QLORA_OK) return st;
     if (!a || !out || M <= 0 || r <= 0) return QLORA_EINVAL;
     if (r > QLORA_MAX_RANK || w->d % 8 != 0) return QLORA_ENOTSUP;
+    if (!linear_shape_ok(M, w->d, w->k, r)) return QLORA_ENOTSUP;
     if (!aligned(a, 16) || !aligned(out, 16)) return QLORA_EALIGN;
     if (!backward && M <= 16 && w->k <= kDecodeMaxK) return QLORA_EINVAL;  // the decode path has no separate GEMM
     const LinWs l = lin_ws(M, w->d, w->k, r);

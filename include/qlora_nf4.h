@@ -46,7 +46,8 @@ extern "C" {
 #define QLORA_OK          0  /* success                                                  */
 #define QLORA_EINVAL      1  /* null pointer, size <= 0, k % block != 0, non-finite alpha */
 #define QLORA_ENOTSUP     2  /* block not 64/128/256, dq_block not 256 or 0, c2_format,
-                                r > 128, tensor too large                                */
+                                r > 128, d k > 2^30 weights, a linear call's sizes beyond
+                                those listed at qlora_linear_workspace                 */
 #define QLORA_EALIGN      3  /* a pointer read/written with 128-bit accesses is not 16-byte aligned */
 #define QLORA_EWORKSPACE  4  /* workspace NULL or smaller than the *_workspace() size     */
 #define QLORA_EHIP        5  /* a HIP launch or runtime error (hipGetLastError)          */
@@ -141,7 +142,11 @@ int qlora_nf4_quantize(const float *W0, const qlora_nf4_weight *w,
 int qlora_nf4_dequantize(const qlora_nf4_weight *w, qlora_bf16 *W_out, void *stream);
 
 /* Bytes of device workspace qlora_linear_fwd / qlora_linear_bwd need for
- * these sizes (the same figure serves both calls; 0 for invalid arguments). */
+ * these sizes (the same figure serves both calls; 0 for invalid arguments).
+ * Sizes every linear call (fwd, bwd, their dropout forms, gemm_only)
+ * supports, else QLORA_ENOTSUP (0 here): d, k <= 2^20; M k, M d and d k at
+ * most 2^30 elements; M r16 <= 2^29 with r16 = r rounded up to 16.  Each
+ * operand is addressed with 32-bit byte offsets inside the kernels. */
 size_t qlora_linear_workspace(int64_t M, int64_t d, int64_t k, int32_t r);
 
 /*

@@ -142,6 +142,13 @@ def _blocks(w: np.ndarray, block: int) -> tuple[np.ndarray, int]:
     return padded.reshape(nb, block), n
 
 
+def block_absmax(w: np.ndarray, block: int = BLOCK) -> np.ndarray:
+    """max |w| of every block of the flattened weights (exact in fp32), the
+    per-block scale of the absmax rule; a ragged tail block is padded with zeros."""
+    blocks, _ = _blocks(w, block)
+    return np.abs(blocks).max(axis=1).astype(np.float32)
+
+
 def quantize_blocks(w: np.ndarray, block: int = BLOCK) -> tuple[np.ndarray, np.ndarray]:
     """NF4-quantize the flattened weights block by block.
 
@@ -152,7 +159,7 @@ def quantize_blocks(w: np.ndarray, block: int = BLOCK) -> tuple[np.ndarray, np.n
     absmax.
     """
     blocks, n = _blocks(w, block)
-    scale = np.abs(blocks).max(axis=1).astype(np.float32)
+    scale = block_absmax(w, block)
     zero_code = int(np.argmin(np.abs(nf4_codebook())))           # the exact 0 (index 7)
     safe = np.where(scale == 0, np.float32(1), scale).astype(np.float32)
     x = (blocks / safe[:, None]).astype(np.float32)              # fp32 IEEE division

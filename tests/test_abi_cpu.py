@@ -75,6 +75,27 @@ FAKE = 0x7F0000000000
 FAKE_MIS = FAKE + 2
 
 
+def test_linear_size_limits():
+    """The linear calls take d, k <= 2^20, M k, M d, d k <= 2^30 and M r16 <= 2^29
+    (r16 = r rounded up to 16); the bounds themselves are accepted."""
+    ws = q.library().qlora_linear_workspace
+    assert ws(1 << 14, 1 << 15, 1 << 15, 64) > 0          # d k = 2^30 (the largest weight)
+    assert ws(1 << 10, 1 << 20, 64, 8) > 0                # M d = 2^30, d = 2^20
+    assert ws(1 << 24, 8, 64, 16) > 0                     # M k = 2^30
+    assert ws(1 << 11, 1 << 20, 64, 8) == 0               # M d = 2^31
+    assert ws(1 << 11, 64, 1 << 20, 8) == 0               # M k = 2^31
+    assert ws(16, 1 << 21, 64, 8) == 0                    # d > 2^20
+    assert ws(16, 8, 1 << 21, 8) == 0                     # k > 2^20
+    assert ws(1 << 22, 64, 64, 128) > 0                   # M r16 = 2^29
+    assert ws(1 << 22, 64, 64, 129) == 0                  # r > 128
+    assert ws((1 << 22) + 8, 64, 64, 128) == 0            # M r16 > 2^29
+    big_d = dict(w=weight(d=1 << 20, k=64), m=1 << 11)    # M d = 2^31
+    assert fwd(**big_d) == q.QLORA_ENOTSUP
+    assert bwd(**big_d) == q.QLORA_ENOTSUP
+    assert gemm_only(**big_d) == q.QLORA_ENOTSUP
+    assert fwd(w=weight(d=8, k=1 << 21)) == q.QLORA_ENOTSUP
+
+
 def weight(d=256, k=512, codes=FAKE, c2=FAKE, c1=FAKE, mean=FAKE, block=64, dq=256):
     return q._CWeight(codes, c2, c1, mean, d, k, block, dq)
 

@@ -123,6 +123,15 @@ def random_weights(seed: int, shape, std: float = W0_STD) -> np.ndarray:
     return out
 
 
+def device_normal(seed: int, shape, std: float = W0_STD, device: str = "cuda"):
+    """N(0, std^2) fp32 drawn on the device by torch's seeded generator, for
+    inputs too large to draw on the host in a test's time (2^30 weights)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32).mul_(std)
+
+
 def random_bf16(seed: int, shape, std: float = 1.0) -> np.ndarray:
     rng = np.random.default_rng(np.random.SeedSequence([seed, 0xBF16]))
     return to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
