@@ -105,10 +105,11 @@ GemmWs gemm_ws(char *base, const LinWs &l) {
                   reinterpret_cast<uint16_t *>(base + l.ext_b), reinterpret_cast<uint16_t *>(base + l.wbf)};
 }
 
-// Dropout parameters: the keep threshold floor(p 2^16) and c = fp32(1 / fp32(1 - p)).
+// Dropout parameters: the keep threshold floor(p 2^32) (exact in fp64; below 2^32
+// for p < 1) and c = fp32(1 / fp32(1 - p)).
 bool dropout_params(float p, uint32_t *thr, float *c) {
     if (!(p >= 0.0f && p < 1.0f)) return false;  // also rejects NaN
-    *thr = (uint32_t)std::floor((double)p * 65536.0);
+    *thr = (uint32_t)std::floor((double)p * 4294967296.0);
     *c = 1.0f / (1.0f - p);
     return true;
 }
@@ -329,10 +330,11 @@ int qlora_lora_dropout(const qlora_bf16 *x, int64_t M, int64_t k, float p, uint6
     return hip_status(launch_lora_dropout(x, M, k, thr, c, seed, xd, static_cast<hipStream_t>(stream)));
 }
 
+// A linear workspace, then Xd [M x k] bf16, then the dX GEMM's fp32 sums [M x k].
 size_t qlora_linear_dropout_workspace(int64_t M, int64_t d, int64_t k, int32_t r) {
     const size_t base = qlora_linear_workspace(M, d, k, r);
     if (base == 0) return 0;
-    return base + round_up(sizeof(uint16_t) * M * k, 256);
+    return base + round_up(sizeof(uint16_t) * M * k, 256) + round_up(sizeof(float) * M * k, 256);
 }
 
 int qlora_linear_fwd_dropout(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M, const qlora_bf16 *A,
@@ -404,9 +406,11 @@ int qlora_linear_bwd_dropout(const qlora_nf4_weight *w, const qlora_bf16 *x, con
     if (e == hipSuccess)
         e = launch_cols_pair(dY, vt_u, d, scale, part_b, dB, 0, xd, vt_g, k, scale, part_a, dA, 1, M, r, red, s);
     if (e == hipSuccess && dX) {
-        // the base term dY What (the GEMM's adapter columns get scale 0), then the masked adapter term
-        e = launch_gemm_dx(nw, dY, M, G, A, r, 0.0f, dX, gemm_ws(base, l), red, s);
-        if (e == hipSuccess) e = launch_dropout_dx_add(dX, M, k, G, r, A, scale * c, thr, seed, s);
+        // the base term dY What in fp32 (the GEMM's adapter columns get scale 0), then the masked
+        // adapter term added to it and the sum rounded once to bf16
+        float *dx_f32 = reinterpret_cast<float *>(base + l.total + round_up(sizeof(uint16_t) * M * k, 256));
+        e = launch_gemm_dx(nw, dY, M, G, A, r, 0.0f, dX, gemm_ws(base, l), red, s, dx_f32);
+        if (e == hipSuccess) e = launch_dropout_dx_add(dx_f32, dX, M, k, G, r, A, scale * c, thr, seed, s);
     } else if (e == hipSuccess) {
         e = launch_cols_reduce(red, s);
     }

@@ -12,11 +12,10 @@
 // The mask comes from Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
 // random numbers: as easy as 1, 2, 3", SC 2011), so the backward regenerates
 // the forward's mask from the seed instead of storing it: element i = m k + col
-// takes the 16-bit half i mod 2 (0: low) of word (i mod 8) div 2 of the block
-// for counter (i div 8 low and high words, 0, 0) and key (seed low, seed high),
-// and is dropped iff that half < floor(p 2^16).
+// uses word i mod 4 of the block for counter (i div 4 low and high words, 0, 0)
+// and key (seed low, seed high), and is dropped iff that word < floor(p 2^32).
 //
-// Both kernels stream: 16 bytes (8 elements, one Philox block) per thread.
+// Both kernels stream: 16 bytes (8 elements, two Philox blocks) per thread.
 #include "launch.hpp"
 
 namespace qnf4 {
@@ -46,14 +45,17 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
     return Philox4{{c0, c1, c2, c3}};
 }
 
-// keep bits of elements 8 t .. 8 t + 7 (bit q: element 8 t + q kept)
+// keep bits of elements 8 t .. 8 t + 7 (bit q: element 8 t + q kept): words of
+// the blocks for counters 2 t (elements 8 t .. + 3) and 2 t + 1 (the next four)
 __device__ __forceinline__ uint32_t keep8(uint64_t t, uint32_t thr, uint32_t s0, uint32_t s1) {
-    const Philox4 a = philox4x32_10((uint32_t)t, (uint32_t)(t >> 32), 0u, 0u, s0, s1);
+    const uint64_t c = 2 * t;
+    const Philox4 a = philox4x32_10((uint32_t)c, (uint32_t)(c >> 32), 0u, 0u, s0, s1);
+    const Philox4 b = philox4x32_10((uint32_t)(c + 1), (uint32_t)((c + 1) >> 32), 0u, 0u, s0, s1);
     uint32_t bits = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        bits |= ((a.w[q] & 0xFFFFu) >= thr ? 1u : 0u) << (2 * q);
-        bits |= ((a.w[q] >> 16) >= thr ? 1u : 0u) << (2 * q + 1);
+        bits |= (a.w[q] >= thr ? 1u : 0u) << q;
+        bits |= (b.w[q] >= thr ? 1u : 0u) << (4 + q);
     }
     return bits;
 }
@@ -79,14 +81,16 @@ __global__ __launch_bounds__(256) void lora_dropout_kernel(const uint4 *__restri
     }
 }
 
-// dX[m][n] = bf16( dX[m][n] + (kept ? sc sum_j G[m][j] A[j][n] : 0) ), j ascending,
-// sc = fl32(s c).  A workgroup covers 4 rows (blockIdx.x) and 2048 columns
+// dX[m][n] = bf16( base[m][n] + (kept ? sc sum_j G[m][j] A[j][n] : 0) ), j ascending,
+// sc = fl32(s c): the fp32 sum of the GEMM's unrounded base term and the masked
+// adapter term, rounded once.  A workgroup covers 4 rows (blockIdx.x) and 2048 columns
 // (blockIdx.y); a thread takes 8 consecutive columns of the 4 rows, so each A
 // load serves 4 rows, and the G values, the same for the whole workgroup, come
 // through scalar loads.
 constexpr int kAddRows = 4;
 
-__global__ __launch_bounds__(256) void dropout_dx_add_kernel(uint4 *__restrict__ dx, int64_t M, int64_t k,
+__global__ __launch_bounds__(256) void dropout_dx_add_kernel(const f32x4 *__restrict__ base,
+                                                             uint4 *__restrict__ dx, int64_t M, int64_t k,
                                                              const float *__restrict__ G, int r,
                                                              const uint16_t *__restrict__ A, float sc, uint32_t thr,
                                                              uint32_t s0, uint32_t s1) {
@@ -122,14 +126,14 @@ __global__ __launch_bounds__(256) void dropout_dx_add_kernel(uint4 *__restrict__
         if (i >= rows) break;
         const int64_t t = ((m0 + i) * k + n) / 8;  // the 8-element item: k % 8 == 0
         const uint32_t keep = keep8((uint64_t)t, thr, s0, s1);
-        const uint4 v = dx[t];
-        const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+        const f32x4 v0 = base[2 * t], v1 = base[2 * t + 1];
+        const float in[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         uint32_t o[4];
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
             const float tlo = (keep >> (2 * h)) & 1u ? sc * acc[i][2 * h] : 0.0f;
             const float thi = (keep >> (2 * h + 1)) & 1u ? sc * acc[i][2 * h + 1] : 0.0f;
-            o[h] = pack_bf16x2(bf16_bits_to_f32(in[h] & 0xFFFFu) + tlo, bf16_bits_to_f32(in[h] >> 16) + thi);
+            o[h] = pack_bf16x2(in[2 * h] + tlo, in[2 * h + 1] + thi);
         }
         dx[t] = uint4{o[0], o[1], o[2], o[3]};
     }
@@ -151,11 +155,11 @@ hipError_t launch_lora_dropout(const uint16_t *x, int64_t M, int64_t k, uint32_t
     return hipGetLastError();
 }
 
-hipError_t launch_dropout_dx_add(uint16_t *dx, int64_t M, int64_t k, const float *G, int r, const uint16_t *A,
-                                 float sc, uint32_t thr, uint64_t seed, hipStream_t st) {
+hipError_t launch_dropout_dx_add(const float *base, uint16_t *dx, int64_t M, int64_t k, const float *G, int r,
+                                 const uint16_t *A, float sc, uint32_t thr, uint64_t seed, hipStream_t st) {
     const dim3 grid((unsigned)((M + kAddRows - 1) / kAddRows), (unsigned)((k / 8 + 255) / 256));
-    hipLaunchKernelGGL(dropout_dx_add_kernel, grid, dim3(256), 0, st, reinterpret_cast<uint4 *>(dx), M, k, G, r, A,
-                       sc, thr, (uint32_t)seed, (uint32_t)(seed >> 32));
+    hipLaunchKernelGGL(dropout_dx_add_kernel, grid, dim3(256), 0, st, reinterpret_cast<const f32x4 *>(base),
+                       reinterpret_cast<uint4 *>(dx), M, k, G, r, A, sc, thr, (uint32_t)seed, (uint32_t)(seed >> 32));
     return hipGetLastError();
 }
 

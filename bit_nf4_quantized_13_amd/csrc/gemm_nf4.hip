@@ -68,6 +68,7 @@ struct GemmArgs {
     const uint16_t *wbf;    // dequantized weight operand [N x ldw] bf16 (non-expanding kernel)
     int64_t ldw;            // forward: What [d x k], ldw = k; dX: What^T [k x ldw], ldw = d rounded up to 64
     uint16_t *out;          // Y or dX [M x N] bf16
+    float *out_f32;         // F32OUT kernels: the fp32 sums [M x N] instead of out
 };
 
 template <int V>
@@ -181,7 +182,9 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // the workgroup (one expansion per output tile row: the choice when the grid
 // has a single tile row).  Otherwise it is transferred like the activation
 // tile from a dequantized bf16 copy written once per call.
-template <bool DX, bool EXPAND>
+// F32OUT: the fp32 sums are stored unrounded (out_f32) for a caller that adds
+// another term before the one bf16 rounding.
+template <bool DX, bool EXPAND, bool F32OUT = false>
 __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Consts tab) {
     // Two stages of the activation tile [512 rows][64 k] and of the weight tile
     // [128 rows][64 k] (160 KiB).  One object per buffer so that the compiler can
@@ -525,8 +528,12 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
         for (int j = 0; j < 8; ++j) {
             const int64_t n = n_base + 16 * j + 4 * g;
             if (n >= p.N) continue;
-            const uint2 o{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
-            *reinterpret_cast<uint2 *>(p.out + m * p.N + n) = o;
+            if constexpr (F32OUT) {
+                *reinterpret_cast<f32x4 *>(p.out_f32 + m * p.N + n) = acc[i][j];
+            } else {
+                const uint2 o{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
+                *reinterpret_cast<uint2 *>(p.out + m * p.N + n) = o;
+            }
         }
     }
 }
@@ -721,9 +728,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a, Nf4Consts tab) {
 
 // core_only: launch the GEMM kernel alone on a workspace that a full launch
 // with the same arguments prepared (block scales, adapter operands, bf16 copy)
+// out_f32 (dX only): store the fp32 sums there instead of bf16 into out
 hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, const float *V,
                   const uint16_t *ext_w, int r, float s, uint16_t *out, const GemmWs &ws,
-                  const ColsReduceJob *red, hipStream_t st, bool core_only = false) {
+                  const ColsReduceJob *red, hipStream_t st, bool core_only = false, float *out_f32 = nullptr) {
     GemmArgs p;
     p.a = a;
     p.M = M;
@@ -739,6 +747,8 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
     p.wbf = ws.wbf;
     p.ldw = dx ? (w.d + 63) / 64 * 64 : w.k;
     p.out = out;
+    p.out_f32 = out_f32;
+    if (out_f32 && !dx) return hipErrorInvalidValue;
     // 32-bit buffer offsets: a 512-row slab of the activation operand and the
     // whole adapter operand must stay below 2 GiB
     if ((int64_t)BM * p.Kd * 2 >= (int64_t(1) << 31) || p.N * p.Ke * 2 >= (int64_t(1) << 31) ||
@@ -784,7 +794,10 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
         else hipLaunchKernelGGL(prep_kernel<false>, pgrid, dim3(256), 0, st, q, nf4_consts());
     }
     const dim3 grid((unsigned)tiles), block(NTHREADS);
-    if (expand) {
+    if (out_f32) {
+        if (expand) hipLaunchKernelGGL((nf4_gemm_kernel<true, true, true>), grid, block, 0, st, p, nf4_consts());
+        else hipLaunchKernelGGL((nf4_gemm_kernel<true, false, true>), grid, block, 0, st, p, nf4_consts());
+    } else if (expand) {
         if (dx) hipLaunchKernelGGL((nf4_gemm_kernel<true, true>), grid, block, 0, st, p, nf4_consts());
         else hipLaunchKernelGGL((nf4_gemm_kernel<false, true>), grid, block, 0, st, p, nf4_consts());
     } else {
@@ -810,8 +823,8 @@ hipError_t launch_gemm_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, co
 
 hipError_t launch_gemm_dx(const Nf4Weights &w, const uint16_t *dy, int64_t M, const float *G,
                           const uint16_t *A, int r, float s, uint16_t *dX, const GemmWs &ws,
-                          const ColsReduceJob *red, hipStream_t st) {
-    return launch(true, w, dy, M, G, A, r, s, dX, ws, red, st);
+                          const ColsReduceJob *red, hipStream_t st, float *dX_f32) {
+    return launch(true, w, dy, M, G, A, r, s, dX, ws, red, st, false, dX_f32);
 }
 
 hipError_t launch_cols_reduce(const ColsReduceJob *red, hipStream_t st) {

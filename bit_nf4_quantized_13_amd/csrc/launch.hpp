@@ -25,9 +25,10 @@ hipError_t launch_dequantize(const uint8_t *codes, const int8_t *c2, const float
 // keeps the element, +0 where it drops it; M k % 8 == 0, 16-byte aligned rows.
 hipError_t launch_lora_dropout(const uint16_t *x, int64_t M, int64_t k, uint32_t thr, float c, uint64_t seed,
                                uint16_t *xd, hipStream_t st);
-// dx[M x k] (bf16, in place) += kept ? sc (G A)[m][n] : 0, with G [M x r] fp32 and A [r x k] bf16.
-hipError_t launch_dropout_dx_add(uint16_t *dx, int64_t M, int64_t k, const float *G, int r, const uint16_t *A,
-                                 float sc, uint32_t thr, uint64_t seed, hipStream_t st);
+// dx[M x k] = bf16( base[m][n] + (kept ? sc (G A)[m][n] : 0) ), one rounding, with base [M x k]
+// fp32, G [M x r] fp32 and A [r x k] bf16.
+hipError_t launch_dropout_dx_add(const float *base, uint16_t *dx, int64_t M, int64_t k, const float *G, int r,
+                                 const uint16_t *A, float sc, uint32_t thr, uint64_t seed, hipStream_t st);
 
 // ---- skinny GEMMs ----------------------------------------------------------
 // out[M x R] (fp32) = In[M x K] (bf16) * W[R x K]^T (bf16), R <= 128.  vt: null,
@@ -88,11 +89,12 @@ hipError_t launch_gemm_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, co
                            hipStream_t st);
 // dX[M x k] = bf16( dY[M x d] What + [hi(sG) | lo(sG)] [A ; A] ),  G [M x r] fp32
 // red: null, or two column reductions (ColsReduceJob) to run in the same
-// preparation launch; launch_cols_reduce runs them alone.
+// preparation launch; launch_cols_reduce runs them alone.  dX_f32: null, or
+// [M x k] fp32 receiving the unrounded sums instead of dX.
 hipError_t launch_cols_reduce(const ColsReduceJob *red, hipStream_t st);
 hipError_t launch_gemm_dx(const Nf4Weights &w, const uint16_t *dy, int64_t M, const float *G,
                           const uint16_t *A, int r, float s, uint16_t *dX, const GemmWs &ws,
-                          const ColsReduceJob *red, hipStream_t st);
+                          const ColsReduceJob *red, hipStream_t st, float *dX_f32 = nullptr);
 
 // The GEMM kernel of launch_gemm_fwd (dx = false) or launch_gemm_dx (dx = true)
 // alone, on a workspace that a full launch with the same arguments prepared.

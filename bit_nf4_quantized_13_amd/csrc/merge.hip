@@ -1,6 +1,6 @@
 // Merging the trained adapter into the weight, and taking it out again:
-//   merge:    W_out = bf16( fp32( What + s S ) )      What = doubleDequant(W_NF4)
-//   unmerge:  W_out = bf16( fp32( W_in - s S ) )      W_in bf16, may be W_out
+//   merge:    W_out = bf16( What + s S )      What = doubleDequant(W_NF4)
+//   unmerge:  W_out = bf16( W_in - s S )      W_in bf16, may be W_out
 // with S[n][k] = sum_j B[n][j] A[j][k] and s = alpha / r.
 //
 // chkda.github.io "Why do we need LoRA and QLoRA?", "Merging LoRA weights for
@@ -12,7 +12,11 @@
 // reproducible bit for bit: S in fp64 with j ascending -- a bf16 x bf16
 // product is exact in fp64, so each step is one fp64 FMA, i.e. one rounding
 // of the exact product added to S -- then s S and the add as two fp64
-// roundings, then fp64 -> fp32 -> bf16, each to nearest even.
+// roundings, then one rounding of that fp64 value to the nearest bf16 (ties
+// to even).  The narrowing goes through fp32 rounded to odd (truncate, then set
+// the last bit if anything was dropped): with 24 >= 8 + 2 significant bits the
+// following fp32 -> bf16 round to nearest even then rounds the fp64 value
+// itself, where a plain fp64 -> fp32 -> bf16 chain could round twice.
 //
 // Bound: r fp64 FMAs per weight against 2.5 bytes of HBM traffic (merge:
 // 0.5 + 1/64 code and constant bytes read, 2 written), so fp64 ALU for large
@@ -125,9 +129,10 @@ __global__ __launch_bounds__(256) void adapter_merge_kernel(const uint8_t *__res
             for (int q = 0; q < 2; ++q) {
                 const double t = s * acc[e][2 * h + q];     // one rounding
                 const double m = (double)base[2 * h + q] + t;  // one rounding
-                f[q] = (float)m;                             // fp64 -> fp32, nearest even
+                const float tz = __double2float_rz(m);       // fp64 -> fp32 rounded to odd
+                f[q] = (double)tz == m ? tz : __uint_as_float(__float_as_uint(tz) | 1u);
             }
-            o[h] = pack_bf16x2(f[0], f[1]);                  // fp32 -> bf16, nearest even
+            o[h] = pack_bf16x2(f[0], f[1]);                  // -> bf16, nearest even: one rounding of m
         }
         *reinterpret_cast<uint4 *>(w_out + n * k + k0) = uint4{o[0], o[1], o[2], o[3]};
     }

@@ -206,10 +206,10 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const qlora_bf16 *x, const qlora
  *        dA = s G^T Xd,  dB = s dY^T U,  dX = dY What + c (Mask o (s G A)),
  * with c = fp32(1 / fp32(1 - p)).  The keep mask is Philox4x32-10 (Salmon et
  * al., "Parallel random numbers: as easy as 1, 2, 3", SC 2011): element
- * i = m k + col of X [M x k] uses the 16-bit half i mod 2 (0: low) of word
- * (i mod 8) div 2 of the block for counter (i div 8 low word, i div 8 high
- * word, 0, 0) and key (seed low, seed high), and is dropped iff that half
- * < floor(p 2^16).  The same (p, seed) in the
+ * i = m k + col of X [M x k] uses word i mod 4 of the block for counter
+ * (i div 4 low word, i div 4 high word, 0, 0) and key (seed low, seed high),
+ * and is dropped iff that word < floor(p 2^32) (p is its fp32 value; the
+ * realised rate is floor(p 2^32) / 2^32).  The same (p, seed) in the
  * forward and the backward gives the same mask; nothing is stored.
  *   p     dropout probability, 0 <= p < 1 (p = 0: the calls without dropout
  *         give the same results); seed any 64-bit value.
@@ -224,7 +224,8 @@ int qlora_lora_dropout(const qlora_bf16 *x, int64_t M, int64_t k, float p, uint6
                        qlora_bf16 *xd, void *stream);
 
 /* Bytes of device workspace the two dropout calls need (a linear workspace
- * plus room for Xd); 0 for invalid arguments. */
+ * plus room for Xd [M x k] bf16 and the backward's fp32 dX sums [M x k]); 0
+ * for invalid arguments. */
 size_t qlora_linear_dropout_workspace(int64_t M, int64_t d, int64_t k, int32_t r);
 
 /*
@@ -242,8 +243,8 @@ int qlora_linear_fwd_dropout(const qlora_nf4_weight *w, const qlora_bf16 *x, int
  * qlora_linear_bwd_dropout -- qlora_linear_bwd with dropout on the adapter
  * input, for the forward with the same p and seed.  Arguments as
  * qlora_linear_bwd plus p and seed (U: that forward's U_save, or NULL to
- * recompute it).  dX: the base term is rounded to bf16 first, then the
- * masked adapter term is added and the sum rounded again.
+ * recompute it).  dX: the base term dY What and the masked adapter term are
+ * added in fp32 and the sum is rounded once to bf16.
  *   ws  >= qlora_linear_dropout_workspace(M, d, k, r) bytes.
  */
 int qlora_linear_bwd_dropout(const qlora_nf4_weight *w, const qlora_bf16 *x, const qlora_bf16 *dY,
@@ -277,10 +278,10 @@ int qlora_linear_gemm_only(const qlora_nf4_weight *w, int32_t backward, const ql
  * reproducible bit for bit:
  *   S[n][k]      = sum over j = 0 .. r-1, ascending, of B[n][j] * A[j][k], in
  *                  fp64 (each product of two bf16 values is exact in fp64)
- *   W_out[n][k]  = BF16( fp32( What[n][k] + s * S[n][k] ) ),  s = fp32(alpha / r)
- * where s * S and the sum are separate fp64 roundings and both narrowings
- * round to nearest even.  To requantize the merged weight, widen W_out to fp32
- * and call qlora_nf4_quantize.
+ *   W_out[n][k]  = BF16( What[n][k] + s * S[n][k] ),  s = fp32(alpha / r)
+ * where s * S and the sum are separate fp64 roundings and the fp64 result is
+ * rounded once to the nearest bf16 (ties to even).  To requantize the merged
+ * weight, widen W_out to fp32 and call qlora_nf4_quantize.
  *   w      the NF4 weight (as for qlora_nf4_dequantize).
  *   A      device bf16 [r x k], 16-byte aligned;  B  device bf16 [d x r].
  *   W_out  device bf16 [d x k], 16-byte aligned, written.  No workspace.
@@ -294,7 +295,7 @@ int qlora_adapter_merge(const qlora_nf4_weight *w, const qlora_bf16 *A, const ql
  * qlora_adapter_unmerge -- take an adapter back out of a merged bf16 weight
  * (chkda, "Merging LoRA weights for inference": keeping base and adapters apart
  * lets one switch adapters):
- *   W_out[n][k] = BF16( fp32( W_in[n][k] - s * S[n][k] ) )
+ *   W_out[n][k] = BF16( W_in[n][k] - s * S[n][k] )   (one rounding, as for the merge)
  * with S and s as in qlora_adapter_merge.  unmerge(merge(What)) recovers What
  * up to the two bf16 roundings: half an ulp of the merged value plus half an
  * ulp of the result, per element.

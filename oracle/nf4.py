@@ -123,6 +123,33 @@ def bf16_rne_bits(x: np.ndarray) -> np.ndarray:
     return ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
 
 
+def bf16_nearest_bits_f64(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to bf16 once: the nearest bf16 value, ties to the
+    one with an even last mantissa bit; returns uint16 bits.
+
+    Written from that definition: the two bf16 neighbours of |x| (8 significant
+    bits, so the float64 pattern truncated to its top 8 significant bits and
+    the next value up) are compared by their exact distances to |x|.  Defined
+    for zero and for magnitudes in the bf16 normal range [2^-126, 2^128).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    mag = np.abs(x)
+    assert np.all((mag == 0) | ((mag >= 2.0 ** -126) & (mag < 2.0 ** 128))), "outside the bf16 normal range"
+    u = mag.view(np.uint64)
+    step = np.uint64(1) << np.uint64(45)                  # 52 - 7 fraction bits dropped
+    lo_b = u & ~(step - np.uint64(1))
+    hi_b = lo_b + step                                    # a carry moves into the exponent, as it should
+    lo, hi = lo_b.view(np.float64), hi_b.view(np.float64)
+    d_lo, d_hi = mag - lo, hi - mag                       # both exact (same binade or Sterbenz)
+    lo_even = (lo_b & step) == 0
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ~lo_even)
+    r = np.where(pick_hi, hi, lo)
+    r = np.where(mag == 0, 0.0, r)
+    bits32 = r.astype(np.float32).view(np.uint32)         # r is a bf16 value: exact in fp32
+    sign = (np.signbit(x).astype(np.uint32) << np.uint32(15))
+    return ((bits32 >> np.uint32(16)) | sign).astype(np.uint16)
+
+
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns to fp32."""
     b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)

@@ -39,15 +39,16 @@ dropout disabled).  Reading R17: dropout acts on the adapter's input only,
 
 with c = fl32(1 / fl32(1 - p)) and the keep mask M drawn by Philox4x32-10
 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3",
-SC 2011) from a 64-bit seed: element i = m k + col takes the 16-bit half
-i mod 2 (0: low) of word (i mod 8) div 2 of the block for counter (i div 8 as
-two 32-bit words, 0, 0) and key (seed low, seed high); it is dropped iff that
-half < floor(p 2^16).
+SC 2011) from a 64-bit seed: element i = m k + col uses word i mod 4 of the
+block for counter (i div 4 as two 32-bit words, 0, 0) and key (seed low, seed
+high); it is dropped iff that word < floor(p 2^32).  The pages fix only the
+rate p (0.05 in fromzero2ai's configuration); comparing a full 32-bit word
+resolves the fp32 value of p to 2^-32, so the realised rate is
+floor(p 2^32) / 2^32.
 
 Merge (chkda "Merging LoRA weights for inference"): W_merged = W0 + s B A,
-in fp64 (merged_weight) and as bf16 under the library's fixed rounding
-(merged_weight_bf16, reading R14: the sum over ranks in fp64 in ascending
-order, two fp64 roundings, then fp32 and bf16 to nearest even).
+in fp64 (merged_weight) and as bf16 (merged_weight_bf16, reading R14: the
+sum computed in fp64, then one rounding to the nearest bf16).
 """
 from __future__ import annotations
 
@@ -104,19 +105,20 @@ def merged_weight(w_hat, a, b, alpha: float) -> np.ndarray:
 
 
 def merged_weight_bf16(base_bits, a, b, alpha: float, sign: float = 1.0) -> np.ndarray:
-    """bf16 bits of base + sign (alpha/r) B A with the merge's fixed rounding
-    (chkda "Merging LoRA weights for inference" gives W0 + (alpha/r) B A and
-    leaves the arithmetic open; reading R14):
+    """bf16 bits of base + sign (alpha/r) B A (chkda "Merging LoRA weights for
+    inference" gives W0 + (alpha/r) B A and leaves the arithmetic open; reading
+    R14): the value computed in fp64, then rounded once to the nearest bf16,
 
         S = sum over j = 0 .. r-1, ascending, of B[:, j] A[j, :]   (fp64; each
             product of two bf16 values is exact, so each step is one rounding)
-        t = s S,  m = base + t                                       (fp64, two roundings)
-        out = bf16(fp32(m))                                          (nearest even, twice)
+        m = base + s S                                               (fp64)
+        out = the bf16 nearest m, ties to even                       (one rounding)
 
-    with s = fp32(alpha / r) as the library computes it.  base_bits: uint16 bf16
-    patterns [d x k] -- What for a merge (sign = +1), the merged weight for an
-    unmerge (sign = -1)."""
-    from .nf4 import bf16_bits_to_f32, bf16_rne_bits
+    with s the fp32 value of alpha / r, the layer's scale (alpha arrives as
+    fp32).  Away from bf16 rounding boundaries this is the exact merge rounded
+    once.  base_bits: uint16 bf16 patterns [d x k] -- What for a merge
+    (sign = +1), the merged weight for an unmerge (sign = -1)."""
+    from .nf4 import bf16_bits_to_f32, bf16_nearest_bits_f64
     a, b = _f64(a), _f64(b)
     r = a.shape[0]
     s = np.float64(np.float32(np.float32(alpha) / np.float32(r))) * np.float64(sign)
@@ -124,7 +126,7 @@ def merged_weight_bf16(base_bits, a, b, alpha: float, sign: float = 1.0) -> np.n
     for j in range(r):
         acc += np.outer(b[:, j], a[j, :])
     m = bf16_bits_to_f32(base_bits).astype(np.float64) + s * acc
-    return bf16_rne_bits(m.astype(np.float32))
+    return bf16_nearest_bits_f64(m)
 
 
 def trainable_parameters(d: int, k: int, r: int) -> int:
@@ -173,10 +175,11 @@ def philox4x32_10(ctr: np.ndarray, key: tuple[int, int]) -> np.ndarray:
 
 
 def dropout_threshold(p: float) -> int:
-    """floor(p 2^16) for the fp32 value of p in [0, 1)."""
+    """floor(p 2^32) for the fp32 value of p in [0, 1) (exact: p 2^32 is a
+    power-of-two scaling of an fp32 value)."""
     p = float(np.float32(p))
     assert 0.0 <= p < 1.0
-    return int(np.floor(p * 2.0 ** 16))
+    return int(np.floor(p * 2.0 ** 32))
 
 
 def dropout_scale(p: float) -> np.float32:
@@ -187,13 +190,12 @@ def dropout_scale(p: float) -> np.float32:
 def dropout_keep_mask(m: int, k: int, p: float, seed: int) -> np.ndarray:
     """Keep mask [m x k] (bool) of reading R17."""
     n = m * k
-    blocks = np.arange((n + 7) // 8, dtype=np.uint64)
+    blocks = np.arange((n + 3) // 4, dtype=np.uint64)
     ctr = np.zeros((blocks.size, 4), dtype=np.uint64)
     ctr[:, 0] = blocks & np.uint64(0xFFFFFFFF)
     ctr[:, 1] = blocks >> np.uint64(32)
-    words = philox4x32_10(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)).reshape(-1)
-    halves = np.stack([words & 0xFFFF, words >> 16], axis=1).reshape(-1)[:n]   # element 2j: low half of word j
-    return (halves.astype(np.int64) >= dropout_threshold(p)).reshape(m, k)
+    words = philox4x32_10(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)).reshape(-1)[:n]
+    return (words.astype(np.int64) >= dropout_threshold(p)).reshape(m, k)
 
 
 def lora_dropout_bits(x_bits: np.ndarray, p: float, seed: int) -> tuple[np.ndarray, np.ndarray]:

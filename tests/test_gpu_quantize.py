@@ -54,6 +54,14 @@ def test_layer4096_full():
     assert_bit_exact(workload_layer("layer4096").w0, "layer4096 4096x4096")
 
 
+@pytest.mark.parametrize("proj", [0, 1])
+def test_decode_workload_weights(proj):
+    """Both weights of the decode workload (4096x4096 and 14336x4096, seed 2):
+    codes, bytes, c2, c1, mean and bf16 weights bit-exact."""
+    wl = WORKLOADS["decode"]
+    assert_bit_exact(workload_layer("decode", proj).w0, f"decode {wl.projections[proj].name}")
+
+
 def test_zero_blocks_zero_groups_and_zero_tensor():
     w = random_weights(12, (16, 64 * 64))
     w[0, :64] = 0.0                   # one all-zero block
