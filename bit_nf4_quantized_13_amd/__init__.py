@@ -23,7 +23,7 @@ import torch
 
 from .build import LIB_PATH
 
-QLORA_OK, QLORA_EINVAL, QLORA_ENOTSUP, QLORA_EALIGN, QLORA_EWORKSPACE, QLORA_EHIP = range(6)
+QLORA_OK, QLORA_EINVAL, QLORA_ENOTSUP, QLORA_EALIGN, QLORA_EWORKSPACE, QLORA_EHIP, QLORA_ESCRATCH = range(7)
 BLOCK = 64
 DQ_BLOCK = 256
 NO_DQ = 0  # dq_block of the format without double quantization (fp32 absmax per block)
@@ -62,6 +62,7 @@ _SIGS = {
     "qlora_linear_workspace": (_SZ, [_I64, _I64, _I64, _I32]),
     "qlora_linear_fwd": (ctypes.c_int, [_WP, _P, _I64, _P, _P, _I32, ctypes.c_float, _P, _P, _P,
                                         _SZ, _P]),
+    "qlora_linear_fwd_noalloc": (ctypes.c_int, [_WP, _P, _I64, _P, _P, _I32, ctypes.c_float, _P, _P, _P]),
     "qlora_linear_bwd": (ctypes.c_int, [_WP, _P, _P, _P, _P, _P, _I64, _I32, ctypes.c_float, _P,
                                         _P, _P, _P, _SZ, _P]),
     "qlora_linear_gemm_only": (ctypes.c_int, [_WP, _I32, _P, _I64, _I32, _P, _P, _SZ, _P]),
@@ -273,6 +274,24 @@ def qlora_linear_fwd(w: NF4Weight, x: torch.Tensor, a: torch.Tensor, b: torch.Te
     return y, u
 
 
+def qlora_linear_fwd_noalloc(w: NF4Weight, x: torch.Tensor, a: torch.Tensor, b: torch.Tensor,
+                             alpha: float, out: torch.Tensor, u_out: torch.Tensor | None = None):
+    """The decode-shaped forward (M <= 16) through qlora_linear_fwd_noalloc: no
+    workspace and no allocation in the call (the caller passes Y, and U if
+    wanted).  Returns (Y, U or None)."""
+    _dev_tensor(x, torch.bfloat16, "x")
+    _dev_tensor(a, torch.bfloat16, "A")
+    _dev_tensor(b, torch.bfloat16, "B")
+    _dev_tensor(out, torch.bfloat16, "Y")
+    if u_out is not None:
+        _dev_tensor(u_out, torch.float32, "U")
+    cw = w.c_struct()
+    _check(_lib.qlora_linear_fwd_noalloc(ctypes.byref(cw), x.data_ptr(), x.shape[0], a.data_ptr(), b.data_ptr(),
+                                         a.shape[0], float(alpha), out.data_ptr(), _ptr(u_out), _stream()),
+           "qlora_linear_fwd_noalloc")
+    return out, u_out
+
+
 def qlora_linear_bwd(w: NF4Weight, x: torch.Tensor, dy: torch.Tensor, a: torch.Tensor,
                      b: torch.Tensor, alpha: float, u: torch.Tensor | None = None,
                      need_dx: bool = True, workspace: torch.Tensor | None = None,
@@ -357,6 +376,7 @@ def adapter_scale(alpha: float, r: int) -> float:
 
 __all__ = [
     "NF4Weight", "QloraError", "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd",
+    "qlora_linear_fwd_noalloc",
     "qlora_linear_bwd", "qlora_linear_gemm_only", "qlora_adapter_merge", "qlora_adapter_unmerge",
     "qlora_lora_dropout",
     "qlora_nf4_codebook", "qlora_nf4_thresholds", "status_str", "library",

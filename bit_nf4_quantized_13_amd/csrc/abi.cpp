@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "launch.hpp"
 
@@ -124,6 +125,59 @@ bool linear_shape_ok(int64_t M, int64_t d, int64_t k, int32_t r) {
     return M <= kMaxPlanes / cols_rank_pad(r);
 }
 
+// ---- the static scratch of qlora_linear_fwd_noalloc ----------------------------
+// Device memory of the allocation-free forward: the decode kernel's counters,
+// its partial sums and, for r > 16, U.  One array per GPU (a __device__ object
+// exists on every device the library runs on), held until the process ends.
+// In host code `scratch` names a host-side stand-in: its device address comes
+// from hipGetSymbolAddress, once per device, and only that address is used.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up on the first call there).
+int scratch_of_current_device(void **addr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QLORA_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return QLORA_EHIP;
+        g_scratch_addr[dev] = p;
+    }
+    *addr = g_scratch_addr[dev];
+    return QLORA_OK;
+}
+
+// Device memory the decode-shaped forward (M <= 16) needs beside its inputs and
+// outputs: counters, partial sums and (r > 16) U.
+struct DecodeWs {
+    size_t ctr, dpart, u, total;
+};
+DecodeWs decode_ws(int64_t M, int64_t d, int64_t k, int r) {
+    DecodeWs l;
+    l.ctr = 0;
+    l.dpart = round_up(decode_counter_bytes(), 256);
+    l.u = l.dpart + round_up(decode_part_bytes(M, d, k), 256);
+    l.total = l.u + round_up(sizeof(float) * M * r, 256);
+    return l;
+}
+
+// The decode-shaped forward: one kernel (U = X A^T fused for r <= 16), or U by
+// the skinny kernel first (into U_save, else u_buf) for r > 16.
+hipError_t decode_forward(const Nf4Weights &nw, const qlora_bf16 *x, int64_t M, const qlora_bf16 *A,
+                          const qlora_bf16 *B, int32_t r, float scale, qlora_bf16 *Y, float *U_save,
+                          unsigned long long *ctr, float *dpart, float *u_buf, hipStream_t s) {
+    if (r <= 16) return launch_decode_fwd(nw, x, M, A, nullptr, B, r, scale, Y, U_save, dpart, ctr, s);
+    float *U = U_save ? U_save : u_buf;
+    hipError_t e = launch_rows_skinny(x, A, M, nw.k, r, U, nullptr, s);
+    if (e == hipSuccess) e = launch_decode_fwd(nw, x, M, nullptr, U, B, r, scale, Y, nullptr, dpart, ctr, s);
+    return e;
+}
+
 int check_linear(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M, const qlora_bf16 *A,
                  const qlora_bf16 *B, int32_t r, float alpha) {
     int st = check_weight(w, true);
@@ -152,6 +206,7 @@ const char *qlora_status_str(int status) {
         case QLORA_EALIGN: return "QLORA_EALIGN: misaligned pointer (16-byte alignment required)";
         case QLORA_EWORKSPACE: return "QLORA_EWORKSPACE: workspace missing or too small";
         case QLORA_EHIP: return "QLORA_EHIP: HIP launch or runtime error";
+        case QLORA_ESCRATCH: return "QLORA_ESCRATCH: the allocation-free call takes M <= 16 and sizes whose scratch fits the library's static 8 MiB";
         default: return "unknown qlora status";
     }
 }
@@ -234,17 +289,34 @@ int qlora_linear_fwd(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M,
     hipError_t e = hipSuccess;
     if (M <= 16 && w->k <= kDecodeMaxK) {
         // HBM-bound: one pass over the codes; U = X A^T in the same kernel for r <= 16
-        if (r <= 16) {
-            e = launch_decode_fwd(nw, x, M, A, nullptr, B, r, scale, Y, U_save, dpart, ctr, s);
-        } else {
-            e = launch_rows_skinny(x, A, M, w->k, r, U, nullptr, s);
-            if (e == hipSuccess) e = launch_decode_fwd(nw, x, M, nullptr, U, B, r, scale, Y, nullptr, dpart, ctr, s);
-        }
+        e = decode_forward(nw, x, M, A, B, r, scale, Y, U_save, ctr, dpart, U, s);
     } else {
         e = launch_rows_skinny(x, A, M, w->k, r, U, nullptr, s);
         if (e == hipSuccess) e = launch_gemm_fwd(nw, x, M, U, B, r, scale, Y, gemm_ws(base, l), s);
     }
     return hip_status(e);
+}
+
+int qlora_linear_fwd_noalloc(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M, const qlora_bf16 *A,
+                             const qlora_bf16 *B, int32_t r, float alpha, qlora_bf16 *Y, float *U_save,
+                             void *stream) {
+    int st = check_linear(w, x, M, A, B, r, alpha);
+    if (st != QLORA_OK) return st;
+    if (!Y) return QLORA_EINVAL;
+    if (!aligned(Y, 16) || (U_save && !aligned(U_save, 4))) return QLORA_EALIGN;
+    if (M > 16 || w->k > kDecodeMaxK) return QLORA_ESCRATCH;
+    const DecodeWs l = decode_ws(M, w->d, w->k, r);
+    if (l.total > kNoAllocScratchBytes) return QLORA_ESCRATCH;
+    void *addr = nullptr;
+    st = scratch_of_current_device(&addr);
+    if (st != QLORA_OK) return st;
+    (void)hipGetLastError();
+    char *base = static_cast<char *>(addr);
+    const float scale = alpha / static_cast<float>(r);
+    return hip_status(decode_forward(nf4_view(w), x, M, A, B, r, scale, Y, U_save,
+                                     reinterpret_cast<unsigned long long *>(base + l.ctr),
+                                     reinterpret_cast<float *>(base + l.dpart), reinterpret_cast<float *>(base + l.u),
+                                     static_cast<hipStream_t>(stream)));
 }
 
 int qlora_linear_bwd(const qlora_nf4_weight *w, const qlora_bf16 *x, const qlora_bf16 *dY,

@@ -29,8 +29,9 @@
  *     undefined (but memory-safe) results.
  *   - Calls are reentrant: the library holds no mutable global state (the
  *     NF4 table is computed once, on first use, behind a thread-safe
- *     initialiser).  Calls that share a workspace must be ordered on one
- *     stream.
+ *     initialiser; qlora_linear_fwd_noalloc keeps the device address of its
+ *     static scratch per device).  Calls that share a workspace must be
+ *     ordered on one stream.
  */
 #ifndef QLORA_NF4_H
 #define QLORA_NF4_H
@@ -51,6 +52,8 @@ extern "C" {
 #define QLORA_EALIGN      3  /* a pointer read/written with 128-bit accesses is not 16-byte aligned */
 #define QLORA_EWORKSPACE  4  /* workspace NULL or smaller than the *_workspace() size     */
 #define QLORA_EHIP        5  /* a HIP launch or runtime error (hipGetLastError)          */
+#define QLORA_ESCRATCH    6  /* qlora_linear_fwd_noalloc: M > 16, or the call's scratch
+                                exceeds the library's static maximum (8 MiB)           */
 
 #define QLORA_NF4_BLOCK     64   /* weights per NF4 block (chkda, "Quantizing and dequantizing with the codebook") */
 #define QLORA_NF4_DQ_BLOCK  256  /* block constants per second-level group (chkda, "Double quantization ...")   */
@@ -174,6 +177,27 @@ size_t qlora_linear_workspace(int64_t M, int64_t d, int64_t k, int32_t r);
 int qlora_linear_fwd(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M,
                      const qlora_bf16 *A, const qlora_bf16 *B, int32_t r, float alpha,
                      qlora_bf16 *Y, float *U_save, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * qlora_linear_fwd_noalloc -- qlora_linear_fwd for decode-shaped calls
+ * (M <= 16) that allocates nothing and takes no workspace: for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  It runs the kernels of
+ * qlora_linear_fwd's M <= 16 path and gives the same bits.  Their device
+ * memory (the decode kernel's counters and partial sums and, for r > 16, U)
+ * is a static array of 8 MiB that the library holds on every GPU it runs on
+ * until the process ends; a call whose needs exceed it returns
+ * QLORA_ESCRATCH, as does M > 16.  Arguments as for qlora_linear_fwd, without
+ * ws and ws_bytes; the current device must be the device of `stream`.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (on different streams, or from different threads without ordering) race and
+ * may return wrong results.  The array keeps the last call's counters, which
+ * the kernel tags on first use and leaves ready for the next call (nothing
+ * needs clearing between calls).
+ */
+int qlora_linear_fwd_noalloc(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M,
+                             const qlora_bf16 *A, const qlora_bf16 *B, int32_t r, float alpha,
+                             qlora_bf16 *Y, float *U_save, void *stream);
 
 /*
  * qlora_linear_bwd -- gradients of the layer for an upstream gradient dY.
@@ -326,7 +350,7 @@ const char *qlora_status_str(int status);
 
 /* ABI version of this header/library pair. */
 int qlora_abi_version(void);
-#define QLORA_ABI_VERSION 2
+#define QLORA_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

@@ -53,7 +53,7 @@ def test_thresholds_are_smallest_fp32_above_midpoints():
 
 
 def test_status_strings():
-    for code in range(6):
+    for code in range(7):
         assert q.status_str(code).startswith("QLORA_")
     assert q.status_str(99) == "unknown qlora status"
 
@@ -171,6 +171,23 @@ def test_bwd_rejects_invalid_arguments(kw, status):
     assert bwd(**kw) == status
 
 
+def fwd_noalloc(w=None, x=FAKE, m=16, a=FAKE, b=FAKE, r=8, alpha=16.0, y=FAKE, u=None):
+    w = w or weight()
+    return q.library().qlora_linear_fwd_noalloc(ctypes.byref(w), x, m, a, b, r, alpha, y, u, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), q.QLORA_EINVAL), (dict(y=None), q.QLORA_EINVAL), (dict(m=0), q.QLORA_EINVAL),
+    (dict(r=129), q.QLORA_ENOTSUP), (dict(alpha=float("nan")), q.QLORA_EINVAL),
+    (dict(w=weight(d=252)), q.QLORA_ENOTSUP), (dict(y=FAKE_MIS), q.QLORA_EALIGN),
+    (dict(u=FAKE + 1), q.QLORA_EALIGN), (dict(m=17), q.QLORA_ESCRATCH), (dict(m=4096), q.QLORA_ESCRATCH),
+])
+def test_fwd_noalloc_rejects_before_touching_the_device(kw, status):
+    """The allocation-free forward checks its arguments like qlora_linear_fwd
+    and refuses sizes beyond its static scratch (M > 16) before any device call."""
+    assert fwd_noalloc(**kw) == status
+
+
 def test_valid_call_without_gpu_reports_hip_error():
     """With no device present a valid call must fail with QLORA_EHIP, not crash."""
     import torch
@@ -178,6 +195,7 @@ def test_valid_call_without_gpu_reports_hip_error():
         pytest.skip("a GPU is present: this check is for hosts without one")
     w = weight()
     assert quant(w) == q.QLORA_EHIP
+    assert fwd_noalloc(m=4) == q.QLORA_EHIP       # no device: no scratch address
 
 
 def test_no_double_quant_format_validation():
