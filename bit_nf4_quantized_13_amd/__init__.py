@@ -368,18 +368,12 @@ def qlora_adapter_unmerge(w_in: torch.Tensor, a: torch.Tensor, b: torch.Tensor, 
     return y
 
 
-def adapter_scale(alpha: float, r: int) -> float:
-    """alpha / r as the library computes it (fp32)."""
-    import numpy as np
-    return float(np.float32(alpha) / np.float32(r))
-
-
 __all__ = [
     "NF4Weight", "QloraError", "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd",
     "qlora_linear_fwd_noalloc",
     "qlora_linear_bwd", "qlora_linear_gemm_only", "qlora_adapter_merge", "qlora_adapter_unmerge",
     "qlora_lora_dropout",
     "qlora_nf4_codebook", "qlora_nf4_thresholds", "status_str", "library",
-    "abi_version", "quantize_workspace_bytes", "linear_workspace_bytes", "adapter_scale",
+    "abi_version", "quantize_workspace_bytes", "linear_workspace_bytes",
     "BLOCK", "DQ_BLOCK", "NO_DQ", "C2_INT8", "C2_FP8_E4M3",
 ]

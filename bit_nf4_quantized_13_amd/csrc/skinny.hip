@@ -33,9 +33,9 @@ __device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
 }
 
 // ---------------------------------------------------------------------------
-// out[M x R] = In[M x K] W[R x K]^T.  One workgroup per 16 rows; the four
-// waves split K in chunks of 128 (round robin) and are summed in LDS in a
-// fixed order.
+// out[M x R] = In[M x K] W[R x K]^T.  One workgroup per 16 rows; its W waves
+// (eight as launched) split K in chunks of 128 (round robin) and are summed
+// in LDS in a fixed order.
 // ---------------------------------------------------------------------------
 constexpr int kRowsMaxTiles = 8;  // R <= 128
 

@@ -147,9 +147,11 @@ int qlora_nf4_dequantize(const qlora_nf4_weight *w, qlora_bf16 *W_out, void *str
 /* Bytes of device workspace qlora_linear_fwd / qlora_linear_bwd need for
  * these sizes (the same figure serves both calls; 0 for invalid arguments).
  * Sizes every linear call (fwd, bwd, their dropout forms, gemm_only)
- * supports, else QLORA_ENOTSUP (0 here): d, k <= 2^20; M k, M d and d k at
- * most 2^30 elements; M r16 <= 2^29 with r16 = r rounded up to 16.  Each
- * operand is addressed with 32-bit byte offsets inside the kernels. */
+ * supports, else QLORA_ENOTSUP (0 here): d % 8 == 0 (each bf16 row of Y and
+ * dY [M x d] starts 16-byte aligned; k % 64 == 0 already holds for X and
+ * dX); d, k <= 2^20; M k, M d and d k at most 2^30 elements; M r16 <= 2^29
+ * with r16 = r rounded up to 16.  Each operand is addressed with 32-bit byte
+ * offsets inside the kernels. */
 size_t qlora_linear_workspace(int64_t M, int64_t d, int64_t k, int32_t r);
 
 /*
