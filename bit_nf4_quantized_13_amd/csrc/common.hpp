@@ -11,7 +11,9 @@ namespace qnf4 {
 struct Nf4Consts {
     float level[16];
     float thresh[15];
-    float pad_;
+    // 1 when every threshold, as y = T 64 + 64 in fp32, lies more than 2^-11
+    // from an integer (the quantize kernel's bucket table relies on it)
+    int bucket_ok;
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

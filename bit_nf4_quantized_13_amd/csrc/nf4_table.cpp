@@ -55,7 +55,11 @@ Nf4Consts build() {
         if (static_cast<double>(f) <= mid) f = std::nextafter(f, INFINITY);
         t.thresh[j] = f;
     }
-    t.pad_ = 0.0f;
+    t.bucket_ok = 1;
+    for (int j = 0; j < 15; ++j) {
+        const float ty = t.thresh[j] * 64.0f + 64.0f;  // the kernel's fp32 arithmetic
+        if (std::fabs(ty - std::nearbyint(ty)) <= 0x1p-11f) t.bucket_ok = 0;
+    }
     return t;
 }
 

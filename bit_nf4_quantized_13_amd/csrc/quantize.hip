@@ -41,18 +41,25 @@ constexpr int kGroup = 256;
 // 64) approximates 64 x + 64 in [0, 128] to within 2.5e-5 (rcp and the two
 // roundings), so bucket i = (uint) y covers x in about [(i - 64)/64, (i -
 // 63)/64): 129 buckets of width 1/64, and the thresholds (at least 0.08 apart)
-// put at most one in each.  Entry i holds the count of thresholds below the
-// bucket and the one inside it (in y units), so code = base + (y >= t).  A y
-// within kBandY (2^-13, five times the error) of that threshold, or not a
-// number (an absmax below 2^-100 or zero reciprocal), takes the exact path:
-// the IEEE quotient compared with all 15 thresholds.  A threshold within kBandY
-// of a bucket edge would make both buckets exact-path-only; no NF4 threshold is
-// (all lie 0.015 or more from an edge in y units).  Two instructions form the
-// index where the previous exponent-and-mantissa bucketing took five.
+// put at most one in each.  Entry i is one fp32 word t'_i: the threshold
+// inside the bucket in y units (ty = T_j 64 + 64, rounded once; 2^100 if there
+// is none) with its four lowest mantissa bits replaced by the count of
+// thresholds below the bucket, so code = (bits(t'_i) & 15) + (y >= t'_i).
+// The replaced bits move t'_i by less than 16 ulp(ty) <= 1.2e-4 (ty < 128),
+// so the fast decision can differ from the exact one only when |y - t'_i| is
+// at most 2^-13 (five times the error of y) + 1.2e-4 < kBandY = 2^-12; such a
+// y, or one that is not a number (an absmax below 2^-100 or zero
+// reciprocal), takes the exact path: the IEEE quotient compared with all 15
+// thresholds.  This needs every ty more than kBandY away from the edges of its
+// bucket (else the neighbouring bucket would have to check it too): the NF4
+// thresholds are 0.015 or more away, which the host verifies once
+// (Nf4Consts::bucket_ok); were it not so, every weight would take the exact
+// path.  One-dword entries keep the table's LDS reads nearly free of bank
+// conflicts, and a lookup costs the wave four VALU operations besides it.
 // a lane's value after a DPP lane permutation within its row of 16 lanes
 template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
 }
 
 constexpr int kLutEntries = 129;
@@ -65,38 +72,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
     void *p = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
     return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, n, 0x00020000);
 }
-constexpr float kBandY = 0x1p-13f;
+constexpr float kBandY = 0x1p-12f;
 
-struct LutEntry {
-    uint32_t base;
-    float thresh;  // the one threshold inside the bucket (y units), or +inf
-    float lo, hi;  // where y must go the exact way
-};
-
-// Entry i (bucket [i, i + 1) of y): its base count and the threshold inside it.
-__device__ void lut_entry(int i, const Nf4Consts &t, LutEntry *out) {
+// Entry i (bucket [i, i + 1) of y), as fp32 bits.
+__device__ uint32_t lut_entry(int i, const Nf4Consts &t) {
     const float lo = (float)i, hi = (float)(i + 1);
-    uint32_t base = 0;
-    float inside = __builtin_inff();
-    bool edge = false;
+    uint32_t base = 0, inside = 0x71800000u;  // 2^100: no threshold in the bucket
     for (int j = 0; j < 15; ++j) {
-        const float ty = t.thresh[j] * 64.0f + 64.0f;  // one rounding (< 2^-16), far inside the band
+        const float ty = t.thresh[j] * 64.0f + 64.0f;  // one rounding (< 2^-17)
         if (ty < lo) ++base;
-        else if (ty < hi) inside = ty;
-        if (fabsf(ty - lo) <= 2.0f * kBandY || fabsf(ty - hi) <= 2.0f * kBandY) edge = true;
+        else if (ty < hi) inside = __float_as_uint(ty);
     }
-    out->base = base;
-    out->thresh = inside;
-    if (edge) {
-        out->lo = -__builtin_inff();
-        out->hi = __builtin_inff();
-    } else if (inside == __builtin_inff()) {
-        out->lo = __builtin_inff();  // no threshold: an empty band
-        out->hi = -__builtin_inff();
-    } else {
-        out->lo = inside - kBandY;
-        out->hi = inside + kBandY;
-    }
+    return (inside & ~15u) | base;
 }
 
 // Each wave owns 64 consecutive blocks of the group: 8 rounds of 8 blocks.
@@ -107,7 +94,7 @@ __global__ __launch_bounds__(256) void nf4_quantize_groups(
     const float *__restrict__ w, int64_t nb, Nf4Consts tab, uint8_t *__restrict__ codes,
     float *__restrict__ absmax, double *__restrict__ group_sum) {
     __shared__ float s_abs[kGroup];
-    __shared__ LutEntry lut[kLutEntries];
+    __shared__ uint32_t lut[kLutEntries];  // fp32 bits, see lut_entry
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t blk0 = (int64_t)blockIdx.x * kGroup;
     s_abs[tid] = 0.0f;  // missing blocks of a ragged last group count as +0.0
@@ -124,7 +111,7 @@ __global__ __launch_bounds__(256) void nf4_quantize_groups(
         v[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
                                               rw, (uint32_t)(local * kBlock * 4 + (lane & 15) * 16), 0, 0));
     }
-    if (tid < kLutEntries) lut_entry(tid, tab, &lut[tid]);
+    if (tid < kLutEntries) lut[tid] = lut_entry(tid, tab);
     // s_abs cleared and the table built before any lane uses them; an LDS-only
     // fence, so the barrier does not wait for the loads above
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -134,21 +121,19 @@ __global__ __launch_bounds__(256) void nf4_quantize_groups(
     // together, one branch for the (rare) exact path
     auto code4 = [&](const float4 &wv, float m, float r64) {
         const float w4[4] = {wv.x, wv.y, wv.z, wv.w};
-        float y[4];
-        LutEntry e[4];
+        float y[4], t[4];
         uint32_t q[4];
         bool slow = false;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             y[c] = __builtin_fmaf(w4[c], r64, 64.0f);
-            const uint32_t i = (uint32_t)fminf(fmaxf(y[c], 0.0f), 128.0f);  // NaN -> 0
-            e[c] = lut[i];
+            t[c] = __uint_as_float(lut[(uint32_t)fminf(fmaxf(y[c], 0.0f), 128.0f)]);  // NaN -> entry 0
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            q[c] = e[c].base + (y[c] >= e[c].thresh ? 1u : 0u);
+            q[c] = (__float_as_uint(t[c]) & 15u) + (y[c] >= t[c] ? 1u : 0u);
             // near a threshold (or y not a number): decide with the exact quotient
-            slow |= !((y[c] > e[c].hi) | (y[c] < e[c].lo));
+            slow |= !(fabsf(y[c] - t[c]) > kBandY);
         }
         if (__builtin_expect(slow, 0)) {
 #pragma unroll
@@ -162,29 +147,45 @@ __global__ __launch_bounds__(256) void nf4_quantize_groups(
         }
         return q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12);
     };
+    // Codes and absmax stay in registers until every block is coded: a global
+    // store issued between the waits for the loads above would be counted with
+    // them (one in-order counter), and each later wait would then hold the wave
+    // until loads it does not need yet have landed.
+    uint32_t pk[8];  // block i's 16 code bits at bits 16 (i % 2) of pk[i / 2]
+    float mv[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int local = wave * 64 + (i >> 1) * 8 + (i & 1) * 4 + (lane >> 4);
-        const int64_t blk = blk0 + local;
-        float m = fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w)));
-        m = fmaxf(m, dpp_f32<0xB1>(m));   // quad_perm [1,0,3,2]
-        m = fmaxf(m, dpp_f32<0x4E>(m));   // quad_perm [2,3,0,1]
-        m = fmaxf(m, dpp_f32<0x141>(m));  // row_half_mirror
-        m = fmaxf(m, dpp_f32<0x140>(m));  // row_mirror: the max of the 16 lanes of the block
+        // |w| of finite values orders like its bit pattern read as an unsigned integer
+        const uint32_t a0 = __float_as_uint(v[i].x) & 0x7FFFFFFFu, a1 = __float_as_uint(v[i].y) & 0x7FFFFFFFu;
+        const uint32_t a2 = __float_as_uint(v[i].z) & 0x7FFFFFFFu, a3 = __float_as_uint(v[i].w) & 0x7FFFFFFFu;
+        uint32_t mb = max(max(a0, a1), max(a2, a3));
+        mb = max(mb, dpp_u32<0xB1>(mb));   // quad_perm [1,0,3,2]
+        mb = max(mb, dpp_u32<0x4E>(mb));   // quad_perm [2,3,0,1]
+        mb = max(mb, dpp_u32<0x141>(mb));  // row_half_mirror
+        mb = max(mb, dpp_u32<0x140>(mb));  // row_mirror: the max of the 16 lanes of the block
+        const float m = __uint_as_float(mb);
         uint32_t packed4 = 0x7777u;  // exact-zero level for an all-zero block
         if (m != 0.0f) {
             // an absmax below 2^-100 (reciprocal near overflow, subnormal
             // operands) takes the exact path for every weight
-            const float r64 = m >= 0x1p-100f ? __builtin_amdgcn_rcpf(m) * 64.0f : __builtin_nanf("");
+            const float r64 = (m >= 0x1p-100f && tab.bucket_ok) ? __builtin_amdgcn_rcpf(m) * 64.0f
+                                                                : __builtin_nanf("");
             packed4 = code4(v[i], m, r64);
         }
+        if (i % 2 == 0) pk[i / 2] = packed4;
+        else pk[i / 2] |= packed4 << 16;
+        mv[i] = m;
+        if ((lane & 15) == 0 && blk0 + local < nb) s_abs[local] = m;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int local = wave * 64 + (i >> 1) * 8 + (i & 1) * 4 + (lane >> 4);
+        const int64_t blk = blk0 + local;
         if (blk < nb) {
-            const uint16_t packed = (uint16_t)packed4;
-            *reinterpret_cast<uint16_t *>(codes + blk * (kBlock / 2) + (lane & 15) * 2) = packed;
-            if ((lane & 15) == 0) {
-                absmax[blk] = m;
-                s_abs[local] = m;
-            }
+            *reinterpret_cast<uint16_t *>(codes + blk * (kBlock / 2) + (lane & 15) * 2) =
+                (uint16_t)(pk[i / 2] >> (16 * (i % 2)));
+            if ((lane & 15) == 0) absmax[blk] = mv[i];
         }
     }
     __syncthreads();
