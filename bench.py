@@ -12,11 +12,18 @@ One step is one pass of the whole hot path over the layer4096 workload
 All inputs are resident in HBM before the timed region.  `value` is the
 forward + backward algorithmic flops per step (4 M d k + 6 M r (d + k)) over
 the measured time of the whole step (quantization included), in TFLOP/s.
+`roofline` is the forward dequant-GEMM kernel, its duration averaged over the
+timed steps (HIP events the library records around it inside the calls,
+qlora_time_next_kernel); the same kernel launched alone is reported beside it.
 
 The same run measures the decode-shaped forward (decode workload: W0 4096 x
 4096 and 14336 x 4096, M in {1, 4, 16}, r = 16, alpha = 32) as GB/s of packed
-NF4 bytes, rotating over weight copies totalling more than 512 MB so that
-neither the 256 MB Infinity Cache nor L2 serves them.
+NF4 bytes and of all algorithmic bytes, per call of a HIP-graph replay of
+calls that rotate over weight copies totalling more than 512 MB (so that
+neither the 256 MB Infinity Cache nor L2 serves them), with events around the
+kernel inside ordinary calls beside it; and the 7B- and
+65B-shaped layers (all seven projections, forward + backward, and the quantize
+of every weight of the layer).
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -74,6 +81,14 @@ def traffic_from_profiles(key: str, source: str):
             return None
         return round(float(kv["hbm_bytes_per_launch"]))
     return None
+
+
+def new_event(torch):
+    """A timing event that exists on the device (torch creates events lazily,
+    at their first record)."""
+    e = torch.cuda.Event(enable_timing=True)
+    e.record()
+    return e
 
 
 class Timer:
@@ -134,17 +149,25 @@ def run_layer_bench(q, torch, steps, warmup):
 
     for _ in range(warmup):
         step(False)
+    # events the library records around each step's two dequant-GEMM kernels
+    # (qlora_time_next_kernel), created up front
+    kev = [[new_event(torch) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     log(f"layer4096: timing {steps} steps")
-    # the timed region: K whole steps, events only at its two ends
+    # the timed region: K whole steps; besides its two end events, only the
+    # markers the library records around the GEMM kernels inside the calls
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
-    for _ in range(steps):
+    for i in range(steps):
+        q.qlora_time_next_kernel("fwd_gemm", kev[i][0], kev[i][1])
+        q.qlora_time_next_kernel("dx_gemm", kev[i][2], kev[i][3])
         step(False)
     ev1.record()
     torch.cuda.synchronize()
+    gemm_fwd_ms = sum(e[0].elapsed_time(e[1]) for e in kev) / steps
+    gemm_dx_ms = sum(e[2].elapsed_time(e[3]) for e in kev) / steps
     wall_ms = (time.perf_counter() - t0) * 1e3
     total_ms = ev0.elapsed_time(ev1)
     ms_step = total_ms / steps
@@ -163,12 +186,18 @@ def run_layer_bench(q, torch, steps, warmup):
         "wall_ms_per_step": wall_ms / steps,
         "tflops_step": flops / (ms_step * 1e-3) / 1e12,
         "tflops_fwd_bwd": flops / (fb_ms * 1e-3) / 1e12,
-        "phases": phases, "flops": flops,
+        "phases": phases, "flops": flops, "gemm_fwd_ms": gemm_fwd_ms, "gemm_dx_ms": gemm_dx_ms,
         "quantize_gbs": (d * k * 4 + d * k // 2 + d * k // 64) / (phases["quantize_ms"] * 1e-3) / 1e9,
     }
 
 
-def run_decode_bench(q, torch, iters=50):
+def run_decode_bench(q, torch, iters=50, graph_replays=10):
+    """Per decode shape: the time per call of `iters` calls on rotating weight
+    copies captured in a HIP graph and replayed (one kernel per call, no host
+    launch gaps: the kernel's duration plus the dispatch between kernels) and,
+    beside it, the interval between HIP events the library records right
+    before and after the kernel inside ordinary calls (which adds the events'
+    own dispatch, about 2 us at these durations)."""
     from workloads import WORKLOADS, workload_layer
     from tests.helpers import to_dev_bf16, to_dev_f32
     wl = WORKLOADS["decode"]
@@ -187,29 +216,113 @@ def run_decode_bench(q, torch, iters=50):
             y = torch.empty((m, p.d), dtype=torch.bfloat16, device="cuda")
             lws = torch.empty(q.linear_workspace_bytes(m, p.d, p.k, wl.r), dtype=torch.uint8,
                               device="cuda")
+
+            def call(it):
+                q.qlora_linear_fwd(ws[it % copies], x, a, b, wl.alpha, save_u=False, out=y, workspace=lws)
             for i in range(copies):
-                q.qlora_linear_fwd(ws[i], x, a, b, wl.alpha, save_u=False, out=y, workspace=lws)
+                call(i)
+            kev = [(new_event(torch), new_event(torch)) for _ in range(iters)]
             torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
             for it in range(iters):
-                q.qlora_linear_fwd(ws[it % copies], x, a, b, wl.alpha, save_u=False, out=y,
-                                   workspace=lws)
-            e1.record()
+                q.qlora_time_next_kernel("decode", kev[it][0], kev[it][1])
+                call(it)
             torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / iters
-            gbs = packed / (us * 1e-6) / 1e9
+            kern_us = sum(e0.elapsed_time(e1) for e0, e1 in kev) * 1e3 / iters
+            # the same calls captured once and replayed
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for it in range(iters):
+                    call(it)
+            torch.cuda.current_stream().wait_stream(side)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for it in range(iters):
+                    call(it)
+            graph.replay()
+            torch.cuda.synchronize()
+            g0 = torch.cuda.Event(enable_timing=True)
+            g1 = torch.cuda.Event(enable_timing=True)
+            g0.record()
+            for _ in range(graph_replays):
+                graph.replay()
+            g1.record()
+            torch.cuda.synchronize()
+            graph_us = g0.elapsed_time(g1) * 1e3 / (graph_replays * iters)
+            del graph
             alg = decode_bytes(m, p.d, p.k, wl.r)
-            out[f"{p.name}_m{m}"] = {"us_per_call": round(us, 3), "kernels_per_call": 1,
+            gbs = packed / (graph_us * 1e-6) / 1e9
+            out[f"{p.name}_m{m}"] = {"graph_us_per_call": round(graph_us, 3), "kernels_per_call": 1,
+                                     "event_bracket_us": round(kern_us, 3),
                                      "packed_gbs": round(gbs, 1),
                                      "hbm_frac_packed": round(gbs / HBM_PEAK_GBS, 4),
                                      "algorithmic_bytes": alg,
-                                     "algorithmic_gbs": round(alg / (us * 1e-6) / 1e9, 1)}
-            log(f"decode {p.name} M={m}: {us:.2f} us/call, {gbs:.0f} GB/s packed")
+                                     "algorithmic_gbs": round(alg / (graph_us * 1e-6) / 1e9, 1)}
+            log(f"decode {p.name} M={m}: graph {graph_us:.2f} us/call, events around the kernel "
+                f"{kern_us:.2f} us, {gbs:.0f} GB/s packed")
         del ws
         torch.cuda.empty_cache()
     return out
+
+
+def run_model_bench(q, torch, name, reps=5, warm=2):
+    """All projections of a model-shaped layer (llama7b: q, k, v, o 4096x4096,
+    gate, up 11008x4096, down 4096x11008, M = 2048, r = 64; llama65b: 8192 and
+    22016 wide, M = 4096, r = 64; alpha = 16): per projection, the quantize of
+    its W0 and forward + backward (event-timed, `reps` calls after `warm`).
+    Inputs with the workload's distributions (W0 ~ N(0, 0.02^2), A ~ N(0,
+    1/r), B ~ N(0, 0.01^2), x, dY ~ N(0, 1)), drawn on the device by torch's
+    seeded generator: these sizes take too long to draw on the host."""
+    from workloads import WORKLOADS, device_normal
+    wl = WORKLOADS[name]
+    m, r, alpha = wl.m[0], wl.r, wl.alpha
+    per, tot_flops, tot_ms, q_ms, n_w = {}, 0, 0.0, 0.0, 0
+    for pi, p in enumerate(wl.projections):
+        d, k = p.d, p.k
+        seed = 1000 * wl.seed + 10 * pi
+        w0 = device_normal(seed, (d, k))
+        a = device_normal(seed + 1, (r, k), std=1.0 / r ** 0.5).to(torch.bfloat16)
+        b = device_normal(seed + 2, (d, r), std=0.01).to(torch.bfloat16)
+        x = device_normal(seed + 3, (m, k), std=1.0).to(torch.bfloat16)
+        dy = device_normal(seed + 4, (m, d), std=1.0).to(torch.bfloat16)
+        wq = q.NF4Weight.empty(d, k)
+        qws = torch.empty(q.quantize_workspace_bytes(d, k), dtype=torch.uint8, device="cuda")
+        lws = torch.empty(q.linear_workspace_bytes(m, d, k, r), dtype=torch.uint8, device="cuda")
+        y = torch.empty((m, d), dtype=torch.bfloat16, device="cuda")
+        u = torch.empty((m, r), dtype=torch.float32, device="cuda")
+        outs = (torch.empty((m, k), dtype=torch.bfloat16, device="cuda"),
+                torch.empty((r, k), dtype=torch.float32, device="cuda"),
+                torch.empty((d, r), dtype=torch.float32, device="cuda"))
+        qm = time_calls(torch, lambda: q.qlora_nf4_quantize(w0, out=wq, workspace=qws), reps)
+        del w0
+
+        def fwd_bwd():
+            q.qlora_linear_fwd(wq, x, a, b, alpha, out=y, u_out=u, workspace=lws)
+            q.qlora_linear_bwd(wq, x, dy, a, b, alpha, u=u, workspace=lws, outs=outs)
+        for _ in range(warm):
+            fwd_bwd()
+        fb = time_calls(torch, fwd_bwd, reps)
+        fl = fwd_flops(m, d, k, r) + bwd_flops(m, d, k, r)
+        per[p.name] = {"d": d, "k": k, "fwd_bwd_ms": round(fb, 4),
+                       "fwd_bwd_tflops": round(fl / (fb * 1e-3) / 1e12, 2), "quantize_us": round(qm * 1e3, 2)}
+        tot_flops += fl
+        tot_ms += fb
+        q_ms += qm
+        n_w += d * k
+        log(f"{name} {p.name} {d}x{k}: fwd+bwd {fb:.3f} ms = {fl / (fb * 1e-3) / 1e12:.0f} TFLOP/s, "
+            f"quantize {qm * 1e3:.1f} us")
+        del wq, qws, lws, y, u, outs, x, dy, a, b
+        torch.cuda.empty_cache()
+    # quantize bytes: fp32 W0 read, packed codes + c2 bytes + c1 and the mean written
+    nb = n_w // 64
+    q_bytes = 4 * n_w + n_w // 2 + nb + 4 * (nb // 256) + 4 * len(wl.projections)
+    return {"workload": f"{name}: {len(wl.projections)} projections, M={m}, r={r}, alpha={alpha}",
+            "fwd_bwd_ms": round(tot_ms, 4), "fwd_bwd_tflops": round(tot_flops / (tot_ms * 1e-3) / 1e12, 2),
+            "fwd_bwd_frac": round(tot_flops / (tot_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "flops": tot_flops, "quantize_weights": n_w, "quantize_ms": round(q_ms, 4),
+            "quantize_gbs": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+            "quantize_hbm_frac": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "per_projection": per}
 
 
 def gemm_flops(m, d, k, r):
@@ -384,7 +497,8 @@ def decode_roofline(decode):
             "frac": round(e["algorithmic_gbs"] / HBM_PEAK_GBS, 4),
             "traffic": traffic_from_profiles("nf4_decode_kernel_w14336x4096_m16", "decode.hip"),
             "kernel": "nf4_decode_kernel (decode forward, 14336 x 4096, M = 16)",
-            "kernel_us": e["us_per_call"], "work_per_launch": f"{e['algorithmic_bytes']} bytes"}
+            "kernel_us": e["graph_us_per_call"], "event_bracket_us": e["event_bracket_us"],
+            "work_per_launch": f"{e['algorithmic_bytes']} bytes"}
 
 
 def pmc_run(q, torch, which):
@@ -464,6 +578,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-models", action="store_true")
     ap.add_argument("--pmc-run", choices=["gemm", "decode"],
                     help="only a short fixed launch sequence for rocprofv3 --pmc passes")
     args = ap.parse_args()
@@ -484,21 +599,30 @@ def main():
 
     ctx, lay = run_layer_bench(q, torch, args.steps, args.warmup)
     m, d, k, r = lay["m"], lay["d"], lay["k"], lay["r"]
-    # dominant kernel: the forward dequant-GEMM (nf4_gemm_kernel), launched alone
+    # dominant kernel: the forward dequant-GEMM (nf4_gemm_kernel), its average
+    # duration inside the timed steps; the same kernel launched alone beside it
+    gemm_ms = lay["gemm_fwd_ms"]
     log("layer4096: timing the forward GEMM kernel alone")
-    gemm_ms = time_gemm_only(q, torch, ctx, max(args.steps, 10))
-    achieved = gemm_flops(m, d, k, r) / (gemm_ms * 1e-3) / 1e12
+    alone_ms = time_gemm_only(q, torch, ctx, max(args.steps, 10))
+    gf = gemm_flops(m, d, k, r)
+    achieved = gf / (gemm_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic_from_profiles("nf4_gemm_kernel_fwd_layer4096", "gemm_nf4.hip"),
-                "kernel": "nf4_gemm_kernel<fwd> (layer4096 forward)",
+                "kernel": "nf4_gemm_kernel<fwd> (layer4096 forward), average inside the timed steps",
                 "kernel_us": round(gemm_ms * 1e3, 2),
-                "work_per_launch": f"2*M*d*k + 2*M*d*r = {gemm_flops(m, d, k, r)} flop"}
+                "work_per_launch": f"2*M*d*k + 2*M*d*r = {gf} flop",
+                "alone_kernel_us": round(alone_ms * 1e3, 2),
+                "alone_frac": round(gf / (alone_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "dx_kernel_us": round(lay["gemm_dx_ms"] * 1e3, 2),
+                "dx_frac": round((2 * m * d * k + 2 * m * k * r) / (lay["gemm_dx_ms"] * 1e-3) / 1e12
+                                 / BF16_PEAK_TFLOPS, 4)}
     log("layer4096: timing the adapter merge")
     merge = run_merge_bench(q, torch, ctx)
     decode = None if args.skip_decode else run_decode_bench(q, torch)
     formats = None if args.skip_decode else {f: run_format_bench(q, torch, ctx, f) for f in ("no_dq", "fp8")}
     dropout = None if args.skip_decode else run_dropout_bench(q, torch, ctx)
+    models = None if args.skip_models else {n: run_model_bench(q, torch, n) for n in ("llama7b", "llama65b")}
     cpu = None
     if not args.skip_cpu_baseline:
         log("cpu baseline: timing the oracle on a bounded sample")
@@ -520,6 +644,7 @@ def main():
         "adapter_merge": merge,
         "other_formats": formats,
         "adapter_dropout": dropout,
+        "model_layers": models,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

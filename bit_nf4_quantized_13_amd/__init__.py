@@ -66,6 +66,7 @@ _SIGS = {
     "qlora_linear_bwd": (ctypes.c_int, [_WP, _P, _P, _P, _P, _P, _I64, _I32, ctypes.c_float, _P,
                                         _P, _P, _P, _SZ, _P]),
     "qlora_linear_gemm_only": (ctypes.c_int, [_WP, _I32, _P, _I64, _I32, _P, _P, _SZ, _P]),
+    "qlora_time_next_kernel": (ctypes.c_int, [_I32, _P, _P]),
     "qlora_adapter_merge": (ctypes.c_int, [_WP, _P, _P, _I32, ctypes.c_float, _P, _P]),
     "qlora_adapter_unmerge": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, ctypes.c_float, _P, _P]),
     "qlora_lora_dropout": (ctypes.c_int, [_P, _I64, _I64, ctypes.c_float, ctypes.c_uint64, _P, _P]),
@@ -341,6 +342,19 @@ def qlora_linear_gemm_only(w: NF4Weight, backward: bool, a: torch.Tensor, r: int
     return out
 
 
+TIMED_KERNELS = {"fwd_gemm": 0, "dx_gemm": 1, "decode": 2}
+
+
+def qlora_time_next_kernel(kernel: str, before, after) -> None:
+    """Measurement only: the next launch of `kernel` ("fwd_gemm", "dx_gemm",
+    "decode") records the torch.cuda.Event `before` right before the kernel and
+    `after` right after it, on the stream the library launches on; read the
+    kernel's duration with before.elapsed_time(after) once it has run.  The
+    events must have been recorded once already (torch creates them lazily)."""
+    _check(_lib.qlora_time_next_kernel(TIMED_KERNELS[kernel], before.cuda_event, after.cuda_event),
+           "qlora_time_next_kernel")
+
+
 def qlora_adapter_merge(w: NF4Weight, a: torch.Tensor, b: torch.Tensor, alpha: float,
                         out: torch.Tensor | None = None) -> torch.Tensor:
     """bf16 [d, k] = What + (alpha/r) B A (qlora_adapter_merge's fixed rounding)."""
@@ -371,7 +385,8 @@ def qlora_adapter_unmerge(w_in: torch.Tensor, a: torch.Tensor, b: torch.Tensor, 
 __all__ = [
     "NF4Weight", "QloraError", "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd",
     "qlora_linear_fwd_noalloc",
-    "qlora_linear_bwd", "qlora_linear_gemm_only", "qlora_adapter_merge", "qlora_adapter_unmerge",
+    "qlora_linear_bwd", "qlora_linear_gemm_only", "qlora_time_next_kernel", "qlora_adapter_merge",
+    "qlora_adapter_unmerge",
     "qlora_lora_dropout",
     "qlora_nf4_codebook", "qlora_nf4_thresholds", "status_str", "library",
     "abi_version", "quantize_workspace_bytes", "linear_workspace_bytes",

@@ -194,6 +194,22 @@ int check_linear(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M, cons
 
 }  // namespace
 
+// ---- the measurement hook (qlora_time_next_kernel) ----------------------------
+namespace {
+std::mutex g_time_mu;
+hipEvent_t g_time_ev[kTimedKernels][2];
+}  // namespace
+
+void qnf4::timing_mark(int kernel, bool after, hipStream_t st) {
+    hipEvent_t e;
+    {
+        std::lock_guard<std::mutex> lock(g_time_mu);
+        e = g_time_ev[kernel][after ? 1 : 0];
+        if (after) g_time_ev[kernel][0] = g_time_ev[kernel][1] = nullptr;
+    }
+    if (e) (void)hipEventRecord(e, st);
+}
+
 extern "C" {
 
 int qlora_abi_version(void) { return QLORA_ABI_VERSION; }
@@ -505,6 +521,14 @@ int qlora_linear_gemm_only(const qlora_nf4_weight *w, int32_t backward, const ql
     const Nf4Weights nw = nf4_view(w);
     return hip_status(launch_gemm_core(backward != 0, nw, a, M, r, out, gemm_ws(static_cast<char *>(ws), l),
                                        static_cast<hipStream_t>(stream)));
+}
+
+int qlora_time_next_kernel(int32_t kernel, void *before, void *after) {
+    if (kernel < 0 || kernel >= kTimedKernels || (before == nullptr) != (after == nullptr)) return QLORA_EINVAL;
+    std::lock_guard<std::mutex> lock(g_time_mu);
+    g_time_ev[kernel][0] = static_cast<hipEvent_t>(before);
+    g_time_ev[kernel][1] = static_cast<hipEvent_t>(after);
+    return QLORA_OK;
 }
 
 }  // extern "C"

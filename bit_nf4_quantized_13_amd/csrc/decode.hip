@@ -606,10 +606,13 @@ DecodePlan decode_plan(int64_t d, int64_t k) {
 
 template <int TW, bool FU, int F>
 hipError_t launch_fu(const DecodeArgs &a, int grid, hipStream_t st) {
+    timing_mark(kTimeDecode, false, st);
     if (a.M == 1) hipLaunchKernelGGL((nf4_decode_kernel<TW, 1, 1, FU, F>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
     else if (a.M <= 8) hipLaunchKernelGGL((nf4_decode_kernel<TW, 4, 1, FU, F>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
     else hipLaunchKernelGGL((nf4_decode_kernel<TW, 4, 2, FU, F>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    timing_mark(kTimeDecode, true, st);
+    return e;
 }
 
 template <int TW, int F>

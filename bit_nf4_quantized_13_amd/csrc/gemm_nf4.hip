@@ -547,7 +547,7 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
 // row for 8 lanes; the 8 x 8 block is transposed in registers (v_perm) and
 // stored as 16-byte column pieces, so no LDS is involved and every store is a
 // contiguous 128-byte row segment per 8 lanes.  (The forward's What, laid out
-// like the codes, is written by a plain stride loop in prep_kernel.)  Narrower
+// like the codes, is written by its own job in prep_kernel.)  Narrower
 // blocks (8 x 4) and two tiles per workgroup with the next one's loads
 // overlapping were both slower.
 __device__ __forceinline__ void dequant_tile_t(int64_t bid, const uint8_t *__restrict__ codes, int fmt, int bshift,
@@ -651,6 +651,8 @@ __device__ __forceinline__ void cols_reduce(const ColsReduceJob &jb, int64_t e) 
     else jb.out[n * jb.R + j] = jb.scale * sum;
 }
 
+constexpr int kWU = 2;  // 8-weight units per thread of the forward What copy
+
 template <bool DX>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a, Nf4Consts tab) {
     int64_t b = blockIdx.x;
@@ -700,23 +702,44 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a, Nf4Consts tab) {
         if constexpr (DX) {
             dequant_tile_t(b, a.codes, a.fmt, a.bshift, a.c2, a.c1, mean, a.d, a.k, a.ldw, tab, a.wbf);
         } else {
-            // What [d x k], row-major like the codes: a stride loop over 8-weight
-            // items (one code dword -> one 16-byte store), the levels in LDS
-            __shared__ float lut[16];
-            if (threadIdx.x < 16) lut[threadIdx.x] = tab.level[threadIdx.x];
-            __syncthreads();
-            const int64_t items = a.d * a.k / 8;
-            const uint32_t *codes4 = reinterpret_cast<const uint32_t *>(a.codes);
-            uint4 *out = reinterpret_cast<uint4 *>(a.wbf);
-            for (int64_t i = b * 256 + threadIdx.x; i < items; i += a.g_t * 256) {
-                const uint32_t c = codes4[i];
-                const float sh = block_scale(a.fmt, a.c2, a.c1, mean, i >> 3, a.bshift);  // 8 items per 64 weights
-                uint4 o;
-                o.x = pack_bf16x2(lut[c & 15] * sh, lut[(c >> 4) & 15] * sh);
-                o.y = pack_bf16x2(lut[(c >> 8) & 15] * sh, lut[(c >> 12) & 15] * sh);
-                o.z = pack_bf16x2(lut[(c >> 16) & 15] * sh, lut[(c >> 20) & 15] * sh);
-                o.w = pack_bf16x2(lut[(c >> 24) & 15] * sh, lut[c >> 28] * sh);
-                out[i] = o;
+            // What [d x k], row-major like the codes.  Wave w of workgroup b
+            // writes the 512 kWU weights from 512 kWU (4 b + w): unit u of lane
+            // l is the 8 weights at 512 u + 8 l (one code dword in, one 16-byte
+            // piece out), so every load and store instruction of a wave covers
+            // one contiguous span; all loads are issued before the first store,
+            // and the workgroups run in several rounds, whose reads and writes
+            // overlap.
+            const int lane = threadIdx.x & 63;
+            float lvf = tab.level[0];
+#pragma unroll
+            for (int j = 1; j < 16; ++j) lvf = (lane & 15) == j ? tab.level[j] : lvf;
+            const int lv = __float_as_int(lvf);
+            const int64_t total = a.d * a.k;  // a multiple of 64
+            const int64_t e0 = (b * 4 + (threadIdx.x >> 6)) * (512 * kWU) + 8 * lane;
+            const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.codes, total / 2);  // past the end: zero
+            uint32_t cw[kWU];
+            float sc[kWU];
+#pragma unroll
+            for (int u = 0; u < kWU; ++u) {
+                const int64_t e = e0 + 512 * u;
+                cw[u] = load4(rc, (uint32_t)(e / 2), 0);
+                const int64_t ec = e < total ? e : total - 64;  // a valid block for units past the end
+                sc[u] = block_scale(a.fmt, a.c2, a.c1, mean, ec >> 6, a.bshift);
+            }
+            uint4 o[kWU];
+#pragma unroll
+            for (int u = 0; u < kWU; ++u) {
+                uint32_t pr[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    pr[q] = pack_bf16x2(level(code_addr(cw[u], 2 * q), lv) * sc[u],
+                                        level(code_addr(cw[u], 2 * q + 1), lv) * sc[u]);
+                o[u] = uint4{pr[0], pr[1], pr[2], pr[3]};
+            }
+#pragma unroll
+            for (int u = 0; u < kWU; ++u) {
+                const int64_t e = e0 + 512 * u;
+                if (e < total) *reinterpret_cast<uint4 *>(a.wbf + e) = o[u];
             }
         }
         return;
@@ -785,8 +808,8 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
         q.g_shat = expand ? (q.nb + 255) / 256 : 0;  // only the expanding GEMM reads the scales
         q.g_a = (M * (p.Ke / 8) + 255) / 256;
         q.g_b = (p.N * (p.Ke / 8) + 255) / 256;
-        // the bf16 copy of What (forward: a stride loop over 8-weight items) or What^T (dX: 64 x 256 tiles)
-        q.g_t = expand ? 0 : ((w.k + 255) / 256) * ((w.d + 63) / 64);
+        // the bf16 copy of What (forward: 2048 kWU weights per workgroup) or What^T (dX: 64 x 256 tiles)
+        q.g_t = expand ? 0 : dx ? ((w.k + 255) / 256) * ((w.d + 63) / 64) : (w.d * w.k + 2048 * kWU - 1) / (2048 * kWU);
         q.g_r0 = (q.red[0].N * q.red[0].R + 255) / 256;
         const int64_t g_r1 = (q.red[1].N * q.red[1].R + 255) / 256;
         const dim3 pgrid((unsigned)(q.g_shat + q.g_a + q.g_b + q.g_t + q.g_r0 + g_r1));
@@ -794,6 +817,7 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
         else hipLaunchKernelGGL(prep_kernel<false>, pgrid, dim3(256), 0, st, q, nf4_consts());
     }
     const dim3 grid((unsigned)tiles), block(NTHREADS);
+    timing_mark(dx ? kTimeDxGemm : kTimeFwdGemm, false, st);
     if (out_f32) {
         if (expand) hipLaunchKernelGGL((nf4_gemm_kernel<true, true, true>), grid, block, 0, st, p, nf4_consts());
         else hipLaunchKernelGGL((nf4_gemm_kernel<true, false, true>), grid, block, 0, st, p, nf4_consts());
@@ -804,7 +828,9 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
         if (dx) hipLaunchKernelGGL((nf4_gemm_kernel<true, false>), grid, block, 0, st, p, nf4_consts());
         else hipLaunchKernelGGL((nf4_gemm_kernel<false, false>), grid, block, 0, st, p, nf4_consts());
     }
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    timing_mark(dx ? kTimeDxGemm : kTimeFwdGemm, true, st);
+    return e;
 }
 
 }  // namespace

@@ -60,6 +60,13 @@ hipError_t launch_cols_pair(const uint16_t *in0, const uint16_t *vt0, int64_t N0
                             float scale1, float *part1, float *out1, int trans1, int64_t M, int R,
                             ColsReduceJob *jobs, hipStream_t s);
 
+// ---- measurement hook (qlora_time_next_kernel) -----------------------------
+// A launcher calls timing_mark(kernel, false, st) right before and
+// timing_mark(kernel, true, st) right after its kernel; each records the
+// event a benchmark asked for, if any, on st (the pair is used once).
+enum TimedKernel : int { kTimeFwdGemm = 0, kTimeDxGemm = 1, kTimeDecode = 2, kTimedKernels = 3 };
+void timing_mark(int kernel, bool after, hipStream_t st);
+
 // ---- fused NF4 dequant GEMMs ----------------------------------------------
 struct Nf4Weights {
     const uint8_t *codes;

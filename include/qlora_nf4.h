@@ -280,7 +280,8 @@ int qlora_linear_bwd_dropout(const qlora_nf4_weight *w, const qlora_bf16 *x, con
                              void *ws, size_t ws_bytes, void *stream);
 
 /*
- * qlora_linear_gemm_only -- the dequant-GEMM kernel of the preceding
+ * qlora_linear_gemm_only -- measurement only (benchmarks; not part of the
+ * layer's computation): the dequant-GEMM kernel of the preceding
  * qlora_linear_fwd (backward = 0) or qlora_linear_bwd (backward = 1) call,
  * launched alone, so that its duration can be measured in isolation.  Those
  * calls first run small preparation kernels (U = X A^T or G = dY B, the
@@ -295,6 +296,20 @@ int qlora_linear_bwd_dropout(const qlora_nf4_weight *w, const qlora_bf16 *x, con
  */
 int qlora_linear_gemm_only(const qlora_nf4_weight *w, int32_t backward, const qlora_bf16 *a, int64_t M,
                            int32_t r, qlora_bf16 *out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * qlora_time_next_kernel -- measurement only (benchmarks): the next launch of
+ * the named kernel records `before` on its stream right before the kernel and
+ * `after` right after it, so that the kernel's own duration can be read with
+ * hipEventElapsedTime while it runs inside ordinary calls.  kernel: 0 the
+ * forward dequant-GEMM (qlora_linear_fwd with M > 16), 1 the dX dequant-GEMM
+ * (qlora_linear_bwd), 2 the decode kernel (qlora_linear_fwd with M <= 16).
+ * The pair is used once; NULL, NULL cancels a pending pair.  Both are
+ * hipEvent_t handles created on the device the calls run on.  The setting is
+ * process-wide: no other thread may launch that kernel meanwhile.
+ * Errors: QLORA_EINVAL (unknown kernel, only one event given).
+ */
+int qlora_time_next_kernel(int32_t kernel, void *before, void *after);
 
 /*
  * qlora_adapter_merge -- fold the adapter into a dense bf16 weight.
@@ -352,7 +367,7 @@ const char *qlora_status_str(int status);
 
 /* ABI version of this header/library pair. */
 int qlora_abi_version(void);
-#define QLORA_ABI_VERSION 3
+#define QLORA_ABI_VERSION 4
 
 #ifdef __cplusplus
 }
