@@ -13,15 +13,15 @@ All inputs are resident in HBM before the timed region.  `value` is the
 forward + backward algorithmic flops per step (4 M d k + 6 M r (d + k)) over
 the measured time of the whole step (quantization included), in TFLOP/s.
 `roofline` is the forward dequant-GEMM kernel, its duration averaged over the
-timed steps (HIP events the library records around it inside the calls,
+timed steps (each launch stamps its own execution span when asked,
 qlora_time_next_kernel); the same kernel launched alone is reported beside it.
 
 The same run measures the decode-shaped forward (decode workload: W0 4096 x
 4096 and 14336 x 4096, M in {1, 4, 16}, r = 16, alpha = 32) as GB/s of packed
-NF4 bytes and of all algorithmic bytes, per call of a HIP-graph replay of
-calls that rotate over weight copies totalling more than 512 MB (so that
-neither the 256 MB Infinity Cache nor L2 serves them), with events around the
-kernel inside ordinary calls beside it; and the 7B- and
+NF4 bytes and of all algorithmic bytes, from the decode kernel's own
+execution span (calls rotating over weight copies totalling more than 512 MB
+so that neither the 256 MB Infinity Cache nor L2 serves them), with the time
+per call of the same calls replayed from a HIP graph beside it; and the 7B- and
 65B-shaped layers (all seven projections, forward + backward, and the quantize
 of every weight of the layer).
 
@@ -83,14 +83,6 @@ def traffic_from_profiles(key: str, source: str):
     return None
 
 
-def new_event(torch):
-    """A timing event that exists on the device (torch creates events lazily,
-    at their first record)."""
-    e = torch.cuda.Event(enable_timing=True)
-    e.record()
-    return e
-
-
 class Timer:
     """HIP events on torch's current stream (the stream the library launches on)."""
 
@@ -149,25 +141,26 @@ def run_layer_bench(q, torch, steps, warmup):
 
     for _ in range(warmup):
         step(False)
-    # events the library records around each step's two dequant-GEMM kernels
-    # (qlora_time_next_kernel), created up front
-    kev = [[new_event(torch) for _ in range(4)] for _ in range(steps)]
+    # execution spans of each timed step's two dequant-GEMM launches
+    # (qlora_time_next_kernel: the kernels stamp them themselves)
+    spans = torch.tensor([[-1, 0]] * (2 * steps), dtype=torch.int64, device="cuda")
     torch.cuda.synchronize()
     log(f"layer4096: timing {steps} steps")
-    # the timed region: K whole steps; besides its two end events, only the
-    # markers the library records around the GEMM kernels inside the calls
+    # the timed region: K whole steps, events only at its two ends
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
     for i in range(steps):
-        q.qlora_time_next_kernel("fwd_gemm", kev[i][0], kev[i][1])
-        q.qlora_time_next_kernel("dx_gemm", kev[i][2], kev[i][3])
+        q.qlora_time_next_kernel("fwd_gemm", spans[2 * i])
+        q.qlora_time_next_kernel("dx_gemm", spans[2 * i + 1])
         step(False)
     ev1.record()
     torch.cuda.synchronize()
-    gemm_fwd_ms = sum(e[0].elapsed_time(e[1]) for e in kev) / steps
-    gemm_dx_ms = sum(e[2].elapsed_time(e[3]) for e in kev) / steps
+    khz = q.wall_clock_khz()
+    dur = q.span_duration_us(spans, khz)
+    gemm_fwd_ms = sum(dur[0::2]) / steps * 1e-3
+    gemm_dx_ms = sum(dur[1::2]) / steps * 1e-3
     wall_ms = (time.perf_counter() - t0) * 1e3
     total_ms = ev0.elapsed_time(ev1)
     ms_step = total_ms / steps
@@ -179,6 +172,7 @@ def run_layer_bench(q, torch, steps, warmup):
     torch.cuda.synchronize()
     phases = {"quantize_ms": tq.total_ms() / steps, "fwd_ms": tf.total_ms() / steps,
               "bwd_ms": tb.total_ms() / steps}
+
     fb_ms = phases["fwd_ms"] + phases["bwd_ms"]
     ctx = (wq, x, a, b, alpha, y, u, lws, r)
     return ctx, {
@@ -192,12 +186,13 @@ def run_layer_bench(q, torch, steps, warmup):
 
 
 def run_decode_bench(q, torch, iters=50, graph_replays=10):
-    """Per decode shape: the time per call of `iters` calls on rotating weight
-    copies captured in a HIP graph and replayed (one kernel per call, no host
-    launch gaps: the kernel's duration plus the dispatch between kernels) and,
-    beside it, the interval between HIP events the library records right
-    before and after the kernel inside ordinary calls (which adds the events'
-    own dispatch, about 2 us at these durations)."""
+    """Per decode shape: the decode kernel's duration (its execution span, which
+    the kernel stamps itself when asked, qlora_time_next_kernel; averaged over
+    `iters` ordinary calls on rotating weight copies; one kernel per call, so
+    this is the per-call sum of kernel durations) and, beside it, the time
+    per call of the same calls captured in a HIP graph and replayed (no host
+    launch gaps)."""
+    khz = q.wall_clock_khz()
     from workloads import WORKLOADS, workload_layer
     from tests.helpers import to_dev_bf16, to_dev_f32
     wl = WORKLOADS["decode"]
@@ -221,13 +216,13 @@ def run_decode_bench(q, torch, iters=50, graph_replays=10):
                 q.qlora_linear_fwd(ws[it % copies], x, a, b, wl.alpha, save_u=False, out=y, workspace=lws)
             for i in range(copies):
                 call(i)
-            kev = [(new_event(torch), new_event(torch)) for _ in range(iters)]
+            spans = torch.tensor([[-1, 0]] * iters, dtype=torch.int64, device="cuda")
             torch.cuda.synchronize()
             for it in range(iters):
-                q.qlora_time_next_kernel("decode", kev[it][0], kev[it][1])
+                q.qlora_time_next_kernel("decode", spans[it])
                 call(it)
             torch.cuda.synchronize()
-            kern_us = sum(e0.elapsed_time(e1) for e0, e1 in kev) * 1e3 / iters
+            kern_us = sum(q.span_duration_us(spans, khz)) / iters
             # the same calls captured once and replayed
             side = torch.cuda.Stream()
             side.wait_stream(torch.cuda.current_stream())
@@ -251,15 +246,16 @@ def run_decode_bench(q, torch, iters=50, graph_replays=10):
             graph_us = g0.elapsed_time(g1) * 1e3 / (graph_replays * iters)
             del graph
             alg = decode_bytes(m, p.d, p.k, wl.r)
-            gbs = packed / (graph_us * 1e-6) / 1e9
-            out[f"{p.name}_m{m}"] = {"graph_us_per_call": round(graph_us, 3), "kernels_per_call": 1,
-                                     "event_bracket_us": round(kern_us, 3),
+            gbs = packed / (kern_us * 1e-6) / 1e9
+            out[f"{p.name}_m{m}"] = {"kernel_us": round(kern_us, 3), "kernels_per_call": 1,
+                                     "graph_us_per_call": round(graph_us, 3),
                                      "packed_gbs": round(gbs, 1),
                                      "hbm_frac_packed": round(gbs / HBM_PEAK_GBS, 4),
                                      "algorithmic_bytes": alg,
-                                     "algorithmic_gbs": round(alg / (graph_us * 1e-6) / 1e9, 1)}
-            log(f"decode {p.name} M={m}: graph {graph_us:.2f} us/call, events around the kernel "
-                f"{kern_us:.2f} us, {gbs:.0f} GB/s packed")
+                                     "algorithmic_gbs": round(alg / (kern_us * 1e-6) / 1e9, 1),
+                                     "algorithmic_gbs_graph": round(alg / (graph_us * 1e-6) / 1e9, 1)}
+            log(f"decode {p.name} M={m}: kernel {kern_us:.2f} us, graph {graph_us:.2f} us/call, "
+                f"{gbs:.0f} GB/s packed")
         del ws
         torch.cuda.empty_cache()
     return out
@@ -497,7 +493,7 @@ def decode_roofline(decode):
             "frac": round(e["algorithmic_gbs"] / HBM_PEAK_GBS, 4),
             "traffic": traffic_from_profiles("nf4_decode_kernel_w14336x4096_m16", "decode.hip"),
             "kernel": "nf4_decode_kernel (decode forward, 14336 x 4096, M = 16)",
-            "kernel_us": e["graph_us_per_call"], "event_bracket_us": e["event_bracket_us"],
+            "kernel_us": e["kernel_us"], "graph_us_per_call": e["graph_us_per_call"],
             "work_per_launch": f"{e['algorithmic_bytes']} bytes"}
 
 

@@ -66,7 +66,8 @@ _SIGS = {
     "qlora_linear_bwd": (ctypes.c_int, [_WP, _P, _P, _P, _P, _P, _I64, _I32, ctypes.c_float, _P,
                                         _P, _P, _P, _SZ, _P]),
     "qlora_linear_gemm_only": (ctypes.c_int, [_WP, _I32, _P, _I64, _I32, _P, _P, _SZ, _P]),
-    "qlora_time_next_kernel": (ctypes.c_int, [_I32, _P, _P]),
+    "qlora_time_next_kernel": (ctypes.c_int, [_I32, _P]),
+    "qlora_wall_clock_khz": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int32)]),
     "qlora_adapter_merge": (ctypes.c_int, [_WP, _P, _P, _I32, ctypes.c_float, _P, _P]),
     "qlora_adapter_unmerge": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, ctypes.c_float, _P, _P]),
     "qlora_lora_dropout": (ctypes.c_int, [_P, _I64, _I64, ctypes.c_float, ctypes.c_uint64, _P, _P]),
@@ -345,14 +346,26 @@ def qlora_linear_gemm_only(w: NF4Weight, backward: bool, a: torch.Tensor, r: int
 TIMED_KERNELS = {"fwd_gemm": 0, "dx_gemm": 1, "decode": 2}
 
 
-def qlora_time_next_kernel(kernel: str, before, after) -> None:
+def qlora_time_next_kernel(kernel: str, span: torch.Tensor | None) -> None:
     """Measurement only: the next launch of `kernel` ("fwd_gemm", "dx_gemm",
-    "decode") records the torch.cuda.Event `before` right before the kernel and
-    `after` right after it, on the stream the library launches on; read the
-    kernel's duration with before.elapsed_time(after) once it has run.  The
-    events must have been recorded once already (torch creates them lazily)."""
-    _check(_lib.qlora_time_next_kernel(TIMED_KERNELS[kernel], before.cuda_event, after.cuda_event),
-           "qlora_time_next_kernel")
+    "decode") records its start and end clock readings into `span` (a device
+    int64 tensor of 2 elements filled with [-1, 0] beforehand: all bits set
+    reads as UINT64_MAX); span_duration_us turns it into microseconds."""
+    if span is not None:
+        _dev_tensor(span, torch.int64, "span")
+    _check(_lib.qlora_time_next_kernel(TIMED_KERNELS[kernel], _ptr(span)), "qlora_time_next_kernel")
+
+
+def wall_clock_khz() -> int:
+    v = ctypes.c_int32(0)
+    _check(_lib.qlora_wall_clock_khz(ctypes.byref(v)), "qlora_wall_clock_khz")
+    return int(v.value)
+
+
+def span_duration_us(spans: torch.Tensor, khz: int):
+    """Durations in microseconds of [n, 2] spans (read back to the host)."""
+    s = spans.detach().cpu().view(-1, 2)
+    return ((s[:, 1] - s[:, 0]).double() * 1e3 / khz).tolist()
 
 
 def qlora_adapter_merge(w: NF4Weight, a: torch.Tensor, b: torch.Tensor, alpha: float,
@@ -385,8 +398,8 @@ def qlora_adapter_unmerge(w_in: torch.Tensor, a: torch.Tensor, b: torch.Tensor, 
 __all__ = [
     "NF4Weight", "QloraError", "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd",
     "qlora_linear_fwd_noalloc",
-    "qlora_linear_bwd", "qlora_linear_gemm_only", "qlora_time_next_kernel", "qlora_adapter_merge",
-    "qlora_adapter_unmerge",
+    "qlora_linear_bwd", "qlora_linear_gemm_only", "qlora_time_next_kernel", "wall_clock_khz",
+    "span_duration_us", "qlora_adapter_merge", "qlora_adapter_unmerge",
     "qlora_lora_dropout",
     "qlora_nf4_codebook", "qlora_nf4_thresholds", "status_str", "library",
     "abi_version", "quantize_workspace_bytes", "linear_workspace_bytes",

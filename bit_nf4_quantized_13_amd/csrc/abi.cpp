@@ -197,17 +197,14 @@ int check_linear(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M, cons
 // ---- the measurement hook (qlora_time_next_kernel) ----------------------------
 namespace {
 std::mutex g_time_mu;
-hipEvent_t g_time_ev[kTimedKernels][2];
+unsigned long long *g_time_span[kTimedKernels];
 }  // namespace
 
-void qnf4::timing_mark(int kernel, bool after, hipStream_t st) {
-    hipEvent_t e;
-    {
-        std::lock_guard<std::mutex> lock(g_time_mu);
-        e = g_time_ev[kernel][after ? 1 : 0];
-        if (after) g_time_ev[kernel][0] = g_time_ev[kernel][1] = nullptr;
-    }
-    if (e) (void)hipEventRecord(e, st);
+unsigned long long *qnf4::timing_take(int kernel) {
+    std::lock_guard<std::mutex> lock(g_time_mu);
+    unsigned long long *sp = g_time_span[kernel];
+    g_time_span[kernel] = nullptr;
+    return sp;
 }
 
 extern "C" {
@@ -523,11 +520,20 @@ int qlora_linear_gemm_only(const qlora_nf4_weight *w, int32_t backward, const ql
                                        static_cast<hipStream_t>(stream)));
 }
 
-int qlora_time_next_kernel(int32_t kernel, void *before, void *after) {
-    if (kernel < 0 || kernel >= kTimedKernels || (before == nullptr) != (after == nullptr)) return QLORA_EINVAL;
+int qlora_time_next_kernel(int32_t kernel, uint64_t *span) {
+    if (kernel < 0 || kernel >= kTimedKernels) return QLORA_EINVAL;
+    if (span && !aligned(span, 8)) return QLORA_EALIGN;
     std::lock_guard<std::mutex> lock(g_time_mu);
-    g_time_ev[kernel][0] = static_cast<hipEvent_t>(before);
-    g_time_ev[kernel][1] = static_cast<hipEvent_t>(after);
+    g_time_span[kernel] = reinterpret_cast<unsigned long long *>(span);
+    return QLORA_OK;
+}
+
+int qlora_wall_clock_khz(int32_t *khz) {
+    if (!khz) return QLORA_EINVAL;
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return QLORA_EHIP;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return QLORA_EHIP;
+    *khz = v;
     return QLORA_OK;
 }
 

@@ -102,6 +102,7 @@ struct DecodeArgs {
     // [s kbs + min(s, kr), +kbs + (s < kr))
     int tb, tr, kbs, kr;
     int bs;                // blocks of 64 << bs weights
+    unsigned long long *span;  // null, or a measurement span (span_start / span_end)
 };
 
 // Device-coherent 16-byte store / load (sc1: not cached non-coherently in the
@@ -158,6 +159,7 @@ __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, N
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g = lane >> 4;
+    if (tid == 0) span_start(p.span);
     // the scalar arguments used before the block loop, requested together (one
     // wait for all of them instead of one per first use)
     asm volatile("" ::"s"(p.S), "s"(p.G), "s"(p.M), "s"(p.r), "s"(p.d), "s"(p.k), "s"(p.tb), "s"(p.tr),
@@ -487,7 +489,10 @@ __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, N
             last_flag = last;
         }
         __syncthreads();
-        if (!last_flag) return;
+        if (!last_flag) {
+            if (tid == 0) span_end(p.span);  // measurement only
+            return;
+        }
         f32x4 pv[DEC_MAX_S], uv[DEC_MAX_S];
 #pragma unroll
         for (int q = 0; q < DEC_MAX_S; ++q) {
@@ -572,6 +577,10 @@ __global__ __launch_bounds__(DEC_THREADS) void nf4_decode_kernel(DecodeArgs p, N
         const float out = ysum[v] + p.s * ad[v];
         p.y[(int64_t)m * d + row] = (uint16_t)(pack_bf16x2(out, 0.0f) & 0xFFFFu);
     }
+    if (p.span && n16 == 0) {  // measurement only: this lane's stores are out
+        __builtin_amdgcn_s_waitcnt(0);
+        span_end(p.span);
+    }
 }
 
 struct DecodePlan {
@@ -606,13 +615,10 @@ DecodePlan decode_plan(int64_t d, int64_t k) {
 
 template <int TW, bool FU, int F>
 hipError_t launch_fu(const DecodeArgs &a, int grid, hipStream_t st) {
-    timing_mark(kTimeDecode, false, st);
     if (a.M == 1) hipLaunchKernelGGL((nf4_decode_kernel<TW, 1, 1, FU, F>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
     else if (a.M <= 8) hipLaunchKernelGGL((nf4_decode_kernel<TW, 4, 1, FU, F>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
     else hipLaunchKernelGGL((nf4_decode_kernel<TW, 4, 2, FU, F>), dim3(grid), dim3(DEC_THREADS), 0, st, a, nf4_consts());
-    const hipError_t e = hipGetLastError();
-    timing_mark(kTimeDecode, true, st);
-    return e;
+    return hipGetLastError();
 }
 
 template <int TW, int F>
@@ -670,6 +676,7 @@ hipError_t launch_decode_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, 
     a.kbs = (int)(kb / pl.S);
     a.kr = (int)(kb % pl.S);
     a.bs = w.bshift;
+    a.span = timing_take(kTimeDecode);
     switch (pl.TW) {
         case 1: return launch_tw<1>(a, w.fmt, pl.grid, st);
         case 2: return launch_tw<2>(a, w.fmt, pl.grid, st);

@@ -9,25 +9,30 @@
 // adapter strength?"), and backpropagation runs through the reconstructed
 // weights into the adapters only.
 //
-// Design (MI355X, one 256-thread workgroup per 512 x 128 output tile):
-//  * Wave w owns output rows [128 w, 128 w + 128) and all 128 columns: 8 x 8
-//    MFMA 16x16x32 tiles, fp32 accumulators in 256 AGPRs.
-//  * The activation operand (X or dY) goes straight from global memory into
-//    registers in the MFMA operand layout: a wave reads only its own rows, so
-//    no LDS staging is needed.  With the 16x16x32 layout one 16-byte load per
-//    lane covers 16 rows x 64 bytes; the 16 loads of the next k-step are spread
-//    one per MFMA group so the vector-memory path never blocks MFMA issue.
-//  * The weight operand is expanded once per workgroup into LDS as bf16
-//    [128 n][64 k] tiles -- BF16(C[code] * scale), bit-identical to
-//    qlora_nf4_dequantize -- in a ring of 4 stages, two k-steps ahead of its
-//    use, so one barrier per two k-steps suffices.  Packed codes and block
-//    scales arrive in registers four steps ahead.  The 16 levels live in a
-//    VGPR (lane j holds C[j % 16]) and are looked up with ds_bpermute; the
-//    lookup, the multiply and the LDS write of each 8-weight piece are spread
-//    over four MFMA groups so their latency hides behind the MFMAs.
-//    Forward: a thread expands 32 consecutive weights of one W0 row.  dX (the
-//    reduction runs over W0 rows): a thread expands 4 rows x 8 columns and
-//    writes them k-contiguous, i.e. the transpose happens in registers.
+// Design (MI355X, one 512-thread workgroup -- 8 waves, two per SIMD -- per
+// 512 x 128 output tile; k-steps of 64):
+//  * Wave w owns output rows [64 w, 64 w + 64) and all 128 columns: 4 x 8
+//    MFMA 16x16x32 tiles, fp32 accumulators in 128 AGPRs.
+//  * Both operand tiles live in LDS in two stages (activation [512][64] and
+//    weight [128][64] bf16, 160 KiB): while step kt runs its MFMAs on one
+//    stage, the tiles of step kt + 1 move into the other, one barrier per
+//    step.  The activation tile (X or dY) goes global -> LDS by buffer_load
+//    ... lds transfers (16 bytes a lane), XOR-swizzled by 16-byte chunks so
+//    that the fragment reads are free of bank conflicts; each wave moves only
+//    its own rows.  The transfers of a step are spread one per MFMA group.
+//  * The weight operand takes one of two forms.  With a single 512-row tile
+//    of M (M <= 512) the kernel expands it from the packed codes (EXPAND):
+//    codes and block scales arrive in registers three steps ahead, the 16
+//    levels live in a VGPR (lane j holds C[j % 16]) and are looked up with
+//    ds_bpermute, then one multiply by the scale and one RNE to bf16 --
+//    bit-identical to qlora_nf4_dequantize -- and the LDS write, spread over
+//    MFMA groups.  Forward: a thread expands 16 consecutive weights of one W0
+//    row; dX (the reduction runs over W0 rows): 2 rows x 8 columns, written
+//    k-contiguous (the transpose happens in registers).  With more row tiles
+//    the preparation kernel writes What (or What^T) in bf16 once per call and
+//    the weight tile moves by the same transfers as the activations:
+//    expanding each weight tile once per row tile costs more than the MFMA
+//    shadow holds (measured: 22 % slower forward, 35 % slower dX at M = 4096).
 //  * The MFMA takes the weight fragment as its first operand, so each lane
 //    ends with 4 consecutive output columns of one row (8-byte stores).
 //  * The adapter term is appended as extra k-steps whose operands the
@@ -69,6 +74,7 @@ struct GemmArgs {
     int64_t ldw;            // forward: What [d x k], ldw = k; dX: What^T [k x ldw], ldw = d rounded up to 64
     uint16_t *out;          // Y or dX [M x N] bf16
     float *out_f32;         // F32OUT kernels: the fp32 sums [M x N] instead of out
+    unsigned long long *span;  // null, or a measurement span (span_start / span_end)
 };
 
 template <int V>
@@ -203,6 +209,7 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, g = lane >> 4;
+    if (tid == 0) span_start(p.span);
     const int64_t tiles_n = (p.N + BN - 1) / BN, tiles_m = (p.M + BM - 1) / BM;
     int64_t mt, nt;
     tile_of(blockIdx.x, tiles_m, tiles_n, mt, nt);
@@ -536,6 +543,11 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
             }
         }
     }
+    if (p.span) {  // measurement only: this workgroup's stores are out
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) span_end(p.span);
+    }
 }
 
 // Transposed dequantized weight operand for the non-expanding dX GEMM: What^T
@@ -771,6 +783,7 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
     p.ldw = dx ? (w.d + 63) / 64 * 64 : w.k;
     p.out = out;
     p.out_f32 = out_f32;
+    p.span = timing_take(dx ? kTimeDxGemm : kTimeFwdGemm);
     if (out_f32 && !dx) return hipErrorInvalidValue;
     // 32-bit buffer offsets: a 512-row slab of the activation operand and the
     // whole adapter operand must stay below 2 GiB
@@ -817,7 +830,6 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
         else hipLaunchKernelGGL(prep_kernel<false>, pgrid, dim3(256), 0, st, q, nf4_consts());
     }
     const dim3 grid((unsigned)tiles), block(NTHREADS);
-    timing_mark(dx ? kTimeDxGemm : kTimeFwdGemm, false, st);
     if (out_f32) {
         if (expand) hipLaunchKernelGGL((nf4_gemm_kernel<true, true, true>), grid, block, 0, st, p, nf4_consts());
         else hipLaunchKernelGGL((nf4_gemm_kernel<true, false, true>), grid, block, 0, st, p, nf4_consts());
@@ -828,9 +840,7 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
         if (dx) hipLaunchKernelGGL((nf4_gemm_kernel<true, false>), grid, block, 0, st, p, nf4_consts());
         else hipLaunchKernelGGL((nf4_gemm_kernel<false, false>), grid, block, 0, st, p, nf4_consts());
     }
-    const hipError_t e = hipGetLastError();
-    timing_mark(dx ? kTimeDxGemm : kTimeFwdGemm, true, st);
-    return e;
+    return hipGetLastError();
 }
 
 }  // namespace

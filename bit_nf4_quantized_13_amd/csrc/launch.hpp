@@ -61,11 +61,20 @@ hipError_t launch_cols_pair(const uint16_t *in0, const uint16_t *vt0, int64_t N0
                             ColsReduceJob *jobs, hipStream_t s);
 
 // ---- measurement hook (qlora_time_next_kernel) -----------------------------
-// A launcher calls timing_mark(kernel, false, st) right before and
-// timing_mark(kernel, true, st) right after its kernel; each records the
-// event a benchmark asked for, if any, on st (the pair is used once).
+// The span buffer a benchmark asked the next launch of `kernel` to fill (null
+// if none; the request is used once).  A kernel given one folds each
+// workgroup's first and last s_memrealtime reading into span[0] (atomic min)
+// and span[1] (atomic max).
 enum TimedKernel : int { kTimeFwdGemm = 0, kTimeDxGemm = 1, kTimeDecode = 2, kTimedKernels = 3 };
-void timing_mark(int kernel, bool after, hipStream_t st);
+unsigned long long *timing_take(int kernel);
+__device__ __forceinline__ void span_start(unsigned long long *span) {
+    if (span) __hip_atomic_fetch_min(span, (unsigned long long)__builtin_amdgcn_s_memrealtime(), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void span_end(unsigned long long *span) {
+    if (span) __hip_atomic_fetch_max(span + 1, (unsigned long long)__builtin_amdgcn_s_memrealtime(),
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // ---- fused NF4 dequant GEMMs ----------------------------------------------
 struct Nf4Weights {

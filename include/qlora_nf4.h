@@ -299,17 +299,27 @@ int qlora_linear_gemm_only(const qlora_nf4_weight *w, int32_t backward, const ql
 
 /*
  * qlora_time_next_kernel -- measurement only (benchmarks): the next launch of
- * the named kernel records `before` on its stream right before the kernel and
- * `after` right after it, so that the kernel's own duration can be read with
- * hipEventElapsedTime while it runs inside ordinary calls.  kernel: 0 the
+ * the named kernel records its own execution span, so that the kernel's
+ * duration can be read while it runs inside ordinary calls.  kernel: 0 the
  * forward dequant-GEMM (qlora_linear_fwd with M > 16), 1 the dX dequant-GEMM
  * (qlora_linear_bwd), 2 the decode kernel (qlora_linear_fwd with M <= 16).
- * The pair is used once; NULL, NULL cancels a pending pair.  Both are
- * hipEvent_t handles created on the device the calls run on.  The setting is
- * process-wide: no other thread may launch that kernel meanwhile.
- * Errors: QLORA_EINVAL (unknown kernel, only one event given).
+ * span: device memory, two uint64 holding {UINT64_MAX, 0} beforehand; each
+ * workgroup of that launch folds the constant-rate clock (s_memrealtime) at
+ * its start into span[0] (atomic min) and after its last store into span[1]
+ * (atomic max), so span[1] - span[0] ticks is the launch's duration
+ * (qlora_wall_clock_khz gives the tick rate).  The request is used once;
+ * NULL cancels a pending one.  It is process-wide: no other thread may launch
+ * that kernel meanwhile.
+ * Errors: QLORA_EINVAL (unknown kernel), QLORA_EALIGN (span not 8-byte
+ * aligned).
  */
-int qlora_time_next_kernel(int32_t kernel, void *before, void *after);
+int qlora_time_next_kernel(int32_t kernel, uint64_t *span);
+
+/* Measurement only: the rate of the clock qlora_time_next_kernel reads, in
+ * kHz, on the current device (hipDeviceAttributeWallClockRate).  QLORA_EHIP
+ * without a device. */
+int qlora_wall_clock_khz(int32_t *khz);
+
 
 /*
  * qlora_adapter_merge -- fold the adapter into a dense bf16 weight.
@@ -367,7 +377,7 @@ const char *qlora_status_str(int status);
 
 /* ABI version of this header/library pair. */
 int qlora_abi_version(void);
-#define QLORA_ABI_VERSION 4
+#define QLORA_ABI_VERSION 5
 
 #ifdef __cplusplus
 }

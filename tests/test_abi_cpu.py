@@ -343,13 +343,14 @@ def test_dropout_calls_reject_invalid_arguments():
     assert fwd_d(y=FAKE_MIS) == q.QLORA_EALIGN
 
 
+
 def test_time_next_kernel_checks_its_arguments():
-    """The measurement hook only stores the event handles; a bad kernel id or a
-    lone event is refused, and NULL, NULL clears whatever was pending."""
+    """The measurement hook only stores the span pointer: a bad kernel id or a
+    misaligned span is refused, and NULL clears whatever was pending."""
     lib = q.library()
-    assert lib.qlora_time_next_kernel(3, None, None) == q.QLORA_EINVAL
-    assert lib.qlora_time_next_kernel(-1, None, None) == q.QLORA_EINVAL
-    assert lib.qlora_time_next_kernel(0, 0x1000, None) == q.QLORA_EINVAL
-    assert lib.qlora_time_next_kernel(2, None, 0x1000) == q.QLORA_EINVAL
+    assert lib.qlora_time_next_kernel(3, None) == q.QLORA_EINVAL
+    assert lib.qlora_time_next_kernel(-1, None) == q.QLORA_EINVAL
+    assert lib.qlora_time_next_kernel(0, 0x1004) == q.QLORA_EALIGN
     for kernel in range(3):
-        assert lib.qlora_time_next_kernel(kernel, None, None) == q.QLORA_OK
+        assert lib.qlora_time_next_kernel(kernel, None) == q.QLORA_OK
+    assert lib.qlora_wall_clock_khz(None) == q.QLORA_EINVAL
