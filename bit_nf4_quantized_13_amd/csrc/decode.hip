@@ -105,8 +105,19 @@ struct DecodeArgs {
     unsigned long long *span;  // null, or a measurement span (span_start / span_end)
 };
 
-// Device-coherent 16-byte store / load (sc1: not cached non-coherently in the
-// per-XCD L2), for partial sums handed from one workgroup to another.
+// Device-coherent 16-byte store / load for partial sums handed from one
+// workgroup to another, possibly on another XCD.  The hand-off is a release /
+// acquire at device scope done with per-instruction scope bits instead of
+// fences: the producer's partials are stored with device scope (sc1: written
+// through the XCD's L2, which is not coherent with the other XCDs'), it waits
+// for every store to be acknowledged at that scope (s_waitcnt vmcnt(0)) before
+// its workgroup's arrival is counted by a device-scope atomic, and the
+// consumer -- the workgroup that sees the last count -- reads the partials
+// with device-scope loads (sc1: not served from its own L2), issued only after
+// the atomic returned.  A device-scope release / acquire fence pair would
+// give the same ordering by writing back and invalidating the whole L2 of
+// both XCDs (about 4 us per call here); the scope bits confine it to the
+// lines of the partials.
 constexpr int DEC_SC1 = 16;
 __device__ __forceinline__ void store16_sc1(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, DEC_SC1);

@@ -84,6 +84,25 @@ def test_decode_workspace_reuse_and_garbage():
         check_decode_workspace(d)
 
 
+@pytest.mark.parametrize("m,d,k", [(1, 16, 4096), (16, 48, 1024), (4, 1016, 4096), (7, 520, 2048),
+                                   (2, 104, 1472), (16, 8, 640)])
+def test_decode_k_split_shapes(m, d, k):
+    """Few row tiles: the decode forward splits k over 2..8 workgroups per tile
+    group (even and uneven block counts per slice), whose partial sums the last
+    one to arrive adds.  Forward parity, and the same bits on a second call on
+    the same workspace (the counters left ready by the first)."""
+    import bit_nf4_quantized_13_amd as q
+    inp = make_layer(47, d + m, d, k, m, 16)
+    check_layer(inp, 32.0, f"decode k-split m={m} d={d} k={k}", want_bwd=False, bf16_rounding_allowance=True)
+    w = q.qlora_nf4_quantize(to_dev_f32(inp.w0))
+    xd, ad, bd = (to_dev_bf16(t) for t in (inp.x, inp.a, inp.b))
+    ws = torch.empty(q.linear_workspace_bytes(m, d, k, 16), dtype=torch.uint8, device="cuda")
+    y1, u1 = q.qlora_linear_fwd(w, xd, ad, bd, 32.0, workspace=ws)
+    y2, u2 = q.qlora_linear_fwd(w, xd, ad, bd, 32.0, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(u1, u2)
+
+
 def check_decode_workspace(d):
     import bit_nf4_quantized_13_amd as q
     say(f"decode workspace garbage / reuse, d={d}")
