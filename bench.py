@@ -497,6 +497,55 @@ def decode_roofline(decode):
             "work_per_launch": f"{e['algorithmic_bytes']} bytes"}
 
 
+def run_gemm_ab(q, torch, reps=20):
+    """The two ways of feeding the weights to the layer4096 GEMMs (M = 4096),
+    interleaved call by call so that clock drift hits both alike: the calls as
+    they run (a bf16 copy of What / What^T written by the preparation launch,
+    then the GEMM that streams it) and, right after each call, the same GEMM
+    work done by the kernel that expands the NF4 codes tile by tile
+    (qlora_linear_gemm_only(expand=True): block scales, then the expanding
+    kernel, on the adapter operands the call prepared).  Event-timed per call;
+    a kernel trace of this run splits each into its launches."""
+    from workloads import WORKLOADS, workload_layer
+    from tests.helpers import to_dev_bf16, to_dev_f32
+    wl = WORKLOADS["layer4096"]
+    m, r, alpha = wl.m[0], wl.r, wl.alpha
+    inp = workload_layer("layer4096")
+    d, k = inp.w0.shape
+    w = q.qlora_nf4_quantize(to_dev_f32(inp.w0))
+    x, a, b, dy = (to_dev_bf16(t) for t in (inp.x, inp.a, inp.b, inp.dy))
+    lws = torch.empty(q.linear_workspace_bytes(m, d, k, r), dtype=torch.uint8, device="cuda")
+    y = torch.empty((m, d), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty_like(y)
+    u = torch.empty((m, r), dtype=torch.float32, device="cuda")
+    outs = (torch.empty((m, k), dtype=torch.bfloat16, device="cuda"), torch.empty((r, k), device="cuda"),
+            torch.empty((d, r), device="cuda"))
+    dx2 = torch.empty_like(outs[0])
+    t = {kk: Timer(torch) for kk in ("fwd_call", "fwd_expand", "bwd_call", "dx_expand")}
+    same = True
+    for it in range(reps + 2):
+        timed = it >= 2
+        e = t["fwd_call"].start()
+        q.qlora_linear_fwd(w, x, a, b, alpha, out=y, u_out=u, workspace=lws)
+        t["fwd_call"].stop(e) if timed else None
+        e = t["fwd_expand"].start()
+        q.qlora_linear_gemm_only(w, False, x, r, y2, lws, expand=True)
+        t["fwd_expand"].stop(e) if timed else None
+        e = t["bwd_call"].start()
+        q.qlora_linear_bwd(w, x, dy, a, b, alpha, u=u, workspace=lws, outs=outs)
+        t["bwd_call"].stop(e) if timed else None
+        e = t["dx_expand"].start()
+        q.qlora_linear_gemm_only(w, True, dy, r, dx2, lws, expand=True)
+        t["dx_expand"].stop(e) if timed else None
+        same = same and bool(torch.equal(y, y2)) and bool(torch.equal(outs[0], dx2))
+    torch.cuda.synchronize()
+    res = {kk: round(v.total_ms() / reps, 4) for kk, v in t.items()}
+    res.update({"same_bits": same, "reps": reps,
+                "workload": f"layer4096: W0 {d}x{k}, M={m}, r={r}; *_call: the whole call (U or G, dA/dB "
+                            "for bwd, the bf16 copy, the GEMM); *_expand: block scales + expanding GEMM"})
+    return res
+
+
 def pmc_run(q, torch, which):
     """A short, fixed sequence of launches for rocprofv3 --pmc counter passes:
     a plain device copy of 256 MiB (the calibration of FETCH_SIZE/WRITE_SIZE),
@@ -577,6 +626,8 @@ def main():
     ap.add_argument("--skip-models", action="store_true")
     ap.add_argument("--pmc-run", choices=["gemm", "decode"],
                     help="only a short fixed launch sequence for rocprofv3 --pmc passes")
+    ap.add_argument("--gemm-ab", action="store_true",
+                    help="only the A/B of the bf16-copy GEMM path against the expanding kernel at M = 4096")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
@@ -591,6 +642,9 @@ def main():
     torch.cuda.set_device(0)
     if args.pmc_run:
         pmc_run(q, torch, args.pmc_run)
+        return
+    if args.gemm_ab:
+        print(json.dumps({"gemm_ab": run_gemm_ab(q, torch)}), flush=True)
         return
 
     ctx, lay = run_layer_bench(q, torch, args.steps, args.warmup)

@@ -65,7 +65,7 @@ _SIGS = {
     "qlora_linear_fwd_noalloc": (ctypes.c_int, [_WP, _P, _I64, _P, _P, _I32, ctypes.c_float, _P, _P, _P]),
     "qlora_linear_bwd": (ctypes.c_int, [_WP, _P, _P, _P, _P, _P, _I64, _I32, ctypes.c_float, _P,
                                         _P, _P, _P, _SZ, _P]),
-    "qlora_linear_gemm_only": (ctypes.c_int, [_WP, _I32, _P, _I64, _I32, _P, _P, _SZ, _P]),
+    "qlora_linear_gemm_only": (ctypes.c_int, [_WP, _I32, _I32, _P, _I64, _I32, _P, _P, _SZ, _P]),
     "qlora_time_next_kernel": (ctypes.c_int, [_I32, _P]),
     "qlora_wall_clock_khz": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int32)]),
     "qlora_adapter_merge": (ctypes.c_int, [_WP, _P, _P, _I32, ctypes.c_float, _P, _P]),
@@ -330,16 +330,17 @@ def qlora_linear_bwd(w: NF4Weight, x: torch.Tensor, dy: torch.Tensor, a: torch.T
 
 
 def qlora_linear_gemm_only(w: NF4Weight, backward: bool, a: torch.Tensor, r: int,
-                           out: torch.Tensor, workspace: torch.Tensor) -> torch.Tensor:
-    """Re-run the dequant-GEMM kernel of the preceding qlora_linear_fwd (a = x,
-    out = Y) or qlora_linear_bwd (a = dY, out = dX) call alone, on the workspace
-    that call prepared (for timing the GEMM in isolation)."""
+                           out: torch.Tensor, workspace: torch.Tensor, expand: bool = False) -> torch.Tensor:
+    """Measurement only: re-run the dequant-GEMM kernel of the preceding
+    qlora_linear_fwd (a = x, out = Y) or qlora_linear_bwd (a = dY, out = dX) call
+    alone, on the workspace that call prepared; expand=True runs the kernel that
+    expands the NF4 codes tile by tile instead (with its block scales)."""
     _dev_tensor(a, torch.bfloat16, "a")
     _dev_tensor(out, torch.bfloat16, "out")
     cw = w.c_struct()
-    _check(_lib.qlora_linear_gemm_only(ctypes.byref(cw), 1 if backward else 0, a.data_ptr(), a.shape[0], r,
-                                       out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()),
-           "qlora_linear_gemm_only")
+    _check(_lib.qlora_linear_gemm_only(ctypes.byref(cw), 1 if backward else 0, 1 if expand else 0, a.data_ptr(),
+                                       a.shape[0], r, out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                       _stream()), "qlora_linear_gemm_only")
     return out
 
 

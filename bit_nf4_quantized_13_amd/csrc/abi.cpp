@@ -502,8 +502,8 @@ int qlora_linear_bwd_dropout(const qlora_nf4_weight *w, const qlora_bf16 *x, con
     return hip_status(e);
 }
 
-int qlora_linear_gemm_only(const qlora_nf4_weight *w, int32_t backward, const qlora_bf16 *a, int64_t M,
-                           int32_t r, qlora_bf16 *out, void *ws, size_t ws_bytes, void *stream) {
+int qlora_linear_gemm_only(const qlora_nf4_weight *w, int32_t backward, int32_t expand, const qlora_bf16 *a,
+                           int64_t M, int32_t r, qlora_bf16 *out, void *ws, size_t ws_bytes, void *stream) {
     int st = check_weight(w, true);
     if (st != QLORA_OK) return st;
     if (!a || !out || M <= 0 || r <= 0) return QLORA_EINVAL;
@@ -517,7 +517,7 @@ int qlora_linear_gemm_only(const qlora_nf4_weight *w, int32_t backward, const ql
     (void)hipGetLastError();
     const Nf4Weights nw = nf4_view(w);
     return hip_status(launch_gemm_core(backward != 0, nw, a, M, r, out, gemm_ws(static_cast<char *>(ws), l),
-                                       static_cast<hipStream_t>(stream)));
+                                       static_cast<hipStream_t>(stream), expand != 0));
 }
 
 int qlora_time_next_kernel(int32_t kernel, uint64_t *span) {

@@ -761,12 +761,17 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a, Nf4Consts tab) {
     cols_reduce(a.red[second ? 1 : 0], (b - (second ? a.g_r0 : 0)) * 256 + threadIdx.x);
 }
 
-// core_only: launch the GEMM kernel alone on a workspace that a full launch
-// with the same arguments prepared (block scales, adapter operands, bf16 copy)
+// What a launch runs: the preparation and the GEMM (kFull); the GEMM kernel alone
+// on a workspace that a full launch with the same arguments prepared (kCoreOnly);
+// or, for measurement, the block scales and the expanding GEMM kernel whatever
+// the number of row tiles, reusing the adapter operands a full launch prepared
+// (kExpandCore).
+enum LaunchWhat : int { kFull = 0, kCoreOnly = 1, kExpandCore = 2 };
+
 // out_f32 (dX only): store the fp32 sums there instead of bf16 into out
 hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, const float *V,
                   const uint16_t *ext_w, int r, float s, uint16_t *out, const GemmWs &ws,
-                  const ColsReduceJob *red, hipStream_t st, bool core_only = false, float *out_f32 = nullptr) {
+                  const ColsReduceJob *red, hipStream_t st, int what = kFull, float *out_f32 = nullptr) {
     GemmArgs p;
     p.a = a;
     p.M = M;
@@ -792,8 +797,21 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
         return hipErrorInvalidValue;
 
     const int64_t tiles_m = (M + BM - 1) / BM, tiles = tiles_m * ((p.N + BN - 1) / BN);
-    const bool expand = tiles_m == 1;
-    if (!core_only) {
+    const bool expand = tiles_m == 1 || what == kExpandCore;
+    if (what == kExpandCore) {
+        PrepArgs q{};
+        q.fmt = w.fmt;
+        q.bshift = w.bshift;
+        q.c2 = w.c2;
+        q.c1 = w.c1;
+        q.mean = w.mean;
+        q.nb = w.d * w.k / 64;
+        q.shat = ws.shat;
+        q.red[0] = q.red[1] = ColsReduceJob{nullptr, 0, 1, 0, 0, 0.0f, nullptr};
+        q.g_shat = (q.nb + 255) / 256;
+        if (dx) hipLaunchKernelGGL(prep_kernel<true>, dim3((unsigned)q.g_shat), dim3(256), 0, st, q, nf4_consts());
+        else hipLaunchKernelGGL(prep_kernel<false>, dim3((unsigned)q.g_shat), dim3(256), 0, st, q, nf4_consts());
+    } else if (what == kFull) {
         PrepArgs q;
         q.fmt = w.fmt;
         q.bshift = w.bshift;
@@ -860,7 +878,7 @@ hipError_t launch_gemm_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, co
 hipError_t launch_gemm_dx(const Nf4Weights &w, const uint16_t *dy, int64_t M, const float *G,
                           const uint16_t *A, int r, float s, uint16_t *dX, const GemmWs &ws,
                           const ColsReduceJob *red, hipStream_t st, float *dX_f32) {
-    return launch(true, w, dy, M, G, A, r, s, dX, ws, red, st, false, dX_f32);
+    return launch(true, w, dy, M, G, A, r, s, dX, ws, red, st, kFull, dX_f32);
 }
 
 hipError_t launch_cols_reduce(const ColsReduceJob *red, hipStream_t st) {
@@ -875,8 +893,8 @@ hipError_t launch_cols_reduce(const ColsReduceJob *red, hipStream_t st) {
 }
 
 hipError_t launch_gemm_core(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, int r, uint16_t *out,
-                            const GemmWs &ws, hipStream_t st) {
-    return launch(dx, w, a, M, nullptr, nullptr, r, 0.0f, out, ws, nullptr, st, true);
+                            const GemmWs &ws, hipStream_t st, bool force_expand) {
+    return launch(dx, w, a, M, nullptr, nullptr, r, 0.0f, out, ws, nullptr, st, force_expand ? kExpandCore : kCoreOnly);
 }
 
 }  // namespace qnf4

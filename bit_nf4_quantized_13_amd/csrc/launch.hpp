@@ -113,9 +113,11 @@ hipError_t launch_gemm_dx(const Nf4Weights &w, const uint16_t *dy, int64_t M, co
                           const ColsReduceJob *red, hipStream_t st, float *dX_f32 = nullptr);
 
 // The GEMM kernel of launch_gemm_fwd (dx = false) or launch_gemm_dx (dx = true)
-// alone, on a workspace that a full launch with the same arguments prepared.
+// alone, on a workspace that a full launch with the same arguments prepared;
+// force_expand: the block scales and the expanding kernel instead, at any M
+// (measurement of the expanding path against the bf16 copy).
 hipError_t launch_gemm_core(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, int r, uint16_t *out,
-                            const GemmWs &ws, hipStream_t st);
+                            const GemmWs &ws, hipStream_t st, bool force_expand = false);
 
 // Adapter merge / unmerge: w_out[d x k] = bf16(fp32(base + s * (B A))) with the
 // sum over ranks in fp64, j ascending; base = doubleDequant(w) when w is not

@@ -159,8 +159,11 @@ size_t qlora_linear_workspace(int64_t M, int64_t d, int64_t k, int32_t r);
  * chkda, "Double quantization and double dequantization" (the full QLoRA
  * expression, Y = X doubleDequant(c1, c2, W_NF4) + X L1 L2 with L1 = A^T,
  * L2 = B^T and the scale alpha/r of "How does alpha/r control adapter
- * strength?").  Products accumulate in fp32.  For M > 16, What is expanded
- * from the NF4 codes on the fly, bit-identical to qlora_nf4_dequantize.  For
+ * strength?").  Products accumulate in fp32.  For 16 < M <= 512 the GEMM
+ * expands What from the NF4 codes tile by tile; for M > 512 the call first
+ * writes a bf16 copy of What (2 d k bytes of the workspace) and the GEMM
+ * streams it (faster there than expanding every weight tile once per 512
+ * rows of X); both bit-identical to qlora_nf4_dequantize.  For
  * M <= 16 (decode) the 64-weight block scale is applied once to the fp32 sum
  * over the block, with the NF4 levels in bf16: the same product, rounded
  * differently (within the library's fwd tolerance of the bf16 What product).
@@ -288,14 +291,18 @@ int qlora_linear_bwd_dropout(const qlora_nf4_weight *w, const qlora_bf16 *x, con
  * dequantized block scales, the adapter operands laid out as extra k-columns,
  * a bf16 copy of What when M > 512) into the workspace and then one GEMM
  * kernel; this call re-runs only the GEMM on that prepared workspace.
+ *   expand  0: the kernel the call ran.  1: the block scales and the GEMM
+ *           kernel that expands What from the NF4 codes tile by tile (the one
+ *           the calls use for M <= 512), at any M, on the adapter operands the
+ *           call prepared -- the two ways of feeding the weights, side by side.
  *   a    the call's x (forward) or dY (backward); M, r, ws as in that call
  *   out  rewritten with the values the call wrote to Y (forward) or dX
- *        (backward)
+ *        (backward): both kernels give the same bits
  * The workspace must not have been used by another call in between.  A
  * forward with M <= 16 has no separate GEMM (one kernel): QLORA_EINVAL.
  */
-int qlora_linear_gemm_only(const qlora_nf4_weight *w, int32_t backward, const qlora_bf16 *a, int64_t M,
-                           int32_t r, qlora_bf16 *out, void *ws, size_t ws_bytes, void *stream);
+int qlora_linear_gemm_only(const qlora_nf4_weight *w, int32_t backward, int32_t expand, const qlora_bf16 *a,
+                           int64_t M, int32_t r, qlora_bf16 *out, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * qlora_time_next_kernel -- measurement only (benchmarks): the next launch of
@@ -377,7 +384,7 @@ const char *qlora_status_str(int status);
 
 /* ABI version of this header/library pair. */
 int qlora_abi_version(void);
-#define QLORA_ABI_VERSION 5
+#define QLORA_ABI_VERSION 6
 
 #ifdef __cplusplus
 }

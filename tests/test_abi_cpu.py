@@ -267,7 +267,7 @@ def test_weight_struct_layout_matches_the_header(tmp_path):
 
 def gemm_only(w=None, backward=0, a=FAKE, m=64, r=8, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
     w = w or weight()
-    return q.library().qlora_linear_gemm_only(ctypes.byref(w), backward, a, m, r, out, ws, ws_bytes, None)
+    return q.library().qlora_linear_gemm_only(ctypes.byref(w), backward, 0, a, m, r, out, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -193,7 +193,9 @@ def test_alpha_zero_gives_base_output_and_zero_adapter_grads():
 @pytest.mark.parametrize("m", [200, 600])
 def test_gemm_only_reruns_the_calls_gemm(m):
     """qlora_linear_gemm_only re-launches just the dequant-GEMM on the workspace
-    the preceding call prepared: the output must be bit-identical."""
+    the preceding call prepared: the output must be bit-identical, also from
+    the kernel that expands the codes tile by tile (M = 600: the call itself
+    used the bf16 copy)."""
     import bit_nf4_quantized_13_amd as q
     say(f"gemm_only M={m}")
     inp = make_layer(44, m, 384, 320, m, 8)
@@ -204,8 +206,15 @@ def test_gemm_only_reruns_the_calls_gemm(m):
     y2 = torch.full_like(y, 7)
     q.qlora_linear_gemm_only(w, False, xd, 8, y2, ws)
     assert torch.equal(y, y2)
+    # the expanding kernel on the same operands (with M > 512 the call itself streams a bf16 copy)
+    y3 = torch.full_like(y, 7)
+    q.qlora_linear_gemm_only(w, False, xd, 8, y3, ws, expand=True)
+    assert torch.equal(y, y3)
     dx, _, _ = q.qlora_linear_bwd(w, xd, dyd, ad, bd, 16.0, u=u, workspace=ws)
     dx2 = torch.full_like(dx, 7)
     q.qlora_linear_gemm_only(w, True, dyd, 8, dx2, ws)
     assert torch.equal(dx, dx2)
+    dx3 = torch.full_like(dx, 7)
+    q.qlora_linear_gemm_only(w, True, dyd, 8, dx3, ws, expand=True)
+    assert torch.equal(dx, dx3)
     torch.cuda.synchronize()
