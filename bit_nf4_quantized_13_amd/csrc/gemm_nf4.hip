@@ -59,7 +59,6 @@ constexpr int NTHREADS = 512;                 // 8 waves, two per SIMD
 constexpr int WM = BM / (NTHREADS / 64);      // rows per wave (64)
 constexpr int MI = WM / 16;                   // 16-row MFMA tiles per wave (4)
 constexpr int A_STAGE = BM * BK * 2;          // 64 KiB activation tile
-constexpr int B_STAGE = BN * BK * 2;          // 16 KiB weight tile
 
 struct GemmArgs {
     const uint16_t *a;      // activation operand [M x Kd] bf16 (X or dY)
@@ -190,11 +189,17 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // tile from a dequantized bf16 copy written once per call.
 // F32OUT: the fp32 sums are stored unrounded (out_f32) for a caller that adds
 // another term before the one bf16 rounding.
-template <bool DX, bool EXPAND, bool F32OUT = false>
+// TN: output columns per tile, 128 or (non-expanding kernel) 64: half as much
+// work per workgroup, for grids whose 128-wide tiles would leave CUs idle.
+template <bool DX, bool EXPAND, bool F32OUT = false, int TN = BN>
 __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Consts tab) {
+    static_assert(TN == 128 || (TN == 64 && !EXPAND), "the expansion fills 128-row weight tiles");
+    constexpr int NJ = TN / 16;          // 16-column MFMA tiles per wave
+    constexpr int WR = TN / 8;           // weight-tile rows each wave moves
+    constexpr int B_STAGE = TN * BK * 2; // weight tile bytes
     // Two stages of the activation tile [512 rows][64 k] and of the weight tile
-    // [128 rows][64 k] (160 KiB).  One object per buffer so that the compiler can
-    // tell them apart when it places waits for the global->LDS transfers.
+    // [TN rows][64 k] (up to 160 KiB).  One object per buffer so that the compiler
+    // can tell them apart when it places waits for the global->LDS transfers.
     __shared__ u32x4 sA0[A_STAGE / 16], sA1[A_STAGE / 16];
     __shared__ u32x4 sB0[B_STAGE / 16], sB1[B_STAGE / 16];
     auto Aof = [&](auto S) __attribute__((always_inline)) -> u32x4 * {
@@ -210,10 +215,10 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, g = lane >> 4;
     if (tid == 0) span_start(p.span);
-    const int64_t tiles_n = (p.N + BN - 1) / BN, tiles_m = (p.M + BM - 1) / BM;
+    const int64_t tiles_n = (p.N + TN - 1) / TN, tiles_m = (p.M + BM - 1) / BM;
     int64_t mt, nt;
     tile_of(blockIdx.x, tiles_m, tiles_n, mt, nt);
-    const int64_t m_base = mt * BM, n_base = nt * BN;
+    const int64_t m_base = mt * BM, n_base = nt * TN;
     const int64_t nK = (p.Kd + BK - 1) / BK;
     const int64_t kb = p.k / 64;  // NF4 blocks per W0 row
 
@@ -253,15 +258,18 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
         return __builtin_bit_cast(uint4, Bof(S)[(s ? frag1 : frag0) + 128 * j]);
     };
     // transfer (non-expanding kernel): rows n_base .., 8 per transfer, wave w moves
-    // rows 16 w .. 16 w + 15; rows past N read as zero
+    // rows WR w .. WR w + WR - 1; rows past N read as zero.  Transfer u lands in rows
+    // whose swizzle term is (4 (WR w / 8 + u) + l / 16) & 7: voff_w0 or voff_w1 by
+    // the parity of WR w / 8 + u.
     const __amdgpu_buffer_rsrc_t rw =
-        make_rsrc(p.wbf + n_base * p.ldw, EXPAND ? 0 : ((p.N - n_base) < BN ? (p.N - n_base) : BN) * p.ldw * 2);
-    const int wrow = 16 * wave + (lane >> 3);  // + 8 u
+        make_rsrc(p.wbf + n_base * p.ldw, EXPAND ? 0 : ((p.N - n_base) < TN ? (p.N - n_base) : TN) * p.ldw * 2);
+    const int wrow = WR * wave + (lane >> 3);  // + 8 u
+    const int wpar = (WR / 8) * wave;
     const uint32_t voff_w0 = (uint32_t)(((int64_t)wrow * p.ldw + 8 * ((lane & 7) ^ ((lane >> 4) & 7))) * 2);
     const uint32_t voff_w1 = (uint32_t)(((int64_t)wrow * p.ldw + 8 * ((lane & 7) ^ (((lane >> 4) + 4) & 7))) * 2);
     const uint32_t wrow8_bytes = (uint32_t)(8 * p.ldw * 2);
     auto issue_w = [&](int64_t kt, auto S, int u) __attribute__((always_inline)) {
-        dma16(rw, Bof(S) + (16 * wave + 8 * u) * 8, u ? voff_w1 : voff_w0,
+        dma16(rw, Bof(S) + (WR * wave + 8 * u) * 8, ((wpar + u) & 1) ? voff_w1 : voff_w0,
               (uint32_t)u * wrow8_bytes + (uint32_t)kt * (BK * 2));
     };
 
@@ -370,7 +378,7 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
 
     // Accumulators: first written by step 0 (MFMA with a zero addend), then
     // accumulated in place (mfma16_acc).
-    f32x4 acc[MI][8];
+    f32x4 acc[MI][NJ];
     uint4 af[2][MI];   // activation fragments: current slice, next slice
     uint4 bq[4];       // weight fragments, two groups ahead
     Wdata w0, w1, w2;  // weight data, rotating over three steps
@@ -401,9 +409,9 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
         const int64_t kn = kt + 1 < nK ? kt + 1 : nK - 1;
         const int64_t kw = kt + 3 < nK ? kt + 3 : nK - 1;
 #pragma unroll
-        for (int grp = 0; grp < 16; ++grp) {
-            const int s = grp >> 3, j = grp & 7;
-            if (grp + 2 < 16) bq[(grp + 2) & 3] = read_b(S{}, (grp + 2) >> 3, (grp + 2) & 7);
+        for (int grp = 0; grp < 2 * NJ; ++grp) {
+            const int s = grp / NJ, j = grp % NJ;
+            if (grp + 2 < 2 * NJ) bq[(grp + 2) & 3] = read_b(S{}, (grp + 2) / NJ, (grp + 2) % NJ);
             if (grp == 0) {
 #pragma unroll
                 for (int i = 0; i < MI; ++i) af[1][i] = read_a(S{}, 1, i);
@@ -414,9 +422,12 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
                 if (j == 1) expand_phase(wc, s, 0, st_w);
                 if (j == 4) expand_phase(wc, s, 1, st_w);
                 if (j == 6) expand_phase(wc, s, 2, st_w);
-            } else {
+            } else if constexpr (TN == 128) {
                 if (grp < 2) issue_w(kn, S1{}, grp);
                 if (grp >= 2 && grp < 10) issue_a(kn, S1{}, grp - 2);
+            } else {  // 8 groups: the weight transfer with the first activation one
+                if (grp == 0) issue_w(kn, S1{}, 0);
+                issue_a(kn, S1{}, grp);
             }
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
@@ -449,8 +460,8 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
 #pragma unroll
             for (int ph = 0; ph < 3; ++ph) expand_phase(w0, c, ph, sB0);
     } else {
-        issue_w(0, IC<0>{}, 0);
-        issue_w(0, IC<0>{}, 1);
+#pragma unroll
+        for (int u = 0; u < WR / 8; ++u) issue_w(0, IC<0>{}, u);
 #pragma unroll
         for (int b = 0; b < 8; ++b) issue_a(0, IC<0>{}, b);
     }
@@ -486,13 +497,13 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
         const uint32_t voff_e0 = (uint32_t)(((int64_t)dma_row * p.Ke + 8 * ((lane & 7) ^ ((lane >> 4) & 7))) * 2);
         const uint32_t voff_e1 = (uint32_t)(((int64_t)dma_row * p.Ke + 8 * ((lane & 7) ^ (((lane >> 4) + 4) & 7))) * 2);
         const uint32_t row8_e = (uint32_t)(8 * p.Ke * 2);
-        // weight-side operand rows n_base .. +127 (clamped to N-1): transfer u of
-        // wave w covers rows 16 w + 8 u .. + 7
+        // weight-side operand rows n_base .. + TN - 1 (clamped to N-1): transfer u of
+        // wave w covers rows WR w + 8 u .. + 7
         const __amdgpu_buffer_rsrc_t reb = make_rsrc(p.ext_b, p.N * p.Ke * 2);
-        uint32_t voff_eb[2];
+        uint32_t voff_eb[WR / 8];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int row = 16 * wave + 8 * u + (lane >> 3);
+        for (int u = 0; u < WR / 8; ++u) {
+            const int row = WR * wave + 8 * u + (lane >> 3);
             int64_t n = n_base + row;
             n = n < p.N ? n : p.N - 1;
             voff_eb[u] = (uint32_t)((n * p.Ke + 8 * ((lane & 7) ^ ((row >> 1) & 7))) * 2);
@@ -504,7 +515,7 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
                 dma16(rea, sA0 + (WM * wave + 8 * b) * 8, (b & 1) ? voff_e1 : voff_e0,
                       (uint32_t)b * row8_e + (uint32_t)e * (BK * 2));
 #pragma unroll
-            for (int u = 0; u < 2; ++u) dma16(reb, sB0 + (16 * wave + 8 * u) * 8, voff_eb[u], (uint32_t)e * (BK * 2));
+            for (int u = 0; u < WR / 8; ++u) dma16(reb, sB0 + (WR * wave + 8 * u) * 8, voff_eb[u], (uint32_t)e * (BK * 2));
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
 #pragma unroll
@@ -512,7 +523,7 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
 #pragma unroll
                 for (int i = 0; i < MI; ++i) af[0][i] = read_a(IC<0>{}, s, i);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
+                for (int j = 0; j < NJ; ++j) {
                     const uint4 b = read_b(IC<0>{}, s, j);
 #pragma unroll
                     for (int i = 0; i < MI; ++i) mfma16_acc(b, af[0][i], acc[i][j]);
@@ -532,7 +543,7 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
         const int64_t m = m_base + WM * wave + 16 * i + r16;
         if (m >= p.M) continue;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             const int64_t n = n_base + 16 * j + 4 * g;
             if (n >= p.N) continue;
             if constexpr (F32OUT) {
@@ -761,6 +772,19 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a, Nf4Consts tab) {
     cols_reduce(a.red[second ? 1 : 0], (b - (second ? a.g_r0 : 0)) * 256 + threadIdx.x);
 }
 
+// Output columns per tile of the non-expanding GEMM.  A 512x64 tile does half
+// the work of a 512x128 one at a higher LDS cost per flop (the activation tile
+// is moved and read for half the columns): measured at 0.85-0.92 of the 128-wide
+// tile's time (M = 2048, K = 4096 and 11008), so kTile64Cost = 0.9.  Rounds of
+// 256 workgroups (one per CU) decide: 64 wins where the 128-wide grid leaves
+// half the CUs idle (M = 2048 against 4096 columns: 128 tiles).
+constexpr double kTile64Cost = 0.9;
+int pick_tile_n(int64_t tiles_m, int64_t N) {
+    const int64_t t128 = tiles_m * ((N + 127) / 128), t64 = tiles_m * ((N + 63) / 64);
+    const double r128 = (double)((t128 + 255) / 256), r64 = (double)((t64 + 255) / 256) * kTile64Cost;
+    return r64 < r128 ? 64 : 128;
+}
+
 // What a launch runs: the preparation and the GEMM (kFull); the GEMM kernel alone
 // on a workspace that a full launch with the same arguments prepared (kCoreOnly);
 // or, for measurement, the block scales and the expanding GEMM kernel whatever
@@ -796,8 +820,10 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
         (int64_t)BM * p.Ke * 2 >= (int64_t(1) << 31))
         return hipErrorInvalidValue;
 
-    const int64_t tiles_m = (M + BM - 1) / BM, tiles = tiles_m * ((p.N + BN - 1) / BN);
+    const int64_t tiles_m = (M + BM - 1) / BM;
     const bool expand = tiles_m == 1 || what == kExpandCore;
+    const int tn = expand ? BN : pick_tile_n(tiles_m, p.N);
+    const int64_t tiles = tiles_m * ((p.N + tn - 1) / tn);
     if (what == kExpandCore) {
         PrepArgs q{};
         q.fmt = w.fmt;
@@ -850,10 +876,14 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
     const dim3 grid((unsigned)tiles), block(NTHREADS);
     if (out_f32) {
         if (expand) hipLaunchKernelGGL((nf4_gemm_kernel<true, true, true>), grid, block, 0, st, p, nf4_consts());
+        else if (tn == 64) hipLaunchKernelGGL((nf4_gemm_kernel<true, false, true, 64>), grid, block, 0, st, p, nf4_consts());
         else hipLaunchKernelGGL((nf4_gemm_kernel<true, false, true>), grid, block, 0, st, p, nf4_consts());
     } else if (expand) {
         if (dx) hipLaunchKernelGGL((nf4_gemm_kernel<true, true>), grid, block, 0, st, p, nf4_consts());
         else hipLaunchKernelGGL((nf4_gemm_kernel<false, true>), grid, block, 0, st, p, nf4_consts());
+    } else if (tn == 64) {
+        if (dx) hipLaunchKernelGGL((nf4_gemm_kernel<true, false, false, 64>), grid, block, 0, st, p, nf4_consts());
+        else hipLaunchKernelGGL((nf4_gemm_kernel<false, false, false, 64>), grid, block, 0, st, p, nf4_consts());
     } else {
         if (dx) hipLaunchKernelGGL((nf4_gemm_kernel<true, false>), grid, block, 0, st, p, nf4_consts());
         else hipLaunchKernelGGL((nf4_gemm_kernel<false, false>), grid, block, 0, st, p, nf4_consts());
