@@ -56,8 +56,13 @@ def test_single_layer_workload():
                                      (64, 264, 128, 7), (130, 256, 256, 33), (33, 512, 1024, 64),
                                      (20, 128, 256, 128), (16, 200, 448, 33), (3, 136, 1088, 16),
                                      (5, 4104, 4096, 16), (16, 64, 64, 1), (16, 1000, 2048, 16),
-                                     (2, 4104, 256, 16), (1, 16408, 256, 16), (16, 16408, 512, 8)])
+                                     (2, 4104, 256, 16), (1, 16408, 256, 16), (16, 16408, 512, 8),
+                                     (700, 328, 192, 8), (1030, 200, 1088, 16), (1100, 4104, 320, 4),
+                                     (1100, 5512, 256, 8)])
 def test_shapes_ranks_and_ragged_tiles(m, d, k, r):
+    """Ranks, ragged M, d, k tiles, the decode path (M <= 16), the expanding GEMM
+    (M <= 512) and the GEMM on the bf16 copy (M > 512) in both tile widths,
+    with partial last tiles."""
     inp = make_layer(21, m * 7 + r, d, k, m, r)
     check_layer(inp, 16.0, f"shape m={m} d={d} k={k} r={r}", bf16_rounding_allowance=True)
 
