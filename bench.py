@@ -345,6 +345,21 @@ def time_gemm_only(q, torch, ctx, iters):
     return e0.elapsed_time(e1) / iters
 
 
+def run_vendor_gemm_context(torch, n=4096, iters=20):
+    """Context only (not part of the layer's path): torch's bf16 GEMM (hipBLASLt
+    on ROCm) on the forward GEMM's shape, M = N = K = 4096, random N(0, 1)
+    operands, event-timed back to back -- the rate a vendor dense bf16 GEMM
+    reaches on this machine, beside the fused dequant-GEMM's."""
+    g = torch.Generator(device="cuda").manual_seed(5)
+    a = torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    ms = time_calls(torch, lambda: torch.mm(a, b, out=c), iters)
+    tf = 2 * n ** 3 / (ms * 1e-3) / 1e12
+    return {"shape": f"{n}x{n}x{n} bf16", "us": round(ms * 1e3, 2), "tflops": round(tf, 1),
+            "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+
+
 def run_merge_bench(q, torch, ctx, iters=20):
     """qlora_adapter_merge on the layer4096 weight (4096 x 4096, r = 8): the
     merged bf16 weight What + (alpha/r) B A, r fp64 FMAs per weight.  Reported
@@ -667,6 +682,7 @@ def main():
                 "dx_kernel_us": round(lay["gemm_dx_ms"] * 1e3, 2),
                 "dx_frac": round((2 * m * d * k + 2 * m * k * r) / (lay["gemm_dx_ms"] * 1e-3) / 1e12
                                  / BF16_PEAK_TFLOPS, 4)}
+    roofline["vendor_bf16_gemm_context"] = run_vendor_gemm_context(torch)
     log("layer4096: timing the adapter merge")
     merge = run_merge_bench(q, torch, ctx)
     decode = None if args.skip_decode else run_decode_bench(q, torch)
