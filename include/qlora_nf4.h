@@ -17,7 +17,9 @@
  * Conventions for every call
  *   - All array arguments are DEVICE pointers, allocated, owned and freed by
  *     the caller; the library never allocates, frees or keeps a pointer past
- *     the call.  Matrices are dense and row-major.
+ *     the call (the one exception is the measurement-only
+ *     qlora_time_next_kernel, which holds its span buffer until the next
+ *     launch of the kernel it names).  Matrices are dense and row-major.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Work is enqueued asynchronously; the library never synchronises.
  *   - Outputs are overwritten, never accumulated; outputs must not alias
@@ -30,7 +32,8 @@
  *   - Calls are reentrant: the library holds no mutable global state (the
  *     NF4 table is computed once, on first use, behind a thread-safe
  *     initialiser; qlora_linear_fwd_noalloc keeps the device address of its
- *     static scratch per device).  Calls that share a workspace must be
+ *     static scratch per device; a pending qlora_time_next_kernel request is
+ *     process-wide, behind a mutex).  Calls that share a workspace must be
  *     ordered on one stream.
  */
 #ifndef QLORA_NF4_H
