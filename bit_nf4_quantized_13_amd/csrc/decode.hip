@@ -659,6 +659,8 @@ hipError_t launch_decode_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, 
                              const uint16_t *B, int r, float s, uint16_t *Y, float *U_save, float *part,
                              unsigned long long *ctr, hipStream_t st) {
     if (M < 1 || M > 16 || (!U && (!A || r > 16)) || w.k > (int64_t(1) << 25)) return hipErrorInvalidValue;
+    if (!U && decode_dot_supported(M, w.d, w.k, r))
+        return launch_decode_dot(w, x, M, A, B, r, s, Y, U_save, timing_take(kTimeDecode), st);
     const DecodePlan pl = decode_plan(w.d, w.k);
     if (pl.S > 1 && (!part || !ctr || pl.G > DEC_MAX_GROUPS)) return hipErrorInvalidValue;
     DecodeArgs a;

@@ -137,5 +137,11 @@ size_t decode_part_bytes(int64_t M, int64_t d, int64_t k);
 hipError_t launch_decode_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, const uint16_t *A, const float *U,
                              const uint16_t *B, int r, float s, uint16_t *Y, float *U_save, float *part,
                              unsigned long long *ctr, hipStream_t st);
+// The same for M <= 2, r <= 16, k <= 4096, d >= 8192, U computed from A, on
+// packed dot products (decode_dot.hip); launch_decode_fwd takes this path
+// whenever decode_dot_supported holds.  span: the measurement span or null.
+bool decode_dot_supported(int64_t M, int64_t d, int64_t k, int r);
+hipError_t launch_decode_dot(const Nf4Weights &w, const uint16_t *x, int64_t M, const uint16_t *A, const uint16_t *B,
+                             int r, float s, uint16_t *Y, float *U_save, unsigned long long *span, hipStream_t st);
 
 }  // namespace qnf4

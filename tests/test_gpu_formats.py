@@ -114,7 +114,7 @@ def test_quantize_layer4096(fmt):
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
-@pytest.mark.parametrize("m,d,k,r", [(1, 256, 512, 8), (16, 4104, 4096, 16), (4, 512, 4096, 16),
+@pytest.mark.parametrize("m,d,k,r", [(1, 256, 512, 8), (1, 8192, 512, 8), (16, 4104, 4096, 16), (4, 512, 4096, 16),
                                      (16, 200, 448, 33), (3, 136, 1088, 16), (64, 264, 128, 7),
                                      (130, 256, 256, 33), (600, 320, 192, 8)])
 def test_linear_forward_backward(fmt, m, d, k, r):
@@ -221,7 +221,7 @@ BLOCK_CASES = [(fmt, blk) for blk in (128, 256) for fmt in ("int8", "no_dq", "fp
 def test_block_sizes(fmt, block):
     """Blocks of 128 and 256 weights in every format: quantize and dequantize
     bit-exact (ragged groups and an all-zero block included), the linear
-    forward and backward on the decode and GEMM paths, and the merge."""
+    forward and backward on both decode kernels and the GEMM paths, and the merge."""
     import bit_nf4_quantized_13_amd as q
     say(f"block {block}, format {fmt}")
     kw = {"double_quant": fmt != "no_dq", "c2_fp8": fmt == "fp8", "block": block}
@@ -244,7 +244,7 @@ def test_block_sizes(fmt, block):
     assert np.array_equal(w.codes.cpu().numpy(), ref["packed"])
     assert np.array_equal(what, want)
 
-    for m, d, k, r in ((16, 4104, 2048, 16), (3, 512, 4096, 33), (600, 320, 4 * block, 8)):
+    for m, d, k, r in ((16, 4104, 2048, 16), (3, 512, 4096, 33), (2, 8192, 1024, 8), (600, 320, 4 * block, 8)):
         say(f"block {block} {fmt} linear m={m} d={d} k={k} r={r}")
         inp = make_layer(65, m + r + block, d, k, m, r)
         wq = q.qlora_nf4_quantize(to_dev_f32(inp.w0), **kw)

@@ -90,12 +90,14 @@ def test_decode_workspace_reuse_and_garbage():
 
 
 @pytest.mark.parametrize("m,d,k", [(1, 16, 4096), (16, 48, 1024), (4, 1016, 4096), (7, 520, 2048),
-                                   (2, 104, 1472), (16, 8, 640)])
+                                   (2, 104, 1472), (16, 8, 640), (5, 1016, 4096), (6, 104, 1472),
+                                   (8, 16, 4096)])
 def test_decode_k_split_shapes(m, d, k):
-    """Few row tiles: the decode forward splits k over 2..8 workgroups per tile
-    group (even and uneven block counts per slice), whose partial sums the last
-    one to arrive adds.  Forward parity, and the same bits on a second call on
-    the same workspace (the counters left ready by the first)."""
+    """Few row tiles: the decode forward splits k over 2..8
+    workgroups per tile group (even and uneven block counts per slice), whose
+    partial sums the last one to arrive adds.  Forward parity, and the
+    same bits on a second call on the same workspace (the counters left ready
+    by the first)."""
     import bit_nf4_quantized_13_amd as q
     inp = make_layer(47, d + m, d, k, m, 16)
     check_layer(inp, 32.0, f"decode k-split m={m} d={d} k={k}", want_bwd=False, bf16_rounding_allowance=True)
@@ -106,6 +108,20 @@ def test_decode_k_split_shapes(m, d, k):
     y2, u2 = q.qlora_linear_fwd(w, xd, ad, bd, 32.0, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(u1, u2)
+
+
+@pytest.mark.parametrize("m,d,k,r", [(1, 8192, 64, 1), (2, 16392, 512, 16), (1, 8200, 1088, 7), (2, 12296, 3200, 9),
+                                     (3, 8200, 1088, 7), (4, 8192, 64, 1)])
+def test_decode_dot_path_shapes(m, d, k, r):
+    """M <= 2, r <= 16, k <= 4096, d >= 8192: the dot-product decode kernel
+    (the decode workloads' own 14336-row shape is in
+    test_decode_shapes_forward), and M = 3, 4 on such shapes through the
+    matrix-core kernel.  Four to eight rounds of 8 rows per workgroup, more
+    workgroups than a round of the chip (d = 16392: 257), k chunks past the
+    row end (k = 64, 1088, 3200), ranks below 16."""
+    inp = make_layer(59, m * 31 + r, d, k, m, r)
+    check_layer(inp, 2.0 * r, f"decode dot m={m} d={d} k={k} r={r}", want_bwd=False,
+                bf16_rounding_allowance=True)
 
 
 def check_decode_workspace(d):

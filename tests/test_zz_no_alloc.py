@@ -28,6 +28,8 @@ def run_pair(q, w, xd, ad, bd, alpha):
     # (seed, d, k, M, r): a larger call, then smaller ones (fewer rows, fewer tiles, k split)
     [(51, 4096, 4096, 16, 16), (52, 512, 1024, 4, 8), (53, 264, 256, 1, 16)],
     [(54, 14336, 4096, 16, 16), (55, 4096, 4096, 1, 32), (56, 136, 1088, 3, 16)],
+    # the dot-product kernel (M <= 2, d >= 8192, no scratch), then a k-split call
+    [(58, 8192, 1024, 2, 16), (59, 264, 256, 1, 16)],
 ])
 def test_noalloc_forward_matches_workspace_forward(cases):
     import bit_nf4_quantized_13_amd as q
