@@ -168,8 +168,10 @@ size_t qlora_linear_workspace(int64_t M, int64_t d, int64_t k, int32_t r);
  * streams it (faster there than expanding every weight tile once per 512
  * rows of X); both bit-identical to qlora_nf4_dequantize.  For
  * M <= 16 (decode) the 64-weight block scale is applied once to the fp32 sum
- * over the block, with the NF4 levels in bf16: the same product, rounded
- * differently (within the library's fwd tolerance of the bf16 What product).
+ * over the block (over each half block with M <= 2, r <= 16, k <= 4096 and
+ * d >= 8192, which take a vector dot-product kernel), with the NF4 levels in
+ * bf16: the same product, rounded differently (within the library's fwd
+ * tolerance of the bf16 What product).
  * A call with M <= 16 and r <= 16 is one kernel (U = X A^T included); it
  * keeps counters in the first 32 KiB of the workspace between calls, which
  * it tags and resets itself: the caller need not clear them, but must not
