@@ -95,6 +95,7 @@ __global__ __launch_bounds__(256) void nf4_quantize_groups(
     float *__restrict__ absmax, double *__restrict__ group_sum) {
     __shared__ float s_abs[kGroup];
     __shared__ uint32_t lut[kLutEntries];  // fp32 bits, see lut_entry
+    __shared__ __attribute__((aligned(16))) uint16_t s_codes[kGroup * kBlock / 4];  // the group's packed codes
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t blk0 = (int64_t)blockIdx.x * kGroup;
     s_abs[tid] = 0.0f;  // missing blocks of a ragged last group count as +0.0
@@ -147,12 +148,11 @@ __global__ __launch_bounds__(256) void nf4_quantize_groups(
         }
         return q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12);
     };
-    // Codes and absmax stay in registers until every block is coded: a global
-    // store issued between the waits for the loads above would be counted with
-    // them (one in-order counter), and each later wait would then hold the wave
-    // until loads it does not need yet have landed.
-    uint32_t pk[8];  // block i's 16 code bits at bits 16 (i % 2) of pk[i / 2]
-    float mv[16];
+    // Codes and absmax go to LDS until every block is coded: a global store
+    // issued between the waits for the loads above would be counted with them
+    // (one in-order counter), and each later wait would then hold the wave
+    // until loads it does not need yet have landed.  From LDS the group's codes
+    // and absmax leave in whole 16-byte pieces per lane.
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int local = wave * 64 + (i >> 1) * 8 + (i & 1) * 4 + (lane >> 4);
@@ -173,22 +173,19 @@ __global__ __launch_bounds__(256) void nf4_quantize_groups(
                                                                 : __builtin_nanf("");
             packed4 = code4(v[i], m, r64);
         }
-        if (i % 2 == 0) pk[i / 2] = packed4;
-        else pk[i / 2] |= packed4 << 16;
-        mv[i] = m;
+        s_codes[local * 16 + (lane & 15)] = (uint16_t)packed4;
         if ((lane & 15) == 0 && blk0 + local < nb) s_abs[local] = m;
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int local = wave * 64 + (i >> 1) * 8 + (i & 1) * 4 + (lane >> 4);
-        const int64_t blk = blk0 + local;
-        if (blk < nb) {
-            *reinterpret_cast<uint16_t *>(codes + blk * (kBlock / 2) + (lane & 15) * 2) =
-                (uint16_t)(pk[i / 2] >> (16 * (i % 2)));
-            if ((lane & 15) == 0) absmax[blk] = mv[i];
-        }
-    }
     __syncthreads();
+    // the group's codes: 256 blocks x 32 bytes, 2 pieces of 16 bytes per thread
+    // (piece p holds half of block p / 2); absmax: one value per thread
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int piece = h * 256 + tid;
+        if (piece / 2 < nloc)
+            reinterpret_cast<uint4 *>(codes + blk0 * (kBlock / 2))[piece] = reinterpret_cast<const uint4 *>(s_codes)[piece];
+    }
+    if (tid < nloc) absmax[blk0 + tid] = s_abs[tid];
     if (wave == 0) {
         // stride-halving tree: h = 128 and 64 in registers, then 32..1 across lanes
         double a0 = (double)s_abs[lane] + (double)s_abs[lane + 128];
