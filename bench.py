@@ -504,12 +504,21 @@ def decode_roofline(decode):
     """The decode forward at M = 16 on the 14336 x 4096 projection: one kernel
     per call, bound by HBM; algorithmic bytes over its event-timed duration."""
     e = decode.get("14336x4096_m16") or next(iter(decode.values()))
-    return {"bound": "hbm", "achieved": e["algorithmic_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(e["algorithmic_gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": traffic_from_profiles("nf4_decode_kernel_w14336x4096_m16", "decode.hip"),
-            "kernel": "nf4_decode_kernel (decode forward, 14336 x 4096, M = 16)",
-            "kernel_us": e["kernel_us"], "graph_us_per_call": e["graph_us_per_call"],
-            "work_per_launch": f"{e['algorithmic_bytes']} bytes"}
+    out = {"bound": "hbm", "achieved": e["algorithmic_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(e["algorithmic_gbs"] / HBM_PEAK_GBS, 4),
+           "traffic": traffic_from_profiles("nf4_decode_kernel_w14336x4096_m16", "decode.hip"),
+           "kernel": "nf4_decode_kernel (decode forward, 14336 x 4096, M = 16)",
+           "kernel_us": e["kernel_us"], "graph_us_per_call": e["graph_us_per_call"],
+           "work_per_launch": f"{e['algorithmic_bytes']} bytes"}
+    e1 = decode.get("14336x4096_m1")
+    if e1:  # one token: the dot-product kernel
+        out["m1"] = {"kernel": "nf4_decode_dot_kernel (decode forward, 14336 x 4096, M = 1)",
+                     "kernel_us": e1["kernel_us"], "graph_us_per_call": e1["graph_us_per_call"],
+                     "achieved": e1["algorithmic_gbs"],
+                     "frac": round(e1["algorithmic_gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profiles("nf4_decode_dot_kernel_w14336x4096_m1", "decode_dot.hip"),
+                     "work_per_launch": f"{e1['algorithmic_bytes']} bytes"}
+    return out
 
 
 def run_gemm_ab(q, torch, reps=20):
@@ -589,6 +598,10 @@ def pmc_run(q, torch, which):
             lws = torch.empty(q.linear_workspace_bytes(16, p.d, p.k, wl.r), dtype=torch.uint8, device="cuda")
             for _ in range(3):
                 q.qlora_linear_fwd(w, x, a, b, wl.alpha, save_u=False, out=y, workspace=lws)
+            if p.d >= 8192:  # one token: the dot-product decode kernel
+                x1, y1 = x[:1].contiguous(), y[:1].contiguous()
+                for _ in range(3):
+                    q.qlora_linear_fwd(w, x1, a, b, wl.alpha, save_u=False, out=y1, workspace=lws)
     torch.cuda.synchronize()
     log(f"pmc run ({which}) done")
 
