@@ -95,8 +95,12 @@ LinWs lin_ws(int64_t M, int64_t d, int64_t k, int r) {
     off += round_up(sizeof(float) * M * r, 256);
     l.vt = off;  // transposed hi / lo planes of U and of G
     off += round_up(sizeof(uint16_t) * 2 * 2 * cols_rank_pad(r) * M, 256);
-    l.part = off;
-    off += round_up(sizeof(float) * cols_splits(M) * (size_t)r * (round_up(d, 64) + k), 256);
+    l.part = off;  // the column reductions' partials, or (before them) the wide-rank row products
+    size_t part_bytes = sizeof(float) * cols_splits(M) * (size_t)r * (round_up(d, 64) + k);
+    const size_t rows_k = rows_split_part_bytes(M, k, r), rows_d = rows_split_part_bytes(M, d, r);
+    part_bytes = part_bytes > rows_k ? part_bytes : rows_k;
+    part_bytes = part_bytes > rows_d ? part_bytes : rows_d;
+    off += round_up(part_bytes, 256);
     l.total = off;
     return l;
 }
@@ -173,7 +177,7 @@ hipError_t decode_forward(const Nf4Weights &nw, const qlora_bf16 *x, int64_t M, 
                           unsigned long long *ctr, float *dpart, float *u_buf, hipStream_t s) {
     if (r <= 16) return launch_decode_fwd(nw, x, M, A, nullptr, B, r, scale, Y, U_save, dpart, ctr, s);
     float *U = U_save ? U_save : u_buf;
-    hipError_t e = launch_rows_skinny(x, A, M, nw.k, r, U, nullptr, s);
+    hipError_t e = launch_rows_skinny(x, A, M, nw.k, r, U, nullptr, nullptr, s);  // M <= 16: no partials
     if (e == hipSuccess) e = launch_decode_fwd(nw, x, M, nullptr, U, B, r, scale, Y, nullptr, dpart, ctr, s);
     return e;
 }
@@ -304,7 +308,7 @@ int qlora_linear_fwd(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M,
         // HBM-bound: one pass over the codes; U = X A^T in the same kernel for r <= 16
         e = decode_forward(nw, x, M, A, B, r, scale, Y, U_save, ctr, dpart, U, s);
     } else {
-        e = launch_rows_skinny(x, A, M, w->k, r, U, nullptr, s);
+        e = launch_rows_skinny(x, A, M, w->k, r, U, nullptr, reinterpret_cast<float *>(base + l.part), s);
         if (e == hipSuccess) e = launch_gemm_fwd(nw, x, M, U, B, r, scale, Y, gemm_ws(base, l), s);
     }
     return hip_status(e);
@@ -361,11 +365,11 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const qlora_bf16 *x, const qlora
     hipError_t e = hipSuccess;
     const float *Uin = U;
     if (!Uin) {  // recompute U = X A^T, with its transposed planes
-        e = launch_rows_skinny(x, A, M, k, r, Uw, vt_u, s);
+        e = launch_rows_skinny(x, A, M, k, r, Uw, vt_u, part, s);
         Uin = Uw;
     }
     if (e == hipSuccess) e = launch_bwd_prep(B, d, r, Bt, U, M, vt_u, s);    // B^T [r x d] (and U's planes)
-    if (e == hipSuccess) e = launch_rows_skinny(dY, Bt, M, d, r, G, vt_g, s);  // G = dY B
+    if (e == hipSuccess) e = launch_rows_skinny(dY, Bt, M, d, r, G, vt_g, part, s);  // G = dY B
     ColsReduceJob red[2];
     float *part_b = part;                                                       // dB = s U^T dY (as [d x r])
     float *part_a = part + (size_t)cols_splits(M) * r * round_up(d, 64);        // dA = s G^T X
@@ -442,7 +446,8 @@ int qlora_linear_fwd_dropout(const qlora_nf4_weight *w, const qlora_bf16 *x, int
     float *U = U_save ? U_save : reinterpret_cast<float *>(base + l.u);
     const Nf4Weights nw = nf4_view(w);
     hipError_t e = launch_lora_dropout(x, M, w->k, thr, c, seed, xd, s);
-    if (e == hipSuccess) e = launch_rows_skinny(xd, A, M, w->k, r, U, nullptr, s);   // U = Xd A^T
+    if (e == hipSuccess)  // U = Xd A^T
+        e = launch_rows_skinny(xd, A, M, w->k, r, U, nullptr, reinterpret_cast<float *>(base + l.part), s);
     if (e == hipSuccess) {
         if (M <= 16 && w->k <= kDecodeMaxK)
             e = launch_decode_fwd(nw, x, M, nullptr, U, B, r, scale, Y, nullptr, reinterpret_cast<float *>(base + l.dpart),
@@ -482,9 +487,9 @@ int qlora_linear_bwd_dropout(const qlora_nf4_weight *w, const qlora_bf16 *x, con
     uint16_t *vt_u = reinterpret_cast<uint16_t *>(base + l.vt);
     uint16_t *vt_g = vt_u + 2 * cols_rank_pad(r) * M;
     hipError_t e = launch_lora_dropout(x, M, k, thr, c, seed, xd, s);           // the forward's Xd again
-    if (e == hipSuccess && !U) e = launch_rows_skinny(xd, A, M, k, r, Uw, vt_u, s);
+    if (e == hipSuccess && !U) e = launch_rows_skinny(xd, A, M, k, r, Uw, vt_u, part, s);
     if (e == hipSuccess) e = launch_bwd_prep(B, d, r, Bt, U, M, vt_u, s);
-    if (e == hipSuccess) e = launch_rows_skinny(dY, Bt, M, d, r, G, vt_g, s);   // G = dY B
+    if (e == hipSuccess) e = launch_rows_skinny(dY, Bt, M, d, r, G, vt_g, part, s);   // G = dY B
     ColsReduceJob red[2];
     float *part_b = part;                                                       // dB = s U^T dY
     float *part_a = part + (size_t)cols_splits(M) * r * round_up(d, 64);        // dA = s G^T Xd

@@ -83,8 +83,9 @@ struct DotArgs {
     unsigned long long *span;  // null, or a measurement span (span_start / span_end)
 };
 
-// MV token rows held in registers (M <= MV), NCH k-chunks per lane (k <= 4096 NCH),
-// F: the ScaleFormat of the block constants.  PD rounds of loads are in flight.
+// MV token rows held in registers (M <= MV), NCH k-chunks per lane (launched with
+// NCH = 1: k <= 4096 over 128 lanes), F: the ScaleFormat of the block constants.
+// PD rounds of loads are in flight (8 for one token row, 4 for two).
 template <int MV, int NCH, int F>
 __global__ __launch_bounds__(DD_THREADS) void nf4_decode_dot_kernel(DotArgs p, Nf4Consts tab) {
     constexpr bool DQ = F != kNoDq;

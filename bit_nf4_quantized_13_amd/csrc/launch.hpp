@@ -35,8 +35,11 @@ hipError_t launch_dropout_dx_add(const float *base, uint16_t *dx, int64_t M, int
 // or [2][Rp][M] bf16 receiving the transposed hi and lo planes of out (rows
 // R..Rp-1 zero), Rp = cols_rank_pad(R).
 int64_t cols_rank_pad(int r);
+// part: rows_split_part_bytes(M, K, R) bytes of scratch for the partial sums
+// of the wide-rank path (null when that is 0).
+size_t rows_split_part_bytes(int64_t M, int64_t K, int R);
 hipError_t launch_rows_skinny(const uint16_t *in, const uint16_t *w, int64_t M, int64_t K, int R,
-                              float *out, uint16_t *vt, hipStream_t s);
+                              float *out, uint16_t *vt, float *part, hipStream_t s);
 // Backward preparation: Bt[r x d] = B[d x r]^T and, when U is given, the
 // transposed hi / lo planes of U [M x r] into vt [2][Rp][M].
 hipError_t launch_bwd_prep(const uint16_t *B, int64_t d, int r, uint16_t *Bt, const float *U, int64_t M,

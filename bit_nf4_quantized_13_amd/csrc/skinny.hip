@@ -123,31 +123,31 @@ __global__ __launch_bounds__(64 * W) void rows_skinny_kernel(const uint16_t *__r
 }
 
 // ---------------------------------------------------------------------------
-// Backward preparation, one launch, one thread per row: workgroups [0, gt)
-// transpose src = B [R = d rows x C = r columns] into dst = B^T [r x d] (thread
-// = row of B: its C values in, one column of B^T out); the rest write the
-// transposed bf16 planes of a given U [M x r] fp32 (thread = row m of U):
+// Backward preparation, one launch, one thread per element: threads [0, R C)
+// transpose src = B [R = d rows x C = r columns] into dst = B^T [r x d]
+// (thread i: column i / R, row i % R); the next M Rp write the transposed bf16
+// planes of a given U [M x r] fp32 (thread: j = i / M, m = i % M):
 // vt[j][m] = hi(U[m][j]), vt[Rp + j][m] = lo(U[m][j]) (zero for r <= j < Rp).
-// Stores of consecutive threads are consecutive; no LDS, no barrier.
+// Stores of consecutive threads are consecutive; enough threads to cover the
+// latency of the strided loads (B and U are small).  No LDS, no barrier.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t *__restrict__ src, int64_t R, int C,
-                                                       uint16_t *__restrict__ dst, int64_t gt,
-                                                       const float *__restrict__ U, int64_t M, int Rp,
-                                                       uint16_t *__restrict__ vt) {
-    if ((int64_t)blockIdx.x >= gt) {
-        const int64_t m = ((int64_t)blockIdx.x - gt) * 256 + threadIdx.x;
-        if (m >= M) return;
-        for (int j = 0; j < Rp; ++j) {
-            const float f = j < C ? U[m * C + j] : 0.0f;
-            const uint32_t hb = pack_bf16x2(f, 0.0f) & 0xFFFFu;
-            vt[(int64_t)j * M + m] = (uint16_t)hb;
-            vt[(int64_t)(Rp + j) * M + m] = (uint16_t)(pack_bf16x2(f - bf16_bits_to_f32(hb), 0.0f) & 0xFFFFu);
-        }
+                                                       uint16_t *__restrict__ dst, const float *__restrict__ U,
+                                                       int64_t M, int Rp, uint16_t *__restrict__ vt) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t nt = R * C;
+    if (i < nt) {
+        const int64_t c = i / R, row = i - c * R;
+        dst[c * R + row] = src[row * C + c];
         return;
     }
-    const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (row >= R) return;
-    for (int c = 0; c < C; ++c) dst[(int64_t)c * R + row] = src[row * C + c];
+    const int64_t iu = i - nt;
+    if (!U || iu >= M * Rp) return;
+    const int64_t j = iu / M, m = iu - j * M;
+    const float f = j < C ? U[m * C + j] : 0.0f;
+    const uint32_t hb = pack_bf16x2(f, 0.0f) & 0xFFFFu;
+    vt[j * M + m] = (uint16_t)hb;
+    vt[(Rp + j) * M + m] = (uint16_t)(pack_bf16x2(f - bf16_bits_to_f32(hb), 0.0f) & 0xFFFFu);
 }
 
 // ---------------------------------------------------------------------------
@@ -303,18 +303,164 @@ __global__ __launch_bounds__(256) void dot_rows_kernel(const uint16_t *__restric
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same product for wide ranks (R > 16) with many rows: every workgroup of
+// rows_skinny_kernel reads all of W (R x K; 512 KiB at R = 64, K = 4096) for
+// its 16 rows, so W dominated the traffic.  Here a workgroup owns MT 16-row
+// tiles and one of S slices of K (whole 128-wide chunks), so W is read once per
+// 16 MT rows; its four waves take the slice's chunks in turn, every MFMA on a
+// W fragment serving the MT row tiles.  The workgroup's sum over its waves (in
+// wave order) is a partial [S][R][M] fp32; rows_reduce_kernel adds the S
+// partials in slice order into out (and its planes).
+// ---------------------------------------------------------------------------
+template <int NT, int MT>
+__global__ __launch_bounds__(256) void rows_split_kernel(const uint16_t *__restrict__ in,
+                                                         const uint16_t *__restrict__ w, int64_t M, int64_t K,
+                                                         int R, int64_t kslice, float *__restrict__ part) {
+    __shared__ f32x4 s_acc[4][NT][64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int i = lane & 15, g = lane >> 4;
+    const int64_t m0 = (int64_t)blockIdx.x * 16 * MT;
+    const int sl = blockIdx.y;
+    const int64_t rows = (M - m0) < 16 * MT ? (M - m0) : 16 * MT;
+    // rows past M and W rows past R read as zero (outside the buffers); pieces
+    // past the slice or past K are zeroed by the selects below
+    const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + m0 * K, rows * K * 2);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (int64_t)R * K * 2);
+    const int64_t kb = sl * kslice;
+    const int64_t ke = (kb + kslice) < K ? (kb + kslice) : K;
+    f32x4 acc[MT][NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int64_t chunks = (ke - kb + 127) / 128;
+    for (int64_t c = wave; c < chunks; c += 4) {
+        // MFMA e of the chunk takes k = 32 e .. 32 e + 31, lane group g its 8 k at 32 e + 8 g
+        const int64_t k0 = kb + c * 128 + 8 * g;
+        uint4 a[MT][4], b[NT][4];
+        bool ok[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ok[e] = k0 + 32 * e < ke;  // K % 8 == 0 and kslice % 128 == 0: pieces wholly in or out
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) a[mt][e] = load16(rin, (uint32_t)(((16 * mt + i) * K + k0 + 32 * e) * 2));
+#pragma unroll
+            for (int t = 0; t < NT; ++t) b[t][e] = load16(rw, (uint32_t)(((t * 16 + i) * K + k0 + 32 * e) * 2));
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const uint4 av = ok[e] ? a[mt][e] : uint4{0, 0, 0, 0};
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[mt][t] = mfma16(av, b[t][e], acc[mt][t]);
+            }
+    }
+    // wave sums, one row tile at a time: wave w adds column tiles w, w + 4 over
+    // the four waves in order; lane (i, g) register r is row 4 g + r, column 16 t + i
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) s_acc[wave][t][lane] = acc[mt][t];
+        __syncthreads();
+        for (int t = wave; t < NT; t += 4) {
+            f32x4 v = s_acc[0][t][lane];
+            for (int q = 1; q < 4; ++q) v += s_acc[q][t][lane];
+            const int j = 16 * t + i;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = m0 + 16 * mt + 4 * g + r;
+                if (row < M && j < R) part[((int64_t)sl * R + j) * M + row] = v[r];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// out[m][j] = the S partials of rows_split_kernel added in slice order; vt: the
+// transposed hi / lo planes as in rows_skinny_kernel (zero for R <= j < Rp).
+// Thread (j, m), m fastest: partial reads and plane stores are contiguous.
+__global__ __launch_bounds__(256) void rows_reduce_kernel(const float *__restrict__ part, int S, int64_t M, int R,
+                                                          float *__restrict__ out, uint16_t *__restrict__ vt,
+                                                          int64_t Rp) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t rc = vt ? Rp : R;
+    if (e >= M * rc) return;
+    const int64_t j = e / M, m = e - j * M;
+    float v = 0.0f;
+    if (j < R) {
+        for (int q = 0; q < S; ++q) v += part[((int64_t)q * R + j) * M + m];
+        out[m * R + j] = v;
+    }
+    if (vt) {
+        const uint32_t hb = pack_bf16x2(v, 0.0f) & 0xFFFFu;
+        vt[j * M + m] = (uint16_t)hb;
+        vt[(Rp + j) * M + m] = (uint16_t)(pack_bf16x2(v - bf16_bits_to_f32(hb), 0.0f) & 0xFFFFu);
+    }
+}
+
+// The split of a wide-rank product over workgroups: MT row tiles per workgroup
+// and S slices of K such that about 256 workgroups of four waves cover it
+// (measured: eight waves, or twice the slices, left waves idle and doubled the
+// partials).
+struct RowsSplit {
+    int mt, S;
+    int64_t groups, kslice;
+};
+RowsSplit rows_split_plan(int64_t M, int64_t K, int R) {
+    RowsSplit p;
+    p.mt = R <= 64 ? 4 : 2;
+    p.groups = (M + 16 * p.mt - 1) / (16 * p.mt);
+    int64_t S = 256 / p.groups;
+    S = S < 1 ? 1 : (S > 16 ? 16 : S);
+    const int64_t chunks = (K + 127) / 128;
+    if (S > chunks) S = chunks;
+    p.kslice = (chunks + S - 1) / S * 128;
+    p.S = (int)((K + p.kslice - 1) / p.kslice);
+    return p;
+}
+bool rows_split_used(int64_t M, int R) { return R > 16 && M >= 256; }
+
 }  // namespace
 
+size_t rows_split_part_bytes(int64_t M, int64_t K, int R) {
+    if (!rows_split_used(M, R)) return 0;
+    return sizeof(float) * (size_t)rows_split_plan(M, K, R).S * (size_t)R * (size_t)M;
+}
+
 hipError_t launch_rows_skinny(const uint16_t *in, const uint16_t *w, int64_t M, int64_t K, int R,
-                              float *out, uint16_t *vt, hipStream_t s) {
+                              float *out, uint16_t *vt, float *part, hipStream_t s) {
     const int64_t Rp = cols_rank_pad(R);
     const dim3 grid((unsigned)((M + 15) / 16));
     const int nt = (R + 15) / 16;
     // decode-sized M: one wave per output element, spread over the chip
-    if (M * R <= 4096) {  // (the choice must not depend on vt: U and its recomputation agree bit for bit)
+    // (the choice of kernel must not depend on vt: U and its recomputation agree bit for bit)
+    if (M * R <= 4096) {
         const int64_t rc = vt ? Rp : R;
         hipLaunchKernelGGL(dot_rows_kernel, dim3((unsigned)((M * rc + 3) / 4)), dim3(256), 0, s, in, w, M, K, R, out,
                            vt, Rp);
+        return hipGetLastError();
+    }
+    if (rows_split_used(M, R)) {
+        if (!part) return hipErrorInvalidValue;
+        const RowsSplit pl = rows_split_plan(M, K, R);
+        const dim3 sgrid((unsigned)pl.groups, (unsigned)pl.S);
+        switch (nt) {
+#define QNF4_SPLIT(NTV, MTV)                                                                                       \
+    case NTV:                                                                                                      \
+        hipLaunchKernelGGL((rows_split_kernel<NTV, MTV>), sgrid, dim3(256), 0, s, in, w, M, K, R, pl.kslice, part); \
+        break;
+            QNF4_SPLIT(2, 4) QNF4_SPLIT(3, 4) QNF4_SPLIT(4, 4)
+            QNF4_SPLIT(5, 2) QNF4_SPLIT(6, 2) QNF4_SPLIT(7, 2) QNF4_SPLIT(8, 2)
+#undef QNF4_SPLIT
+            default: return hipErrorInvalidValue;
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t rc = vt ? Rp : R;
+        hipLaunchKernelGGL(rows_reduce_kernel, dim3((unsigned)((M * rc + 255) / 256)), dim3(256), 0, s, part, pl.S, M,
+                           R, out, vt, Rp);
         return hipGetLastError();
     }
     switch (nt) {
@@ -336,9 +482,8 @@ int64_t cols_rank_pad(int r) { return (r + 15) / 16 * 16; }
 hipError_t launch_bwd_prep(const uint16_t *B, int64_t d, int r, uint16_t *Bt, const float *U, int64_t M,
                            uint16_t *vt, hipStream_t s) {
     const int Rp = (int)cols_rank_pad(r);
-    const int64_t gt = (d + 255) / 256;
-    const int64_t gu = U ? (M + 255) / 256 : 0;
-    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)(gt + gu)), dim3(256), 0, s, B, d, r, Bt, gt, U, M, Rp, vt);
+    const int64_t n = d * r + (U ? M * Rp : 0);
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, B, d, r, Bt, U, M, Rp, vt);
     return hipGetLastError();
 }
 

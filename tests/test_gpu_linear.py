@@ -58,11 +58,13 @@ def test_single_layer_workload():
                                      (5, 4104, 4096, 16), (16, 64, 64, 1), (16, 1000, 2048, 16),
                                      (2, 4104, 256, 16), (1, 16408, 256, 16), (16, 16408, 512, 8),
                                      (700, 328, 192, 8), (1030, 200, 1088, 16), (1100, 4104, 320, 4),
-                                     (1100, 5512, 256, 8)])
+                                     (1100, 5512, 256, 8), (300, 320, 192, 33), (600, 264, 1088, 64),
+                                     (260, 200, 448, 128), (1030, 136, 4096, 17)])
 def test_shapes_ranks_and_ragged_tiles(m, d, k, r):
     """Ranks, ragged M, d, k tiles, the decode path (M <= 16), the expanding GEMM
     (M <= 512) and the GEMM on the bf16 copy (M > 512) in both tile widths,
-    with partial last tiles."""
+    with partial last tiles; r > 16 with M >= 256 takes the split-K row
+    products for U and G (ragged row groups and slices, r = 17 .. 128)."""
     inp = make_layer(21, m * 7 + r, d, k, m, r)
     check_layer(inp, 16.0, f"shape m={m} d={d} k={k} r={r}", bf16_rounding_allowance=True)
 
@@ -181,10 +183,14 @@ def test_one_hot_inputs_return_dequantized_weights_exactly():
     assert np.array_equal(what, ref)
 
 
-def test_recomputed_u_matches_saved_u_and_runs_are_deterministic():
+@pytest.mark.parametrize("m,r", [(200, 16), (520, 64)])
+def test_recomputed_u_matches_saved_u_and_runs_are_deterministic(m, r):
+    """Reruns give the same bits, and a backward that recomputes U (and its
+    planes) matches one given the forward's U bit for bit -- with r = 64 and
+    M >= 256 through the split-K row products and their reduction."""
     import bit_nf4_quantized_13_amd as q
-    say("determinism / U recompute")
-    inp = make_layer(41, 0, 512, 512, 200, 16)
+    say(f"determinism / U recompute m={m} r={r}")
+    inp = make_layer(41, r, 512, 512, m, r)
     w = q.qlora_nf4_quantize(to_dev_f32(inp.w0))
     xd, ad, bd, dyd = (to_dev_bf16(t) for t in (inp.x, inp.a, inp.b, inp.dy))
     y1, u1 = q.qlora_linear_fwd(w, xd, ad, bd, 32.0)
