@@ -23,7 +23,10 @@ execution span (calls rotating over weight copies totalling more than 512 MB
 so that neither the 256 MB Infinity Cache nor L2 serves them), with the time
 per call of the same calls replayed from a HIP graph beside it; and the 7B- and
 65B-shaped layers (all seven projections, forward + backward, and the quantize
-of every weight of the layer).
+of every weight of the layer).  Calls short enough for the binding's host work
+to matter (quantize of one projection, merge, dropout, the other formats'
+quantize and decode) are timed as captured calls replayed from a HIP graph;
+forward + backward pairs as back-to-back calls between two events.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -289,7 +292,10 @@ def run_model_bench(q, torch, name, reps=5, warm=2):
         outs = (torch.empty((m, k), dtype=torch.bfloat16, device="cuda"),
                 torch.empty((r, k), dtype=torch.float32, device="cuda"),
                 torch.empty((d, r), dtype=torch.float32, device="cuda"))
-        qm = time_calls(torch, lambda: q.qlora_nf4_quantize(w0, out=wq, workspace=qws), reps)
+        # quantize: the calls captured in a HIP graph and replayed (a single call is
+        # about as short as the binding's host work per call, which back-to-back
+        # eager calls would measure instead)
+        qm = time_graph(torch, lambda: q.qlora_nf4_quantize(w0, out=wq, workspace=qws), reps)
         del w0
 
         def fwd_bwd():
@@ -368,17 +374,7 @@ def run_merge_bench(q, torch, ctx, iters=20):
     w, x, a, b, alpha, y, u, lws, r = ctx
     d, k = w.d, w.k
     out = torch.empty((d, k), dtype=torch.bfloat16, device="cuda")
-    for _ in range(3):
-        q.qlora_adapter_merge(w, a, b, alpha, out=out)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(iters):
-        q.qlora_adapter_merge(w, a, b, alpha, out=out)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / iters
+    ms = time_graph(torch, lambda: q.qlora_adapter_merge(w, a, b, alpha, out=out), iters)
     nb = d * k // 64
     nbytes = d * k // 2 + nb + 4 * ((nb + 255) // 256) + 4 + 2 * r * k + 2 * d * r + 2 * d * k
     return {"us_per_call": round(ms * 1e3, 3), "algorithmic_bytes": nbytes,
@@ -402,6 +398,33 @@ def time_calls(torch, fn, iters):
     return e0.elapsed_time(e1) / iters
 
 
+def time_graph(torch, fn, iters, replays=4):
+    """Average ms of fn() per call: `iters` calls captured once in a HIP graph
+    (after warm-up calls on a side stream), then the graph replayed `replays`
+    times between two events on torch's current stream."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(iters):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) / (replays * iters)
+
+
 def run_format_bench(q, torch, ctx, fmt, iters=20):
     """A further storage format of the block constants -- "no_dq" (one fp32
     absmax per block) or "fp8" (double quantization with c2 in OCP FP8 e4m3):
@@ -421,7 +444,7 @@ def run_format_bench(q, torch, ctx, fmt, iters=20):
     da = torch.empty((r, k), dtype=torch.float32, device="cuda")
     db = torch.empty((d, r), dtype=torch.float32, device="cuda")
     log(f"{fmt}: layer4096 quantize / fwd+bwd")
-    q_ms = time_calls(torch, lambda: q.qlora_nf4_quantize(w0, out=wq, workspace=qws), iters)
+    q_ms = time_graph(torch, lambda: q.qlora_nf4_quantize(w0, out=wq, workspace=qws), iters)
 
     def fwd_bwd():
         q.qlora_linear_fwd(wq, x, a, b, alpha, out=y, u_out=u, workspace=lws)
@@ -450,7 +473,7 @@ def run_format_bench(q, torch, ctx, fmt, iters=20):
     def dec():
         q.qlora_linear_fwd(ws[it[0] % copies], dx_, da_, db_, wl.alpha, save_u=False, out=dy_, workspace=dws)
         it[0] += 1
-    dec_us = time_calls(torch, dec, 50) * 1e3
+    dec_us = time_graph(torch, dec, 50) * 1e3
     alg = packed + dconst + 2 * dm * p.k + 2 * wl.r * p.k + 2 * p.d * wl.r + 2 * dm * p.d
     del ws
     torch.cuda.empty_cache()
@@ -485,7 +508,7 @@ def run_dropout_bench(q, torch, ctx, p=0.05, iters=20):
         q.qlora_linear_fwd(w, x, a, b, alpha, out=y, u_out=u, workspace=ws, dropout=p, seed=1234)
         q.qlora_linear_bwd(w, x, dy, a, b, alpha, u=u, workspace=ws, outs=(dx, da, db), dropout=p, seed=1234)
     fb_ms = time_calls(torch, fwd_bwd, iters)
-    drop_ms = time_calls(torch, lambda: q.qlora_lora_dropout(x, p, 1234, out=xd), iters)
+    drop_ms = time_graph(torch, lambda: q.qlora_lora_dropout(x, p, 1234, out=xd), iters)
     flops = fwd_flops(m, d, k, r) + bwd_flops(m, d, k, r)
     return {"p": p, "fwd_bwd_ms": round(fb_ms, 4), "fwd_bwd_tflops": round(flops / (fb_ms * 1e-3) / 1e12, 3),
             "lora_dropout_us": round(drop_ms * 1e3, 2),
