@@ -10,16 +10,20 @@
 // weights into the adapters only.
 //
 // Design (MI355X, one 512-thread workgroup -- 8 waves, two per SIMD -- per
-// 512 x 128 output tile; k-steps of 64):
-//  * Wave w owns output rows [64 w, 64 w + 64) and all 128 columns: 4 x 8
-//    MFMA 16x16x32 tiles, fp32 accumulators in 128 AGPRs.
-//  * Both operand tiles live in LDS in two stages (activation [512][64] and
-//    weight [128][64] bf16, 160 KiB): while step kt runs its MFMAs on one
+// output tile; k-steps of 64):
+//  * Tiles: 512 x 128 when the weight tile is expanded in the kernel (M <=
+//    512, one tile row), else 256 x 256, or 256 x 128 where 256 x 256 tiles
+//    would leave CUs idle.  A wave owns 64 output rows and all 128 columns
+//    (512 x 128) or one column half (256-row tiles): 4 x 8 (4 x 4) MFMA
+//    16x16x32 tiles, fp32 accumulators in AGPRs.
+//  * Both operand tiles live in LDS in two stages (activation [TM][64] and
+//    weight [TN][64] bf16, up to 160 KiB): while step kt runs its MFMAs on one
 //    stage, the tiles of step kt + 1 move into the other, one barrier per
 //    step.  The activation tile (X or dY) goes global -> LDS by buffer_load
 //    ... lds transfers (16 bytes a lane), XOR-swizzled by 16-byte chunks so
-//    that the fragment reads are free of bank conflicts; each wave moves only
-//    its own rows.  The transfers of a step are spread one per MFMA group.
+//    that the fragment reads are free of bank conflicts; each wave moves an
+//    eighth of the rows.  The transfers of a step are spread over its MFMA
+//    groups.
 //  * The weight operand takes one of two forms.  With a single 512-row tile
 //    of M (M <= 512) the kernel expands it from the packed codes (EXPAND):
 //    codes and block scales arrive in registers three steps ahead, the 16
@@ -58,7 +62,6 @@ constexpr int BM = 512, BN = 128, BK = 64;
 constexpr int NTHREADS = 512;                 // 8 waves, two per SIMD
 constexpr int WM = BM / (NTHREADS / 64);      // rows per wave (64)
 constexpr int MI = WM / 16;                   // 16-row MFMA tiles per wave (4)
-constexpr int A_STAGE = BM * BK * 2;          // 64 KiB activation tile
 
 struct GemmArgs {
     const uint16_t *a;      // activation operand [M x Kd] bf16 (X or dY)
@@ -189,18 +192,31 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // tile from a dequantized bf16 copy written once per call.
 // F32OUT: the fp32 sums are stored unrounded (out_f32) for a caller that adds
 // another term before the one bf16 rounding.
-// TN: output columns per tile, 128 or (non-expanding kernel) 64: half as much
-// work per workgroup, for grids whose 128-wide tiles would leave CUs idle.
-template <bool DX, bool EXPAND, bool F32OUT = false, int TN = BN>
+// TM x TN: output rows x columns per tile, each of the 8 waves owning a block
+// of 64 rows:
+//   512 x 128  waves 8 x 1 of 64 x 128: the expanding kernel (one tile row, so
+//              each weight tile is expanded once);
+//   256 x 256  waves 4 x 2 of 64 x 128 (non-expanding): the same MFMA and
+//              fragment-read work per wave as 512 x 128 with a fifth fewer tile
+//              bytes moved into LDS per k-step (32 + 32 KiB against 64 + 16 KiB);
+//   256 x 128  waves 4 x 2 of 64 x 64 (non-expanding): half the work per
+//              workgroup, for grids whose 256 x 256 tiles would leave CUs idle.
+// With 256-row tiles (SQ) two waves read each activation row.
+template <bool DX, bool EXPAND, bool F32OUT = false, int TN = BN, int TM = BM>
 __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Consts tab) {
-    static_assert(TN == 128 || (TN == 64 && !EXPAND), "the expansion fills 128-row weight tiles");
-    constexpr int NJ = TN / 16;          // 16-column MFMA tiles per wave
+    static_assert((TM == 512 && TN == 128 && EXPAND) || (TM == 256 && (TN == 256 || TN == 128) && !EXPAND),
+                  "tile shapes: 512 x 128 (expanding), 256 x 256 and 256 x 128");
+    constexpr bool SQ = TM == 256;
+    constexpr int WNC = SQ ? TN / 2 : TN;  // output columns per wave
+    constexpr int NJ = WNC / 16;         // 16-column MFMA tiles per wave
     constexpr int WR = TN / 8;           // weight-tile rows each wave moves
+    constexpr int AR = TM / 8;           // activation-tile rows each wave moves
     constexpr int B_STAGE = TN * BK * 2; // weight tile bytes
-    // Two stages of the activation tile [512 rows][64 k] and of the weight tile
+    constexpr int A_ST = TM * BK * 2;    // activation tile bytes
+    // Two stages of the activation tile [TM rows][64 k] and of the weight tile
     // [TN rows][64 k] (up to 160 KiB).  One object per buffer so that the compiler
     // can tell them apart when it places waits for the global->LDS transfers.
-    __shared__ u32x4 sA0[A_STAGE / 16], sA1[A_STAGE / 16];
+    __shared__ u32x4 sA0[A_ST / 16], sA1[A_ST / 16];
     __shared__ u32x4 sB0[B_STAGE / 16], sB1[B_STAGE / 16];
     auto Aof = [&](auto S) __attribute__((always_inline)) -> u32x4 * {
         if constexpr (decltype(S)::value == 0) return sA0;
@@ -213,12 +229,13 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = SQ ? (wave & 3) : wave, wn = SQ ? (wave >> 2) : 0;  // the wave's 64-row, WNC-column block
     const int r16 = lane & 15, g = lane >> 4;
     if (tid == 0) span_start(p.span);
-    const int64_t tiles_n = (p.N + TN - 1) / TN, tiles_m = (p.M + BM - 1) / BM;
+    const int64_t tiles_n = (p.N + TN - 1) / TN, tiles_m = (p.M + TM - 1) / TM;
     int64_t mt, nt;
     tile_of(blockIdx.x, tiles_m, tiles_n, mt, nt);
-    const int64_t m_base = mt * BM, n_base = nt * TN;
+    const int64_t m_base = mt * TM, n_base = nt * TN;
     const int64_t nK = (p.Kd + BK - 1) / BK;
     const int64_t kb = p.k / 64;  // NF4 blocks per W0 row
 
@@ -229,33 +246,36 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
     const int lv = __float_as_int(lvf);
 
     // ---- activation tile: global -> LDS transfers of 8 rows x 128 B ---------------
-    // Wave w moves and reads only its own rows WM w .. WM w + WM - 1 (transfer b:
-    // rows WM w + 8 b ..).  Lane l lands in row 8 b + l / 8, physical chunk l % 8,
-    // which holds logical chunk (l % 8) ^ ((row >> 1) & 7) = (l % 8) ^ ((l / 16 + 4 b) & 7).
+    // Wave w moves rows AR w .. AR w + AR - 1 (transfer b: rows AR w + 8 b ..): with
+    // 512-row tiles exactly the rows it reads, with 256-row tiles (SQ) half of the
+    // rows of its own and of one other wave.  Lane l lands in row 8 b + l / 8,
+    // physical chunk l % 8, which holds logical chunk (l % 8) ^ ((row >> 1) & 7) =
+    // (l % 8) ^ ((l / 16 + 4 b) & 7) (AR w is a multiple of 16).
     // Rows past M read as zero.  Pieces past Kd (dX with d % 64 != 0) read the
     // next row's data: finite values that meet weight rows that are exactly zero.
-    const int64_t rows_here = (p.M - m_base) < BM ? (p.M - m_base) : BM;
+    const int64_t rows_here = (p.M - m_base) < TM ? (p.M - m_base) : TM;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + m_base * p.Kd, rows_here * p.Kd * 2);
-    const int dma_row = WM * wave + (lane >> 3);  // + 8 b
+    const int dma_row = AR * wave + (lane >> 3);  // + 8 b
     const uint32_t voff_a0 = (uint32_t)(((int64_t)dma_row * p.Kd + 8 * ((lane & 7) ^ ((lane >> 4) & 7))) * 2);
     const uint32_t voff_a1 = (uint32_t)(((int64_t)dma_row * p.Kd + 8 * ((lane & 7) ^ (((lane >> 4) + 4) & 7))) * 2);
     const uint32_t row8_bytes = (uint32_t)(8 * p.Kd * 2);
     auto issue_a = [&](int64_t kt, auto S, int b) __attribute__((always_inline)) {
-        dma16(ra, Aof(S) + (WM * wave + 8 * b) * 8, (b & 1) ? voff_a1 : voff_a0,
+        dma16(ra, Aof(S) + (AR * wave + 8 * b) * 8, (b & 1) ? voff_a1 : voff_a0,
               (uint32_t)b * row8_bytes + (uint32_t)kt * (BK * 2));
     };
-    // fragment reads (A: row WM w + 16 i + r16; B: row 16 j + r16; chunk 4 s + g),
-    // physical chunk (4 s + g) ^ ((r16 >> 1) & 7) in both tiles
+    // fragment reads (A: row WM wm + 16 i + r16; B: row WNC wn + 16 j + r16; chunk
+    // 4 s + g), physical chunk (4 s + g) ^ ((r16 >> 1) & 7) in both tiles
     const int frag0 = r16 * 8 + ((0 + g) ^ ((r16 >> 1) & 7));  // in 16-byte units
     const int frag1 = r16 * 8 + ((4 + g) ^ ((r16 >> 1) & 7));
-    const int arow = WM * wave * 8;
+    const int arow = WM * wm * 8;
+    const int brow = WNC * wn * 8;
     auto read_a = [&](auto S, int s, int i) __attribute__((always_inline)) -> uint4 {
         return __builtin_bit_cast(uint4, Aof(S)[arow + (s ? frag1 : frag0) + 128 * i]);
     };
 
-    // ---- weight tiles [128 n][64 k], same chunk layout ------------------------------
+    // ---- weight tiles [TN n][64 k], same chunk layout -------------------------------
     auto read_b = [&](auto S, int s, int j) __attribute__((always_inline)) -> uint4 {
-        return __builtin_bit_cast(uint4, Bof(S)[(s ? frag1 : frag0) + 128 * j]);
+        return __builtin_bit_cast(uint4, Bof(S)[brow + (s ? frag1 : frag0) + 128 * j]);
     };
     // transfer (non-expanding kernel): rows n_base .., 8 per transfer, wave w moves
     // rows WR w .. WR w + WR - 1; rows past N read as zero.  Transfer u lands in rows
@@ -422,12 +442,14 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
                 if (j == 1) expand_phase(wc, s, 0, st_w);
                 if (j == 4) expand_phase(wc, s, 1, st_w);
                 if (j == 6) expand_phase(wc, s, 2, st_w);
-            } else if constexpr (TN == 128) {
+            } else if constexpr (TN == 256) {  // 16 groups: 4 + 4 transfers, alternating
+                if (grp < 8) {
+                    if (grp & 1) issue_a(kn, S1{}, grp >> 1);
+                    else issue_w(kn, S1{}, grp >> 1);
+                }
+            } else {  // 256 x 128, 8 groups: 2 + 4 transfers
                 if (grp < 2) issue_w(kn, S1{}, grp);
-                if (grp >= 2 && grp < 10) issue_a(kn, S1{}, grp - 2);
-            } else {  // 8 groups: the weight transfer with the first activation one
-                if (grp == 0) issue_w(kn, S1{}, 0);
-                issue_a(kn, S1{}, grp);
+                else if (grp < 6) issue_a(kn, S1{}, grp - 2);
             }
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
@@ -440,9 +462,15 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
         // this step, issued after them, may still be in flight); expansion
         // writes done
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kWloads));
+        if constexpr (!SQ) {  // rows this wave moved itself
 #pragma unroll
-        for (int i = 0; i < MI; ++i) af[0][i] = read_a(S1{}, 0, i);
+            for (int i = 0; i < MI; ++i) af[0][i] = read_a(S1{}, 0, i);
+        }
         __builtin_amdgcn_s_barrier();
+        if constexpr (SQ) {  // rows other waves moved too
+#pragma unroll
+            for (int i = 0; i < MI; ++i) af[0][i] = read_a(S1{}, 0, i);
+        }
         bq[0] = read_b(S1{}, 0, 0);
         bq[1] = read_b(S1{}, 0, 1);
         sched_fence();
@@ -463,12 +491,18 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
 #pragma unroll
         for (int u = 0; u < WR / 8; ++u) issue_w(0, IC<0>{}, u);
 #pragma unroll
-        for (int b = 0; b < 8; ++b) issue_a(0, IC<0>{}, b);
+        for (int b = 0; b < AR / 8; ++b) issue_a(0, IC<0>{}, b);
     }
     __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (!SQ) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i) af[0][i] = read_a(IC<0>{}, 0, i);
+        for (int i = 0; i < MI; ++i) af[0][i] = read_a(IC<0>{}, 0, i);
+    }
     __syncthreads();
+    if constexpr (SQ) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) af[0][i] = read_a(IC<0>{}, 0, i);
+    }
     bq[0] = read_b(IC<0>{}, 0, 0);
     bq[1] = read_b(IC<0>{}, 0, 1);
 
@@ -511,8 +545,8 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
         const int64_t nE = p.Ke / BK;
         for (int64_t e = 0; e < nE; ++e) {
 #pragma unroll
-            for (int b = 0; b < 8; ++b)
-                dma16(rea, sA0 + (WM * wave + 8 * b) * 8, (b & 1) ? voff_e1 : voff_e0,
+            for (int b = 0; b < AR / 8; ++b)
+                dma16(rea, sA0 + (AR * wave + 8 * b) * 8, (b & 1) ? voff_e1 : voff_e0,
                       (uint32_t)b * row8_e + (uint32_t)e * (BK * 2));
 #pragma unroll
             for (int u = 0; u < WR / 8; ++u) dma16(reb, sB0 + (WR * wave + 8 * u) * 8, voff_eb[u], (uint32_t)e * (BK * 2));
@@ -540,11 +574,11 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
     // ---- epilogue: lane holds D[m = 16 i + r16][n = 16 j + 4 g .. + 3] ----------------
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-        const int64_t m = m_base + WM * wave + 16 * i + r16;
+        const int64_t m = m_base + WM * wm + 16 * i + r16;
         if (m >= p.M) continue;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            const int64_t n = n_base + 16 * j + 4 * g;
+            const int64_t n = n_base + WNC * wn + 16 * j + 4 * g;
             if (n >= p.N) continue;
             if constexpr (F32OUT) {
                 *reinterpret_cast<f32x4 *>(p.out_f32 + m * p.N + n) = acc[i][j];
@@ -772,17 +806,23 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a, Nf4Consts tab) {
     cols_reduce(a.red[second ? 1 : 0], (b - (second ? a.g_r0 : 0)) * 256 + threadIdx.x);
 }
 
-// Output columns per tile of the non-expanding GEMM.  A 512x64 tile does half
-// the work of a 512x128 one at a higher LDS cost per flop (the activation tile
-// is moved and read for half the columns): measured at 0.85-0.92 of the 128-wide
-// tile's time (M = 2048, K = 4096 and 11008), so kTile64Cost = 0.9.  Rounds of
-// 256 workgroups (one per CU) decide: 64 wins where the 128-wide grid leaves
-// half the CUs idle (M = 2048 against 4096 columns: 128 tiles).
-constexpr double kTile64Cost = 0.9;
-int pick_tile_n(int64_t tiles_m, int64_t N) {
-    const int64_t t128 = tiles_m * ((N + 127) / 128), t64 = tiles_m * ((N + 63) / 64);
-    const double r128 = (double)((t128 + 255) / 256), r64 = (double)((t64 + 255) / 256) * kTile64Cost;
-    return r64 < r128 ? 64 : 128;
+// Tile shape of the non-expanding GEMM: 256 x 256, or the narrow 256 x 128
+// (half the work per workgroup at a higher LDS cost per flop: the activation
+// tile is moved and read for half the columns), measured at 0.66 of the wide
+// tile's time (143 against 109 us for two rounds of narrow against one of wide
+// tiles, M = d = k = 4096), so kNarrowCost = 0.7.  Rounds of 256 workgroups
+// (one per CU) decide: narrow wins where the wide grid leaves CUs idle (M =
+// 2048 against 4096 columns: 128 wide tiles).
+constexpr double kNarrowCost = 0.7;
+struct TileShape {
+    int tm, tn;
+};
+int64_t tile_count(TileShape t, int64_t M, int64_t N) { return ((M + t.tm - 1) / t.tm) * ((N + t.tn - 1) / t.tn); }
+TileShape pick_tile(int64_t M, int64_t N) {
+    const TileShape wide{256, 256}, narrow{256, 128};
+    const double rw = (double)((tile_count(wide, M, N) + 255) / 256);
+    const double rn = (double)((tile_count(narrow, M, N) + 255) / 256) * kNarrowCost;
+    return rn < rw ? narrow : wide;
 }
 
 // What a launch runs: the preparation and the GEMM (kFull); the GEMM kernel alone
@@ -822,8 +862,8 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
 
     const int64_t tiles_m = (M + BM - 1) / BM;
     const bool expand = tiles_m == 1 || what == kExpandCore;
-    const int tn = expand ? BN : pick_tile_n(tiles_m, p.N);
-    const int64_t tiles = tiles_m * ((p.N + tn - 1) / tn);
+    const TileShape ts = expand ? TileShape{BM, BN} : pick_tile(M, p.N);
+    const int64_t tiles = tile_count(ts, M, p.N);
     if (what == kExpandCore) {
         PrepArgs q{};
         q.fmt = w.fmt;
@@ -874,20 +914,26 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
         else hipLaunchKernelGGL(prep_kernel<false>, pgrid, dim3(256), 0, st, q, nf4_consts());
     }
     const dim3 grid((unsigned)tiles), block(NTHREADS);
+#define QNF4_GEMM(DXV, EXV, F32V, TNV, TMV) \
+    hipLaunchKernelGGL((nf4_gemm_kernel<DXV, EXV, F32V, TNV, TMV>), grid, block, 0, st, p, nf4_consts())
+#define QNF4_GEMM_SHAPES(DXV, F32V)                                 \
+    do {                                                            \
+        if (ts.tn == 256) QNF4_GEMM(DXV, false, F32V, 256, 256);    \
+        else QNF4_GEMM(DXV, false, F32V, 128, 256);                 \
+    } while (0)
     if (out_f32) {
-        if (expand) hipLaunchKernelGGL((nf4_gemm_kernel<true, true, true>), grid, block, 0, st, p, nf4_consts());
-        else if (tn == 64) hipLaunchKernelGGL((nf4_gemm_kernel<true, false, true, 64>), grid, block, 0, st, p, nf4_consts());
-        else hipLaunchKernelGGL((nf4_gemm_kernel<true, false, true>), grid, block, 0, st, p, nf4_consts());
+        if (expand) QNF4_GEMM(true, true, true, 128, 512);
+        else QNF4_GEMM_SHAPES(true, true);
     } else if (expand) {
-        if (dx) hipLaunchKernelGGL((nf4_gemm_kernel<true, true>), grid, block, 0, st, p, nf4_consts());
-        else hipLaunchKernelGGL((nf4_gemm_kernel<false, true>), grid, block, 0, st, p, nf4_consts());
-    } else if (tn == 64) {
-        if (dx) hipLaunchKernelGGL((nf4_gemm_kernel<true, false, false, 64>), grid, block, 0, st, p, nf4_consts());
-        else hipLaunchKernelGGL((nf4_gemm_kernel<false, false, false, 64>), grid, block, 0, st, p, nf4_consts());
+        if (dx) QNF4_GEMM(true, true, false, 128, 512);
+        else QNF4_GEMM(false, true, false, 128, 512);
+    } else if (dx) {
+        QNF4_GEMM_SHAPES(true, false);
     } else {
-        if (dx) hipLaunchKernelGGL((nf4_gemm_kernel<true, false>), grid, block, 0, st, p, nf4_consts());
-        else hipLaunchKernelGGL((nf4_gemm_kernel<false, false>), grid, block, 0, st, p, nf4_consts());
+        QNF4_GEMM_SHAPES(false, false);
     }
+#undef QNF4_GEMM_SHAPES
+#undef QNF4_GEMM
     return hipGetLastError();
 }
 

@@ -59,11 +59,14 @@ def test_single_layer_workload():
                                      (2, 4104, 256, 16), (1, 16408, 256, 16), (16, 16408, 512, 8),
                                      (700, 328, 192, 8), (1030, 200, 1088, 16), (1100, 4104, 320, 4),
                                      (1100, 5512, 256, 8), (300, 320, 192, 33), (600, 264, 1088, 64),
-                                     (260, 200, 448, 128), (1030, 136, 4096, 17)])
+                                     (260, 200, 448, 128), (1030, 136, 4096, 17),
+                                     (1100, 6600, 320, 8), (1100, 264, 6592, 8)])
 def test_shapes_ranks_and_ragged_tiles(m, d, k, r):
     """Ranks, ragged M, d, k tiles, the decode path (M <= 16), the expanding GEMM
-    (M <= 512) and the GEMM on the bf16 copy (M > 512) in both tile widths,
-    with partial last tiles; r > 16 with M >= 256 takes the split-K row
+    (M <= 512) and the GEMM on the bf16 copy (M > 512) in its tile shapes
+    (256 x 128 for most; 256 x 256 for the forward at m = 1100, d = 6600 and for
+    dX at m = 1100, k = 6592, over d = 264 not a multiple of 64), with partial
+    last tiles; r > 16 with M >= 256 takes the split-K row
     products for U and G (ragged row groups and slices, r = 17 .. 128)."""
     inp = make_layer(21, m * 7 + r, d, k, m, r)
     check_layer(inp, 16.0, f"shape m={m} d={d} k={k} r={r}", bf16_rounding_allowance=True)
