@@ -67,7 +67,7 @@ QuantWs quant_ws(int64_t d, int64_t k, int block) {
 }
 
 struct LinWs {
-    size_t ctr, dpart, shat, ext_a, ext_b, wbf, u, bt, g, vt, part, total;
+    size_t ctr, dpart, shat, ext_a, ext_b, wbf, kpart, kpart_bytes, u, bt, g, vt, part, total;
 };
 // The decode counters sit first, at the same offset for every shape, so that no
 // other call's data ever lands on them.
@@ -87,6 +87,9 @@ LinWs lin_ws(int64_t M, int64_t d, int64_t k, int r) {
     off += round_up(sizeof(uint16_t) * (d > k ? d : k) * ke, 256);
     l.wbf = off;
     off += round_up(sizeof(uint16_t) * gemm_wbf_elems(M, d, k), 256);
+    l.kpart = off;  // the GEMMs' split-K partial sums
+    l.kpart_bytes = gemm_ksplit_bytes(M, d, k);
+    off += round_up(l.kpart_bytes, 256);
     l.u = off;
     off += round_up(sizeof(float) * M * r, 256);
     l.bt = off;
@@ -107,7 +110,8 @@ LinWs lin_ws(int64_t M, int64_t d, int64_t k, int r) {
 
 GemmWs gemm_ws(char *base, const LinWs &l) {
     return GemmWs{reinterpret_cast<float *>(base + l.shat), reinterpret_cast<uint16_t *>(base + l.ext_a),
-                  reinterpret_cast<uint16_t *>(base + l.ext_b), reinterpret_cast<uint16_t *>(base + l.wbf)};
+                  reinterpret_cast<uint16_t *>(base + l.ext_b), reinterpret_cast<uint16_t *>(base + l.wbf),
+                  reinterpret_cast<float *>(base + l.kpart), l.kpart_bytes};
 }
 
 // Dropout parameters: the keep threshold floor(p 2^32) (exact in fp64; below 2^32

@@ -76,6 +76,9 @@ struct GemmArgs {
     int64_t ldw;            // forward: What [d x k], ldw = k; dX: What^T [k x ldw], ldw = d rounded up to 64
     uint16_t *out;          // Y or dX [M x N] bf16
     float *out_f32;         // F32OUT kernels: the fp32 sums [M x N] instead of out
+    float *part;            // null, or (split K) the fp32 partial sums [S][M x N], added by ksplit_reduce_kernel
+    int64_t ks_len;         // k-steps per slice of K (split K; else nK)
+    int S;                  // slices of K
     unsigned long long *span;  // null, or a measurement span (span_start / span_end)
 };
 
@@ -233,10 +236,16 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
     const int r16 = lane & 15, g = lane >> 4;
     if (tid == 0) span_start(p.span);
     const int64_t tiles_n = (p.N + TN - 1) / TN, tiles_m = (p.M + TM - 1) / TM;
+    // split K: workgroup b takes slice b / tiles of the k-steps for tile b % tiles
+    // (slice-major, so that each slice's tiles keep the XCD-aware order)
+    const int64_t tiles = tiles_m * tiles_n;
+    const int slice = (int)(blockIdx.x / tiles);
     int64_t mt, nt;
-    tile_of(blockIdx.x, tiles_m, tiles_n, mt, nt);
+    tile_of(blockIdx.x - (int64_t)slice * tiles, tiles_m, tiles_n, mt, nt);
     const int64_t m_base = mt * TM, n_base = nt * TN;
     const int64_t nK = (p.Kd + BK - 1) / BK;
+    const int64_t k_lo = slice * p.ks_len;                                   // this workgroup's k-steps
+    const int64_t k_hi = k_lo + p.ks_len < nK ? k_lo + p.ks_len : nK;       // [k_lo, k_hi), never empty
     const int64_t kb = p.k / 64;  // NF4 blocks per W0 row
 
     // NF4 level table: lane j holds C[j % 16]
@@ -426,8 +435,8 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
         const Wdata &wc = Wset(IC<(R + 1) % 3>{});
         Wdata &wl = Wset(IC<R % 3>{});
         u32x4 *const st_w = Bof(S1{});
-        const int64_t kn = kt + 1 < nK ? kt + 1 : nK - 1;
-        const int64_t kw = kt + 3 < nK ? kt + 3 : nK - 1;
+        const int64_t kn = kt + 1 < k_hi ? kt + 1 : k_hi - 1;
+        const int64_t kw = kt + 3 < k_hi ? kt + 3 : k_hi - 1;
 #pragma unroll
         for (int grp = 0; grp < 2 * NJ; ++grp) {
             const int s = grp / NJ, j = grp % NJ;
@@ -476,22 +485,22 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
         sched_fence();
     };
 
-    // ---- prologue: A(0) and weight tile 0 in LDS; weight data of steps 1, 2 loaded ----
+    // ---- prologue: A(k_lo) and weight tile k_lo in LDS; weight data of the next two steps loaded ----
     if constexpr (EXPAND) {
-        load_w(0, w0);
+        load_w(k_lo, w0);
 #pragma unroll
-        for (int b = 0; b < 8; ++b) issue_a(0, IC<0>{}, b);
-        load_w(nK > 1 ? 1 : 0, w1);
-        load_w(nK > 2 ? 2 : nK - 1, w2);
+        for (int b = 0; b < 8; ++b) issue_a(k_lo, IC<0>{}, b);
+        load_w(k_lo + 1 < k_hi ? k_lo + 1 : k_lo, w1);
+        load_w(k_lo + 2 < k_hi ? k_lo + 2 : k_hi - 1, w2);
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int ph = 0; ph < 3; ++ph) expand_phase(w0, c, ph, sB0);
     } else {
 #pragma unroll
-        for (int u = 0; u < WR / 8; ++u) issue_w(0, IC<0>{}, u);
+        for (int u = 0; u < WR / 8; ++u) issue_w(k_lo, IC<0>{}, u);
 #pragma unroll
-        for (int b = 0; b < AR / 8; ++b) issue_a(0, IC<0>{}, b);
+        for (int b = 0; b < AR / 8; ++b) issue_a(k_lo, IC<0>{}, b);
     }
     __builtin_amdgcn_s_waitcnt(0);
     if constexpr (!SQ) {
@@ -506,10 +515,10 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
     bq[0] = read_b(IC<0>{}, 0, 0);
     bq[1] = read_b(IC<0>{}, 0, 1);
 
-    // ---- main k-loop: step 0 peeled, then six steps per trip -------------------------
-    step(0, IC<0>{}, IC<1>{});
-    int64_t kt = 1;
-    for (; kt + 6 <= nK; kt += 6) {
+    // ---- main k-loop: step k_lo peeled, then six steps per trip ----------------------
+    step(k_lo, IC<0>{}, IC<1>{});
+    int64_t kt = k_lo + 1;
+    for (; kt + 6 <= k_hi; kt += 6) {
         step(kt + 0, IC<1>{}, IC<0>{});
         step(kt + 1, IC<2>{}, IC<0>{});
         step(kt + 2, IC<3>{}, IC<0>{});
@@ -517,14 +526,14 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
         step(kt + 4, IC<5>{}, IC<0>{});
         step(kt + 5, IC<0>{}, IC<0>{});
     }
-    if (kt < nK) step(kt, IC<1>{}, IC<0>{});
-    if (kt + 1 < nK) step(kt + 1, IC<2>{}, IC<0>{});
-    if (kt + 2 < nK) step(kt + 2, IC<3>{}, IC<0>{});
-    if (kt + 3 < nK) step(kt + 3, IC<4>{}, IC<0>{});
-    if (kt + 4 < nK) step(kt + 4, IC<5>{}, IC<0>{});
+    if (kt < k_hi) step(kt, IC<1>{}, IC<0>{});
+    if (kt + 1 < k_hi) step(kt + 1, IC<2>{}, IC<0>{});
+    if (kt + 2 < k_hi) step(kt + 2, IC<3>{}, IC<0>{});
+    if (kt + 3 < k_hi) step(kt + 3, IC<4>{}, IC<0>{});
+    if (kt + 4 < k_hi) step(kt + 4, IC<5>{}, IC<0>{});
 
-    // ---- adapter term: Ke/64 extra k-steps, operands laid out in memory ------------
-    {
+    // ---- adapter term: Ke/64 extra k-steps, operands laid out in memory (last slice) ----
+    if (slice == p.S - 1) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         const __amdgpu_buffer_rsrc_t rea = make_rsrc(p.ext_a + m_base * p.Ke, rows_here * p.Ke * 2);
@@ -566,10 +575,10 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
-        // the epilogue reads the accumulators with VALU instructions: let the
-        // last MFMAs (inline asm, invisible to the hazard recognizer) drain
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
     }
+    // the epilogue reads the accumulators with VALU instructions: let the
+    // last MFMAs (inline asm, invisible to the hazard recognizer) drain
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
 
     // ---- epilogue: lane holds D[m = 16 i + r16][n = 16 j + 4 g .. + 3] ----------------
 #pragma unroll
@@ -580,7 +589,9 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
         for (int j = 0; j < NJ; ++j) {
             const int64_t n = n_base + WNC * wn + 16 * j + 4 * g;
             if (n >= p.N) continue;
-            if constexpr (F32OUT) {
+            if (p.part) {
+                *reinterpret_cast<f32x4 *>(p.part + ((int64_t)slice * p.M + m) * p.N + n) = acc[i][j];
+            } else if constexpr (F32OUT) {
                 *reinterpret_cast<f32x4 *>(p.out_f32 + m * p.N + n) = acc[i][j];
             } else {
                 const uint2 o{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
@@ -825,6 +836,56 @@ TileShape pick_tile(int64_t M, int64_t N) {
     return rn < rw ? narrow : wide;
 }
 
+// Slices of K for a grid of `tiles` output tiles over nK k-steps: with at most
+// half a round of tiles (<= 128 workgroups for 256 CUs), enough slices to fill
+// about one round, at most 8 and at least 4 k-steps (256 k) each; their fp32
+// partial sums are added by ksplit_reduce_kernel.  One slice otherwise.
+int ksplit_slices(int64_t tiles, int64_t nK) {
+    if (tiles > 128) return 1;
+    int64_t S = 256 / tiles;
+    S = S < 8 ? S : 8;
+    S = S < nK / 4 ? S : nK / 4;
+    if (S < 2) return 1;
+    const int64_t len = (nK + S - 1) / S;
+    return (int)((nK + len - 1) / len);  // no empty slice
+}
+
+// out[e] = sum over s of part[s][e] in slice order, rounded once to bf16 (or
+// stored in fp32 to out_f32); four consecutive elements per thread.
+__global__ __launch_bounds__(256) void ksplit_reduce_kernel(const float *__restrict__ part, int S, int64_t MN,
+                                                            uint16_t *__restrict__ out, float *__restrict__ out_f32) {
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e >= MN) return;  // MN % 4 == 0
+    f32x4 v = *reinterpret_cast<const f32x4 *>(part + e);
+    for (int q = 1; q < S; ++q) {
+        const f32x4 t = *reinterpret_cast<const f32x4 *>(part + (int64_t)q * MN + e);
+        v = f32x4{v[0] + t[0], v[1] + t[1], v[2] + t[2], v[3] + t[3]};
+    }
+    if (out_f32) *reinterpret_cast<f32x4 *>(out_f32 + e) = v;
+    else *reinterpret_cast<uint2 *>(out + e) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+
+// Tiles and slices of K of one GEMM launch.
+struct GemmGrid {
+    TileShape ts;
+    int64_t tiles;
+    int S;
+    int64_t ks_len;
+};
+GemmGrid gemm_grid(int64_t M, int64_t N, int64_t Kd, bool force_expand) {
+    GemmGrid g;
+    const bool expand = (M + BM - 1) / BM == 1 || force_expand;
+    g.ts = expand ? TileShape{BM, BN} : pick_tile(M, N);
+    g.tiles = tile_count(g.ts, M, N);
+    const int64_t nK = (Kd + BK - 1) / BK;
+    g.S = ksplit_slices(g.tiles, nK);
+    g.ks_len = (nK + g.S - 1) / g.S;
+    return g;
+}
+size_t ksplit_bytes(const GemmGrid &g, int64_t M, int64_t N) {
+    return g.S > 1 ? sizeof(float) * (size_t)g.S * (size_t)M * (size_t)N : 0;
+}
+
 // What a launch runs: the preparation and the GEMM (kFull); the GEMM kernel alone
 // on a workspace that a full launch with the same arguments prepared (kCoreOnly);
 // or, for measurement, the block scales and the expanding GEMM kernel whatever
@@ -862,8 +923,15 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
 
     const int64_t tiles_m = (M + BM - 1) / BM;
     const bool expand = tiles_m == 1 || what == kExpandCore;
-    const TileShape ts = expand ? TileShape{BM, BN} : pick_tile(M, p.N);
-    const int64_t tiles = tile_count(ts, M, p.N);
+    GemmGrid gg = gemm_grid(M, p.N, p.Kd, what == kExpandCore);
+    if (ksplit_bytes(gg, M, p.N) > ws.kpart_bytes) {  // a workspace sized for the other kernel choice
+        gg.S = 1;
+        gg.ks_len = (p.Kd + BK - 1) / BK;
+    }
+    const TileShape ts = gg.ts;
+    p.S = gg.S;
+    p.ks_len = gg.ks_len;
+    p.part = gg.S > 1 ? ws.kpart : nullptr;
     if (what == kExpandCore) {
         PrepArgs q{};
         q.fmt = w.fmt;
@@ -913,7 +981,7 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
         if (dx) hipLaunchKernelGGL(prep_kernel<true>, pgrid, dim3(256), 0, st, q, nf4_consts());
         else hipLaunchKernelGGL(prep_kernel<false>, pgrid, dim3(256), 0, st, q, nf4_consts());
     }
-    const dim3 grid((unsigned)tiles), block(NTHREADS);
+    const dim3 grid((unsigned)(gg.tiles * gg.S)), block(NTHREADS);
 #define QNF4_GEMM(DXV, EXV, F32V, TNV, TMV) \
     hipLaunchKernelGGL((nf4_gemm_kernel<DXV, EXV, F32V, TNV, TMV>), grid, block, 0, st, p, nf4_consts())
 #define QNF4_GEMM_SHAPES(DXV, F32V)                                 \
@@ -934,12 +1002,23 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
     }
 #undef QNF4_GEMM_SHAPES
 #undef QNF4_GEMM
+    if (gg.S > 1) {
+        const int64_t MN = M * p.N;
+        hipLaunchKernelGGL(ksplit_reduce_kernel, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0, st, ws.kpart, gg.S,
+                           MN, out_f32 ? nullptr : out, out_f32);
+    }
     return hipGetLastError();
 }
 
 }  // namespace
 
 int64_t gemm_ext_cols(int r) { return (2 * (int64_t)r + BK - 1) / BK * BK; }
+
+size_t gemm_ksplit_bytes(int64_t M, int64_t d, int64_t k) {
+    const size_t fwd = ksplit_bytes(gemm_grid(M, d, k, false), M, d);
+    const size_t dx = ksplit_bytes(gemm_grid(M, k, d, false), M, k);
+    return fwd > dx ? fwd : dx;
+}
 
 int64_t gemm_wbf_elems(int64_t M, int64_t d, int64_t k) {
     return (M + BM - 1) / BM > 1 ? k * ((d + 63) / 64 * 64) : 0;

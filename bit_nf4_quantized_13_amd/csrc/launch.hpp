@@ -99,8 +99,15 @@ struct GemmWs {
     uint16_t *ext_a;
     uint16_t *ext_b;
     uint16_t *wbf;
+    float *kpart;          // split-K partial sums (gemm_ksplit_bytes)
+    size_t kpart_bytes;
 };
 int64_t gemm_ext_cols(int r);
+// Bytes of fp32 partial sums the GEMMs of an M-row call split over K need (the
+// larger of the forward's and dX's; 0 when neither splits): grids that leave
+// most CUs idle (M <= 512 expands the weight tiles in 512 x 128 tiles, one tile
+// row) take their k-steps in up to 8 slices.  At most 64 MiB.
+size_t gemm_ksplit_bytes(int64_t M, int64_t d, int64_t k);
 int64_t gemm_wbf_elems(int64_t M, int64_t d, int64_t k);
 // Y[M x d] = bf16( X[M x k] What^T + [hi(sU) | lo(sU)] [B | B]^T ),  U [M x r] fp32.
 hipError_t launch_gemm_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, const float *U,

@@ -166,8 +166,12 @@ size_t qlora_linear_workspace(int64_t M, int64_t d, int64_t k, int32_t r);
  * expands What from the NF4 codes tile by tile; for M > 512 the call first
  * writes a bf16 copy of What (2 d k bytes of the workspace) and the GEMM
  * streams it (faster there than expanding every weight tile once per 512
- * rows of X); both bit-identical to qlora_nf4_dequantize.  For
- * M <= 16 (decode) the 64-weight block scale is applied once to the fp32 sum
+ * rows of X); both bit-identical to qlora_nf4_dequantize.  Where the
+ * output tiles alone would leave most of the GPU idle (e.g. M <= 512 against
+ * a few thousand columns), the GEMM's k-steps run in up to 8 slices whose
+ * fp32 partial sums (up to 64 MiB of the workspace) are added in slice order
+ * before the one rounding to bf16: the sum is associated differently from an
+ * unsplit call, deterministically.  For M <= 16 (decode) the 64-weight block scale is applied once to the fp32 sum
  * over the block (over each half block with M <= 2, r <= 16, k <= 4096 and
  * d >= 8192, which take a vector dot-product kernel), with the NF4 levels in
  * bf16: the same product, rounded differently (within the library's fwd
