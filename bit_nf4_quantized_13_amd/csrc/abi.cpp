@@ -308,9 +308,14 @@ int qlora_linear_fwd(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M,
     float *dpart = reinterpret_cast<float *>(base + l.dpart);
     unsigned long long *ctr = reinterpret_cast<unsigned long long *>(base + l.ctr);
     hipError_t e = hipSuccess;
-    if (M <= 16 && w->k <= kDecodeMaxK) {
-        // HBM-bound: one pass over the codes; U = X A^T in the same kernel for r <= 16
-        e = decode_forward(nw, x, M, A, B, r, scale, Y, U_save, ctr, dpart, U, s);
+    if (M <= kDecodeChunkRows && w->k <= kDecodeMaxK) {
+        // HBM-bound: one pass over the codes per 16-row chunk of X; U = X A^T in the
+        // same kernel for r <= 16
+        for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += 16) {
+            const int64_t mc = M - m0 < 16 ? M - m0 : 16;
+            e = decode_forward(nw, x + m0 * w->k, mc, A, B, r, scale, Y + m0 * w->d, U_save ? U_save + m0 * r : nullptr,
+                               ctr, dpart, U + m0 * r, s);
+        }
     } else {
         e = launch_rows_skinny(x, A, M, w->k, r, U, nullptr, reinterpret_cast<float *>(base + l.part), s);
         if (e == hipSuccess) e = launch_gemm_fwd(nw, x, M, U, B, r, scale, Y, gemm_ws(base, l), s);
@@ -519,7 +524,8 @@ int qlora_linear_gemm_only(const qlora_nf4_weight *w, int32_t backward, int32_t 
     if (r > QLORA_MAX_RANK || w->d % 8 != 0) return QLORA_ENOTSUP;
     if (!linear_shape_ok(M, w->d, w->k, r)) return QLORA_ENOTSUP;
     if (!aligned(a, 16) || !aligned(out, 16)) return QLORA_EALIGN;
-    if (!backward && M <= 16 && w->k <= kDecodeMaxK) return QLORA_EINVAL;  // the decode path has no separate GEMM
+    if (!backward && M <= kDecodeChunkRows && w->k <= kDecodeMaxK)
+        return QLORA_EINVAL;  // the decode path has no separate GEMM
     const LinWs l = lin_ws(M, w->d, w->k, r);
     if (!ws || ws_bytes < l.total) return QLORA_EWORKSPACE;
     if (!aligned(ws, 16)) return QLORA_EALIGN;

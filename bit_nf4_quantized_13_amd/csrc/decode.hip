@@ -649,7 +649,7 @@ hipError_t launch_tw(const DecodeArgs &a, int fmt, int grid, hipStream_t st) {
 size_t decode_counter_bytes() { return sizeof(unsigned long long) * DEC_MAX_GROUPS; }
 
 size_t decode_part_bytes(int64_t M, int64_t d, int64_t k) {
-    if (M < 1 || M > 16) return 0;
+    if (M < 1 || M > kDecodeChunkRows) return 0;  // per 16-row chunk: the same for every chunk
     const DecodePlan pl = decode_plan(d, k);
     if (pl.S == 1) return 0;
     return sizeof(f32x4) * (size_t)pl.grid * 64 * ((size_t)pl.TW + 1);

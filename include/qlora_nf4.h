@@ -171,11 +171,13 @@ size_t qlora_linear_workspace(int64_t M, int64_t d, int64_t k, int32_t r);
  * a few thousand columns), the GEMM's k-steps run in up to 8 slices whose
  * fp32 partial sums (up to 64 MiB of the workspace) are added in slice order
  * before the one rounding to bf16: the sum is associated differently from an
- * unsplit call, deterministically.  For M <= 16 (decode) the 64-weight block scale is applied once to the fp32 sum
- * over the block (over each half block with M <= 2, r <= 16, k <= 4096 and
- * d >= 8192, which take a vector dot-product kernel), with the NF4 levels in
- * bf16: the same product, rounded differently (within the library's fwd
- * tolerance of the bf16 What product).
+ * unsplit call, deterministically.  For M <= 16 (decode; M <= 64 as
+ * consecutive 16-row chunks of X, one decode launch each, the same bits as
+ * separate calls on the chunks) the 64-weight block scale is applied once to
+ * the fp32 sum over the block (over each half block with M <= 2, r <= 16,
+ * k <= 4096 and d >= 8192, which take a vector dot-product kernel), with the
+ * NF4 levels in bf16: the same product, rounded differently (within the
+ * library's fwd tolerance of the bf16 What product).
  * A call with M <= 16 and r <= 16 is one kernel (U = X A^T included); it
  * keeps counters in the first 32 KiB of the workspace between calls, which
  * it tags and resets itself: the caller need not clear them, but must not

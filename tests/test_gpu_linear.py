@@ -96,13 +96,14 @@ def test_decode_workspace_reuse_and_garbage():
 
 @pytest.mark.parametrize("m,d,k", [(1, 16, 4096), (16, 48, 1024), (4, 1016, 4096), (7, 520, 2048),
                                    (2, 104, 1472), (16, 8, 640), (5, 1016, 4096), (6, 104, 1472),
-                                   (8, 16, 4096)])
+                                   (8, 16, 4096), (40, 1016, 4096), (17, 48, 1024)])
 def test_decode_k_split_shapes(m, d, k):
     """Few row tiles: the decode forward splits k over 2..8
     workgroups per tile group (even and uneven block counts per slice), whose
     partial sums the last one to arrive adds.  Forward parity, and the
     same bits on a second call on the same workspace (the counters left ready
-    by the first)."""
+    by the first).  M = 17, 40: 16-row chunks, one launch each, sharing the
+    counters and partial sums in stream order."""
     import bit_nf4_quantized_13_amd as q
     inp = make_layer(47, d + m, d, k, m, 16)
     check_layer(inp, 32.0, f"decode k-split m={m} d={d} k={k}", want_bwd=False, bf16_rounding_allowance=True)
@@ -116,17 +117,35 @@ def test_decode_k_split_shapes(m, d, k):
 
 
 @pytest.mark.parametrize("m,d,k,r", [(1, 8192, 64, 1), (2, 16392, 512, 16), (1, 8200, 1088, 7), (2, 12296, 3200, 9),
-                                     (3, 8200, 1088, 7), (4, 8192, 64, 1)])
+                                     (3, 8200, 1088, 7), (4, 8192, 64, 1), (34, 8200, 1088, 7)])
 def test_decode_dot_path_shapes(m, d, k, r):
     """M <= 2, r <= 16, k <= 4096, d >= 8192: the dot-product decode kernel
     (the decode workloads' own 14336-row shape is in
     test_decode_shapes_forward), and M = 3, 4 on such shapes through the
-    matrix-core kernel.  Four to eight rounds of 8 rows per workgroup, more
+    matrix-core kernel; M = 34: two 16-row chunks, then two rows on the
+    dot-product kernel.  Four to eight rounds of 8 rows per workgroup, more
     workgroups than a round of the chip (d = 16392: 257), k chunks past the
     row end (k = 64, 1088, 3200), ranks below 16."""
     inp = make_layer(59, m * 31 + r, d, k, m, r)
     check_layer(inp, 2.0 * r, f"decode dot m={m} d={d} k={k} r={r}", want_bwd=False,
                 bf16_rounding_allowance=True)
+
+
+def test_decode_chunks_equal_separate_calls():
+    """A forward of 17..64 rows runs the decode kernel on consecutive 16-row
+    chunks of X: the same bits (Y and U) as separate calls on the chunks."""
+    import bit_nf4_quantized_13_amd as q
+    for m, d, k, r in ((40, 4096, 1024, 16), (35, 8200, 512, 8), (33, 520, 2048, 24), (64, 1016, 1024, 4)):
+        inp = make_layer(61, m + r, d, k, m, r)
+        w = q.qlora_nf4_quantize(to_dev_f32(inp.w0))
+        xd, ad, bd = (to_dev_bf16(t) for t in (inp.x, inp.a, inp.b))
+        ws = torch.empty(q.linear_workspace_bytes(m, d, k, r), dtype=torch.uint8, device="cuda")
+        y, u = q.qlora_linear_fwd(w, xd, ad, bd, 2.0 * r, workspace=ws)
+        parts = [q.qlora_linear_fwd(w, xd[m0:m0 + 16].contiguous(), ad, bd, 2.0 * r, workspace=ws)
+                 for m0 in range(0, m, 16)]
+        torch.cuda.synchronize()
+        assert torch.equal(y, torch.cat([p_[0] for p_ in parts])), (m, d, k, r)
+        assert torch.equal(u, torch.cat([p_[1] for p_ in parts])), (m, d, k, r)
 
 
 def check_decode_workspace(d):
