@@ -75,8 +75,8 @@ struct GemmArgs {
     const uint16_t *wbf;    // dequantized weight operand [N x ldw] bf16 (non-expanding kernel)
     int64_t ldw;            // forward: What [d x k], ldw = k; dX: What^T [k x ldw], ldw = d rounded up to 64
     uint16_t *out;          // Y or dX [M x N] bf16
-    float *out_f32;         // F32OUT kernels: the fp32 sums [M x N] instead of out
-    float *part;            // null, or (split K) the fp32 partial sums [S][M x N], added by ksplit_reduce_kernel
+    float *out_f32;         // F32OUT kernels: the fp32 sums [S][M x N] instead of out (split K: one plane per
+                            // slice, added by ksplit_reduce_kernel)
     int64_t ks_len;         // k-steps per slice of K (split K; else nK)
     int S;                  // slices of K
     unsigned long long *span;  // null, or a measurement span (span_start / span_end)
@@ -195,22 +195,25 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // tile from a dequantized bf16 copy written once per call.
 // F32OUT: the fp32 sums are stored unrounded (out_f32) for a caller that adds
 // another term before the one bf16 rounding.
-// TM x TN: output rows x columns per tile, each of the 8 waves owning a block
-// of 64 rows:
-//   512 x 128  waves 8 x 1 of 64 x 128: the expanding kernel (one tile row, so
-//              each weight tile is expanded once);
+// TM x TN: output rows x columns per tile, the 8 waves in TM / 64 rows of
+// 64-row blocks by 512 / TM columns:
+//   TM x 128   (TM = 64, 128, 256, 512) the expanding kernel, which has a single
+//              tile row (each weight tile expanded once): TM the smallest that
+//              holds M, so few tokens do not run empty rows through the MFMAs;
 //   256 x 256  waves 4 x 2 of 64 x 128 (non-expanding): the same MFMA and
 //              fragment-read work per wave as 512 x 128 with a fifth fewer tile
 //              bytes moved into LDS per k-step (32 + 32 KiB against 64 + 16 KiB);
 //   256 x 128  waves 4 x 2 of 64 x 64 (non-expanding): half the work per
 //              workgroup, for grids whose 256 x 256 tiles would leave CUs idle.
-// With 256-row tiles (SQ) two waves read each activation row.
+// Below 512 rows (SQ) several waves read each activation row.
 template <bool DX, bool EXPAND, bool F32OUT = false, int TN = BN, int TM = BM>
 __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Consts tab) {
-    static_assert((TM == 512 && TN == 128 && EXPAND) || (TM == 256 && (TN == 256 || TN == 128) && !EXPAND),
-                  "tile shapes: 512 x 128 (expanding), 256 x 256 and 256 x 128");
-    constexpr bool SQ = TM == 256;
-    constexpr int WNC = SQ ? TN / 2 : TN;  // output columns per wave
+    static_assert((EXPAND && TN == 128 && (TM == 64 || TM == 128 || TM == 256 || TM == 512)) ||
+                      (!EXPAND && TM == 256 && (TN == 256 || TN == 128)),
+                  "tile shapes: TM x 128 (expanding), 256 x 256 and 256 x 128");
+    constexpr bool SQ = TM < 512;
+    constexpr int WGM = TM / 64;           // waves along the rows
+    constexpr int WNC = TN / (8 / WGM);    // output columns per wave
     constexpr int NJ = WNC / 16;         // 16-column MFMA tiles per wave
     constexpr int WR = TN / 8;           // weight-tile rows each wave moves
     constexpr int AR = TM / 8;           // activation-tile rows each wave moves
@@ -232,20 +235,22 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = SQ ? (wave & 3) : wave, wn = SQ ? (wave >> 2) : 0;  // the wave's 64-row, WNC-column block
+    const int wm = wave % WGM, wn = wave / WGM;  // the wave's 64-row, WNC-column block
     const int r16 = lane & 15, g = lane >> 4;
     if (tid == 0) span_start(p.span);
     const int64_t tiles_n = (p.N + TN - 1) / TN, tiles_m = (p.M + TM - 1) / TM;
     // split K: workgroup b takes slice b / tiles of the k-steps for tile b % tiles
     // (slice-major, so that each slice's tiles keep the XCD-aware order)
-    const int64_t tiles = tiles_m * tiles_n;
-    const int slice = (int)(blockIdx.x / tiles);
+    // (32-bit scalars: a grid below 2^31 workgroups, nK below 2^15; wider or
+    // divergent-looking bounds cost the k-loop registers)
+    const uint32_t tiles = (uint32_t)(tiles_m * tiles_n);
+    const int slice = (int)((uint32_t)blockIdx.x / tiles);
     int64_t mt, nt;
-    tile_of(blockIdx.x - (int64_t)slice * tiles, tiles_m, tiles_n, mt, nt);
+    tile_of(blockIdx.x - slice * tiles, tiles_m, tiles_n, mt, nt);
     const int64_t m_base = mt * TM, n_base = nt * TN;
-    const int64_t nK = (p.Kd + BK - 1) / BK;
-    const int64_t k_lo = slice * p.ks_len;                                   // this workgroup's k-steps
-    const int64_t k_hi = k_lo + p.ks_len < nK ? k_lo + p.ks_len : nK;       // [k_lo, k_hi), never empty
+    const int nK = (int)((p.Kd + BK - 1) / BK);
+    const int k_lo = __builtin_amdgcn_readfirstlane(slice * (int)p.ks_len);  // this workgroup's k-steps
+    const int k_hi = __builtin_amdgcn_readfirstlane(k_lo + (int)p.ks_len < nK ? k_lo + (int)p.ks_len : nK);  // never empty
     const int64_t kb = p.k / 64;  // NF4 blocks per W0 row
 
     // NF4 level table: lane j holds C[j % 16]
@@ -256,10 +261,11 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
 
     // ---- activation tile: global -> LDS transfers of 8 rows x 128 B ---------------
     // Wave w moves rows AR w .. AR w + AR - 1 (transfer b: rows AR w + 8 b ..): with
-    // 512-row tiles exactly the rows it reads, with 256-row tiles (SQ) half of the
-    // rows of its own and of one other wave.  Lane l lands in row 8 b + l / 8,
-    // physical chunk l % 8, which holds logical chunk (l % 8) ^ ((row >> 1) & 7) =
-    // (l % 8) ^ ((l / 16 + 4 b) & 7) (AR w is a multiple of 16).
+    // 512-row tiles exactly the rows it reads, with fewer rows (SQ) a share of rows
+    // that several waves read.  Lane l lands in row AR w + 8 b + l / 8, physical
+    // chunk l % 8, which holds logical chunk (l % 8) ^ ((row >> 1) & 7) =
+    // (l % 8) ^ ((l / 16 + 4 (AR w / 8 + b)) & 7): voff_a0 or voff_a1 by the
+    // parity of AR w / 8 + b.
     // Rows past M read as zero.  Pieces past Kd (dX with d % 64 != 0) read the
     // next row's data: finite values that meet weight rows that are exactly zero.
     const int64_t rows_here = (p.M - m_base) < TM ? (p.M - m_base) : TM;
@@ -268,8 +274,9 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
     const uint32_t voff_a0 = (uint32_t)(((int64_t)dma_row * p.Kd + 8 * ((lane & 7) ^ ((lane >> 4) & 7))) * 2);
     const uint32_t voff_a1 = (uint32_t)(((int64_t)dma_row * p.Kd + 8 * ((lane & 7) ^ (((lane >> 4) + 4) & 7))) * 2);
     const uint32_t row8_bytes = (uint32_t)(8 * p.Kd * 2);
+    const int apar = (AR / 8) * wave;  // 8-row groups before this wave's first: the parity of the swizzle term
     auto issue_a = [&](int64_t kt, auto S, int b) __attribute__((always_inline)) {
-        dma16(ra, Aof(S) + (AR * wave + 8 * b) * 8, (b & 1) ? voff_a1 : voff_a0,
+        dma16(ra, Aof(S) + (AR * wave + 8 * b) * 8, ((apar + b) & 1) ? voff_a1 : voff_a0,
               (uint32_t)b * row8_bytes + (uint32_t)kt * (BK * 2));
     };
     // fragment reads (A: row WM wm + 16 i + r16; B: row WNC wn + 16 j + r16; chunk
@@ -446,11 +453,19 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
                 for (int i = 0; i < MI; ++i) af[1][i] = read_a(S{}, 1, i);
             }
             if constexpr (EXPAND) {
-                if (grp < 8) issue_a(kn, S1{}, grp);
-                if (grp == 8) load_w(kw, wl);  // after the transfers: the end-of-step wait counts on it
-                if (j == 1) expand_phase(wc, s, 0, st_w);
-                if (j == 4) expand_phase(wc, s, 1, st_w);
-                if (j == 6) expand_phase(wc, s, 2, st_w);
+                // the AR / 8 transfers first, then the weight-data loads (the
+                // end-of-step wait counts on their being last); the three phases
+                // of piece s spread over the slice's groups in order
+                constexpr int nA = AR / 8;
+                constexpr int gW = nA < 2 * NJ - 1 ? nA : 2 * NJ - 1;
+                constexpr int j0 = NJ == 8 ? 1 : NJ == 4 ? 1 : 0;
+                constexpr int j1 = NJ == 8 ? 4 : NJ == 4 ? 2 : NJ - 1;
+                constexpr int j2 = NJ == 8 ? 6 : NJ == 4 ? 3 : NJ - 1;
+                if (grp < nA) issue_a(kn, S1{}, grp);
+                if (grp == gW) load_w(kw, wl);
+                if (j == j0) expand_phase(wc, s, 0, st_w);
+                if (j == j1) expand_phase(wc, s, 1, st_w);
+                if (j == j2) expand_phase(wc, s, 2, st_w);
             } else if constexpr (TN == 256) {  // 16 groups: 4 + 4 transfers, alternating
                 if (grp < 8) {
                     if (grp & 1) issue_a(kn, S1{}, grp >> 1);
@@ -481,7 +496,7 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
             for (int i = 0; i < MI; ++i) af[0][i] = read_a(S1{}, 0, i);
         }
         bq[0] = read_b(S1{}, 0, 0);
-        bq[1] = read_b(S1{}, 0, 1);
+        bq[1] = read_b(S1{}, 1 / NJ, 1 % NJ);
         sched_fence();
     };
 
@@ -489,7 +504,7 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
     if constexpr (EXPAND) {
         load_w(k_lo, w0);
 #pragma unroll
-        for (int b = 0; b < 8; ++b) issue_a(k_lo, IC<0>{}, b);
+        for (int b = 0; b < AR / 8; ++b) issue_a(k_lo, IC<0>{}, b);
         load_w(k_lo + 1 < k_hi ? k_lo + 1 : k_lo, w1);
         load_w(k_lo + 2 < k_hi ? k_lo + 2 : k_hi - 1, w2);
 #pragma unroll
@@ -513,7 +528,7 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
         for (int i = 0; i < MI; ++i) af[0][i] = read_a(IC<0>{}, 0, i);
     }
     bq[0] = read_b(IC<0>{}, 0, 0);
-    bq[1] = read_b(IC<0>{}, 0, 1);
+    bq[1] = read_b(IC<0>{}, 1 / NJ, 1 % NJ);
 
     // ---- main k-loop: step k_lo peeled, then six steps per trip ----------------------
     step(k_lo, IC<0>{}, IC<1>{});
@@ -555,7 +570,7 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
         for (int64_t e = 0; e < nE; ++e) {
 #pragma unroll
             for (int b = 0; b < AR / 8; ++b)
-                dma16(rea, sA0 + (AR * wave + 8 * b) * 8, (b & 1) ? voff_e1 : voff_e0,
+                dma16(rea, sA0 + (AR * wave + 8 * b) * 8, ((apar + b) & 1) ? voff_e1 : voff_e0,
                       (uint32_t)b * row8_e + (uint32_t)e * (BK * 2));
 #pragma unroll
             for (int u = 0; u < WR / 8; ++u) dma16(reb, sB0 + (WR * wave + 8 * u) * 8, voff_eb[u], (uint32_t)e * (BK * 2));
@@ -589,10 +604,8 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
         for (int j = 0; j < NJ; ++j) {
             const int64_t n = n_base + WNC * wn + 16 * j + 4 * g;
             if (n >= p.N) continue;
-            if (p.part) {
-                *reinterpret_cast<f32x4 *>(p.part + ((int64_t)slice * p.M + m) * p.N + n) = acc[i][j];
-            } else if constexpr (F32OUT) {
-                *reinterpret_cast<f32x4 *>(p.out_f32 + m * p.N + n) = acc[i][j];
+            if constexpr (F32OUT) {
+                *reinterpret_cast<f32x4 *>(p.out_f32 + ((int64_t)slice * p.M + m) * p.N + n) = acc[i][j];
             } else {
                 const uint2 o{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
                 *reinterpret_cast<uint2 *>(p.out + m * p.N + n) = o;
@@ -875,7 +888,9 @@ struct GemmGrid {
 GemmGrid gemm_grid(int64_t M, int64_t N, int64_t Kd, bool force_expand) {
     GemmGrid g;
     const bool expand = (M + BM - 1) / BM == 1 || force_expand;
-    g.ts = expand ? TileShape{BM, BN} : pick_tile(M, N);
+    // the expanding kernel: the fewest 64-row blocks that hold M (one tile row)
+    const int tm = force_expand || M > 256 ? BM : M > 128 ? 256 : M > 64 ? 128 : 64;
+    g.ts = expand ? TileShape{tm, BN} : pick_tile(M, N);
     g.tiles = tile_count(g.ts, M, N);
     const int64_t nK = (Kd + BK - 1) / BK;
     g.S = ksplit_slices(g.tiles, nK);
@@ -931,7 +946,10 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
     const TileShape ts = gg.ts;
     p.S = gg.S;
     p.ks_len = gg.ks_len;
-    p.part = gg.S > 1 ? ws.kpart : nullptr;
+    // split K: the fp32 kernels write one plane of partial sums per slice into the
+    // workspace, which ksplit_reduce_kernel adds into out / out_f32
+    const bool f32k = out_f32 || gg.S > 1;
+    if (gg.S > 1) p.out_f32 = ws.kpart;
     if (what == kExpandCore) {
         PrepArgs q{};
         q.fmt = w.fmt;
@@ -989,17 +1007,30 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
         if (ts.tn == 256) QNF4_GEMM(DXV, false, F32V, 256, 256);    \
         else QNF4_GEMM(DXV, false, F32V, 128, 256);                 \
     } while (0)
-    if (out_f32) {
-        if (expand) QNF4_GEMM(true, true, true, 128, 512);
-        else QNF4_GEMM_SHAPES(true, true);
+#define QNF4_GEMM_EXPAND(DXV, F32V)                                  \
+    do {                                                             \
+        if (ts.tm == 64) QNF4_GEMM(DXV, true, F32V, 128, 64);        \
+        else if (ts.tm == 128) QNF4_GEMM(DXV, true, F32V, 128, 128); \
+        else if (ts.tm == 256) QNF4_GEMM(DXV, true, F32V, 128, 256); \
+        else QNF4_GEMM(DXV, true, F32V, 128, 512);                   \
+    } while (0)
+    if (f32k) {
+        if (expand) {
+            if (dx) QNF4_GEMM_EXPAND(true, true);
+            else QNF4_GEMM_EXPAND(false, true);
+        } else {
+            if (dx) QNF4_GEMM_SHAPES(true, true);
+            else QNF4_GEMM_SHAPES(false, true);
+        }
     } else if (expand) {
-        if (dx) QNF4_GEMM(true, true, false, 128, 512);
-        else QNF4_GEMM(false, true, false, 128, 512);
+        if (dx) QNF4_GEMM_EXPAND(true, false);
+        else QNF4_GEMM_EXPAND(false, false);
     } else if (dx) {
         QNF4_GEMM_SHAPES(true, false);
     } else {
         QNF4_GEMM_SHAPES(false, false);
     }
+#undef QNF4_GEMM_EXPAND
 #undef QNF4_GEMM_SHAPES
 #undef QNF4_GEMM
     if (gg.S > 1) {

@@ -144,9 +144,10 @@ hipError_t launch_adapter_merge(const Nf4Weights *w, const uint16_t *w_in, int64
 // kernel tags them on first use and leaves them ready for the next call).
 // Forwards of up to kDecodeChunkRows rows run it on consecutive 16-row chunks
 // of X (one launch each, sharing part and ctr in stream order): the weight is
-// streamed once per chunk, which beats the GEMM's fixed costs up to 64 rows
-// (4096 x 4096: 17.5 us for 32 rows against 39 us; 14336 x 4096: 29 against 74).
-constexpr int64_t kDecodeChunkRows = 64;
+// streamed once per chunk, which beats the GEMM (64-row tiles, split K) for
+// two chunks (4096 x 4096: 17.8-18.5 us against 22.7-22.9 for 17-32 rows;
+// 14336 x 4096: 29-31 against 42.5) but not for three.
+constexpr int64_t kDecodeChunkRows = 32;
 size_t decode_counter_bytes();
 size_t decode_part_bytes(int64_t M, int64_t d, int64_t k);
 hipError_t launch_decode_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, const uint16_t *A, const float *U,

@@ -171,7 +171,7 @@ size_t qlora_linear_workspace(int64_t M, int64_t d, int64_t k, int32_t r);
  * a few thousand columns), the GEMM's k-steps run in up to 8 slices whose
  * fp32 partial sums (up to 64 MiB of the workspace) are added in slice order
  * before the one rounding to bf16: the sum is associated differently from an
- * unsplit call, deterministically.  For M <= 16 (decode; M <= 64 as
+ * unsplit call, deterministically.  For M <= 16 (decode; M <= 32 as
  * consecutive 16-row chunks of X, one decode launch each, the same bits as
  * separate calls on the chunks) the 64-weight block scale is applied once to
  * the fp32 sum over the block (over each half block with M <= 2, r <= 16,

@@ -276,7 +276,7 @@ def gemm_only(w=None, backward=0, a=FAKE, m=96, r=8, out=FAKE, ws=FAKE, ws_bytes
     (dict(a=FAKE_MIS), q.QLORA_EALIGN), (dict(out=FAKE_MIS), q.QLORA_EALIGN),
     (dict(ws=None), q.QLORA_EWORKSPACE), (dict(ws_bytes=64), q.QLORA_EWORKSPACE),
     (dict(m=16), q.QLORA_EINVAL),                      # decode-sized forward: no separate GEMM
-    (dict(m=64), q.QLORA_EINVAL),                      # up to 64 rows: decode in 16-row chunks
+    (dict(m=32), q.QLORA_EINVAL),                      # up to 32 rows: decode in 16-row chunks
     (dict(w=weight(codes=None)), q.QLORA_EINVAL),
 ])
 def test_gemm_only_rejects_invalid_arguments(kw, status):

@@ -60,14 +60,18 @@ def test_single_layer_workload():
                                      (700, 328, 192, 8), (1030, 200, 1088, 16), (1100, 4104, 320, 4),
                                      (1100, 5512, 256, 8), (300, 320, 192, 33), (600, 264, 1088, 64),
                                      (260, 200, 448, 128), (1030, 136, 4096, 17),
-                                     (1100, 6600, 320, 8), (1100, 264, 6592, 8)])
+                                     (1100, 6600, 320, 8), (1100, 264, 6592, 8), (100, 264, 1024, 16),
+                                     (200, 1032, 2048, 8)])
 def test_shapes_ranks_and_ragged_tiles(m, d, k, r):
-    """Ranks, ragged M, d, k tiles, the decode path (M <= 16), the expanding GEMM
-    (M <= 512) and the GEMM on the bf16 copy (M > 512) in its tile shapes
-    (256 x 128 for most; 256 x 256 for the forward at m = 1100, d = 6600 and for
-    dX at m = 1100, k = 6592, over d = 264 not a multiple of 64), with partial
-    last tiles; r > 16 with M >= 256 takes the split-K row
-    products for U and G (ragged row groups and slices, r = 17 .. 128)."""
+    """Ranks, ragged M, d, k tiles, the decode path (M <= 16; 16-row chunks up to
+    32), the expanding GEMM (M <= 512) in 64-, 128-, 256- and 512-row tiles and
+    the GEMM on the bf16 copy (M > 512) in its tile shapes (256 x 128 for most;
+    256 x 256 for the forward at m = 1100, d = 6600 and for dX at m = 1100,
+    k = 6592, over d = 264 not a multiple of 64), with partial last tiles; K
+    split over 2-8 slices where the tiles leave most CUs idle (ragged last
+    slices, also over d = 1032 not a multiple of 64); r > 16 with M >= 256
+    takes the split-K row products for U and G (ragged row groups and slices,
+    r = 17 .. 128)."""
     inp = make_layer(21, m * 7 + r, d, k, m, r)
     check_layer(inp, 16.0, f"shape m={m} d={d} k={k} r={r}", bf16_rounding_allowance=True)
 
@@ -96,13 +100,13 @@ def test_decode_workspace_reuse_and_garbage():
 
 @pytest.mark.parametrize("m,d,k", [(1, 16, 4096), (16, 48, 1024), (4, 1016, 4096), (7, 520, 2048),
                                    (2, 104, 1472), (16, 8, 640), (5, 1016, 4096), (6, 104, 1472),
-                                   (8, 16, 4096), (40, 1016, 4096), (17, 48, 1024)])
+                                   (8, 16, 4096), (32, 1016, 4096), (17, 48, 1024)])
 def test_decode_k_split_shapes(m, d, k):
     """Few row tiles: the decode forward splits k over 2..8
     workgroups per tile group (even and uneven block counts per slice), whose
     partial sums the last one to arrive adds.  Forward parity, and the
     same bits on a second call on the same workspace (the counters left ready
-    by the first).  M = 17, 40: 16-row chunks, one launch each, sharing the
+    by the first).  M = 17, 32: 16-row chunks, one launch each, sharing the
     counters and partial sums in stream order."""
     import bit_nf4_quantized_13_amd as q
     inp = make_layer(47, d + m, d, k, m, 16)
@@ -117,12 +121,12 @@ def test_decode_k_split_shapes(m, d, k):
 
 
 @pytest.mark.parametrize("m,d,k,r", [(1, 8192, 64, 1), (2, 16392, 512, 16), (1, 8200, 1088, 7), (2, 12296, 3200, 9),
-                                     (3, 8200, 1088, 7), (4, 8192, 64, 1), (34, 8200, 1088, 7)])
+                                     (3, 8200, 1088, 7), (4, 8192, 64, 1), (18, 8200, 1088, 7)])
 def test_decode_dot_path_shapes(m, d, k, r):
     """M <= 2, r <= 16, k <= 4096, d >= 8192: the dot-product decode kernel
     (the decode workloads' own 14336-row shape is in
     test_decode_shapes_forward), and M = 3, 4 on such shapes through the
-    matrix-core kernel; M = 34: two 16-row chunks, then two rows on the
+    matrix-core kernel; M = 18: a 16-row chunk, then two rows on the
     dot-product kernel.  Four to eight rounds of 8 rows per workgroup, more
     workgroups than a round of the chip (d = 16392: 257), k chunks past the
     row end (k = 64, 1088, 3200), ranks below 16."""
@@ -132,10 +136,10 @@ def test_decode_dot_path_shapes(m, d, k, r):
 
 
 def test_decode_chunks_equal_separate_calls():
-    """A forward of 17..64 rows runs the decode kernel on consecutive 16-row
+    """A forward of 17..32 rows runs the decode kernel on consecutive 16-row
     chunks of X: the same bits (Y and U) as separate calls on the chunks."""
     import bit_nf4_quantized_13_amd as q
-    for m, d, k, r in ((40, 4096, 1024, 16), (35, 8200, 512, 8), (33, 520, 2048, 24), (64, 1016, 1024, 4)):
+    for m, d, k, r in ((32, 4096, 1024, 16), (27, 8200, 512, 8), (17, 520, 2048, 24), (31, 1016, 1024, 4)):
         inp = make_layer(61, m + r, d, k, m, r)
         w = q.qlora_nf4_quantize(to_dev_f32(inp.w0))
         xd, ad, bd = (to_dev_bf16(t) for t in (inp.x, inp.a, inp.b))
