@@ -44,6 +44,10 @@
 //    [W' | W' | 0] (hi = bf16(v), lo = bf16(v - hi), rows padded to a
 //    multiple of 64).
 //  * Workgroups are renumbered so each XCD walks a contiguous run of tiles.
+//  * Split K: a grid of at most 128 tiles (most CUs idle) runs each tile's
+//    k-steps in up to 8 slices, slice-major; each slice writes its fp32 sums
+//    as a plane of its own (the adapter's k-steps go to the last slice) and
+//    ksplit_reduce_kernel adds the planes in slice order and rounds once.
 //
 // MFMA v_mfma_f32_16x16x32_bf16 layout (wave64), g = lane / 16:
 //   first operand  (16 x 32): lane l holds P[l % 16][8 g .. 8 g + 7]
