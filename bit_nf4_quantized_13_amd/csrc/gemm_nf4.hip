@@ -600,6 +600,8 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
 
     // ---- epilogue: lane holds D[m = 16 i + r16][n = 16 j + 4 g .. + 3] ----------------
+    // (bf16 output in 16-byte pieces, 64 contiguous bytes per row and tile pair:
+    // with 8-byte pieces the stores took 3.5 us more of a 109 us launch)
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
         const int64_t m = m_base + WM * wm + 16 * i + r16;
@@ -607,9 +609,27 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int64_t n = n_base + WNC * wn + 16 * j + 4 * g;
-            if (n >= p.N) continue;
+            if ((F32OUT || NJ == 1) && n >= p.N) continue;
             if constexpr (F32OUT) {
                 *reinterpret_cast<f32x4 *>(p.out_f32 + ((int64_t)slice * p.M + m) * p.N + n) = acc[i][j];
+            } else if constexpr (NJ >= 2) {
+                // tiles j, j + 1 (j even) leave as 16-byte pieces: lane g takes tile
+                // j + g / 2, columns 8 (g % 2) .. + 7, gathered from lanes 2 (g % 2)
+                // and 2 (g % 2) + 1 of the same row (four lanes write 64 contiguous bytes)
+                if (j & 1) continue;
+                const uint32_t p0x = pack_bf16x2(acc[i][j][0], acc[i][j][1]), p0y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+                const uint32_t p1x = pack_bf16x2(acc[i][j + 1][0], acc[i][j + 1][1]),
+                               p1y = pack_bf16x2(acc[i][j + 1][2], acc[i][j + 1][3]);
+                const int srcA = (r16 + 16 * (2 * (g & 1))) * 4, srcB = (r16 + 16 * (2 * (g & 1) + 1)) * 4;
+                const bool t1 = g >= 2;
+                auto pull = [&](int src, uint32_t v0, uint32_t v1) __attribute__((always_inline)) -> uint32_t {
+                    const uint32_t a0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v0);
+                    const uint32_t a1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v1);
+                    return t1 ? a1 : a0;
+                };
+                const uint4 o{pull(srcA, p0x, p1x), pull(srcA, p0y, p1y), pull(srcB, p0x, p1x), pull(srcB, p0y, p1y)};
+                const int64_t n8 = n_base + WNC * wn + 16 * (j + (g >> 1)) + 8 * (g & 1);
+                if (n8 < p.N) *reinterpret_cast<uint4 *>(p.out + m * p.N + n8) = o;
             } else {
                 const uint2 o{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
                 *reinterpret_cast<uint2 *>(p.out + m * p.N + n) = o;
