@@ -655,6 +655,11 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
 // like the codes, is written by its own job in prep_kernel.)  Narrower
 // blocks (8 x 4) and two tiles per workgroup with the next one's loads
 // overlapping were both slower.
+// The dequantized weight copy is stored with device scope (sc1: written
+// through the XCD's L2 into the memory-side cache the GEMM reads it from), so
+// the end of the preparation launch has no dirty L2 lines of it to write back:
+// 0.6-0.8 us less per launch at 4096 x 4096, the GEMM's reads unchanged.
+constexpr int kCopyPolicy = 16;  // cache-policy bits of the copy's stores: sc1
 __device__ __forceinline__ void dequant_tile_t(int64_t bid, const uint8_t *__restrict__ codes, int fmt, int bshift,
                                                const int8_t *__restrict__ c2, const float *__restrict__ c1,
                                                float mean, int64_t d, int64_t k, int64_t ldw, const Nf4Consts &tab,
@@ -666,6 +671,7 @@ __device__ __forceinline__ void dequant_tile_t(int64_t bid, const uint8_t *__res
     const int64_t n0 = td * 64 + 8 * ng;   // first of this thread's 8 W0 rows
     const int64_t k0 = tk * 256 + 8 * kg;  // first of its 8 columns
     if (k0 >= k) return;                   // k % 64 == 0: whole 8-column groups
+    const __amdgpu_buffer_rsrc_t rout = make_rsrc(out, k * ldw * 2);
     float lvf = tab.level[0];
 #pragma unroll
     for (int j = 1; j < 16; ++j) lvf = (lane & 15) == j ? tab.level[j] : lvf;
@@ -700,7 +706,8 @@ __device__ __forceinline__ void dequant_tile_t(int64_t bid, const uint8_t *__res
         for (int e2 = 0; e2 < 4; ++e2)
             o[e2] = (c & 1) ? __builtin_amdgcn_perm(v[2 * e2 + 1][c >> 1], v[2 * e2][c >> 1], 0x07060302u)
                             : __builtin_amdgcn_perm(v[2 * e2 + 1][c >> 1], v[2 * e2][c >> 1], 0x05040100u);
-        *reinterpret_cast<uint4 *>(out + (k0 + c) * ldw + n0) = uint4{o[0], o[1], o[2], o[3]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, uint4{o[0], o[1], o[2], o[3]}), rout,
+                                               (uint32_t)(((k0 + c) * ldw + n0) * 2), 0, kCopyPolicy);
     }
 }
 
@@ -822,6 +829,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a, Nf4Consts tab) {
             const int64_t total = a.d * a.k;  // a multiple of 64
             const int64_t e0 = (b * 4 + (threadIdx.x >> 6)) * (512 * kWU) + 8 * lane;
             const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.codes, total / 2);  // past the end: zero
+            const __amdgpu_buffer_rsrc_t rw_out = make_rsrc(a.wbf, total * 2);
             uint32_t cw[kWU];
             float sc[kWU];
 #pragma unroll
@@ -844,7 +852,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a, Nf4Consts tab) {
 #pragma unroll
             for (int u = 0; u < kWU; ++u) {
                 const int64_t e = e0 + 512 * u;
-                if (e < total) *reinterpret_cast<uint4 *>(a.wbf + e) = o[u];
+                if (e < total)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o[u]), rw_out, (uint32_t)(e * 2), 0,
+                                                           kCopyPolicy);
             }
         }
         return;
