@@ -63,6 +63,10 @@ namespace qnf4 {
 namespace {
 
 constexpr int BM = 512, BN = 128, BK = 64;
+// The bf16 output pieces are stored with device scope (sc1: written through
+// the XCD's L2), so the launch ends without a writeback of dirty output lines:
+// 1.2-1.4 us less per 4096^3 launch than write-back stores, same bits.
+constexpr int kOutPolicy = 16;
 constexpr int NTHREADS = 512;                 // 8 waves, two per SIMD
 constexpr int WM = BM / (NTHREADS / 64);      // rows per wave (64)
 constexpr int MI = WM / 16;                   // 16-row MFMA tiles per wave (4)
@@ -602,6 +606,7 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
     // ---- epilogue: lane holds D[m = 16 i + r16][n = 16 j + 4 g .. + 3] ----------------
     // (bf16 output in 16-byte pieces, 64 contiguous bytes per row and tile pair:
     // with 8-byte pieces the stores took 3.5 us more of a 109 us launch)
+    const __amdgpu_buffer_rsrc_t rout_y = make_rsrc(p.out, F32OUT ? 0 : p.M * p.N * 2);
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
         const int64_t m = m_base + WM * wm + 16 * i + r16;
@@ -629,7 +634,9 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
                 };
                 const uint4 o{pull(srcA, p0x, p1x), pull(srcA, p0y, p1y), pull(srcB, p0x, p1x), pull(srcB, p0y, p1y)};
                 const int64_t n8 = n_base + WNC * wn + 16 * (j + (g >> 1)) + 8 * (g & 1);
-                if (n8 < p.N) *reinterpret_cast<uint4 *>(p.out + m * p.N + n8) = o;
+                if (n8 < p.N)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rout_y,
+                                                           (uint32_t)((m * p.N + n8) * 2), 0, kOutPolicy);
             } else {
                 const uint2 o{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
                 *reinterpret_cast<uint2 *>(p.out + m * p.N + n) = o;
