@@ -377,8 +377,12 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const qlora_bf16 *x, const qlora
         e = launch_rows_skinny(x, A, M, k, r, Uw, vt_u, part, s);
         Uin = Uw;
     }
-    if (e == hipSuccess) e = launch_bwd_prep(B, d, r, Bt, U, M, vt_u, s);    // B^T [r x d] (and U's planes)
-    if (e == hipSuccess) e = launch_rows_skinny(dY, Bt, M, d, r, G, vt_g, part, s);  // G = dY B
+    if (rows_bt_supported(M, r, B)) {                                           // G = dY B (and U's planes)
+        if (e == hipSuccess) e = launch_rows_bt(dY, B, M, d, r, G, vt_g, U, vt_u, s);
+    } else {
+        if (e == hipSuccess) e = launch_bwd_prep(B, d, r, Bt, U, M, vt_u, s);    // B^T [r x d] (and U's planes)
+        if (e == hipSuccess) e = launch_rows_skinny(dY, Bt, M, d, r, G, vt_g, part, s);  // G = dY B
+    }
     ColsReduceJob red[2];
     float *part_b = part;                                                       // dB = s U^T dY (as [d x r])
     float *part_a = part + (size_t)cols_splits(M) * r * round_up(d, 64);        // dA = s G^T X
@@ -497,8 +501,12 @@ int qlora_linear_bwd_dropout(const qlora_nf4_weight *w, const qlora_bf16 *x, con
     uint16_t *vt_g = vt_u + 2 * cols_rank_pad(r) * M;
     hipError_t e = launch_lora_dropout(x, M, k, thr, c, seed, xd, s);           // the forward's Xd again
     if (e == hipSuccess && !U) e = launch_rows_skinny(xd, A, M, k, r, Uw, vt_u, part, s);
-    if (e == hipSuccess) e = launch_bwd_prep(B, d, r, Bt, U, M, vt_u, s);
-    if (e == hipSuccess) e = launch_rows_skinny(dY, Bt, M, d, r, G, vt_g, part, s);   // G = dY B
+    if (rows_bt_supported(M, r, B)) {                                            // G = dY B (and U's planes)
+        if (e == hipSuccess) e = launch_rows_bt(dY, B, M, d, r, G, vt_g, U, vt_u, s);
+    } else {
+        if (e == hipSuccess) e = launch_bwd_prep(B, d, r, Bt, U, M, vt_u, s);
+        if (e == hipSuccess) e = launch_rows_skinny(dY, Bt, M, d, r, G, vt_g, part, s);   // G = dY B
+    }
     ColsReduceJob red[2];
     float *part_b = part;                                                       // dB = s U^T dY
     float *part_a = part + (size_t)cols_splits(M) * r * round_up(d, 64);        // dA = s G^T Xd

@@ -42,6 +42,11 @@ hipError_t launch_rows_skinny(const uint16_t *in, const uint16_t *w, int64_t M, 
                               float *out, uint16_t *vt, float *part, hipStream_t s);
 // Backward preparation: Bt[r x d] = B[d x r]^T and, when U is given, the
 // transposed hi / lo planes of U [M x r] into vt [2][Rp][M].
+// G = dY B (r <= 16, M r > 4096, B 16-byte aligned) from B as stored, with U's
+// planes when U is given: the backward preparation and rows_skinny in one launch
+bool rows_bt_supported(int64_t M, int R, const void *B);
+hipError_t launch_rows_bt(const uint16_t *dY, const uint16_t *B, int64_t M, int64_t d, int R, float *G, uint16_t *vt_g,
+                          const float *U, uint16_t *vt_u, hipStream_t s);
 hipError_t launch_bwd_prep(const uint16_t *B, int64_t d, int r, uint16_t *Bt, const float *U, int64_t M,
                            uint16_t *vt, hipStream_t s);
 // Two column reductions in one launch (job 1 skipped when in1 is null):

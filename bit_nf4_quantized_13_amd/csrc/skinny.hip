@@ -123,6 +123,115 @@ __global__ __launch_bounds__(64 * W) void rows_skinny_kernel(const uint16_t *__r
 }
 
 // ---------------------------------------------------------------------------
+// G = dY B for ranks r <= 16 with B in its stored layout [d x r], and, when a
+// U is given, U's transposed bf16 hi + lo planes: one launch in place of the
+// backward preparation (B^T, U's planes) followed by rows_skinny_kernel.
+// The same chunks of 128 k, waves and MFMA order as rows_skinny_kernel<1, W,
+// CPI>, so G and its planes come out bit for bit the same.  The second MFMA
+// operand (lane (j, g): B[k .. k + 7][j]) has its k strided in memory, so each
+// wave loads the B rows of its chunk whole (16-byte pieces of the contiguous
+// 128 r values, B 16-byte aligned) and writes them transposed into its own
+// LDS buffer B^T [16][128] (rows 272 bytes apart: the 16 fragment rows fall on
+// distinct banks), from which it reads the fragments; LDS operations of one
+// wave run in order, so the buffer needs no barrier between chunks.  A
+// workgroup's 16 rows of U become their planes exactly as the preparation
+// launch formed them.
+// ---------------------------------------------------------------------------
+template <int W, int CPI>
+__global__ __launch_bounds__(64 * W) void rows_bt_kernel(const uint16_t *__restrict__ in,
+                                                         const uint16_t *__restrict__ bmat, int64_t M, int64_t K,
+                                                         int R, uint32_t rinv, float *__restrict__ out,
+                                                         uint16_t *__restrict__ vt, int64_t Rp,
+                                                         const float *__restrict__ u_in, uint16_t *__restrict__ vt_u) {
+    constexpr int PITCH = 136;  // bf16 per row of the B^T buffer: 128 + 8
+    __shared__ f32x4 s_acc[W][64];
+    __shared__ __attribute__((aligned(16))) uint16_t s_bt[W][16 * PITCH];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int i = lane & 15, g = lane >> 4;
+    const int64_t m0 = (int64_t)blockIdx.x * 16;
+    const int64_t rows = (M - m0) < 16 ? (M - m0) : 16;
+    const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + m0 * K, rows * K * 2);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(bmat, K * R * 2);  // rows past K read as zero
+    uint16_t *const bt = &s_bt[wave][0];
+    // rows R .. 15 of the buffer stay zero (their columns of G are never stored)
+    for (int q = lane; q < 16 * PITCH / 8; q += 64) reinterpret_cast<uint4 *>(bt)[q] = uint4{0, 0, 0, 0};
+    if (u_in) {  // U's planes for this workgroup's rows: vt_u[j][m] = hi(U[m][j]), vt_u[Rp + j][m] = lo(U[m][j])
+        for (int idx = tid; idx < 16 * Rp; idx += 64 * W) {
+            const int64_t j = idx / 16, m = m0 + idx % 16;
+            if (m < M) {
+                const float f = j < R ? u_in[m * R + j] : 0.0f;
+                const uint32_t hb = pack_bf16x2(f, 0.0f) & 0xFFFFu;
+                vt_u[j * M + m] = (uint16_t)hb;
+                vt_u[(Rp + j) * M + m] = (uint16_t)(pack_bf16x2(f - bf16_bits_to_f32(hb), 0.0f) & 0xFFFFu);
+            }
+        }
+    }
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int npc = 16 * R;  // 16-byte pieces of B per chunk (128 rows x R values)
+    const int64_t chunks = (K + 127) / 128;
+    for (int64_t c = wave; c < chunks; c += CPI * W) {
+        uint4 a[CPI][4], bp[CPI][4];
+        bool ok[CPI][4];
+#pragma unroll
+        for (int u = 0; u < CPI; ++u) {
+            const int64_t ch = c + W * u;
+            const int64_t k0 = ch * 128 + 8 * g;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ok[u][e] = k0 + 32 * e < K;  // K % 8 == 0: pieces are entirely inside or outside
+                a[u][e] = load16(rin, (uint32_t)((i * K + k0 + 32 * e) * 2));
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {  // piece lane + 64 q of the chunk (at most 4 x 64 = 16 x 16)
+                const int pc = lane + 64 * q;
+                bp[u][q] = load16(rb, pc < npc && ch < chunks ? (uint32_t)(ch * 256 * R + 16 * pc) : 0x80000000u);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < CPI; ++u) {
+            // this chunk's B rows into the buffer as B^T: value e of the chunk is B[e / R][e % R]
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int pc = lane + 64 * q;
+                if (pc < npc) {
+                    const uint32_t wv[4] = {bp[u][q].x, bp[u][q].y, bp[u][q].z, bp[u][q].w};
+#pragma unroll
+                    for (int h = 0; h < 8; ++h) {
+                        const uint32_t e = 8u * (uint32_t)pc + (uint32_t)h;
+                        const uint32_t kk = (e * rinv) >> 16, j = e - kk * (uint32_t)R;
+                        bt[j * PITCH + kk] = (uint16_t)((h & 1) ? (wv[h >> 1] >> 16) : (wv[h >> 1] & 0xFFFFu));
+                    }
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint4 bf = *reinterpret_cast<const uint4 *>(bt + i * PITCH + 32 * e + 8 * g);
+                const uint4 av = ok[u][e] ? a[u][e] : uint4{0, 0, 0, 0};
+                acc = mfma16(av, bf, acc);
+            }
+        }
+    }
+    s_acc[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        f32x4 v = s_acc[0][lane];
+        for (int q = 1; q < W; ++q) v += s_acc[q][lane];
+        const int j = i;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t row = m0 + 4 * g + r;
+            if (row < M && j < R) out[row * R + j] = v[r];
+            if (vt && row < M && j < Rp) {  // transposed bf16 hi + lo planes (zero rows past R)
+                const float f = j < R ? v[r] : 0.0f;
+                const uint32_t hb = pack_bf16x2(f, 0.0f) & 0xFFFFu;
+                vt[(int64_t)j * M + row] = (uint16_t)hb;
+                vt[(Rp + j) * M + row] = (uint16_t)(pack_bf16x2(f - bf16_bits_to_f32(hb), 0.0f) & 0xFFFFu);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Backward preparation, one launch, one thread per element: threads [0, R C)
 // transpose src = B [R = d rows x C = r columns] into dst = B^T [r x d]
 // (thread i: column i / R, row i % R); the next M Rp write the transposed bf16
@@ -478,6 +587,20 @@ hipError_t launch_rows_skinny(const uint16_t *in, const uint16_t *w, int64_t M, 
 }
 
 int64_t cols_rank_pad(int r) { return (r + 15) / 16 * 16; }
+
+bool rows_bt_supported(int64_t M, int R, const void *B) {
+    return R <= 16 && M * R > 4096 && reinterpret_cast<uintptr_t>(B) % 16 == 0;
+}
+
+hipError_t launch_rows_bt(const uint16_t *dY, const uint16_t *B, int64_t M, int64_t d, int R, float *G, uint16_t *vt_g,
+                          const float *U, uint16_t *vt_u, hipStream_t s) {
+    if (!rows_bt_supported(M, R, B)) return hipErrorInvalidValue;
+    const int64_t Rp = cols_rank_pad(R);
+    const uint32_t rinv = (65536u + (uint32_t)R - 1) / (uint32_t)R;  // e / R = (e rinv) >> 16 for e < 2048
+    hipLaunchKernelGGL((rows_bt_kernel<8, 4>), dim3((unsigned)((M + 15) / 16)), dim3(512), 0, s, dY, B, M, d, R, rinv,
+                       G, vt_g, Rp, U, vt_u);
+    return hipGetLastError();
+}
 
 hipError_t launch_bwd_prep(const uint16_t *B, int64_t d, int r, uint16_t *Bt, const float *U, int64_t M,
                            uint16_t *vt, hipStream_t s) {
