@@ -230,6 +230,29 @@ def test_recomputed_u_matches_saved_u_and_runs_are_deterministic(m, r):
     assert torch.equal(da, g1[1]) and torch.equal(db, g1[2])
 
 
+@pytest.mark.parametrize("m,d,k,r", [(4096, 512, 512, 8), (1400, 1032, 320, 3), (300, 264, 512, 16)])
+def test_backward_g_paths_agree(m, d, k, r):
+    """G = dY B runs straight from B as stored when B is 16-byte aligned (one
+    launch, with U's planes) and through a transposed copy of B otherwise (B
+    only 2-byte aligned): both give the same bits, with the forward's U and
+    with U recomputed.  d % 128 != 0 puts a partial chunk of B rows at the end."""
+    import bit_nf4_quantized_13_amd as q
+    say(f"backward G paths m={m} d={d} k={k} r={r}")
+    inp = make_layer(43, r, d, k, m, r)
+    w = q.qlora_nf4_quantize(to_dev_f32(inp.w0))
+    xd, ad, bd, dyd = (to_dev_bf16(t) for t in (inp.x, inp.a, inp.b, inp.dy))
+    store = torch.empty(d * r + 1, dtype=torch.bfloat16, device="cuda")
+    b_off = store[1:].view(d, r)
+    b_off.copy_(bd)
+    assert b_off.data_ptr() % 16 != 0 and bd.data_ptr() % 16 == 0
+    _, u = q.qlora_linear_fwd(w, xd, ad, bd, 32.0)
+    for uu in (u, None):
+        g1 = q.qlora_linear_bwd(w, xd, dyd, ad, bd, 32.0, u=uu)
+        g2 = q.qlora_linear_bwd(w, xd, dyd, ad, b_off, 32.0, u=uu)
+        for t1, t2 in zip(g1, g2):
+            assert torch.equal(t1, t2)
+
+
 def test_alpha_zero_gives_base_output_and_zero_adapter_grads():
     import bit_nf4_quantized_13_amd as q
     say("alpha = 0")
