@@ -23,6 +23,23 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Large outputs stored with device scope (sc1: written through the XCD's L2
+// into the memory-side cache): the launch then does not end on a writeback of
+// its dirty L2 lines, and the next kernel finds the data in the memory-side
+// cache as before.  out_rsrc covers [base, base + bytes) (bytes < 2^32).
+constexpr int kDeviceScopeStore = 16;  // cache-policy bits of the store: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const void *base, int64_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const int n = (int)__builtin_amdgcn_readfirstlane((uint32_t)bytes);
+    void *p = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ void store16_dev(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, byte_off, 0, kDeviceScopeStore);
+}
+
 // Two fp32 values -> packed bf16x2 (lo in bits 0..15), round to nearest even
 // (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

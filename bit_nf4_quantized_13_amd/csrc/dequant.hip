@@ -23,6 +23,7 @@ __global__ __launch_bounds__(256) void nf4_dequantize_kernel(
     if (threadIdx.x < 16) lut[threadIdx.x] = tab.level[threadIdx.x];
     __syncthreads();
     const float mean = fmt != kNoDq ? *mean_p : 0.0f;
+    const __amdgpu_buffer_rsrc_t rout = out_rsrc(out, items * 16);
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < items; i += stride) {
         const uint32_t c = codes4[i];
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(256) void nf4_dequantize_kernel(
         o.y = pack_bf16x2(lut[(c >> 8) & 15] * sh, lut[(c >> 12) & 15] * sh);
         o.z = pack_bf16x2(lut[(c >> 16) & 15] * sh, lut[(c >> 20) & 15] * sh);
         o.w = pack_bf16x2(lut[(c >> 24) & 15] * sh, lut[c >> 28] * sh);
-        out[i] = o;
+        store16_dev(rout, (uint32_t)(i * 16), o);
     }
 }
 

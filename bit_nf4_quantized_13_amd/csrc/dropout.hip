@@ -63,6 +63,7 @@ __device__ __forceinline__ uint32_t keep8(uint64_t t, uint32_t thr, uint32_t s0,
 __global__ __launch_bounds__(256) void lora_dropout_kernel(const uint4 *__restrict__ x, int64_t items, uint32_t thr,
                                                            float c, uint32_t s0, uint32_t s1,
                                                            uint4 *__restrict__ xd) {
+    const __amdgpu_buffer_rsrc_t rout = out_rsrc(xd, items * 16);
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < items; t += stride) {
         const uint4 v = x[t];
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(256) void lora_dropout_kernel(const uint4 *__restri
             const uint32_t m = ((keep >> (2 * h)) & 1u ? 0x0000FFFFu : 0u) | ((keep >> (2 * h + 1)) & 1u ? 0xFFFF0000u : 0u);
             o[h] = p & m;  // dropped: +0
         }
-        xd[t] = uint4{o[0], o[1], o[2], o[3]};
+        store16_dev(rout, (uint32_t)(t * 16), uint4{o[0], o[1], o[2], o[3]});
     }
 }
 
@@ -98,6 +99,7 @@ __global__ __launch_bounds__(256) void dropout_dx_add_kernel(const f32x4 *__rest
     const int64_t m0 = (int64_t)blockIdx.x * kAddRows;
     if (n >= k) return;
     const int rows = M - m0 < kAddRows ? (int)(M - m0) : kAddRows;
+    const __amdgpu_buffer_rsrc_t rout = out_rsrc(dx, M * k * 2);
     float acc[kAddRows][8];
 #pragma unroll
     for (int i = 0; i < kAddRows; ++i)
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(256) void dropout_dx_add_kernel(const f32x4 *__rest
             const float thi = (keep >> (2 * h + 1)) & 1u ? sc * acc[i][2 * h + 1] : 0.0f;
             o[h] = pack_bf16x2(in[2 * h] + tlo, in[2 * h + 1] + thi);
         }
-        dx[t] = uint4{o[0], o[1], o[2], o[3]};
+        store16_dev(rout, (uint32_t)(t * 16), uint4{o[0], o[1], o[2], o[3]});
     }
 }
 

@@ -48,6 +48,7 @@ __global__ __launch_bounds__(256) void adapter_merge_kernel(const uint8_t *__res
     const int64_t r0 = ((int64_t)blockIdx.x / tiles_c) * kMRows, c0 = ((int64_t)blockIdx.x % tiles_c) * kMCols;
     const int ng = tid & 7, kg = tid >> 3;
     const int64_t n0 = r0 + 8 * ng;  // this thread's rows n0 .. n0 + 7
+    const __amdgpu_buffer_rsrc_t rout = out_rsrc(w_out, d * k * 2);
     const int64_t k0 = c0 + 8 * kg;  // and columns k0 .. k0 + 7 (k % 8 == 0: all in or all out)
     if (tid < 16) lut[tid] = tab.level[tid];
 
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(256) void adapter_merge_kernel(const uint8_t *__res
             }
             o[h] = pack_bf16x2(f[0], f[1]);                  // -> bf16, nearest even: one rounding of m
         }
-        *reinterpret_cast<uint4 *>(w_out + n * k + k0) = uint4{o[0], o[1], o[2], o[3]};
+        store16_dev(rout, (uint32_t)((n * k + k0) * 2), uint4{o[0], o[1], o[2], o[3]});
     }
 }
 
