@@ -317,8 +317,15 @@ int qlora_linear_fwd(const qlora_nf4_weight *w, const qlora_bf16 *x, int64_t M,
                                ctr, dpart, U + m0 * r, s);
         }
     } else {
-        e = launch_rows_skinny(x, A, M, w->k, r, U, nullptr, reinterpret_cast<float *>(base + l.part), s);
-        if (e == hipSuccess) e = launch_gemm_fwd(nw, x, M, U, B, r, scale, Y, gemm_ws(base, l), s);
+        float *part = reinterpret_cast<float *>(base + l.part);
+        if (rows_split_partials_used(M, r)) {  // U's partials, added by the GEMM's preparation launch
+            int S = 0;
+            e = launch_rows_split_partials(x, A, M, w->k, r, part, &S, s);
+            if (e == hipSuccess) e = launch_gemm_fwd(nw, x, M, nullptr, B, r, scale, Y, gemm_ws(base, l), s, part, S, U);
+        } else {
+            e = launch_rows_skinny(x, A, M, w->k, r, U, nullptr, part, s);
+            if (e == hipSuccess) e = launch_gemm_fwd(nw, x, M, U, B, r, scale, Y, gemm_ws(base, l), s);
+        }
     }
     return hip_status(e);
 }

@@ -735,6 +735,9 @@ struct PrepArgs {
     int64_t nb;
     float *shat;
     const float *V;
+    const float *Vpart;  // or V's S partial sums [S][r][M], added here in slice order
+    int Vs;
+    float *Vout;         // with Vpart: V [M x r] stored
     int64_t M;
     int r;
     float s;
@@ -781,6 +784,35 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a, Nf4Consts tab) {
         return;
     }
     b -= a.g_shat;
+    if (b < a.g_a && a.Vpart) {
+        // ext_a from the partial sums of V: thread (c, row), rows fastest so that the
+        // partial reads are contiguous.  c < r: V[row][c] = the S partials added in slice
+        // order from +0 (rows_reduce_kernel's additions; all S loads issued first), stored,
+        // and its hi / lo columns c and r + c of ext_a; r <= c < Ke - r: the zero column r + c
+        const int64_t x = b * 256 + threadIdx.x;
+        const int64_t row = x % a.M, c = x / a.M;
+        if (c >= a.Ke - a.r) return;
+        uint16_t *const dst = a.ext_a + row * a.Ke;
+        if (c >= a.r) {
+            dst[a.r + c] = 0;
+            return;
+        }
+        constexpr int kMaxParts = 16;
+        float pv[kMaxParts];
+#pragma unroll
+        for (int sl = 0; sl < kMaxParts; ++sl)
+            pv[sl] = sl < a.Vs ? a.Vpart[((int64_t)sl * a.r + c) * a.M + row] : 0.0f;
+        float sum = 0.0f;
+#pragma unroll
+        for (int sl = 0; sl < kMaxParts; ++sl)
+            if (sl < a.Vs) sum += pv[sl];
+        a.Vout[row * a.r + c] = sum;
+        const float f = a.s * sum;
+        const uint32_t hb = pack_bf16x2(f, 0.0f) & 0xFFFFu;
+        dst[c] = (uint16_t)hb;
+        dst[a.r + c] = (uint16_t)(pack_bf16x2(f - bf16_bits_to_f32(hb), 0.0f) & 0xFFFFu);
+        return;
+    }
     if (b < a.g_a + a.g_b) {
         const uint32_t cgs = (uint32_t)(a.Ke / 8);  // 8-column groups per row
         const bool is_a = b < a.g_a;
@@ -952,7 +984,8 @@ enum LaunchWhat : int { kFull = 0, kCoreOnly = 1, kExpandCore = 2 };
 // out_f32 (dX only): store the fp32 sums there instead of bf16 into out
 hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, const float *V,
                   const uint16_t *ext_w, int r, float s, uint16_t *out, const GemmWs &ws,
-                  const ColsReduceJob *red, hipStream_t st, int what = kFull, float *out_f32 = nullptr) {
+                  const ColsReduceJob *red, hipStream_t st, int what = kFull, float *out_f32 = nullptr,
+                  const float *Vpart = nullptr, int Vs = 0, float *Vout = nullptr) {
     GemmArgs p;
     p.a = a;
     p.M = M;
@@ -1014,6 +1047,9 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
         q.nb = w.d * w.k / 64;
         q.shat = ws.shat;
         q.V = V;
+        q.Vpart = Vpart;
+        q.Vs = Vs;
+        q.Vout = Vout;
         q.M = M;
         q.r = r;
         q.s = s;
@@ -1030,7 +1066,7 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
         q.red[0] = red ? red[0] : ColsReduceJob{nullptr, 0, 1, 0, 0, 0.0f, nullptr};
         q.red[1] = red ? red[1] : ColsReduceJob{nullptr, 0, 1, 0, 0, 0.0f, nullptr};
         q.g_shat = expand ? (q.nb + 255) / 256 : 0;  // only the expanding GEMM reads the scales
-        q.g_a = (M * (p.Ke / 8) + 255) / 256;
+        q.g_a = Vpart ? (M * (p.Ke - r) + 255) / 256 : (M * (p.Ke / 8) + 255) / 256;
         q.g_b = (p.N * (p.Ke / 8) + 255) / 256;
         // the bf16 copy of What (forward: 2048 kWU weights per workgroup) or What^T (dX: 64 x 256 tiles)
         q.g_t = expand ? 0 : dx ? ((w.k + 255) / 256) * ((w.d + 63) / 64) : (w.d * w.k + 2048 * kWU - 1) / (2048 * kWU);
@@ -1098,8 +1134,9 @@ int64_t gemm_wbf_elems(int64_t M, int64_t d, int64_t k) {
 
 hipError_t launch_gemm_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, const float *U,
                            const uint16_t *B, int r, float s, uint16_t *Y, const GemmWs &ws,
-                           hipStream_t st) {
-    return launch(false, w, x, M, U, B, r, s, Y, ws, nullptr, st);
+                           hipStream_t st, const float *Upart, int Us, float *Uout) {
+    if (!U && (!Upart || Us < 1 || Us > 16 || !Uout)) return hipErrorInvalidValue;
+    return launch(false, w, x, M, U, B, r, s, Y, ws, nullptr, st, kFull, nullptr, Upart, Us, Uout);
 }
 
 hipError_t launch_gemm_dx(const Nf4Weights &w, const uint16_t *dy, int64_t M, const float *G,

@@ -47,6 +47,11 @@ hipError_t launch_rows_skinny(const uint16_t *in, const uint16_t *w, int64_t M, 
 bool rows_bt_supported(int64_t M, int R, const void *B);
 hipError_t launch_rows_bt(const uint16_t *dY, const uint16_t *B, int64_t M, int64_t d, int R, float *G, uint16_t *vt_g,
                           const float *U, uint16_t *vt_u, hipStream_t s);
+// The wide-rank row products of launch_rows_skinny (r > 16, M >= 256) without
+// their reduction: S partials [S][R][M] for launch_gemm_fwd to add.
+bool rows_split_partials_used(int64_t M, int R);
+hipError_t launch_rows_split_partials(const uint16_t *in, const uint16_t *w, int64_t M, int64_t K, int R, float *part,
+                                      int *S, hipStream_t s);
 hipError_t launch_bwd_prep(const uint16_t *B, int64_t d, int r, uint16_t *Bt, const float *U, int64_t M,
                            uint16_t *vt, hipStream_t s);
 // Two column reductions in one launch (job 1 skipped when in1 is null):
@@ -115,9 +120,12 @@ int64_t gemm_ext_cols(int r);
 size_t gemm_ksplit_bytes(int64_t M, int64_t d, int64_t k);
 int64_t gemm_wbf_elems(int64_t M, int64_t d, int64_t k);
 // Y[M x d] = bf16( X[M x k] What^T + [hi(sU) | lo(sU)] [B | B]^T ),  U [M x r] fp32.
+// Upart (U null): U's S partial sums [S][r][M] of rows_split, added in slice
+// order by the preparation launch (the additions of rows_reduce), which also
+// stores U into Uout [M x r].
 hipError_t launch_gemm_fwd(const Nf4Weights &w, const uint16_t *x, int64_t M, const float *U,
                            const uint16_t *B, int r, float s, uint16_t *Y, const GemmWs &ws,
-                           hipStream_t st);
+                           hipStream_t st, const float *Upart = nullptr, int Us = 0, float *Uout = nullptr);
 // dX[M x k] = bf16( dY[M x d] What + [hi(sG) | lo(sG)] [A ; A] ),  G [M x r] fp32
 // red: null, or two column reductions (ColsReduceJob) to run in the same
 // preparation launch; launch_cols_reduce runs them alone.  dX_f32: null, or

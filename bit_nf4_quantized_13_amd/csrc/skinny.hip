@@ -538,6 +538,27 @@ size_t rows_split_part_bytes(int64_t M, int64_t K, int R) {
     return sizeof(float) * (size_t)rows_split_plan(M, K, R).S * (size_t)R * (size_t)M;
 }
 
+bool rows_split_partials_used(int64_t M, int R) { return rows_split_used(M, R); }
+
+hipError_t launch_rows_split_partials(const uint16_t *in, const uint16_t *w, int64_t M, int64_t K, int R, float *part,
+                                      int *S, hipStream_t s) {
+    if (!rows_split_used(M, R) || !part) return hipErrorInvalidValue;
+    const RowsSplit pl = rows_split_plan(M, K, R);
+    const dim3 sgrid((unsigned)pl.groups, (unsigned)pl.S);
+    switch ((R + 15) / 16) {
+#define QNF4_SPLIT(NTV, MTV)                                                                                       \
+    case NTV:                                                                                                      \
+        hipLaunchKernelGGL((rows_split_kernel<NTV, MTV>), sgrid, dim3(256), 0, s, in, w, M, K, R, pl.kslice, part); \
+        break;
+        QNF4_SPLIT(2, 4) QNF4_SPLIT(3, 4) QNF4_SPLIT(4, 4)
+        QNF4_SPLIT(5, 2) QNF4_SPLIT(6, 2) QNF4_SPLIT(7, 2) QNF4_SPLIT(8, 2)
+#undef QNF4_SPLIT
+        default: return hipErrorInvalidValue;
+    }
+    *S = pl.S;
+    return hipGetLastError();
+}
+
 hipError_t launch_rows_skinny(const uint16_t *in, const uint16_t *w, int64_t M, int64_t K, int R,
                               float *out, uint16_t *vt, float *part, hipStream_t s) {
     const int64_t Rp = cols_rank_pad(R);
