@@ -653,15 +653,17 @@ __global__ __launch_bounds__(NTHREADS) void nf4_gemm_kernel(GemmArgs p, Nf4Const
 // Transposed dequantized weight operand for the non-expanding dX GEMM: What^T
 // [k x ldw] with zero columns d .. ldw-1, bf16, bit-identical to
 // qlora_nf4_dequantize (the block scale is doubleDequant's, computed here from
-// c2, c1 and the mean).  One workgroup per 64 W0 rows x 256 columns; thread t
-// expands an 8 x 8 block: rows 8 (t % 8) .., columns 8 (t / 8) .. (inside one
-// NF4 block, so one scale per row).  Code reads are 32 contiguous bytes per
-// row for 8 lanes; the 8 x 8 block is transposed in registers (v_perm) and
-// stored as 16-byte column pieces, so no LDS is involved and every store is a
-// contiguous 128-byte row segment per 8 lanes.  (The forward's What, laid out
-// like the codes, is written by its own job in prep_kernel.)  Narrower
-// blocks (8 x 4) and two tiles per workgroup with the next one's loads
-// overlapping were both slower.
+// c2, c1 and the mean).  One workgroup per 64 W0 rows x 1024 columns; thread t
+// expands an 8 x 32 block: rows 8 (t % 8) .., columns 32 (t / 8) .. (half of
+// one NF4 block, so one scale per row).  Each code load is a 16-byte piece, so
+// the 8 lanes of a row read 128 contiguous bytes; the block is transposed in
+// registers (v_perm) and stored as 16-byte column pieces, so no LDS is
+// involved and every store is a contiguous 128-byte row segment per 8 lanes.
+// (The forward's What, laid out like the codes, is written by its own job in
+// prep_kernel.)  Against 8 x 8 blocks (4-byte code pieces, 32-byte row
+// segments per load, a scale lookup per 8 weights): 13.1 against 15.5 us for
+// the dX preparation at 4096 x 4096, same bits; narrower blocks (8 x 4) and
+// two tiles per workgroup with the next one's loads overlapping were slower.
 // The dequantized weight copy is stored with device scope (sc1: written
 // through the XCD's L2 into the memory-side cache the GEMM reads it from), so
 // the end of the preparation launch has no dirty L2 lines of it to write back:
@@ -672,42 +674,43 @@ __device__ __forceinline__ void dequant_tile_t(int64_t bid, const uint8_t *__res
                                                float mean, int64_t d, int64_t k, int64_t ldw, const Nf4Consts &tab,
                                                uint16_t *__restrict__ out) {
     const int tid = threadIdx.x, lane = tid & 63;
-    const int64_t ct = (k + 255) / 256;
+    const int64_t ct = (k + 1023) / 1024;
     const int64_t tk = bid % ct, td = bid / ct;
     const int ng = tid & 7, kg = tid >> 3;
-    const int64_t n0 = td * 64 + 8 * ng;   // first of this thread's 8 W0 rows
-    const int64_t k0 = tk * 256 + 8 * kg;  // first of its 8 columns
-    if (k0 >= k) return;                   // k % 64 == 0: whole 8-column groups
+    const int64_t n0 = td * 64 + 8 * ng;    // first of this thread's 8 W0 rows
+    const int64_t k0 = tk * 1024 + 32 * kg;  // first of its 32 columns
+    if (k0 >= k) return;                     // k % 64 == 0: whole 32-column groups
     const __amdgpu_buffer_rsrc_t rout = make_rsrc(out, k * ldw * 2);
     float lvf = tab.level[0];
 #pragma unroll
     for (int j = 1; j < 16; ++j) lvf = (lane & 15) == j ? tab.level[j] : lvf;
     const int lv = __float_as_int(lvf);
     const int64_t kb = k / 64;
-    uint32_t cw[8];
+    uint4 cw[8];
     float sc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int64_t n = n0 + e;
-        const int64_t jb = n * kb + k0 / 64;
-        cw[e] = n < d ? *reinterpret_cast<const uint32_t *>(codes + n * (k / 2) + k0 / 2) : 0u;
-        sc[e] = n < d ? block_scale(fmt, c2, c1, mean, jb, bshift) : 0.0f;
+        cw[e] = n < d ? *reinterpret_cast<const uint4 *>(codes + n * (k / 2) + k0 / 2) : uint4{0, 0, 0, 0};
+        sc[e] = n < d ? block_scale(fmt, c2, c1, mean, n * kb + k0 / 64, bshift) : 0.0f;
     }
     // v[e][q]: row e, columns 2 q, 2 q + 1 (bf16 pair)
-    uint32_t v[8][4];
+    uint32_t v[8][16];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t wv[4] = {cw[e].x, cw[e].y, cw[e].z, cw[e].w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t x = pack_bf16x2(level(code_addr(cw[e], 2 * q), lv) * sc[e],
-                                           level(code_addr(cw[e], 2 * q + 1), lv) * sc[e]);
+        for (int q = 0; q < 16; ++q) {
+            const uint32_t x = pack_bf16x2(level(code_addr(wv[q >> 2], 2 * (q & 3)), lv) * sc[e],
+                                           level(code_addr(wv[q >> 2], 2 * (q & 3) + 1), lv) * sc[e]);
             v[e][q] = n0 + e < d ? x : 0u;  // rows past d: zero columns of What^T
         }
+    }
     // column c of the block: rows 0..7 packed as 4 bf16 pairs
     // (rows 2 e2, 2 e2 + 1) = low halves (c even) or high halves (c odd)
     // of v[2 e2][c / 2] and v[2 e2 + 1][c / 2]
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < 32; ++c) {
         uint32_t o[4];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2)
@@ -1068,8 +1071,8 @@ hipError_t launch(bool dx, const Nf4Weights &w, const uint16_t *a, int64_t M, co
         q.g_shat = expand ? (q.nb + 255) / 256 : 0;  // only the expanding GEMM reads the scales
         q.g_a = Vpart ? (M * (p.Ke - r) + 255) / 256 : (M * (p.Ke / 8) + 255) / 256;
         q.g_b = (p.N * (p.Ke / 8) + 255) / 256;
-        // the bf16 copy of What (forward: 2048 kWU weights per workgroup) or What^T (dX: 64 x 256 tiles)
-        q.g_t = expand ? 0 : dx ? ((w.k + 255) / 256) * ((w.d + 63) / 64) : (w.d * w.k + 2048 * kWU - 1) / (2048 * kWU);
+        // the bf16 copy of What (forward: 2048 kWU weights per workgroup) or What^T (dX: 64 x 1024 tiles)
+        q.g_t = expand ? 0 : dx ? ((w.k + 1023) / 1024) * ((w.d + 63) / 64) : (w.d * w.k + 2048 * kWU - 1) / (2048 * kWU);
         q.g_r0 = (q.red[0].N * q.red[0].R + 255) / 256;
         const int64_t g_r1 = (q.red[1].N * q.red[1].R + 255) / 256;
         const dim3 pgrid((unsigned)(q.g_shat + q.g_a + q.g_b + q.g_t + q.g_r0 + g_r1));
