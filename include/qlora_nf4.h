@@ -229,7 +229,9 @@ int qlora_linear_fwd_noalloc(const qlora_nf4_weight *w, const qlora_bf16 *x, int
  *   dA  device fp32 [r x k], written;  dB device fp32 [d x r], written
  *   ws  device workspace of >= qlora_linear_workspace(M, d, k, r) bytes.
  * Reductions over M run in a fixed order: results are bit-identical on
- * every run.
+ * every run.  With r <= 16 and B 16-byte aligned, G is formed from B as
+ * stored in one launch (otherwise B is first copied transposed into the
+ * workspace); both give the same bits.
  */
 int qlora_linear_bwd(const qlora_nf4_weight *w, const qlora_bf16 *x, const qlora_bf16 *dY,
                      const qlora_bf16 *A, const qlora_bf16 *B, const float *U,
